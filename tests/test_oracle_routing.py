@@ -1,0 +1,127 @@
+"""Pins for oracle.routing.
+
+* top-D with lower-index ties == brute-force enumeration of every D-subset
+  (maximum score sum, ties broken lexicographically on block ids)
+* Eq 7 on constructed score vectors: clip to k_min, clip to k_max, the exact
+  count in between, and a score exactly on tau
+* summaries: batch mean == the incremental Eq 11 form; pool-then-dot equals
+  mean of per-query scores; a partial block divides by its own count
+* causal candidate sets, first rows, decode's current block
+* planted relevance is found (statistical sanity only)
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+from oracle import routing, problem
+from dynamic_block_sparse_amd import workloads as wk
+
+
+def _brute_topd(g, cands, d):
+    best = None
+    for sub in itertools.combinations(sorted(cands), d):
+        key = (sum(g[j] for j in sub), tuple(-j for j in sub))
+        # maximise the sum; among equal sums prefer the lexicographically smallest ids
+        if best is None or key[0] > best[0][0] or (key[0] == best[0][0] and tuple(sub) < best[1]):
+            best = (key, tuple(sub))
+    return set(best[1]) if best else set()
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_equals_brute_force_with_ties(seed):
+    rng = np.random.default_rng(seed)
+    nb = 9
+    # integer-valued scores force many exact ties
+    g = rng.integers(-3, 4, size=nb).astype(np.float64)
+    r = nb - 1
+    forced = routing.forced_blocks(r, nb, "prefill", forced_first=bool(seed % 2))
+    cands = routing.candidate_blocks(r, nb, "prefill", forced)
+    for k_b in range(len(forced), len(forced) + len(cands) + 2):
+        row = routing.select_row(g, cands, forced, "topk", k_b, 4, 2.0)
+        picks = set(j for j in row if j >= 0) - set(forced)
+        d = min(max(k_b - len(forced), 0), len(cands))
+        assert picks == _brute_topd(g, cands, d)
+        assert row[:len(forced)] == forced
+        assert row.count(-1) == k_b - len(forced) - d
+
+
+def test_eq7_threshold_counts():
+    cands = list(range(100))
+    forced = [100]
+    # clip low: only one candidate within tau of the max -> count 2 -> k_min 4
+    g = np.full(101, -10.0)
+    g[5] = 1.0
+    assert routing.budget(g, cands, forced, "threshold", 64, 4, 2.0) == 4
+    # clip high: every candidate at the same score -> count 101 -> k_max 64
+    g = np.zeros(101)
+    assert routing.budget(g, cands, forced, "threshold", 64, 4, 2.0) == 64
+    # exact count in between, including a score exactly on tau (inclusive)
+    g = np.full(101, -10.0)
+    g[[3, 7, 11, 20, 50]] = [5.0, 4.0, 3.5, 3.0, 2.0]   # tau = 5 - 2 = 3.0
+    assert routing.budget(g, cands, forced, "threshold", 64, 4, 2.0) == 1 + 4
+    row = routing.select_row(g, cands, forced, "threshold", 64, 4, 2.0)
+    assert set(row) - {-1} == {100, 3, 7, 11, 20}
+
+
+def test_summaries_batch_equals_incremental_and_partial_block():
+    rng = np.random.default_rng(3)
+    b, d, n = 8, 5, 21
+    k = rng.standard_normal((n, d))
+    c = routing.block_summaries(k, n, b)
+    assert c.shape == (3, d)
+    for j in range(3):
+        lo, hi = j * b, min((j + 1) * b, n)
+        inc = routing.incremental_summary(k[lo:hi])
+        assert np.max(np.abs(inc[-1] - c[j])) < 1e-14
+    # partial block: 5 valid keys, divided by 5 not by b
+    assert np.allclose(c[2] * 5, k[16:21].sum(axis=0), atol=1e-13)
+    # padding past the length never enters a summary
+    k2 = k.copy()
+    k2[21:] = 1e6
+    assert np.array_equal(routing.block_summaries(np.vstack([k, np.full((3, d), 1e6)]), n, b), c)
+
+
+def test_pool_then_dot_identity():
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((64, 16))
+    c = rng.standard_normal((10, 16))
+    g = routing.pooled_scores([q], c, "mean")
+    assert np.max(np.abs(g - q.mean(axis=0) @ c.T)) < 1e-12
+    # max pooling is over per-query scores, not an elementwise max of q
+    gm = routing.pooled_scores([q], c, "max")
+    assert np.max(np.abs(gm - (q @ c.T).max(axis=0))) < 1e-14
+    assert np.max(np.abs(gm - q.max(axis=0) @ c.T)) > 1e-3
+    # shared GQA routing averages the per-head pooled scores
+    q2 = rng.standard_normal((64, 16))
+    gs = routing.pooled_scores([q, q2], c, "mean")
+    assert np.max(np.abs(gs - np.concatenate([q, q2]).mean(axis=0) @ c.T)) < 1e-12
+
+
+def test_candidates_and_forced():
+    assert routing.forced_blocks(0, 8, "prefill", False) == [0]
+    assert routing.forced_blocks(0, 8, "prefill", True) == [0]
+    assert routing.forced_blocks(5, 8, "prefill", True) == [0, 5]
+    assert routing.candidate_blocks(5, 8, "prefill", [0, 5]) == [1, 2, 3, 4]
+    assert routing.forced_blocks(0, 2048, "decode", False) == [2047]
+    assert routing.candidate_blocks(0, 2048, "decode", [2047]) == list(range(2047))
+    g = np.zeros(8)
+    assert routing.select_row(g, [], [0], "topk", 3, 4, 2.0) == [0, -1, -1]
+
+
+def test_planted_blocks_are_routed():
+    w = wk.PREFILL_MHA.replace(heads_q=2, heads_kv=2, seqlen=2048, head_dim=64)
+    inp = wk.make_inputs(w, "cpu")
+    qs, ks, _ = wk.per_sequence(inp)
+    J, _ = problem.route(qs, ks, inp.lengths, w.block, "prefill", w.qpool, w.share_gqa,
+                         w.select, w.k_b, w.k_min, w.tau_rel, w.forced_first)
+    J = np.asarray(J).reshape(w.heads_q, -1, w.k_b)
+    hits, total = 0, 0
+    for h in range(w.heads_q):
+        planted = inp.planted[(0, h)]
+        for r in range(J.shape[1]):
+            for j in planted:
+                if j < r:
+                    total += 1
+                    hits += int(j in J[h, r])
+    assert total > 0 and hits / total > 0.9
