@@ -1,0 +1,291 @@
+"""dynamic_block_sparse_amd -- dynamic block-sparse attention on AMD MI355X (gfx950).
+
+A thin ctypes binding over libsparse_attn.so (C ABI in include/sparse_attn.h).
+The binding only marshals arguments: it turns torch tensors into device
+pointers, sizes workspaces and raises on a nonzero status.  Every step of the
+path (summaries, routing, worklist, attention) runs in the library's HIP
+kernels; there is no Python or CPU fallback.  PyTorch provides device memory
+and the current stream.
+
+    import dynamic_block_sparse_amd as dbs
+    prob = dbs.Problem.fixed(batch=1, heads_q=16, heads_kv=16, head_dim=128, seqlen=8192,
+                             dtype="bf16")
+    cfg = dbs.RouteConfig(k_b=16)
+    J, summ = dbs.route(prob, cfg, q, k)
+    wl = dbs.build_worklist(prob, cfg, J)
+    o, lse = dbs.fwd(prob, cfg, wl, q, k, v)
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsparse_attn.so")
+
+SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = 0, 1, 2, 3, 4
+SA_WL_ERR_RANGE, SA_WL_ERR_ACAUSAL = 1, 2
+SA_F32, SA_BF16 = 0, 1
+SA_PREFILL, SA_DECODE = 0, 1
+SA_POOL_MEAN, SA_POOL_MAX = 0, 1
+SA_SELECT_TOPK, SA_SELECT_THRESHOLD = 0, 1
+SA_FORCE_CURRENT, SA_FORCE_FIRST = 1, 2
+
+EXPORTED = ["sparse_attn_sizes", "sparse_attn_workspace_size", "sparse_attn_route",
+            "sparse_attn_build_worklist", "sparse_attn_fwd", "sparse_attn_status_string"]
+
+
+class SAError(RuntimeError):
+    def __init__(self, call: str, status: int, text: str):
+        super().__init__(f"{call} failed: status {status} ({text})")
+        self.status = status
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads_q", ctypes.c_int32),
+                ("heads_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("block", ctypes.c_int32), ("seqlen", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("mode", ctypes.c_int32),
+                ("cu_seqlens", ctypes.c_void_p), ("total_tokens", ctypes.c_int32),
+                ("total_blocks", ctypes.c_int32), ("max_blocks", ctypes.c_int32)]
+
+
+class _RouteCfg(ctypes.Structure):
+    _fields_ = [("qpool", ctypes.c_int32), ("share_gqa", ctypes.c_int32),
+                ("select", ctypes.c_int32), ("k_b", ctypes.c_int32),
+                ("k_min", ctypes.c_int32), ("tau_rel", ctypes.c_float),
+                ("forced", ctypes.c_uint32)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libsparse_attn.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m dynamic_block_sparse_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, R = ctypes.POINTER(_Problem), ctypes.POINTER(_RouteCfg)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.sparse_attn_sizes.argtypes = [P, R, ctypes.POINTER(i64), ctypes.POINTER(i32),
+                                      ctypes.POINTER(i64), ctypes.POINTER(i32), ctypes.POINTER(i64)]
+    lib.sparse_attn_sizes.restype = ctypes.c_int
+    lib.sparse_attn_workspace_size.argtypes = [P, R, i32, i32]
+    lib.sparse_attn_workspace_size.restype = sz
+    lib.sparse_attn_route.argtypes = [P, R, vp, vp, vp, i32, vp, vp, sz, vp]
+    lib.sparse_attn_route.restype = ctypes.c_int
+    lib.sparse_attn_build_worklist.argtypes = [P, R, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]
+    lib.sparse_attn_build_worklist.restype = ctypes.c_int
+    lib.sparse_attn_fwd.argtypes = [P, R, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+    lib.sparse_attn_fwd.restype = ctypes.c_int
+    lib.sparse_attn_status_string.argtypes = [ctypes.c_int]
+    lib.sparse_attn_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(call: str, status: int):
+    if status != SA_OK:
+        text = load_library().sparse_attn_status_string(status).decode()
+        raise SAError(call, status, text)
+
+
+@dataclasses.dataclass
+class Problem:
+    """Geometry of one call (mirrors sa_problem)."""
+
+    batch: int
+    heads_q: int
+    heads_kv: int
+    head_dim: int
+    seqlen: int                  # fixed n / decode L; 0 for packed varlen
+    dtype: str = "bf16"          # "bf16" | "f32"
+    mode: str = "prefill"        # "prefill" | "decode"
+    block: int = 64
+    cu_seqlens: Optional[torch.Tensor] = None   # int32 [batch+1] on the device
+    lengths: Optional[list] = None              # host copy of the varlen lengths
+
+    @staticmethod
+    def fixed(batch, heads_q, heads_kv, head_dim, seqlen, dtype="bf16"):
+        return Problem(batch, heads_q, heads_kv, head_dim, seqlen, dtype, "prefill")
+
+    @staticmethod
+    def decode(batch, heads_q, heads_kv, head_dim, cache_len, dtype="bf16"):
+        return Problem(batch, heads_q, heads_kv, head_dim, cache_len, dtype, "decode")
+
+    @staticmethod
+    def varlen(lengths, heads_q, heads_kv, head_dim, cu_seqlens, dtype="bf16"):
+        return Problem(len(lengths), heads_q, heads_kv, head_dim, 0, dtype, "prefill",
+                       cu_seqlens=cu_seqlens, lengths=list(lengths))
+
+    def to_c(self) -> _Problem:
+        p = _Problem()
+        p.batch, p.heads_q, p.heads_kv, p.head_dim = self.batch, self.heads_q, self.heads_kv, self.head_dim
+        p.block, p.seqlen = self.block, self.seqlen
+        p.dtype = SA_BF16 if self.dtype == "bf16" else SA_F32
+        p.mode = SA_DECODE if self.mode == "decode" else SA_PREFILL
+        if self.cu_seqlens is not None:
+            p.cu_seqlens = self.cu_seqlens.data_ptr()
+            nb = [-(-int(x) // self.block) for x in self.lengths]
+            p.total_tokens = int(sum(self.lengths))
+            p.total_blocks = int(sum(nb))
+            p.max_blocks = int(max(nb))
+        return p
+
+
+@dataclasses.dataclass
+class RouteConfig:
+    """Routing settings (mirrors sa_route_cfg)."""
+
+    k_b: int = 16
+    qpool: str = "mean"          # "mean" | "max"
+    share_gqa: bool = False
+    select: str = "topk"         # "topk" | "threshold"
+    k_min: int = 4
+    tau_rel: float = 2.0
+    force_first: bool = False
+
+    def to_c(self) -> _RouteCfg:
+        c = _RouteCfg()
+        c.qpool = SA_POOL_MAX if self.qpool == "max" else SA_POOL_MEAN
+        c.share_gqa = int(bool(self.share_gqa))
+        c.select = SA_SELECT_THRESHOLD if self.select == "threshold" else SA_SELECT_TOPK
+        c.k_b, c.k_min, c.tau_rel = self.k_b, self.k_min, self.tau_rel
+        c.forced = SA_FORCE_CURRENT | (SA_FORCE_FIRST if self.force_first else 0)
+        return c
+
+
+@dataclasses.dataclass
+class Sizes:
+    rows: int
+    width_max: int
+    nnz_cap: int
+    n_buckets: int
+    kv_blocks: int
+
+
+@dataclasses.dataclass
+class Worklist:
+    row_ptr: torch.Tensor
+    col_idx: torch.Tensor
+    row_perm: torch.Tensor
+    bucket_ptr: torch.Tensor
+    err: torch.Tensor
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def sizes(prob: Problem, cfg: RouteConfig) -> Sizes:
+    lib = load_library()
+    r, nnz, kv = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    w, nb = ctypes.c_int32(), ctypes.c_int32()
+    p, c = prob.to_c(), cfg.to_c()
+    _check("sparse_attn_sizes", lib.sparse_attn_sizes(ctypes.byref(p), ctypes.byref(c), ctypes.byref(r),
+                                                      ctypes.byref(w), ctypes.byref(nnz), ctypes.byref(nb),
+                                                      ctypes.byref(kv)))
+    return Sizes(r.value, w.value, nnz.value, nb.value, kv.value)
+
+
+def workspace_size(prob: Problem, cfg: RouteConfig, which: int, num_splits: int = 0) -> int:
+    p, c = prob.to_c(), cfg.to_c()
+    return int(load_library().sparse_attn_workspace_size(ctypes.byref(p), ctypes.byref(c), which, num_splits))
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def summaries_shape(prob: Problem):
+    if prob.cu_seqlens is not None:
+        nb = sum(-(-int(x) // prob.block) for x in prob.lengths)
+        return (prob.heads_kv, nb, prob.head_dim)
+    nb = -(-prob.seqlen // prob.block)
+    return (prob.batch, prob.heads_kv, nb, prob.head_dim)
+
+
+def route(prob: Problem, cfg: RouteConfig, q: torch.Tensor, k: Optional[torch.Tensor],
+          summaries: Optional[torch.Tensor] = None, summaries_in: bool = False,
+          J: Optional[torch.Tensor] = None):
+    """sparse_attn_route: returns (J int32 [rows, k_b], fp32 summaries)."""
+    lib = load_library()
+    sz = sizes(prob, cfg)
+    dev = q.device
+    if summaries is None:
+        summaries = torch.empty(summaries_shape(prob), dtype=torch.float32, device=dev)
+    if J is None:
+        J = torch.empty((sz.rows, cfg.k_b), dtype=torch.int32, device=dev)
+    p, c = prob.to_c(), cfg.to_c()
+    wsb = workspace_size(prob, cfg, 0)
+    ws = _workspace(wsb, dev)
+    _check("sparse_attn_route", lib.sparse_attn_route(
+        ctypes.byref(p), ctypes.byref(c), _ptr(q), _ptr(k), _ptr(summaries), int(summaries_in),
+        _ptr(J), _ptr(ws), wsb, _stream(dev)))
+    return J, summaries
+
+
+def build_worklist(prob: Problem, cfg: RouteConfig, J: torch.Tensor, out: Optional[Worklist] = None) -> Worklist:
+    """sparse_attn_build_worklist: returns the CSR worklist (device tensors)."""
+    lib = load_library()
+    sz = sizes(prob, cfg)
+    dev = J.device
+    if out is None:
+        out = Worklist(row_ptr=torch.empty(sz.rows + 1, dtype=torch.int32, device=dev),
+                       col_idx=torch.empty(max(sz.nnz_cap, 1), dtype=torch.int32, device=dev),
+                       row_perm=torch.empty(max(sz.rows, 1), dtype=torch.int32, device=dev),
+                       bucket_ptr=torch.empty(sz.n_buckets + 1, dtype=torch.int32, device=dev),
+                       err=torch.zeros(1, dtype=torch.int32, device=dev))
+    else:
+        out.err.zero_()
+    p, c = prob.to_c(), cfg.to_c()
+    wsb = workspace_size(prob, cfg, 1)
+    ws = _workspace(wsb, dev)
+    _check("sparse_attn_build_worklist", lib.sparse_attn_build_worklist(
+        ctypes.byref(p), ctypes.byref(c), _ptr(J), _ptr(out.row_ptr), _ptr(out.col_idx),
+        out.col_idx.numel(), _ptr(out.row_perm), _ptr(out.bucket_ptr), _ptr(out.err),
+        _ptr(ws), wsb, _stream(dev)))
+    return out
+
+
+def fwd(prob: Problem, cfg: RouteConfig, wl: Worklist, q, k, v, o=None, lse=None,
+        want_lse: bool = True, num_splits: int = 0, workspace: Optional[torch.Tensor] = None):
+    """sparse_attn_fwd: returns (O, LSE or None)."""
+    lib = load_library()
+    dev = q.device
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
+    p, c = prob.to_c(), cfg.to_c()
+    wsb = workspace_size(prob, cfg, 2, num_splits)
+    ws = workspace if workspace is not None and workspace.numel() >= wsb else _workspace(wsb, dev)
+    _check("sparse_attn_fwd", lib.sparse_attn_fwd(
+        ctypes.byref(p), ctypes.byref(c), _ptr(wl.row_ptr), _ptr(wl.col_idx), _ptr(wl.row_perm),
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), num_splits, _ptr(ws), wsb, _stream(dev)))
+    return o, lse
+
+
+def problem_for(w, inp) -> Problem:
+    """Problem geometry for a workload's inputs (see workloads.py)."""
+    if w.mode == "decode":
+        return Problem.decode(w.batch, w.heads_q, w.heads_kv, w.head_dim, w.seqlen, w.dtype)
+    if w.varlen:
+        return Problem.varlen(inp.lengths, w.heads_q, w.heads_kv, w.head_dim, inp.cu_seqlens, w.dtype)
+    return Problem.fixed(w.batch, w.heads_q, w.heads_kv, w.head_dim, w.seqlen, w.dtype)
+
+
+def config_for(w) -> RouteConfig:
+    return RouteConfig(k_b=w.k_b, qpool=w.qpool, share_gqa=w.share_gqa, select=w.select,
+                       k_min=w.k_min, tau_rel=w.tau_rel, force_first=w.forced_first)

@@ -1,0 +1,63 @@
+"""Build libsparse_attn.so (gfx950) in-tree with hipcc.
+
+    python -m dynamic_block_sparse_amd.build
+
+The library is a plain C-ABI shared object (include/sparse_attn.h); no torch
+headers are involved.  Every HIP source is compiled for gfx950 only, with
+packed-fp32 instruction selection turned off (-packed-fp32-ops).
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libsparse_attn.so")
+SOURCES = ["sparse_attn_abi.hip", "route.hip", "worklist.hip", "attn_fwd.hip", "attn_decode.hip"]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+
+def compile_flags():
+    return ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-munsafe-fp-atomics", "-I", INCLUDE, "-I", CSRC]
+
+
+def build(verbose: bool = False, jobs: int = 0) -> str:
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = []
+    procs = []
+    for src in SOURCES:
+        obj = os.path.join(objdir, src.replace(".hip", ".o"))
+        cmd = [HIPCC, *compile_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+        objs.append(obj)
+    failed = []
+    for src, p in procs:
+        out = p.communicate()[0].decode(errors="replace")
+        # the host pass does not know the packed-fp32 feature flag; that warning is expected
+        lines = [ln for ln in out.splitlines() if "packed-fp32-ops" not in ln]
+        if p.returncode != 0 or (verbose and lines):
+            print("\n".join(lines), file=sys.stderr)
+        if p.returncode != 0:
+            failed.append(src)
+    if failed:
+        raise RuntimeError("hipcc failed for: " + ", ".join(failed))
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

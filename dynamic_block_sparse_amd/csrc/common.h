@@ -1,0 +1,182 @@
+// Shared device-side definitions for the block-sparse attention kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sparse_attn.h"
+
+namespace sa {
+
+constexpr int kBlock = 64;      // b: tokens per block (query and key)
+constexpr int kWave = 64;       // CDNA wavefront width
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Geometry resolved on the host and passed by value to every kernel.
+// Token (s, h, t) of Q lives at q + s*q_seq + h*q_head + (tok0(s) + t)*d;
+// K/V likewise with the kv strides.  Summary (s, h, j) lives at
+// summaries + (s*sum_seq + h*sum_head + blk0(s) + j)*d.
+struct Geom {
+  int batch, hq, hkv, group;   // group = hq / hkv
+  int hr;                      // routing heads (hkv when shared, else hq)
+  int hpr;                     // query heads served by one row (group when shared, else 1)
+  int share;                   // 1 when the routing head is the KV head
+  int d;                       // head_dim
+  int mode;                    // SA_PREFILL / SA_DECODE
+  int n;                       // fixed length n / decode cached L; 0 when varlen
+  int varlen;
+  const int32_t* cu_seqlens;   // device [batch+1] (varlen)
+  const int32_t* cu_blocks;    // device [batch+1] block offsets (varlen; in workspace)
+  int total_blocks;            // summary slots per kv head plane (varlen) / per (s, h) N (fixed)
+  int max_blocks;              // largest per-sequence block count
+  int64_t rows;                // worklist rows
+  int64_t q_seq, q_head;       // element strides of Q/O (varlen: q_seq = 0)
+  int64_t kv_seq, kv_head;     // element strides of K/V
+  int64_t sum_seq, sum_head;   // summary strides in blocks (varlen: sum_seq = 0)
+  int64_t lse_seq, lse_head;   // strides of the lse array in tokens
+};
+
+struct RowInfo {
+  int s, h, r;        // sequence, routing head, query block (decode: last block)
+  int len;            // valid tokens (decode: cached length)
+  int nblk;           // key blocks of the sequence
+  int tok0;           // first token of the sequence in the packed layout (0 if fixed)
+  int blk0;           // first block slot of the sequence (varlen), 0 if fixed
+};
+
+__device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+__device__ __forceinline__ int seq_len(const Geom& g, int s) {
+  return g.varlen ? (g.cu_seqlens[s + 1] - g.cu_seqlens[s]) : g.n;
+}
+
+// Map a worklist row id to (sequence, routing head, query block).
+__device__ __forceinline__ RowInfo decode_row(const Geom& g, int64_t row) {
+  RowInfo ri;
+  if (g.mode == SA_DECODE) {
+    ri.s = (int)(row / g.hr);
+    ri.h = (int)(row % g.hr);
+    ri.len = g.n;
+    ri.nblk = ceil_div(g.n, kBlock);
+    ri.r = ri.nblk - 1;
+    ri.tok0 = 0;
+    ri.blk0 = 0;
+    return ri;
+  }
+  if (!g.varlen) {
+    int nb = ceil_div(g.n, kBlock);
+    int64_t per_seq = (int64_t)g.hr * nb;
+    ri.s = (int)(row / per_seq);
+    int64_t rem = row - (int64_t)ri.s * per_seq;
+    ri.h = (int)(rem / nb);
+    ri.r = (int)(rem % nb);
+    ri.len = g.n;
+    ri.nblk = nb;
+    ri.tok0 = 0;
+    ri.blk0 = 0;
+    return ri;
+  }
+  // varlen: row = hr * cu_blocks[s] + h * N_s + r; find s by binary search
+  int lo = 0, hi = g.batch - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if ((int64_t)g.hr * g.cu_blocks[mid] <= row) lo = mid; else hi = mid - 1;
+  }
+  ri.s = lo;
+  int b0 = g.cu_blocks[lo];
+  int nb = g.cu_blocks[lo + 1] - b0;
+  int64_t rem = row - (int64_t)g.hr * b0;
+  ri.h = (int)(rem / nb);
+  ri.r = (int)(rem % nb);
+  ri.tok0 = g.cu_seqlens[lo];
+  ri.len = g.cu_seqlens[lo + 1] - ri.tok0;
+  ri.nblk = nb;
+  ri.blk0 = b0;
+  return ri;
+}
+
+__device__ __forceinline__ int64_t q_offset(const Geom& g, int s, int h, int tok0, int t) {
+  return (int64_t)s * g.q_seq + (int64_t)h * g.q_head + (int64_t)(tok0 + t) * g.d;
+}
+__device__ __forceinline__ int64_t kv_offset(const Geom& g, int s, int h, int tok0, int t) {
+  return (int64_t)s * g.kv_seq + (int64_t)h * g.kv_head + (int64_t)(tok0 + t) * g.d;
+}
+__device__ __forceinline__ int64_t sum_offset(const Geom& g, int s, int h, int blk0, int j) {
+  return ((int64_t)s * g.sum_seq + (int64_t)h * g.sum_head + blk0 + j) * g.d;
+}
+__device__ __forceinline__ int64_t lse_offset(const Geom& g, int s, int h, int tok0, int t) {
+  return (int64_t)s * g.lse_seq + (int64_t)h * g.lse_head + tok0 + t;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+
+template <typename T> __device__ __forceinline__ float to_f32(T x);
+template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ float to_f32<__bf16>(__bf16 x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
+
+// Wave-level reductions (64 lanes) via cross-lane shuffles.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ int wave_incl_scan_i(int v) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int t = __shfl_up(v, o, kWave);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// Exclusive scan across an NT-thread workgroup.  `sh` holds NT/64 ints.  All
+// threads must call it; *total receives the workgroup sum.
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int v, int* sh, int* total) {
+  constexpr int NW = NT / kWave;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int inc = wave_incl_scan_i(v);
+  __syncthreads();
+  if (lane == kWave - 1) sh[wave] = inc;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int x = sh[w];
+    before += (w < wave) ? x : 0;
+    tot += x;
+  }
+  *total = tot;
+  return before + inc - v;
+}
+
+// Lane mask of lanes below the current one (for ballot-based compaction).
+__device__ __forceinline__ uint64_t lanes_below() {
+  unsigned lane = __lane_id();
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+}  // namespace sa

@@ -1,0 +1,36 @@
+// Internal launcher declarations (host side) for libsparse_attn.
+#pragma once
+
+#include "common.h"
+
+namespace sa {
+
+// Block offsets of a packed batch: cu_blocks[s] = sum_{s' < s} ceil(len_s' / b).
+int launch_cu_blocks(const int32_t* cu_seqlens, int32_t* cu_blocks, int batch, hipStream_t st);
+
+int launch_summary(const Geom& g, int dtype, const void* k, float* summ, int slots,
+                   hipStream_t st);
+size_t route_smem_bytes(const Geom& g, int qpool);
+int launch_route(const Geom& g, const sa_route_cfg& rc, int dtype, const void* q,
+                 const float* summ, int32_t* J, hipStream_t st);
+
+struct WorklistBufs {
+  const int32_t* J;
+  int32_t *row_ptr, *col_idx, *row_perm, *bucket_ptr, *err;
+  int32_t *tmp_cols, *tmp_len;   // workspace: [rows * width_pad], [rows]
+};
+int launch_worklist(const Geom& g, const sa_route_cfg& rc, int width_max, int n_buckets,
+                    const WorklistBufs& b, hipStream_t st);
+
+struct FwdBufs {
+  const int32_t *row_ptr, *col_idx, *row_perm;
+  const void *q, *k, *v;
+  void* o;
+  float* lse;
+  float* part;     // decode partials (workspace)
+};
+int launch_prefill(const Geom& g, int dtype, const FwdBufs& b, hipStream_t st);
+int launch_decode(const Geom& g, int dtype, const FwdBufs& b, int splits, hipStream_t st);
+size_t decode_partials_bytes(const Geom& g, int splits);
+
+}  // namespace sa

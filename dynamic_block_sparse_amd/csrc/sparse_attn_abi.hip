@@ -1,0 +1,274 @@
+// C-ABI entry points: host-side validation, geometry, workspace carving, launches.
+// Nothing here allocates, synchronises or keeps state between calls.
+#include <math.h>
+#include <string.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace sa {
+namespace {
+
+constexpr int kMaxWidth = 128;        // k_b + forced blocks per row
+constexpr int kMaxRouteBlocks = 8192; // candidate scores kept in LDS by the router
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int popcount2(uint32_t f) { return (int)(f & 1u) + (int)((f >> 1) & 1u); }
+
+struct Plan {
+  Geom g;
+  int width_max = 0;
+  int n_buckets = 0;
+  int64_t kv_slots = 0;   // summary slots
+  int64_t nnz_cap = 0;
+};
+
+int validate(const sa_problem* p, const sa_route_cfg* rc, Plan* out) {
+  if (!p || !rc || !out) return SA_ERR_INVALID_ARG;
+  if (p->batch < 1 || p->heads_q < 1 || p->heads_kv < 1 || p->heads_q % p->heads_kv != 0)
+    return SA_ERR_INVALID_ARG;
+  if (p->dtype != SA_F32 && p->dtype != SA_BF16) return SA_ERR_INVALID_ARG;
+  if (p->mode != SA_PREFILL && p->mode != SA_DECODE) return SA_ERR_INVALID_ARG;
+  if (p->block != kBlock) return SA_ERR_UNSUPPORTED;
+  if (p->head_dim != 64 && p->head_dim != 128) return SA_ERR_UNSUPPORTED;
+  if (rc->qpool != SA_POOL_MEAN && rc->qpool != SA_POOL_MAX) return SA_ERR_INVALID_ARG;
+  if (rc->share_gqa != 0 && rc->share_gqa != 1) return SA_ERR_INVALID_ARG;
+  if (rc->select != SA_SELECT_TOPK && rc->select != SA_SELECT_THRESHOLD) return SA_ERR_INVALID_ARG;
+  if (!(rc->forced & SA_FORCE_CURRENT) || (rc->forced & ~3u)) return SA_ERR_INVALID_ARG;
+  const int nforced = popcount2(rc->forced);
+  if (rc->k_b < nforced || rc->k_b + nforced > kMaxWidth) return SA_ERR_INVALID_ARG;
+  if (rc->select == SA_SELECT_THRESHOLD &&
+      (rc->k_min < 0 || !isfinite(rc->tau_rel) || rc->tau_rel < 0.f))
+    return SA_ERR_INVALID_ARG;
+
+  Geom& g = out->g;
+  memset(&g, 0, sizeof(g));
+  g.batch = p->batch;
+  g.hq = p->heads_q;
+  g.hkv = p->heads_kv;
+  g.group = p->heads_q / p->heads_kv;
+  g.share = rc->share_gqa;
+  g.hr = g.share ? g.hkv : g.hq;
+  g.hpr = g.share ? g.group : 1;
+  g.d = p->head_dim;
+  g.mode = p->mode;
+  const int64_t d = g.d;
+  if (p->mode == SA_DECODE) {
+    if (p->cu_seqlens || p->seqlen < 1) return SA_ERR_INVALID_ARG;
+    g.n = p->seqlen;
+    const int nb = (g.n + kBlock - 1) / kBlock;
+    g.max_blocks = nb;
+    g.total_blocks = nb;
+    g.rows = (int64_t)g.batch * g.hr;
+    g.q_seq = (int64_t)g.hq * d;
+    g.q_head = d;
+    g.kv_seq = (int64_t)g.hkv * g.n * d;
+    g.kv_head = (int64_t)g.n * d;
+    g.sum_seq = (int64_t)g.hkv * nb;
+    g.sum_head = nb;
+    g.lse_seq = g.hq;
+    g.lse_head = 1;
+    out->kv_slots = (int64_t)g.batch * nb;
+  } else if (p->cu_seqlens) {
+    if (p->seqlen != 0 || p->total_tokens < 1 || p->total_blocks < p->batch ||
+        p->max_blocks < 1 || p->max_blocks > p->total_blocks)
+      return SA_ERR_INVALID_ARG;
+    g.varlen = 1;
+    g.cu_seqlens = p->cu_seqlens;
+    g.n = 0;
+    g.max_blocks = p->max_blocks;
+    g.total_blocks = p->total_blocks;
+    g.rows = (int64_t)g.hr * p->total_blocks;
+    g.q_seq = 0;
+    g.q_head = (int64_t)p->total_tokens * d;
+    g.kv_seq = 0;
+    g.kv_head = (int64_t)p->total_tokens * d;
+    g.sum_seq = 0;
+    g.sum_head = p->total_blocks;
+    g.lse_seq = 0;
+    g.lse_head = p->total_tokens;
+    out->kv_slots = p->total_blocks;
+  } else {
+    if (p->seqlen < 1) return SA_ERR_INVALID_ARG;
+    g.n = p->seqlen;
+    const int nb = (g.n + kBlock - 1) / kBlock;
+    g.max_blocks = nb;
+    g.total_blocks = nb;
+    g.rows = (int64_t)g.batch * g.hr * nb;
+    g.q_seq = (int64_t)g.hq * g.n * d;
+    g.q_head = (int64_t)g.n * d;
+    g.kv_seq = (int64_t)g.hkv * g.n * d;
+    g.kv_head = (int64_t)g.n * d;
+    g.sum_seq = (int64_t)g.hkv * nb;
+    g.sum_head = nb;
+    g.lse_seq = (int64_t)g.hq * g.n;
+    g.lse_head = g.n;
+    out->kv_slots = (int64_t)g.batch * nb;
+  }
+  out->width_max = rc->k_b + nforced;
+  int nbk = 1;
+  while ((4 << (nbk - 1)) < out->width_max) ++nbk;
+  out->n_buckets = nbk;
+  out->nnz_cap = g.rows * out->width_max;
+  if (out->nnz_cap > INT32_MAX || g.rows > INT32_MAX) return SA_ERR_UNSUPPORTED;
+  return SA_OK;
+}
+
+size_t ws_cu_blocks(const Plan& pl) {
+  return pl.g.varlen ? align_up((size_t)(pl.g.batch + 1) * sizeof(int32_t)) : 0;
+}
+
+int auto_splits(const Plan& pl) {
+  const int64_t target = 4096;
+  int64_t s = (target + pl.g.rows - 1) / pl.g.rows;
+  int64_t cap = pl.width_max / 4;
+  if (cap < 1) cap = 1;
+  if (s > cap) s = cap;
+  if (s > 64) s = 64;
+  return s < 1 ? 1 : (int)s;
+}
+
+size_t ws_size(const Plan& pl, int which, int splits) {
+  size_t sz = ws_cu_blocks(pl);
+  if (which == 1) {
+    sz += align_up((size_t)pl.g.rows * kMaxWidth * sizeof(int32_t));
+    sz += align_up((size_t)pl.g.rows * sizeof(int32_t));
+  } else if (which == 2 && pl.g.mode == SA_DECODE) {
+    sz += align_up(decode_partials_bytes(pl.g, splits));
+  }
+  return sz;
+}
+
+int prep_cu_blocks(Plan& pl, void* ws, hipStream_t st) {
+  if (!pl.g.varlen) return SA_OK;
+  int32_t* cb = reinterpret_cast<int32_t*>(ws);
+  pl.g.cu_blocks = cb;
+  return launch_cu_blocks(pl.g.cu_seqlens, cb, pl.g.batch, st);
+}
+
+}  // namespace
+}  // namespace sa
+
+using namespace sa;
+
+extern "C" {
+
+const char* sparse_attn_status_string(int status) {
+  switch (status) {
+    case SA_OK: return "ok";
+    case SA_ERR_INVALID_ARG: return "invalid argument";
+    case SA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SA_ERR_WORKSPACE: return "workspace or capacity too small";
+    case SA_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int sparse_attn_sizes(const sa_problem* p, const sa_route_cfg* rc, int64_t* rows,
+                      int32_t* width_max, int64_t* nnz_cap, int32_t* n_buckets,
+                      int64_t* kv_blocks) {
+  Plan pl;
+  const int st = validate(p, rc, &pl);
+  if (st != SA_OK) return st;
+  if (rows) *rows = pl.g.rows;
+  if (width_max) *width_max = pl.width_max;
+  if (nnz_cap) *nnz_cap = pl.nnz_cap;
+  if (n_buckets) *n_buckets = pl.n_buckets;
+  if (kv_blocks) *kv_blocks = pl.kv_slots;
+  return SA_OK;
+}
+
+size_t sparse_attn_workspace_size(const sa_problem* p, const sa_route_cfg* rc, int32_t which,
+                                  int32_t num_splits) {
+  Plan pl;
+  if (validate(p, rc, &pl) != SA_OK || which < 0 || which > 2) return 0;
+  const int splits = num_splits > 0 ? num_splits : auto_splits(pl);
+  return ws_size(pl, which, splits);
+}
+
+int sparse_attn_route(const sa_problem* p, const sa_route_cfg* rc, const void* q, const void* k,
+                      float* summaries, int32_t summaries_in, int32_t* J, void* ws,
+                      size_t ws_bytes, void* stream) {
+  Plan pl;
+  int st = validate(p, rc, &pl);
+  if (st != SA_OK) return st;
+  if (!q || !summaries || !J || (!summaries_in && !k)) return SA_ERR_INVALID_ARG;
+  if (summaries_in != 0 && summaries_in != 1) return SA_ERR_INVALID_ARG;
+  if (pl.g.max_blocks > kMaxRouteBlocks) return SA_ERR_UNSUPPORTED;
+  if (ws_bytes < ws_size(pl, 0, 1) || (ws_size(pl, 0, 1) && !ws)) return SA_ERR_WORKSPACE;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if ((st = prep_cu_blocks(pl, ws, hs)) != SA_OK) return st;
+  if (!summaries_in) {
+    if ((st = launch_summary(pl.g, p->dtype, k, summaries, (int)pl.kv_slots, hs)) != SA_OK) return st;
+  }
+  return launch_route(pl.g, *rc, p->dtype, q, summaries, J, hs);
+}
+
+int sparse_attn_build_worklist(const sa_problem* p, const sa_route_cfg* rc, const int32_t* J,
+                               int32_t* row_ptr, int32_t* col_idx, int64_t nnz_cap,
+                               int32_t* row_perm, int32_t* bucket_ptr, int32_t* err, void* ws,
+                               size_t ws_bytes, void* stream) {
+  Plan pl;
+  int st = validate(p, rc, &pl);
+  if (st != SA_OK) return st;
+  if (!J || !row_ptr || !col_idx || !row_perm || !bucket_ptr || !err || !ws)
+    return SA_ERR_INVALID_ARG;
+  if (nnz_cap < pl.nnz_cap) return SA_ERR_WORKSPACE;
+  if (ws_bytes < ws_size(pl, 1, 1)) return SA_ERR_WORKSPACE;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if ((st = prep_cu_blocks(pl, ws, hs)) != SA_OK) return st;
+  unsigned char* w = reinterpret_cast<unsigned char*>(ws) + ws_cu_blocks(pl);
+  WorklistBufs b;
+  b.J = J;
+  b.row_ptr = row_ptr;
+  b.col_idx = col_idx;
+  b.row_perm = row_perm;
+  b.bucket_ptr = bucket_ptr;
+  b.err = err;
+  b.tmp_cols = reinterpret_cast<int32_t*>(w);
+  b.tmp_len = reinterpret_cast<int32_t*>(w + align_up((size_t)pl.g.rows * kMaxWidth * sizeof(int32_t)));
+  return launch_worklist(pl.g, *rc, pl.width_max, pl.n_buckets, b, hs);
+}
+
+int sparse_attn_fwd(const sa_problem* p, const sa_route_cfg* rc, const int32_t* row_ptr,
+                    const int32_t* col_idx, const int32_t* row_perm, const void* q,
+                    const void* k, const void* v, void* o, float* lse, int32_t num_splits,
+                    void* ws, size_t ws_bytes, void* stream) {
+  Plan pl;
+  int st = validate(p, rc, &pl);
+  if (st != SA_OK) return st;
+  if (!row_ptr || !col_idx || !row_perm || !q || !k || !v || !o) return SA_ERR_INVALID_ARG;
+  if (num_splits < 0 || num_splits > 256) return SA_ERR_INVALID_ARG;
+  if (p->dtype == SA_BF16 && p->head_dim != 128) return SA_ERR_UNSUPPORTED;
+  // bf16 kernels serve 1, 2 or 4 query heads per row in prefill (2 wavefronts
+  // per head in one workgroup), up to 8 in decode
+  if (p->dtype == SA_BF16) {
+    const int h = pl.g.hpr;
+    const bool ok = h == 1 || h == 2 || h == 4 || (h == 8 && p->mode == SA_DECODE);
+    if (!ok) return SA_ERR_UNSUPPORTED;
+  }
+  const int splits = num_splits > 0 ? num_splits : auto_splits(pl);
+  const size_t need = ws_size(pl, 2, splits);
+  if (ws_bytes < need || (need && !ws)) return SA_ERR_WORKSPACE;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if ((st = prep_cu_blocks(pl, ws, hs)) != SA_OK) return st;
+  FwdBufs b;
+  b.row_ptr = row_ptr;
+  b.col_idx = col_idx;
+  b.row_perm = row_perm;
+  b.q = q;
+  b.k = k;
+  b.v = v;
+  b.o = o;
+  b.lse = lse;
+  b.part = nullptr;
+  if (p->mode == SA_DECODE) {
+    b.part = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(ws) + ws_cu_blocks(pl));
+    return launch_decode(pl.g, p->dtype, b, splits, hs);
+  }
+  return launch_prefill(pl.g, p->dtype, b, hs);
+}
+
+}  // extern "C"

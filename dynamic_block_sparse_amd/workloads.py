@@ -181,7 +181,11 @@ def make_inputs(w: Workload, device="cpu", lengths=None) -> Inputs:
     """Draw Q, K, V for workload `w` on `device` (fp32 draws, one rounding to dtype)."""
     dev = torch.device(device)
     d, b = w.head_dim, w.block
-    lengths = list(lengths) if lengths is not None else seq_lengths(w)
+    if lengths is not None:
+        lengths = list(lengths)
+        w = w.replace(batch=len(lengths))
+    else:
+        lengths = seq_lengths(w)
     dt = w.torch_dtype
     units = list(_plant_units(w, lengths))
     kplant = {}   # (s, hk) -> (blocks, u)
@@ -268,6 +272,28 @@ def per_sequence(inp: Inputs):
             vs.append(inp.v[:, a:e].double().cpu().numpy())
     else:
         for s in range(w.batch):
+            qs.append(inp.q[s].double().cpu().numpy())
+            ks.append(inp.k[s].double().cpu().numpy())
+            vs.append(inp.v[s].double().cpu().numpy())
+    return qs, ks, vs
+
+
+def per_sequence_subset(inp: Inputs, seqs):
+    """Like per_sequence, for the listed sequences only (lists aligned with `seqs`)."""
+    w = inp.w
+    offs = np.concatenate([[0], np.cumsum(inp.lengths)])
+    qs, ks, vs = [], [], []
+    for s in seqs:
+        if w.mode == "decode":
+            qs.append(inp.q[s].unsqueeze(1).double().cpu().numpy())
+            ks.append(inp.k[s].double().cpu().numpy())
+            vs.append(inp.v[s].double().cpu().numpy())
+        elif w.varlen:
+            a, e = int(offs[s]), int(offs[s + 1])
+            qs.append(inp.q[:, a:e].double().cpu().numpy())
+            ks.append(inp.k[:, a:e].double().cpu().numpy())
+            vs.append(inp.v[:, a:e].double().cpu().numpy())
+        else:
             qs.append(inp.q[s].double().cpu().numpy())
             ks.append(inp.k[s].double().cpu().numpy())
             vs.append(inp.v[s].double().cpu().numpy())

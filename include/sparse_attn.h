@@ -1,0 +1,193 @@
+/*
+ * sparse_attn.h -- dynamic coarse-grained block-sparse attention on AMD gfx950.
+ *
+ * C ABI of libsparse_attn.so.  Three calls carry the method:
+ *
+ *   sparse_attn_route            Q, K            -> block index table J
+ *   sparse_attn_build_worklist   J               -> sorted, deduplicated CSR worklist
+ *   sparse_attn_fwd              Q, K, V, worklist -> O (and log-sum-exp)
+ *
+ * The method ([P2] "2.1 Coarse-grained selection: from content grouping to
+ * dynamic sparse blocks", PaperTrace sparse-attention 2-1; [P3] "From index to
+ * kernel", PaperTrace sparse-attention 5-1):
+ *   - tokens are cut into blocks of b = 64; each query block r is routed to at
+ *     most k_b key blocks, giving J of shape [B, H, N_q, k_b]  ([P2] opening
+ *     paragraph, [P2] §1.2 Eq 1);
+ *   - routing scores mean-pooled key-block summaries against a pooled query
+ *     ([P2] §2.1 Eq 6), selects top-k or a clipped threshold count ([P2] Eq 7),
+ *     scores only complete history blocks and always adds the current block
+ *     ([P2] §2.1 "causal boundary", §4.1);
+ *   - the worklist sorts each row by address, drops duplicates and builds CSR
+ *     row pointers / column indices grouped by length bucket ([P2] §1.2,
+ *     §3.1 "index-to-kernel acceptance table"; [P3] "from index output to
+ *     worklist");
+ *   - the attention kernel loads only the listed K/V tiles, computes exact
+ *     Q K^T / sqrt(d) ([P2] Eq 2) with causal and padding masks, and merges
+ *     tiles with the online softmax of [P2] Eq 3-5; decode splits a row's tiles
+ *     into groups whose partial (m, l, u) states are merged by the same rule
+ *     ([P2] §2.2; [P3] "sparse softmax numerics").
+ *
+ * Conventions shared by every call
+ *   - Pointers marked (device) are device memory owned by the caller; pointers
+ *     marked (host) are host memory read during the call only.  The library
+ *     allocates nothing, keeps no global state, never synchronises the
+ *     stream, and enqueues all work on `stream` (a hipStream_t; NULL is the
+ *     null stream).  Calls are reentrant.
+ *   - Host-detectable problems (bad sizes, unsupported shapes, null pointers,
+ *     workspace too small) return a nonzero status before anything is
+ *     enqueued.  Data-dependent problems found on the device (block ids out of
+ *     range or acausal) set bits in the caller's device word `err`; the
+ *     offending entries are dropped.  Nothing falls back silently to another
+ *     path ([P2] §3.1 "dense fallback": failures are not hidden).
+ *   - Block ids are sequence-local logical ids ([P2] §2.1 variable-length
+ *     paragraph; [P2] §3.1 "summaries are cache state"); all index data are
+ *     int32 ([P2] §3.1 index dtype paragraph).
+ *
+ * Layouts (contiguous, row-major; d = head_dim; elements of `dtype`)
+ *   fixed-length prefill   Q, O [B, Hq, n, d]      K, V [B, Hkv, n, d]
+ *   packed varlen prefill  Q, O [Hq, T, d]         K, V [Hkv, T, d]
+ *                          cu_seqlens [B + 1] int32 token offsets
+ *   decode                 Q, O [S, Hq, d]         K, V [S, Hkv, L, d]
+ *   log-sum-exp            same as Q without d, fp32
+ *   summaries (fp32)       fixed / decode [B, Hkv, N, d];  varlen [Hkv, sum_s N_s, d]
+ *   J (int32)              rows x k_b, rows in (sequence, routing head, query
+ *                          block) row-major order; decode has one row per
+ *                          (sequence, routing head)
+ *   Query head h uses KV head h / (Hq / Hkv).  With share_gqa the routing
+ *   head is the KV head and one row serves its Hq / Hkv query heads;
+ *   otherwise the routing head is the query head.
+ */
+#ifndef SPARSE_ATTN_H_
+#define SPARSE_ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every call. */
+#define SA_OK 0
+#define SA_ERR_INVALID_ARG 1   /* null pointer, inconsistent sizes, bad enum */
+#define SA_ERR_UNSUPPORTED 2   /* valid but not implemented (head_dim, block, dtype combo) */
+#define SA_ERR_WORKSPACE 3     /* workspace or output capacity too small */
+#define SA_ERR_HIP 4           /* a HIP launch failed */
+
+/* Device error bits written (OR-ed) into the worklist's `err` word. */
+#define SA_WL_ERR_RANGE 1      /* an id < -1 or >= the sequence's block count */
+#define SA_WL_ERR_ACAUSAL 2    /* prefill: an id after the row's query block */
+
+#define SA_F32 0
+#define SA_BF16 1
+#define SA_PREFILL 0
+#define SA_DECODE 1
+#define SA_POOL_MEAN 0
+#define SA_POOL_MAX 1
+#define SA_SELECT_TOPK 0
+#define SA_SELECT_THRESHOLD 1
+#define SA_FORCE_CURRENT 1u    /* the query's own block (prefill: r; decode: last); required */
+#define SA_FORCE_FIRST 2u      /* block 0 (a global sink branch, [P2] §3.2 union) */
+
+/* Problem geometry (host struct, read during the call). */
+typedef struct sa_problem {
+  int32_t batch;          /* B sequences (decode: S) */
+  int32_t heads_q;        /* Hq */
+  int32_t heads_kv;       /* Hkv; Hq % Hkv == 0 */
+  int32_t head_dim;       /* d: 64 or 128 */
+  int32_t block;          /* b: 64 */
+  int32_t seqlen;         /* fixed-length n, or decode cached length L; 0 for packed varlen */
+  int32_t dtype;          /* SA_F32 or SA_BF16 (Q, K, V, O) */
+  int32_t mode;           /* SA_PREFILL or SA_DECODE */
+  const int32_t* cu_seqlens; /* (device) [batch + 1] packed varlen offsets, else NULL */
+  int32_t total_tokens;   /* varlen: cu_seqlens[batch] (host-known); else ignored */
+  int32_t total_blocks;   /* varlen: sum_s ceil(len_s / b) (host-known); else ignored */
+  int32_t max_blocks;     /* varlen: max_s ceil(len_s / b) (host-known); else ignored */
+} sa_problem;
+
+/* Routing settings (host struct). */
+typedef struct sa_route_cfg {
+  int32_t qpool;          /* SA_POOL_MEAN or SA_POOL_MAX (max over per-query scores) */
+  int32_t share_gqa;      /* 1: one routing head per KV head, scores averaged over its query heads */
+  int32_t select;         /* SA_SELECT_TOPK or SA_SELECT_THRESHOLD */
+  int32_t k_b;            /* J width: top-k budget incl. forced blocks, or k_max; k_b + forced <= 128 */
+  int32_t k_min;          /* threshold: lower clip of Eq 7 */
+  float tau_rel;          /* threshold: tau_r = max_j g_rj - tau_rel */
+  uint32_t forced;        /* SA_FORCE_* bits; SA_FORCE_CURRENT must be set */
+} sa_route_cfg;
+
+/* Host-side sizes derived from the geometry (no device work).
+ *   rows       worklist rows R (prefill: H_r * total blocks; decode: S * H_r)
+ *   width_max  widest possible worklist row: k_b + number of forced bits
+ *   nnz_cap    R * width_max: a col_idx capacity that can never overflow
+ *   n_buckets  NB: buckets 4, 8, ..., 4 * 2^(NB-1) cover width_max
+ *   kv_blocks  summary slots (B * N, or total_blocks for varlen)
+ * Returns SA_OK or SA_ERR_INVALID_ARG / SA_ERR_UNSUPPORTED. */
+int sparse_attn_sizes(const sa_problem* p, const sa_route_cfg* rc, int64_t* rows,
+                      int32_t* width_max, int64_t* nnz_cap, int32_t* n_buckets,
+                      int64_t* kv_blocks);
+
+/* Bytes of device workspace needed by call `which` (0 route, 1 worklist,
+ * 2 fwd).  For fwd in decode mode `num_splits` is the split-KV group count
+ * (0 = the library's choice, the same one sparse_attn_fwd makes).  Returns 0
+ * for an invalid problem. */
+size_t sparse_attn_workspace_size(const sa_problem* p, const sa_route_cfg* rc, int32_t which,
+                                  int32_t num_splits);
+
+/* Routing ([P2] §2.1 Eq 6 and Eq 7; causal protocol of [P2] §2.1 and §4.1).
+ *   q, k        (device) inputs in the layouts above
+ *   summaries   (device, fp32) block summaries c_j = mean of the block's valid
+ *               keys.  summaries_in = 0: computed from k and written here (this
+ *               is the cache state of [P2] §3.1); summaries_in = 1: read from
+ *               here (decode keeps them with the KV cache) and k is not read.
+ *   J           (device, int32) [rows, k_b]: forced blocks ascending, then the
+ *               selected history blocks ascending, then -1 padding.
+ *   Per row: candidates are the complete history blocks j < r (decode: j < N-1)
+ *   that are not forced; score g_j = pool over the block's valid queries of
+ *   q . c_j (no 1/sqrt(d)), averaged over the row's query heads; keep the top
+ *   D = min(max(K_r - |F|, 0), |C|) by (score desc, id asc), where K_r = k_b
+ *   (top-k) or min(k_b, max(k_min, |F| + #{g_j >= max g - tau_rel})).
+ *   Scores are fp32; ties closer than fp32 rounding may order differently from
+ *   an exact evaluation. */
+int sparse_attn_route(const sa_problem* p, const sa_route_cfg* rc, const void* q, const void* k,
+                      float* summaries, int32_t summaries_in, int32_t* J, void* ws,
+                      size_t ws_bytes, void* stream);
+
+/* Worklist ([P2] §1.2, §3.1 CSR form; [P3] "from index output to worklist").
+ *   J           (device) [rows, k_b] block ids; -1 = empty slot
+ *   row_ptr     (device) [rows + 1] exclusive scan of row lengths
+ *   col_idx     (device) [nnz_cap]; row i holds its ascending unique ids at
+ *               col_idx[row_ptr[i] .. row_ptr[i+1])
+ *   row_perm    (device) [rows] rows sorted by (bucket asc, row asc)
+ *   bucket_ptr  (device) [n_buckets + 1] row_perm ranges per bucket; bucket of
+ *               a row = smallest power of two >= max(length, 4)
+ *   err         (device) one int32, OR-ed with SA_WL_ERR_* bits (caller zeroes it)
+ *   Each row = ascending unique({valid J entries} U forced blocks). */
+int sparse_attn_build_worklist(const sa_problem* p, const sa_route_cfg* rc, const int32_t* J,
+                               int32_t* row_ptr, int32_t* col_idx, int64_t nnz_cap,
+                               int32_t* row_perm, int32_t* bucket_ptr, int32_t* err, void* ws,
+                               size_t ws_bytes, void* stream);
+
+/* Attention over the worklist ([P2] Eq 2-5; [P3] "sparse softmax numerics").
+ *   q, k, v     (device) inputs; o (device) output, same layout and dtype as q
+ *   lse         (device, fp32, nullable) m + ln(l) of the scaled logits per query
+ *   row_ptr, col_idx, row_perm  (device) a worklist from sparse_attn_build_worklist
+ *   Prefill: query i of block r attends key p iff block(p) is in the row,
+ *   p <= i and p < the sequence length.  Decode: the single query attends every
+ *   cached position of the listed blocks; the row's tiles are cut into
+ *   num_splits groups (0 = library's choice) whose partial (m, l, u) states are
+ *   merged with Eq 3-5.  Accumulation and softmax are fp32; bf16 inputs use
+ *   bf16 matrix-core products with P rounded to bf16 before P V. */
+int sparse_attn_fwd(const sa_problem* p, const sa_route_cfg* rc, const int32_t* row_ptr,
+                    const int32_t* col_idx, const int32_t* row_perm, const void* q,
+                    const void* k, const void* v, void* o, float* lse, int32_t num_splits,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* Human-readable text for a status code (static string). */
+const char* sparse_attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_ATTN_H_ */

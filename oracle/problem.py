@@ -46,7 +46,8 @@ def route(qs, ks, lengths, b, mode, qpool, share_gqa, select, k_b, k_min, tau_re
     seqs: subset of sequence ids to route (others left as None rows).
     Returns (J_rows or None-filled list, scores list aligned with row_table).
     """
-    hq, hkv = qs[0].shape[0], ks[0].shape[0]
+    first = next(i for i, x in enumerate(qs) if x is not None)
+    hq, hkv = qs[first].shape[0], ks[first].shape[0]
     route_heads = hkv if share_gqa else hq
     table = row_table(lengths, b, mode, route_heads)
     j_rows = [None] * len(table)
@@ -78,7 +79,8 @@ def attention_rows(qs, ks, vs, lengths, b, mode, share_gqa, row_ids, row_blocks)
     row_blocks[i]: the worklist set W of row i.  Returns {row id: list over the
     row's query heads of (head, query token indices, masked_attention dict)}.
     """
-    hq, hkv = qs[0].shape[0], ks[0].shape[0]
+    first = next(i for i, x in enumerate(qs) if x is not None)
+    hq, hkv = qs[first].shape[0], ks[first].shape[0]
     group = hq // hkv
     route_heads = hkv if share_gqa else hq
     table = row_table(lengths, b, mode, route_heads)

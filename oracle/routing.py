@@ -172,17 +172,22 @@ def route_sequence(q: np.ndarray, k: np.ndarray, length: int, b: int, mode: str,
         else:
             heads = [hr]
             kvh = hr // group
+        # every (query, block) score of every head at once, then pool per query block
+        pooled = []
+        for h in heads:
+            n_tok = length if mode == "prefill" else 1
+            s = q[h, :n_tok].astype(np.float64) @ summaries[kvh].T     # [tokens, N]
+            rows = []
+            for r in range(n_rows):
+                lo, hi = (r * b, min((r + 1) * b, length)) if mode == "prefill" else (0, 1)
+                rows.append(s[lo:hi].mean(axis=0) if qpool == "mean" else s[lo:hi].max(axis=0))
+            pooled.append(np.stack(rows))
+        g_rows = np.mean(np.stack(pooled), axis=0)                      # mean over the head group
         for r in range(n_rows):
-            if mode == "prefill":
-                lo, hi = r * b, min((r + 1) * b, length)
-                q_group = [q[h, lo:hi] for h in heads]
-                cur = r
-            else:
-                q_group = [q[h, 0:1] for h in heads]
-                cur = n_blk - 1
+            cur = r if mode == "prefill" else n_blk - 1
             forced = forced_blocks(cur, n_blk, mode, forced_first)
             cands = candidate_blocks(cur, n_blk, mode, forced)
-            g = pooled_scores(q_group, summaries[kvh], qpool)
+            g = g_rows[r]
             J[hr, r] = select_row(g, cands, forced, select, k_b, k_min, tau_rel)
             scores[hr][r] = (g, cands, forced)
     if return_scores:

@@ -1,0 +1,114 @@
+"""CPU checks of the C-ABI library: it loads, exports every declared symbol,
+computes host-side sizes, and rejects bad arguments before touching a GPU.
+
+No call here reaches a kernel launch: every argument set either fails host
+validation or goes to the pure-host size queries.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dynamic_block_sparse_amd as dbs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"\b(sparse_attn_\w+)\s*\(", text)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dbs.LIB_PATH):
+        pytest.fail("libsparse_attn.so is not built (python -m dynamic_block_sparse_amd.build)")
+    return dbs.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared()
+    assert set(dbs.EXPORTED) <= set(declared)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def _prob(**kw):
+    base = dict(batch=1, heads_q=16, heads_kv=16, head_dim=128, seqlen=8192, dtype="bf16", mode="prefill")
+    base.update(kw)
+    return dbs.Problem(**base)
+
+
+def test_sizes_prefill_mha(lib):
+    s = dbs.sizes(_prob(), dbs.RouteConfig(k_b=16))
+    assert s.rows == 16 * 128
+    assert s.width_max == 17
+    assert s.nnz_cap == 16 * 128 * 17
+    assert s.n_buckets == 4          # 4, 8, 16, 32
+    assert s.kv_blocks == 128
+
+
+def test_sizes_gqa_shared_and_decode(lib):
+    s = dbs.sizes(_prob(batch=2, heads_q=32, heads_kv=8, seqlen=32768),
+                  dbs.RouteConfig(k_b=32, share_gqa=True, force_first=True))
+    assert s.rows == 2 * 8 * 512 and s.width_max == 34 and s.n_buckets == 5
+    d = dbs.sizes(dbs.Problem.decode(64, 32, 8, 128, 131072), dbs.RouteConfig(k_b=64, share_gqa=True))
+    assert d.rows == 64 * 8 and d.width_max == 65 and d.n_buckets == 6 and d.kv_blocks == 64 * 2048
+
+
+def test_workspace_sizes(lib):
+    p, c = _prob(), dbs.RouteConfig(k_b=16)
+    assert dbs.workspace_size(p, c, 0) == 0
+    assert dbs.workspace_size(p, c, 1) >= 2048 * 128 * 4
+    dp = dbs.Problem.decode(64, 32, 8, 128, 131072)
+    dc = dbs.RouteConfig(k_b=64, share_gqa=True)
+    w8 = dbs.workspace_size(dp, dc, 2, 8)
+    assert w8 >= 512 * 8 * 4 * 130 * 4
+    assert dbs.workspace_size(dp, dc, 2, 0) > 0
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(heads_q=12, heads_kv=8), dbs.SA_ERR_INVALID_ARG),     # Hq % Hkv
+    (dict(head_dim=96), dbs.SA_ERR_UNSUPPORTED),
+    (dict(block=32), dbs.SA_ERR_UNSUPPORTED),
+    (dict(seqlen=0), dbs.SA_ERR_INVALID_ARG),                   # fixed length needs n >= 1
+    (dict(batch=0), dbs.SA_ERR_INVALID_ARG),
+])
+def test_invalid_problem_rejected(lib, bad, status):
+    with pytest.raises(dbs.SAError) as e:
+        dbs.sizes(_prob(**bad), dbs.RouteConfig(k_b=16))
+    assert e.value.status == status
+
+
+@pytest.mark.parametrize("cfg", [
+    dbs.RouteConfig(k_b=0),
+    dbs.RouteConfig(k_b=1, force_first=True),        # two forced blocks do not fit
+    dbs.RouteConfig(k_b=128),                        # row wider than 128 slots
+    dbs.RouteConfig(k_b=8, select="threshold", tau_rel=-1.0),
+])
+def test_invalid_config_rejected(lib, cfg):
+    with pytest.raises(dbs.SAError) as e:
+        dbs.sizes(_prob(), cfg)
+    assert e.value.status == dbs.SA_ERR_INVALID_ARG
+
+
+def test_calls_validate_before_any_launch(lib):
+    """Null pointers / small capacities fail with a status; nothing is enqueued."""
+    p, c = _prob().to_c(), dbs.RouteConfig(k_b=16).to_c()
+    P, C = ctypes.byref(p), ctypes.byref(c)
+    assert lib.sparse_attn_route(P, C, None, None, None, 0, None, None, 0, None) == dbs.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_build_worklist(P, C, 8, 8, 8, 10, 8, 8, 8, 8, 10**9, None) == dbs.SA_ERR_WORKSPACE
+    assert lib.sparse_attn_build_worklist(P, C, 8, 8, 8, 10**9, 8, 8, 8, 8, 10, None) == dbs.SA_ERR_WORKSPACE
+    assert lib.sparse_attn_fwd(P, C, None, 8, 8, 8, 8, 8, 8, None, 0, None, 0, None) == dbs.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_fwd(P, C, 8, 8, 8, 8, 8, 8, 8, None, -1, None, 0, None) == dbs.SA_ERR_INVALID_ARG
+    # bf16 with head_dim 64 is not implemented by the attention kernel
+    p64 = _prob(head_dim=64).to_c()
+    assert lib.sparse_attn_fwd(ctypes.byref(p64), C, 8, 8, 8, 8, 8, 8, 8, None, 0, None, 0, None) \
+        == dbs.SA_ERR_UNSUPPORTED
+    assert lib.sparse_attn_status_string(dbs.SA_ERR_HIP) == b"HIP launch failed"

@@ -1,0 +1,178 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Small cases run the oracle over every row; they span several tiles, ragged
+tails (lengths not a multiple of 64), GQA sharing, forced first blocks,
+packed variable-length batches, threshold selection and split-KV decode.
+The full-size problem settings check routing and the worklist on every row
+(or on whole sequences for the largest ones) and the output on sampled rows:
+blocks 0, 1 and N-1 plus random blocks of every (sequence, routing head).
+"""
+import numpy as np
+import pytest
+import torch
+
+import dynamic_block_sparse_amd as dbs
+from dynamic_block_sparse_amd import workloads as wk
+
+from parity import TOL, check_output, check_router, check_worklist, run_gpu, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    dbs.load_library()
+    return torch.device("cuda:0")
+
+
+def _full_check(w, inp, run, seqs=None, rows=None):
+    r = check_router(w, inp, run, seqs=seqs)
+    print(f"[{w.name}] router rows checked {r['checked']} bad {len(r['bad'])} tie-band rows {r['tie_rows']}",
+          flush=True)
+    assert not r["bad"], f"router mismatches outside the tie band at rows {r['bad'][:10]}"
+    check_worklist(w, inp, run)
+    ids = rows if rows is not None else list(range(run.J.shape[0]))
+    o = check_output(w, inp, run, ids)
+    mx, mean = TOL[w.dtype]
+    print(f"[{w.name}] output max-abs {o['max_abs']:.3e} mean-abs {o['mean_abs']:.3e} "
+          f"lse max-abs {o['lse_max_abs']:.3e} over {o['n']} values", flush=True)
+    assert o["max_abs"] <= mx
+    assert o["mean_abs"] <= mean
+
+
+SMALL = [
+    wk.TINY_F32,
+    wk.TINY_F32_DENSE,
+    wk.TINY_F32.replace(name="tiny_f32_ragged_n500_d128_mean", seqlen=500, head_dim=128, qpool="mean", k_b=4),
+    wk.PREFILL_MHA.replace(name="mha_small_h3_n1000_kb16", heads_q=3, heads_kv=3, seqlen=1000),
+    wk.PREFILL_MHA.replace(name="mha_small_h2_n700_kb5_maxpool", heads_q=2, heads_kv=2, seqlen=700,
+                           k_b=5, qpool="max"),
+    wk.PREFILL_GQA.replace(name="gqa_small_b2_hq8_hkv2_n1500_kb8", heads_q=8, heads_kv=2, seqlen=1500, k_b=8),
+    wk.PREFILL_GQA.replace(name="gqa_unshared_b1_hq4_hkv2_n640", batch=1, heads_q=4, heads_kv=2, seqlen=640,
+                           k_b=6, share_gqa=False, forced_first=False),
+    wk.PREFILL_GQA.replace(name="gqa_small_g2_b1_hq4_hkv2_n900", batch=1, heads_q=4, heads_kv=2, seqlen=900,
+                           k_b=7),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_small_fixed(dev, w):
+    print(f"case {w.name}", flush=True)
+    inp = wk.make_inputs(w, dev)
+    run = run_gpu(w, inp)
+    _full_check(w, inp, run)
+
+
+def test_small_varlen_threshold(dev):
+    w = wk.VARLEN.replace(name="varlen_small_thresh", heads_q=8, heads_kv=2, k_b=16)
+    lengths = [700, 1344, 64, 2000, 1]
+    print(f"case {w.name} lengths {lengths}", flush=True)
+    inp = wk.make_inputs(w, dev, lengths=lengths)
+    w = inp.w
+    run = run_gpu(w, inp)
+    _full_check(w, inp, run)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 8])
+def test_small_decode_splits(dev, splits):
+    w = wk.DECODE.replace(name=f"decode_small_s{splits}", batch=3, heads_q=8, heads_kv=2, seqlen=1000,
+                          k_b=8)
+    print(f"case {w.name}", flush=True)
+    inp = wk.make_inputs(w, dev)
+    run = run_gpu(w, inp, num_splits=splits)
+    _full_check(w, inp, run)
+
+
+def test_decode_unshared_heads(dev):
+    w = wk.DECODE.replace(name="decode_unshared", batch=2, heads_q=4, heads_kv=4, seqlen=777, k_b=5,
+                          share_gqa=False, plant_scope="kv")
+    inp = wk.make_inputs(w, dev)
+    run = run_gpu(w, inp)
+    _full_check(w, inp, run)
+
+
+def test_worklist_adversarial_J(dev):
+    """User-supplied J: duplicates, all -1 rows, out-of-range and acausal ids."""
+    w = wk.PREFILL_MHA.replace(name="wl_adversarial", heads_q=2, heads_kv=2, seqlen=640, k_b=6)
+    prob = dbs.Problem.fixed(1, 2, 2, 128, 640)
+    cfg = dbs.config_for(w)
+    rng = np.random.default_rng(0)
+    rows = 2 * 10
+    J = rng.integers(-1, 10, size=(rows, 6))
+    J[0] = -1
+    J[1] = [0, 0, 0, 0, 0, 0]
+    J[3] = [2, 2, -1, 1, 1, 0]
+    J[5] = [11, -7, 3, 3, 9, -1]       # out of range, and acausal 9 > r = 5
+    Jt = torch.as_tensor(J, dtype=torch.int32, device=dev)
+    wl = dbs.build_worklist(prob, cfg, Jt)
+    torch.cuda.synchronize()
+
+    class R:
+        pass
+
+    run = R()
+    run.J = J
+    nnz = int(wl.row_ptr[rows].item())
+    run.wl = dict(row_ptr=wl.row_ptr.cpu().numpy(), col_idx=wl.col_idx[:nnz].cpu().numpy(),
+                  row_perm=wl.row_perm.cpu().numpy(), bucket_ptr=wl.bucket_ptr.cpu().numpy(),
+                  err=int(wl.err.item()))
+    inp = wk.Inputs(w, None, None, None, [640], None, {})
+    ref = check_worklist(w, inp, run)
+    assert ref["err"] == dbs.SA_WL_ERR_RANGE | dbs.SA_WL_ERR_ACAUSAL
+
+
+def test_run_to_run_deterministic(dev):
+    w = wk.PREFILL_GQA.replace(name="determinism", heads_q=8, heads_kv=2, seqlen=2048, k_b=8)
+    inp = wk.make_inputs(w, dev)
+    a = run_gpu(w, inp)
+    b = run_gpu(w, inp)
+    assert np.array_equal(a.J, b.J)
+    for key in ("row_ptr", "col_idx", "row_perm", "bucket_ptr"):
+        assert np.array_equal(a.wl[key], b.wl[key])
+    assert torch.equal(a.o, b.o)
+
+
+# ---------------------------------------------------------------------------
+# Full-size problem settings.
+
+def test_full_tiny_f32(dev):
+    for w in (wk.TINY_F32, wk.TINY_F32_DENSE):
+        inp = wk.make_inputs(w, dev)
+        run = run_gpu(w, inp)
+        _full_check(w, inp, run)
+
+
+def test_full_prefill_mha(dev):
+    w = wk.PREFILL_MHA
+    print(f"case {w.name}", flush=True)
+    inp = wk.make_inputs(w, dev)
+    run = run_gpu(w, inp)
+    _full_check(w, inp, run, rows=sample_rows(w, inp, per_seq_head=3))
+
+
+def test_full_prefill_gqa(dev):
+    w = wk.PREFILL_GQA
+    print(f"case {w.name}", flush=True)
+    inp = wk.make_inputs(w, dev)
+    run = run_gpu(w, inp)
+    _full_check(w, inp, run, seqs=[1], rows=sample_rows(w, inp, per_seq_head=2, seqs=[1]))
+
+
+def test_full_varlen(dev):
+    w = wk.VARLEN
+    print(f"case {w.name} lengths {wk.seq_lengths(w)}", flush=True)
+    inp = wk.make_inputs(w, dev)
+    run = run_gpu(w, inp)
+    lens = inp.lengths
+    seqs = [int(np.argmin(lens)), int(np.argmax(lens))]
+    _full_check(w, inp, run, seqs=seqs, rows=sample_rows(w, inp, per_seq_head=1, seqs=seqs))
+
+
+def test_full_decode(dev):
+    w = wk.DECODE
+    print(f"case {w.name}", flush=True)
+    inp = wk.make_inputs(w, dev)
+    run = run_gpu(w, inp)
+    seqs = [0, 17, 63]
+    _full_check(w, inp, run, seqs=seqs, rows=sample_rows(w, inp, seqs=seqs))

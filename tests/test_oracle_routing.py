@@ -125,3 +125,23 @@ def test_planted_blocks_are_routed():
                     total += 1
                     hits += int(j in J[h, r])
     assert total > 0 and hits / total > 0.9
+
+
+@pytest.mark.parametrize("qpool,share", [("mean", False), ("max", False), ("mean", True), ("max", True)])
+def test_route_sequence_matches_row_by_row_definition(qpool, share):
+    """The batched per-head scoring in route_sequence equals pooled_scores row by row."""
+    rng = np.random.default_rng(5)
+    hq, hkv, n, d, b = 4, 2, 150, 8, 16
+    q = rng.standard_normal((hq, n, d))
+    k = rng.standard_normal((hkv, n, d))
+    J, sc = routing.route_sequence(q, k, n, b, "prefill", qpool, share, "topk", 4, 4, 2.0, True,
+                                   return_scores=True)
+    G = hq // hkv
+    for hr in range(J.shape[0]):
+        heads = list(range(hr * G, (hr + 1) * G)) if share else [hr]
+        kvh = hr if share else hr // G
+        c = routing.block_summaries(k[kvh], n, b)
+        for r in range(J.shape[1]):
+            lo, hi = r * b, min((r + 1) * b, n)
+            g = routing.pooled_scores([q[h, lo:hi] for h in heads], c, qpool)
+            assert np.max(np.abs(g - sc[hr][r][0])) < 1e-12
