@@ -218,30 +218,39 @@ def summaries_shape(prob: Problem):
 
 def route(prob: Problem, cfg: RouteConfig, q: torch.Tensor, k: Optional[torch.Tensor],
           summaries: Optional[torch.Tensor] = None, summaries_in: bool = False,
-          J: Optional[torch.Tensor] = None):
+          J: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
     """sparse_attn_route: returns (J int32 [rows, k_b], fp32 summaries)."""
     lib = load_library()
-    sz = sizes(prob, cfg)
     dev = q.device
     if summaries is None:
         summaries = torch.empty(summaries_shape(prob), dtype=torch.float32, device=dev)
     if J is None:
-        J = torch.empty((sz.rows, cfg.k_b), dtype=torch.int32, device=dev)
+        J = torch.empty((sizes(prob, cfg).rows, cfg.k_b), dtype=torch.int32, device=dev)
     p, c = prob.to_c(), cfg.to_c()
     wsb = workspace_size(prob, cfg, 0)
-    ws = _workspace(wsb, dev)
+    ws = workspace if workspace is not None and workspace.numel() >= wsb else _workspace(wsb, dev)
     _check("sparse_attn_route", lib.sparse_attn_route(
         ctypes.byref(p), ctypes.byref(c), _ptr(q), _ptr(k), _ptr(summaries), int(summaries_in),
         _ptr(J), _ptr(ws), wsb, _stream(dev)))
     return J, summaries
 
 
-def build_worklist(prob: Problem, cfg: RouteConfig, J: torch.Tensor, out: Optional[Worklist] = None) -> Worklist:
+def alloc_worklist(prob: Problem, cfg: RouteConfig, device) -> Worklist:
+    sz = sizes(prob, cfg)
+    return Worklist(row_ptr=torch.empty(sz.rows + 1, dtype=torch.int32, device=device),
+                    col_idx=torch.empty(max(sz.nnz_cap, 1), dtype=torch.int32, device=device),
+                    row_perm=torch.empty(max(sz.rows, 1), dtype=torch.int32, device=device),
+                    bucket_ptr=torch.empty(sz.n_buckets + 1, dtype=torch.int32, device=device),
+                    err=torch.zeros(1, dtype=torch.int32, device=device))
+
+
+def build_worklist(prob: Problem, cfg: RouteConfig, J: torch.Tensor, out: Optional[Worklist] = None,
+                   workspace: Optional[torch.Tensor] = None) -> Worklist:
     """sparse_attn_build_worklist: returns the CSR worklist (device tensors)."""
     lib = load_library()
-    sz = sizes(prob, cfg)
     dev = J.device
     if out is None:
+        sz = sizes(prob, cfg)
         out = Worklist(row_ptr=torch.empty(sz.rows + 1, dtype=torch.int32, device=dev),
                        col_idx=torch.empty(max(sz.nnz_cap, 1), dtype=torch.int32, device=dev),
                        row_perm=torch.empty(max(sz.rows, 1), dtype=torch.int32, device=dev),
@@ -251,7 +260,7 @@ def build_worklist(prob: Problem, cfg: RouteConfig, J: torch.Tensor, out: Option
         out.err.zero_()
     p, c = prob.to_c(), cfg.to_c()
     wsb = workspace_size(prob, cfg, 1)
-    ws = _workspace(wsb, dev)
+    ws = workspace if workspace is not None and workspace.numel() >= wsb else _workspace(wsb, dev)
     _check("sparse_attn_build_worklist", lib.sparse_attn_build_worklist(
         ctypes.byref(p), ctypes.byref(c), _ptr(J), _ptr(out.row_ptr), _ptr(out.col_idx),
         out.col_idx.numel(), _ptr(out.row_perm), _ptr(out.bucket_ptr), _ptr(out.err),
