@@ -24,7 +24,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 def compile_flags():
     return ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-munsafe-fp-atomics", "-I", INCLUDE, "-I", CSRC]
+            "-munsafe-fp-atomics", "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+            "-I", INCLUDE, "-I", CSRC]
 
 
 def build(verbose: bool = False, jobs: int = 0) -> str:

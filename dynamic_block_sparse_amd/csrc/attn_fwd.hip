@@ -29,25 +29,105 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 // --------------------------------------------------------------------------
 // bf16 MFMA prefill kernel (d = 128).
-template <int HPR>
-__global__ void __launch_bounds__(128 * HPR) prefill_bf16_kernel(Geom g, FwdBufs a) {
-  constexpr int D = 128;
-  constexpr int NT = 128 * HPR;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * 64 * D * 2];
-  unsigned char* kt = lds;                 // K  [64 keys][128 d]  16-byte units swizzled
-  unsigned char* vt = lds + 64 * D * 2;    // V^T [128 d][64 keys]  8-byte units swizzled
+//
+// LDS per stage: K [64 keys][128 d] and V [64 keys][128 d], both row-major in
+// 16-byte chunks with an XOR swizzle on the chunk index, filled straight from
+// HBM with 16-byte global->LDS loads (no staging registers; the swizzle is
+// applied by permuting the per-lane source addresses).  NBUF = 2 double-
+// buffers the stages: the next tile's loads are in flight while the current
+// tile is computed.  V^T operands come from the LDS transpose read
+// (ds_read_b64_tr_b16): in each 16-lane group it returns, to lane i, the
+// i-th column of the 4 x 16 block that the group's lanes read row-wise.
 
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-  const int64_t row = a.row_perm[g.rows - 1 - (int64_t)blockIdx.x];   // longest rows first
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+#define SA_LDS __attribute__((address_space(3)))
+
+__device__ __forceinline__ int ksw(int key) { return key & 15; }
+// V rows: the four rows a transpose read touches land in distinct bank groups
+__device__ __forceinline__ int vsw(int key) { return ((key & 3) << 2) + ((key & 2)); }
+
+// 16-byte global->LDS load: lane l's 16 bytes land at lds_wave_base + 16 l.
+// Issued as inline assembly so that the compiler's wait-count insertion does
+// not treat every later LDS read as dependent on it (it would otherwise wait
+// for all loads, including the next tile's prefetch); the kernel waits for
+// these loads explicitly with wait_vmcnt before each barrier.
+__device__ __forceinline__ void load_lds16(const void* g, const unsigned char* lds_wave_base) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(SA_LDS const unsigned char*)lds_wave_base;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(g), "s"(m0) : "memory", "m0");
+}
+
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Block -> position in the worklist's (longest-first) row order.  Runs of G
+// consecutive rows (same KV head, neighbouring query blocks) go to one XCD:
+// workgroups are dispatched round-robin over the 8 XCDs, so block b runs on
+// XCD b % 8 and its run is [8G m + (b % 8) G, ... + G).
+__device__ __forceinline__ int64_t xcd_schedule(int64_t b, int64_t rows, int G) {
+  const int64_t span = 8 * (int64_t)G;
+  const int64_t base = (b / span) * span;
+  if (G <= 1 || base + span > rows) return b;
+  return base + (b % 8) * G + (b / 8) % G;
+}
+
+template <int HPR, int NBUF>
+__global__ void __launch_bounds__(128 * HPR) prefill_bf16_kernel(Geom g, FwdBufs a, int xcd_run) {
+  constexpr int D = 128;
+  constexpr int NW = 2 * HPR;               // wavefronts: 2 per query head
+  constexpr int TILE = 64 * D * 2;          // bytes of one K (or V) tile
+  constexpr int LOADS = 2 * (TILE / 1024) / NW;   // 1 KB wave loads per tile per wave
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[NBUF * 2 * TILE];
+
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int64_t pos = xcd_schedule(blockIdx.x, g.rows, xcd_run);
+  const int64_t row = a.row_perm[g.rows - 1 - pos];   // longest rows first
   const RowInfo ri = decode_row(g, row);
   const int kvh = g.share ? ri.h : ri.h / g.group;
   const int head = (g.share ? ri.h * g.group : ri.h) + wave / 2;
   const int half = lane / 32, l32 = lane % 32;
-  const int qpos = ri.r * kBlock + (wave % 2) * 32 + l32;    // this lane's query token
+  const int qpos = ri.r * kBlock + (wave % 2) * 32 + l32;
   const bool qvalid = qpos < ri.len;
   const __bf16* q = (const __bf16*)a.q;
-  const __bf16* k = (const __bf16*)a.k;
-  const __bf16* v = (const __bf16*)a.v;
+  const unsigned char* kbytes = (const unsigned char*)a.k;
+  const unsigned char* vbytes = (const unsigned char*)a.v;
+
+  const int t_begin = a.row_ptr[row], ntiles = a.row_ptr[row + 1] - t_begin;
+  // the row's tile ids, one per lane (a row holds at most 128 tiles); read back
+  // with readlane so the loop issues no memory load (and no wait) for them
+  const int jl0 = lane < ntiles ? a.col_idx[t_begin + lane] : 0;
+  const int jl1 = lane + 64 < ntiles ? a.col_idx[t_begin + 64 + lane] : 0;
+  auto tile_id = [&](int it) {
+    return it < 64 ? __builtin_amdgcn_readlane(jl0, it) : __builtin_amdgcn_readlane(jl1, it - 64);
+  };
+
+  // issue the 16-byte global->LDS loads of tile `it` into stage `buf`
+  auto issue = [&](int it, int buf) {
+    const int j = tile_id(it);
+    const int cnt = min(kBlock, ri.len - j * kBlock);
+    const int64_t off = kv_offset(g, ri.s, kvh, ri.tok0, j * kBlock) * 2;
+    unsigned char* kt = lds + buf * 2 * TILE;
+    unsigned char* vt = kt + TILE;
+    const int sub = lane >> 4, cl = lane & 15;
+#pragma unroll
+    for (int i = wave; i < 16; i += NW) {
+      const int key = 4 * i + sub;
+      const int kc = min(key, cnt - 1);      // rows past the end: any valid row (masked later)
+      load_lds16(kbytes + off + kc * 256 + ((cl ^ ksw(key)) << 4), kt + i * 1024);
+    }
+#pragma unroll
+    for (int i = wave; i < 16; i += NW) {
+      const int key = 4 * i + sub;
+      const int kc = min(key, cnt - 1);
+      load_lds16(vbytes + off + kc * 256 + ((cl ^ vsw(key)) << 4), vt + i * 1024);
+    }
+  };
+  if (ntiles > 0) issue(0, 0);
 
   // Q as the B operand of S^T = K Q^T: lane holds Q[qpos][16 ks + 8 half .. +8]
   bf16x8 qreg[8];
@@ -61,50 +141,30 @@ __global__ void __launch_bounds__(128 * HPR) prefill_bf16_kernel(Geom g, FwdBufs
   }
 
   const float c2 = kLog2e * 0.08838834764831845f;   // log2(e) / sqrt(128)
+  // m is kept in raw score units; it is raised only when a row max grows by
+  // more than 8 / c2 (exp2 headroom 2^8), so most tiles skip the rescale.
+  const float grow = 8.0f / c2;
   float m = -INFINITY, lsum = 0.f;
   f32x16 oacc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
 
-  const int t_begin = a.row_ptr[row], t_end = a.row_ptr[row + 1];
-  for (int t = t_begin; t < t_end; ++t) {
-    const int j = a.col_idx[t];
-    const int cnt = min(kBlock, ri.len - j * kBlock);     // valid keys in the tile
-    __syncthreads();   // previous tile fully consumed
-    {
-      const __bf16* kb = k + kv_offset(g, ri.s, kvh, ri.tok0, j * kBlock);
-      for (int qi = tid; qi < 64 * 16; qi += NT) {
-        const int key = qi >> 4, c = qi & 15;
-        u32x4 x = key < cnt ? *reinterpret_cast<const u32x4*>(kb + key * D + c * 8) : u32x4{0, 0, 0, 0};
-        *reinterpret_cast<u32x4*>(kt + key * 256 + ((c ^ (key & 15)) << 4)) = x;
-      }
-      const __bf16* vb = v + kv_offset(g, ri.s, kvh, ri.tok0, j * kBlock);
-      for (int p = tid; p < 256; p += NT) {
-        const int kq = p >> 4, c = p & 15;
-        u32x4 x[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kq * 4 + i;
-          x[i] = key < cnt ? *reinterpret_cast<const u32x4*>(vb + key * D + c * 8) : u32x4{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int dd = 0; dd < 8; ++dd) {
-          const int w = dd >> 1;
-          uint32_t lo, hi;
-          if (dd & 1) {
-            lo = (x[0][w] >> 16) | (x[1][w] & 0xffff0000u);
-            hi = (x[2][w] >> 16) | (x[3][w] & 0xffff0000u);
-          } else {
-            lo = (x[0][w] & 0xffffu) | (x[1][w] << 16);
-            hi = (x[2][w] & 0xffffu) | (x[3][w] << 16);
-          }
-          const int d = c * 8 + dd;
-          const int sw = (d & 15) ^ (d >> 4);
-          *reinterpret_cast<u32x2*>(vt + d * 128 + ((kq ^ sw) << 3)) = u32x2{lo, hi};
-        }
-      }
+  // per-lane transpose-read geometry: 16-lane group gi = lane / 16
+  const int gi = lane >> 4, li = lane & 15;
+  const int vh = gi >> 1, vdh = gi & 1;
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = NBUF == 2 ? (it & 1) : 0;
+    if (NBUF == 2 && it + 1 < ntiles) {
+      issue(it + 1, buf ^ 1);
+      wait_vmcnt<LOADS>();
+    } else {
+      wait_vmcnt<0>();
     }
-    __syncthreads();
+    block_barrier();
+    const unsigned char* kt = lds + buf * 2 * TILE;
+    const unsigned char* vt = kt + TILE;
+    const int j = tile_id(it);
 
     // S^T[key][row] for keys kb*32 + (8*(i/4) + 4*half + i%4), row = l32
     f32x16 sacc[2];
@@ -115,11 +175,10 @@ __global__ void __launch_bounds__(128 * HPR) prefill_bf16_kernel(Geom g, FwdBufs
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         const int c = ks * 2 + half;
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(kt + key * 256 + ((c ^ (key & 15)) << 4));
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(kt + key * 256 + ((c ^ ksw(key)) << 4));
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[ks], sacc[kb], 0, 0, 0);
       }
     }
-    // masks: only the diagonal tile (causal) or a tile past the sequence end
     if (j == ri.r || j * kBlock + kBlock > ri.len) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -136,49 +195,55 @@ __global__ void __launch_bounds__(128 * HPR) prefill_bf16_kernel(Geom g, FwdBufs
 #pragma unroll
       for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sacc[kb][i]);
     mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
-    const float mnew = fmaxf(m, mt);
-    const float msafe = mnew == -INFINITY ? 0.f : mnew;
-    const float alpha = exp2f((m - msafe) * c2);
-    const float moff = -msafe * c2;
+    if (__any(mt > m + grow)) {           // some row's max grew: move to the new max
+      const float mnew = fmaxf(m, mt);
+      const float msafe = mnew == -INFINITY ? 0.f : mnew;
+      const float alpha = __builtin_amdgcn_exp2f((m - msafe) * c2);
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      m = mnew;
+    }
+    const float moff = -(m == -INFINITY ? 0.f : m) * c2;
     float rs = 0.f;
     bf16x8 pb[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = exp2f(fmaf(sacc[kb][i], c2, moff));
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c2, moff));
         rs += p;
         pb[kb][i / 8][i % 8] = (__bf16)p;
       }
     }
     rs += __shfl_xor(rs, 32, kWave);
-    lsum = lsum * alpha + rs;
-    m = mnew;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+    lsum += rs;
 
     // O^T[d][row] += V^T[d][keys] P^T[keys][row]; k-slot (half, e) of step
     // (kb, ks) is key kb*32 + 16 ks + 8 (e/4) + 4 half + e%4, matching the
     // P^T values this lane holds in sacc[kb][8 ks + e].
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-      const int d = db * 32 + l32;
-      const int sw = (d & 15) ^ (d >> 4);
-      const unsigned char* vrow = vt + d * 128;
+      const int d = db * 32 + 16 * vdh + 4 * (li & 3);
+      const int chunk = d >> 3, h8 = (d >> 2) & 1;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const int u1 = 8 * kb + 4 * ks + half;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + ((u1 ^ sw) << 3));
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + (((u1 + 2) ^ sw) << 3));
-          const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+          const int key0 = kb * 32 + 16 * ks + 4 * vh + (li >> 2);
+          const int key1 = key0 + 8;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (SA_LDS i16x4*)(vt + key0 * 256 + ((chunk ^ vsw(key0)) << 4) + h8 * 8));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (SA_LDS i16x4*)(vt + key1 * 256 + ((chunk ^ vsw(key1)) << 4) + h8 * 8));
+          const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kb][ks], oacc[db], 0, 0, 0);
         }
       }
     }
+    block_barrier();   // every wave is done with this stage before it is refilled
   }
 
   if (qvalid) {
@@ -289,10 +354,11 @@ int launch_prefill(const Geom& g, int dtype, const FwdBufs& b, hipStream_t st) {
   if (dtype == SA_F32) return launch_f32(g, b, st);
   if (g.d != 128) return SA_ERR_UNSUPPORTED;
   dim3 grid((unsigned)g.rows);
+  const int run = 8;   // rows per XCD run
   switch (g.hpr) {
-    case 1: prefill_bf16_kernel<1><<<grid, 128, 0, st>>>(g, b); break;
-    case 2: prefill_bf16_kernel<2><<<grid, 256, 0, st>>>(g, b); break;
-    case 4: prefill_bf16_kernel<4><<<grid, 512, 0, st>>>(g, b); break;
+    case 1: prefill_bf16_kernel<1, 2><<<grid, 128, 0, st>>>(g, b, run); break;
+    case 2: prefill_bf16_kernel<2, 2><<<grid, 256, 0, st>>>(g, b, run); break;
+    case 4: prefill_bf16_kernel<4, 2><<<grid, 512, 0, st>>>(g, b, run); break;
     default: return SA_ERR_UNSUPPORTED;
   }
   return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
