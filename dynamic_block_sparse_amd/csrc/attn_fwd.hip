@@ -75,12 +75,17 @@ __device__ __forceinline__ int64_t xcd_schedule(int64_t b, int64_t rows, int G) 
   return base + (b % 8) * G + (b / 8) % G;
 }
 
-template <int HPR, int NBUF>
+// PIPE = 0: one stage, loads then compute; PIPE = 2: one stage, V(t) and K(t+1)
+// loads overlap S(t) / softmax / P V(t); PIPE = R >= 3: an (R-1)-stage ring,
+// tile t+R-2 is issued while tile t is computed.
+template <int HPR, int PIPE>
 __global__ void __launch_bounds__(128 * HPR) prefill_bf16_kernel(Geom g, FwdBufs a, int xcd_run) {
+  constexpr int NBUF = PIPE >= 3 ? PIPE - 1 : 1;
   constexpr int D = 128;
   constexpr int NW = 2 * HPR;               // wavefronts: 2 per query head
   constexpr int TILE = 64 * D * 2;          // bytes of one K (or V) tile
   constexpr int LOADS = 2 * (TILE / 1024) / NW;   // 1 KB wave loads per tile per wave
+  constexpr int HALF_LOADS = LOADS / 2;           // of K or of V alone
   __shared__ __attribute__((aligned(1024))) unsigned char lds[NBUF * 2 * TILE];
 
   const int tid = threadIdx.x, lane = tid % kWave;
@@ -106,20 +111,26 @@ __global__ void __launch_bounds__(128 * HPR) prefill_bf16_kernel(Geom g, FwdBufs
     return it < 64 ? __builtin_amdgcn_readlane(jl0, it) : __builtin_amdgcn_readlane(jl1, it - 64);
   };
 
-  // issue the 16-byte global->LDS loads of tile `it` into stage `buf`
-  auto issue = [&](int it, int buf) {
+  // 16-byte global->LDS loads of tile `it`: K into kt, V into vt
+  const int sub = lane >> 4, cl = lane & 15;
+  auto tile_off = [&](int it, int* cnt) {
     const int j = tile_id(it);
-    const int cnt = min(kBlock, ri.len - j * kBlock);
-    const int64_t off = kv_offset(g, ri.s, kvh, ri.tok0, j * kBlock) * 2;
-    unsigned char* kt = lds + buf * 2 * TILE;
-    unsigned char* vt = kt + TILE;
-    const int sub = lane >> 4, cl = lane & 15;
+    *cnt = min(kBlock, ri.len - j * kBlock);
+    return kv_offset(g, ri.s, kvh, ri.tok0, j * kBlock) * 2;
+  };
+  auto issue_k = [&](int it, unsigned char* kt) {
+    int cnt;
+    const int64_t off = tile_off(it, &cnt);
 #pragma unroll
     for (int i = wave; i < 16; i += NW) {
       const int key = 4 * i + sub;
       const int kc = min(key, cnt - 1);      // rows past the end: any valid row (masked later)
       load_lds16(kbytes + off + kc * 256 + ((cl ^ ksw(key)) << 4), kt + i * 1024);
     }
+  };
+  auto issue_v = [&](int it, unsigned char* vt) {
+    int cnt;
+    const int64_t off = tile_off(it, &cnt);
 #pragma unroll
     for (int i = wave; i < 16; i += NW) {
       const int key = 4 * i + sub;
@@ -127,7 +138,20 @@ __global__ void __launch_bounds__(128 * HPR) prefill_bf16_kernel(Geom g, FwdBufs
       load_lds16(vbytes + off + kc * 256 + ((cl ^ vsw(key)) << 4), vt + i * 1024);
     }
   };
-  if (ntiles > 0) issue(0, 0);
+  auto issue = [&](int it, int buf) {
+    issue_k(it, lds + buf * 2 * TILE);
+    issue_v(it, lds + buf * 2 * TILE + TILE);
+  };
+  if (ntiles > 0) {
+    if (PIPE == 2) {
+      issue_k(0, lds);
+    } else {
+#pragma unroll
+      for (int p = 0; p < NBUF - 1; ++p)
+        if (p < ntiles) issue(p, p);
+      if (NBUF == 1) issue(0, 0);
+    }
+  }
 
   // Q as the B operand of S^T = K Q^T: lane holds Q[qpos][16 ks + 8 half .. +8]
   bf16x8 qreg[8];
@@ -154,16 +178,35 @@ __global__ void __launch_bounds__(128 * HPR) prefill_bf16_kernel(Geom g, FwdBufs
   const int vh = gi >> 1, vdh = gi & 1;
 
   for (int it = 0; it < ntiles; ++it) {
-    const int buf = NBUF == 2 ? (it & 1) : 0;
-    if (NBUF == 2 && it + 1 < ntiles) {
-      issue(it + 1, buf ^ 1);
-      wait_vmcnt<LOADS>();
-    } else {
+    const int buf = NBUF > 1 ? it % NBUF : 0;
+    unsigned char* kt = lds + buf * 2 * TILE;
+    unsigned char* vt = kt + TILE;
+    if (PIPE == 2) {
+      // K(it) landed (only it is outstanding); every wave is past P V(it-1)
       wait_vmcnt<0>();
+      block_barrier();
+      issue_v(it, vt);
+    } else if (NBUF > 1) {
+      // the ring slot of tile it+NBUF-1 was last read at iteration it-1,
+      // which ended with a barrier; keep NBUF-1 tiles in flight
+      const int nxt = it + NBUF - 1;
+      if (nxt < ntiles) {
+        issue(nxt, nxt % NBUF);
+        wait_vmcnt<(NBUF - 1) * LOADS>();
+      } else {
+        // no new issue: tiles it+1 .. min(it+NBUF-2, ntiles-1) may stay in flight
+        const int younger = min(NBUF - 2, ntiles - 1 - it);
+        if (younger >= 3) wait_vmcnt<3 * LOADS>();
+        else if (younger == 2) wait_vmcnt<2 * LOADS>();
+        else if (younger == 1) wait_vmcnt<LOADS>();
+        else wait_vmcnt<0>();
+      }
+      block_barrier();
+    } else {
+      if (it > 0) issue(it, 0);   // the previous iteration ended with a barrier
+      wait_vmcnt<0>();
+      block_barrier();
     }
-    block_barrier();
-    const unsigned char* kt = lds + buf * 2 * TILE;
-    const unsigned char* vt = kt + TILE;
     const int j = tile_id(it);
 
     // S^T[key][row] for keys kb*32 + (8*(i/4) + 4*half + i%4), row = l32
@@ -178,6 +221,10 @@ __global__ void __launch_bounds__(128 * HPR) prefill_bf16_kernel(Geom g, FwdBufs
         const bf16x8 av = *reinterpret_cast<const bf16x8*>(kt + key * 256 + ((c ^ ksw(key)) << 4));
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[ks], sacc[kb], 0, 0, 0);
       }
+    }
+    if (PIPE == 2 && it + 1 < ntiles) {
+      block_barrier();          // every wave has read K(it): refill it with K(it+1)
+      issue_k(it + 1, kt);
     }
     if (j == ri.r || j * kBlock + kBlock > ri.len) {
 #pragma unroll
@@ -221,6 +268,12 @@ __global__ void __launch_bounds__(128 * HPR) prefill_bf16_kernel(Geom g, FwdBufs
     rs += __shfl_xor(rs, 32, kWave);
     lsum += rs;
 
+    if (PIPE == 2) {
+      // V(it) landed; K(it+1) may still be in flight
+      if (it + 1 < ntiles) wait_vmcnt<HALF_LOADS>();
+      else wait_vmcnt<0>();
+      block_barrier();
+    }
     // O^T[d][row] += V^T[d][keys] P^T[keys][row]; k-slot (half, e) of step
     // (kb, ks) is key kb*32 + 16 ks + 8 (e/4) + 4 half + e%4, matching the
     // P^T values this lane holds in sacc[kb][8 ks + e].
@@ -243,7 +296,7 @@ __global__ void __launch_bounds__(128 * HPR) prefill_bf16_kernel(Geom g, FwdBufs
         }
       }
     }
-    block_barrier();   // every wave is done with this stage before it is refilled
+    if (PIPE != 2) block_barrier();   // every wave is done with this stage before it is refilled
   }
 
   if (qvalid) {
@@ -354,11 +407,16 @@ int launch_prefill(const Geom& g, int dtype, const FwdBufs& b, hipStream_t st) {
   if (dtype == SA_F32) return launch_f32(g, b, st);
   if (g.d != 128) return SA_ERR_UNSUPPORTED;
   dim3 grid((unsigned)g.rows);
-  const int run = 8;   // rows per XCD run
+  // One LDS stage (32 KB) per workgroup: four MHA workgroups fit on a CU, so
+  // each SIMD runs two wavefronts from different workgroups whose softmax and
+  // MFMA phases interleave.  Measured on MI355X this beats a 2-4 stage ring
+  // (64-128 KB, fewer workgroups per CU) for both MHA and 4-head GQA rows; MHA
+  // rows gain a little more from overlapping V(t) / K(t+1) with compute.
+  const int run = 32;   // rows per XCD run
   switch (g.hpr) {
     case 1: prefill_bf16_kernel<1, 2><<<grid, 128, 0, st>>>(g, b, run); break;
-    case 2: prefill_bf16_kernel<2, 2><<<grid, 256, 0, st>>>(g, b, run); break;
-    case 4: prefill_bf16_kernel<4, 2><<<grid, 512, 0, st>>>(g, b, run); break;
+    case 2: prefill_bf16_kernel<2, 0><<<grid, 256, 0, st>>>(g, b, run); break;
+    case 4: prefill_bf16_kernel<4, 0><<<grid, 512, 0, st>>>(g, b, run); break;
     default: return SA_ERR_UNSUPPORTED;
   }
   return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
