@@ -8,13 +8,17 @@
 //
 // One wavefront per (row, split), row = (sequence, routing head); the row's
 // query heads (the KV head's group when routing is shared) share every K/V
-// tile it streams.  Per 64-key tile:
-//   * S = Q K^T on v_mfma_f32_16x16x32_bf16 with the heads as the M dimension
-//     (K goes straight from HBM into the B operand in 16-byte loads);
-//   * softmax in the log2 domain, one lane per key, per-head max / sum by
-//     wavefront reductions;
-//   * P V on the vector ALU: lane = (8-column chunk, key phase), each 16-byte
-//     V load feeds G * 8 FMAs; phases are summed once per split.
+// tile it streams.  Per 64-key tile, with the heads as the N dimension of
+// v_mfma_f32_16x16x32_bf16 (16 slots, the first G used):
+//   * S^T = K Q^T: K goes straight from HBM into the A operand in 16-byte
+//     loads (key = lane % 16 of each 16-key block), so each lane ends up
+//     with 16 scores of one head;
+//   * softmax in the log2 domain: the per-head max / sum over 64 keys is the
+//     lane's own 16 values plus two cross-row swaps;
+//   * O^T = V^T P^T: V is copied HBM -> LDS with 16-byte global->LDS loads
+//     (16 KB per wavefront, chunk-swizzled) and read back transposed with
+//     ds_read_b64_tr_b16; P^T is the S^T accumulator converted in place.
+// Up to ten wavefronts per CU (LDS-bound) keep ~300 KB of loads in flight.
 #include "common.h"
 #include "kernels.h"
 
@@ -27,11 +31,25 @@ size_t decode_partials_bytes(const Geom& g, int splits) {
   return (size_t)g.rows * splits * g.hpr * (g.d + 2) * sizeof(float);
 }
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+#define SA_LDS __attribute__((address_space(3)))
+
+__device__ __forceinline__ void dec_load_lds16(const void* g, const unsigned char* lds_wave_base) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(SA_LDS const unsigned char*)lds_wave_base;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(g), "s"(m0) : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void dec_wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// V rows: the 8 rows two 16-lane groups read together map to 16 distinct slots
+__device__ __forceinline__ int dec_vsw(int key) { return (key & 7) << 1; }
+
 template <int G>
-__global__ void __launch_bounds__(64) decode_split_kernel(Geom g, FwdBufs a, int splits) {
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) decode_split_kernel(Geom g, FwdBufs a, int splits) {
   constexpr int D = 128;
-  __shared__ float sbuf[16][64];    // S[head][key] (log2-scaled)
-  __shared__ float pbuf[64][G];     // P[key][head]
+  __shared__ __attribute__((aligned(1024))) unsigned char vt[64 * D * 2];
   const int lane = threadIdx.x;
   const int64_t item = blockIdx.x;
   const int64_t row = item / splits;
@@ -41,123 +59,127 @@ __global__ void __launch_bounds__(64) decode_split_kernel(Geom g, FwdBufs a, int
   const int h0 = g.share ? ri.h * g.group : ri.h;
   const int t0 = a.row_ptr[row], nt = a.row_ptr[row + 1] - t0;
   const int per = (nt + splits - 1) / splits;
-  const int tb = t0 + min(sp * per, nt), te = t0 + min((sp + 1) * per, nt);
+  const int tb = min(sp * per, nt), te = min((sp + 1) * per, nt);
   const __bf16* q = (const __bf16*)a.q;
-  const __bf16* k = (const __bf16*)a.k;
-  const __bf16* v = (const __bf16*)a.v;
+  const unsigned char* kbytes = (const unsigned char*)a.k;
+  const unsigned char* vbytes = (const unsigned char*)a.v;
   const float c2 = kLog2eD / sqrtf((float)D);
+  const int hs = lane & 15, grp = lane >> 4;
 
-  // A operand: Q[head slot = lane % 16][d = 32 ks + 8 (lane / 16) .. +8]
-  bf16x8 qa[4];
-  {
-    const int hs = lane % 16;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      u32x4 x = {0, 0, 0, 0};
-      if (hs < G) x = *reinterpret_cast<const u32x4*>(q + q_offset(g, ri.s, h0 + hs, 0, 0) + ks * 32 + (lane / 16) * 8);
-      qa[ks] = __builtin_bit_cast(bf16x8, x);
-    }
-  }
-  float m[G], l[G], acc[G][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = -INFINITY;
-    l[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-  }
-  const int chunk = lane % 16, phase = lane / 16;
+  // tile ids of this split, one per lane (a split holds at most 64 tiles)
+  const int jl = tb + lane < te ? a.col_idx[t0 + tb + lane] : 0;
 
-  for (int t = tb; t < te; ++t) {
-    const int j = a.col_idx[t];
+  // B operand of S^T = K Q^T: Q[head slot = lane % 16][d = 32 ks + 8 grp .. +8]
+  bf16x8 qb[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    u32x4 x = {0, 0, 0, 0};
+    if (hs < G) x = *reinterpret_cast<const u32x4*>(q + q_offset(g, ri.s, h0 + hs, 0, 0) + ks * 32 + grp * 8);
+    qb[ks] = __builtin_bit_cast(bf16x8, x);
+  }
+  const float grow = 8.0f;   // log2 headroom before the running max must move
+  float m = -INFINITY, l = 0.f;
+  f32x4 oacc[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int t = 0; t < te - tb; ++t) {
+    const int j = __builtin_amdgcn_readlane(jl, t);
     const int cnt = min(kBlock, ri.len - j * kBlock);
-    const __bf16* kb = k + kv_offset(g, ri.s, kvh, 0, j * kBlock);
-    const __bf16* vb = v + kv_offset(g, ri.s, kvh, 0, j * kBlock);
-    // V loads for this lane's 16 keys (issued before the QK products)
-    u32x4 vr[16];
+    const int64_t off = kv_offset(g, ri.s, kvh, 0, j * kBlock) * 2;
+    // K: A operand of S^T, key = 16 mb + lane % 16, d = 32 ks + 8 grp
+    u32x4 kr[4][4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int key = min(16 * mb + hs, cnt - 1);   // rows past the end: any valid row (masked)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        kr[mb][ks] = *reinterpret_cast<const u32x4*>(kbytes + off + key * 256 + ks * 64 + grp * 16);
+    }
+    // V: HBM -> LDS, 16 wave loads of 1 KB (4 key rows each)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int key = 4 * i + phase;
-      vr[i] = key < cnt ? *reinterpret_cast<const u32x4*>(vb + key * D + chunk * 8) : u32x4{0, 0, 0, 0};
+      const int key = 4 * i + grp;
+      const int kc = min(key, cnt - 1);
+      dec_load_lds16(vbytes + off + kc * 256 + (((lane & 15) ^ dec_vsw(key)) << 4), vt + i * 1024);
     }
-    // S[head][key] for keys nb*16 + lane%16, heads 4*(lane/16) + i
+    // S^T[key = 16 mb + 4 grp + i][head = lane % 16]
+    f32x4 sacc[4];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-      const int key = nb * 16 + (lane % 16);
+    for (int mb = 0; mb < 4; ++mb) {
+      sacc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        u32x4 x = key < cnt ? *reinterpret_cast<const u32x4*>(kb + key * D + ks * 32 + (lane / 16) * 8)
-                            : u32x4{0, 0, 0, 0};
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], __builtin_bit_cast(bf16x8, x), sacc, 0, 0, 0);
+      for (int ks = 0; ks < 4; ++ks)
+        sacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[mb][ks]), qb[ks],
+                                                          sacc[mb], 0, 0, 0);
+    }
+    float mt = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x = sacc[mb][i] * c2;
+        if (16 * mb + 4 * grp + i >= cnt) x = -INFINITY;
+        sacc[mb][i] = x;
+        mt = fmaxf(mt, x);
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sbuf[4 * (lane / 16) + i][key] = sacc[i] * c2;
     }
-    __syncthreads();
-    float alpha[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float x = lane < cnt ? sbuf[h][lane] : -INFINITY;
-      const float mt = wave_max(x);
-      const float mnew = fmaxf(m[h], mt);
+    mt = max_xor32(max_xor16(mt));
+    if (__any(mt > m + grow)) {
+      const float mnew = fmaxf(m, mt);
       const float msafe = mnew == -INFINITY ? 0.f : mnew;
-      alpha[h] = exp2f(m[h] - msafe);
-      const float p = exp2f(x - msafe);
-      pbuf[lane][h] = p;
-      l[h] = l[h] * alpha[h] + wave_sum(p);
-      m[h] = mnew;
+      const float alpha = __builtin_amdgcn_exp2f(m - msafe);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) oacc[db][i] *= alpha;
+      m = mnew;
     }
-    __syncthreads();
+    const float moff = m == -INFINITY ? 0.f : m;
+    float rs = 0.f;
+    bf16x8 pb[2];
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+    for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] *= alpha[h];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = 4 * i + phase;
-      float pv[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) pv[h] = pbuf[key][h];
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float lo = bf16_lo(vr[i][w]), hi = bf16_hi(vr[i][w]);
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          acc[h][2 * w] = fmaf(pv[h], lo, acc[h][2 * w]);
-          acc[h][2 * w + 1] = fmaf(pv[h], hi, acc[h][2 * w + 1]);
-        }
+      for (int i = 0; i < 4; ++i) {
+        const float p = __builtin_amdgcn_exp2f(sacc[mb][i] - moff);
+        rs += p;
+        pb[mb >> 1][(mb & 1) * 4 + i] = (__bf16)p;
       }
     }
-  }
-  // sum the four key phases
+    l += sum_xor32(sum_xor16(rs));
+    dec_wait_vmcnt<0>();   // V landed in LDS
+    // O^T[d = 16 db + 4 grp + i][head] += V^T P^T; k-slot (grp, e) of step ks
+    // is key 32 ks + 16 (e / 4) + 4 grp + e % 4, as held in sacc[2 ks + e / 4][e % 4]
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+    for (int db = 0; db < 8; ++db) {
+      const int d = 16 * db + 4 * (hs & 3);
+      const int chunk = d >> 3, h8 = (d >> 2) & 1;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      acc[h][e] += __shfl_xor(acc[h][e], 16, kWave);
-      acc[h][e] += __shfl_xor(acc[h][e], 32, kWave);
+      for (int ks = 0; ks < 2; ++ks) {
+        const int key0 = 32 * ks + 4 * grp + (hs >> 2);
+        const int key1 = key0 + 16;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (SA_LDS i16x4*)(vt + key0 * 256 + ((chunk ^ dec_vsw(key0)) << 4) + h8 * 8));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (SA_LDS i16x4*)(vt + key1 * 256 + ((chunk ^ dec_vsw(key1)) << 4) + h8 * 8));
+        const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[ks], oacc[db], 0, 0, 0);
+      }
     }
+    // the next tile's V loads overwrite vt: every transpose read above has
+    // returned (the MFMAs consumed them), so no further wait is needed
+  }
   float* part = a.part + ((int64_t)row * splits + sp) * G * (D + 2);
-  if (phase == 0) {
+  if (hs < G) {
+    float* ph = part + hs * (D + 2);
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      f32x4 u0, u1;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        u0[e] = acc[h][e];
-        u1[e] = acc[h][4 + e];
-      }
-      float* ph = part + h * (D + 2);
-      *reinterpret_cast<f32x4*>(ph + chunk * 8) = u0;
-      *reinterpret_cast<f32x4*>(ph + chunk * 8 + 4) = u1;
-    }
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      part[h * (D + 2) + D] = m[h];
-      part[h * (D + 2) + D + 1] = l[h];
+    for (int db = 0; db < 8; ++db)
+      *reinterpret_cast<f32x4*>(ph + 16 * db + 4 * grp) = oacc[db];
+    if (grp == 0) {
+      ph[D] = m;
+      ph[D + 1] = l;
     }
   }
 }
@@ -202,6 +224,7 @@ int launch_decode(const Geom& g, int dtype, const FwdBufs& b, int splits, hipStr
     case 2: decode_split_kernel<2><<<items, 64, 0, st>>>(g, b, splits); break;
     case 4: decode_split_kernel<4><<<items, 64, 0, st>>>(g, b, splits); break;
     case 8: decode_split_kernel<8><<<items, 64, 0, st>>>(g, b, splits); break;
+    case 16: decode_split_kernel<16><<<items, 64, 0, st>>>(g, b, splits); break;
     default: return SA_ERR_UNSUPPORTED;
   }
   if (hipGetLastError() != hipSuccess) return SA_ERR_HIP;

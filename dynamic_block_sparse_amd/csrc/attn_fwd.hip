@@ -241,7 +241,7 @@ __global__ void __launch_bounds__(128 * HPR) prefill_bf16_kernel(Geom g, FwdBufs
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sacc[kb][i]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+    mt = max_xor32(mt);
     if (__any(mt > m + grow)) {           // some row's max grew: move to the new max
       const float mnew = fmaxf(m, mt);
       const float msafe = mnew == -INFINITY ? 0.f : mnew;
@@ -265,7 +265,7 @@ __global__ void __launch_bounds__(128 * HPR) prefill_bf16_kernel(Geom g, FwdBufs
         pb[kb][i / 8][i % 8] = (__bf16)p;
       }
     }
-    rs += __shfl_xor(rs, 32, kWave);
+    rs = sum_xor32(rs);
     lsum += rs;
 
     if (PIPE == 2) {

@@ -173,6 +173,32 @@ __device__ __forceinline__ int block_excl_scan(int v, int* sh, int* total) {
   return before + inc - v;
 }
 
+// Cross-lane pair exchanges (gfx950 v_permlane16_swap / v_permlane32_swap).
+// With the same value in both operands, the two results of a swap hold, in
+// every lane, that lane's value and the value of its partner lane (lane ^ 16,
+// resp. lane ^ 32), in some order; combining them with a commutative op gives
+// the pairwise reduction.
+__device__ __forceinline__ float max_xor16(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Lane mask of lanes below the current one (for ballot-based compaction).
 __device__ __forceinline__ uint64_t lanes_below() {
   unsigned lane = __lane_id();

@@ -120,14 +120,26 @@ size_t ws_cu_blocks(const Plan& pl) {
   return pl.g.varlen ? align_up((size_t)(pl.g.batch + 1) * sizeof(int32_t)) : 0;
 }
 
+// Decode split count.  A split holds at most 64 tiles (one per lane of the
+// wavefront that streams it), so at least ceil(width / 64) splits are used.
+// By default enough splits are made for ~8 wavefronts per CU, each streaming
+// >= 4 tiles (measured on MI355X: 8 per CU beats the LDS-bound maximum of 10).
+int min_splits(const Plan& pl) { return (pl.width_max + 63) / 64; }
+
 int auto_splits(const Plan& pl) {
-  const int64_t target = 4096;
+  const int64_t target = 2048;
   int64_t s = (target + pl.g.rows - 1) / pl.g.rows;
   int64_t cap = pl.width_max / 4;
   if (cap < 1) cap = 1;
   if (s > cap) s = cap;
   if (s > 64) s = 64;
+  if (s < min_splits(pl)) s = min_splits(pl);
   return s < 1 ? 1 : (int)s;
+}
+
+int resolve_splits(const Plan& pl, int requested) {
+  if (requested <= 0) return auto_splits(pl);
+  return requested < min_splits(pl) ? min_splits(pl) : requested;
 }
 
 size_t ws_size(const Plan& pl, int which, int splits) {
@@ -184,8 +196,7 @@ size_t sparse_attn_workspace_size(const sa_problem* p, const sa_route_cfg* rc, i
                                   int32_t num_splits) {
   Plan pl;
   if (validate(p, rc, &pl) != SA_OK || which < 0 || which > 2) return 0;
-  const int splits = num_splits > 0 ? num_splits : auto_splits(pl);
-  return ws_size(pl, which, splits);
+  return ws_size(pl, which, resolve_splits(pl, num_splits));
 }
 
 int sparse_attn_route(const sa_problem* p, const sa_route_cfg* rc, const void* q, const void* k,
@@ -249,7 +260,7 @@ int sparse_attn_fwd(const sa_problem* p, const sa_route_cfg* rc, const int32_t* 
     const bool ok = h == 1 || h == 2 || h == 4 || (h == 8 && p->mode == SA_DECODE);
     if (!ok) return SA_ERR_UNSUPPORTED;
   }
-  const int splits = num_splits > 0 ? num_splits : auto_splits(pl);
+  const int splits = resolve_splits(pl, num_splits);
   const size_t need = ws_size(pl, 2, splits);
   if (ws_bytes < need || (need && !ws)) return SA_ERR_WORKSPACE;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);

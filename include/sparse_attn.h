@@ -175,8 +175,9 @@ int sparse_attn_build_worklist(const sa_problem* p, const sa_route_cfg* rc, cons
  *   Prefill: query i of block r attends key p iff block(p) is in the row,
  *   p <= i and p < the sequence length.  Decode: the single query attends every
  *   cached position of the listed blocks; the row's tiles are cut into
- *   num_splits groups (0 = library's choice) whose partial (m, l, u) states are
- *   merged with Eq 3-5.  Accumulation and softmax are fp32; bf16 inputs use
+ *   num_splits groups (0 = library's choice; raised to at least
+ *   ceil((k_b + forced) / 64)) whose partial (m, l, u) states are merged with
+ *   Eq 3-5.  Accumulation and softmax are fp32; bf16 inputs use
  *   bf16 matrix-core products with P rounded to bf16 before P V. */
 int sparse_attn_fwd(const sa_problem* p, const sa_route_cfg* rc, const int32_t* row_ptr,
                     const int32_t* col_idx, const int32_t* row_perm, const void* q,
