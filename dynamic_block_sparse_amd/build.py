@@ -22,7 +22,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
 def compile_flags():
-    return ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    return ["--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-munsafe-fp-atomics", "-mllvm", "-amdgpu-mfma-vgpr-form=1",
             "-I", INCLUDE, "-I", CSRC]

@@ -20,6 +20,8 @@
 //     16-byte / 8-byte units so the MFMA operand reads are bank-conflict free;
 //   * tiles are visited in the worklist's ascending address order ([P2] §1.2).
 // fp32 path: a plain SIMT kernel (one lane per query row), exact-fp32 softmax.
+#include <utility>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -75,9 +77,168 @@ __device__ __forceinline__ int64_t xcd_schedule(int64_t b, int64_t rows, int G) 
   return base + (b % 8) * G + (b / 8) % G;
 }
 
-// PIPE = 0: one stage, loads then compute; PIPE = 2: one stage, V(t) and K(t+1)
-// loads overlap S(t) / softmax / P V(t); PIPE = R >= 3: an (R-1)-stage ring,
-// tile t+R-2 is issued while tile t is computed.
+// --------------------------------------------------------------------------
+// Tile steps shared by the bf16 kernels.  Layouts:
+//   S^T accumulator sacc[kb][i] of a lane = key kb*32 + 8*(i/4) + 4*half + i%4
+//     of query row l32 (v_mfma_f32_32x32x16_bf16 output layout);
+//   P^T operand pb[kb][ks] = the same values rounded to bf16, k-slot (half, e)
+//     of step (kb, ks) = key kb*32 + 16 ks + 8 (e/4) + 4 half + e%4;
+//   O^T accumulator oacc[db] = d in block db, query row l32.
+//
+// Scores come out of the MFMA in log2 units and already offset by the row's
+// running reference m: Q is pre-scaled by log2(e)/sqrt(d) when it is loaded,
+// and the S^T accumulator starts at -m instead of 0 (m = -inf before a row's
+// first tile, when it starts at 0).  The softmax then needs one exp2 per
+// score and no multiply-add.  m moves only when a row maximum exceeds it by
+// more than kGrow (exp2 headroom 2^8), so most tiles skip the rescale of O.
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+constexpr float kGrow = 8.0f;
+
+// S^T[key][row] = K Q^T for the 64 keys of the K tile at kt, accumulated onto
+// the reference offset
+__device__ __forceinline__ void s_tile(f32x16 (&sacc)[2], const unsigned char* kt, const bf16x8 (&qreg)[8],
+                                       float m, int l32, int half) {
+  const float init = m == -INFINITY ? 0.f : -m;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sacc[kb][i] = init;
+    const int key = kb * 32 + l32;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const int c = ks * 2 + half;
+      const bf16x8 av = *reinterpret_cast<const bf16x8*>(kt + key * 256 + ((c ^ ksw(key)) << 4));
+      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[ks], sacc[kb], 0, 0, 0);
+    }
+  }
+}
+
+// Mask, row maximum, lazy rescale, P = exp2(S - m) in bf16 and the row sum of
+// those bf16 weights ([P2] §1.2 Eq 3-5).  `kbase` is the tile's first key
+// position; `masked` says whether any key of the tile can be masked for this
+// row (the diagonal block, or a block that runs past the sequence end).
+__device__ __forceinline__ void softmax_tile(f32x16 (&sacc)[2], bf16x8 (&pb)[2][2], f32x16 (&oacc)[4],
+                                             float& m, float& lsum, bool masked, int kbase, int qpos,
+                                             int len, int half) {
+  if (masked) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kpos = kbase + kb * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+        if (kpos > qpos || kpos >= len) sacc[kb][i] = -INFINITY;
+      }
+    }
+  }
+  float m0 = -INFINITY, m1 = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    m0 = fmaxf(m0, sacc[0][i]);
+    m1 = fmaxf(m1, sacc[1][i]);
+  }
+  const float mt = max_xor32(fmaxf(m0, m1));   // row maximum, relative to m
+  if (__any(m == -INFINITY || mt > kGrow)) {
+    asm volatile("");   // a real branch: the rescale is rare, never speculate it
+    const bool first = m == -INFINITY;
+    const float shift = first ? mt : fmaxf(mt, 0.f);
+    const float alpha = first ? 0.f : __builtin_amdgcn_exp2f(-shift);
+    lsum *= alpha;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[kb][i] -= shift;
+    m = (first ? 0.f : m) + shift;
+  }
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) pb[kb][i / 8][i % 8] = (__bf16)__builtin_amdgcn_exp2f(sacc[kb][i]);
+  // the normaliser sums the bf16 weights that P V actually uses
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float r[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        bf16x2 pair;
+        pair[0] = pb[kb][h][2 * e];
+        pair[1] = pb[kb][h][2 * e + 1];
+        r[e] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, r[e], false);
+      }
+  lsum += sum_xor32((r[0] + r[1]) + (r[2] + r[3]));
+}
+
+// O^T[d][row] += V^T[d][keys] P^T[keys][row] for the V tile at vt; V^T
+// operands come from LDS transpose reads of the row-major V tile
+__device__ __forceinline__ void pv_tile(f32x16 (&oacc)[4], const bf16x8 (&pb)[2][2], const unsigned char* vt,
+                                        int lane) {
+  const int gi = lane >> 4, li = lane & 15;
+  const int vh = gi >> 1, vdh = gi & 1;
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const int d = db * 32 + 16 * vdh + 4 * (li & 3);
+    const int chunk = d >> 3, h8 = (d >> 2) & 1;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int key0 = kb * 32 + 16 * ks + 4 * vh + (li >> 2);
+        const int key1 = key0 + 8;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (SA_LDS i16x4*)(vt + key0 * 256 + ((chunk ^ vsw(key0)) << 4) + h8 * 8));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (SA_LDS i16x4*)(vt + key1 * 256 + ((chunk ^ vsw(key1)) << 4) + h8 * 8));
+        const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kb][ks], oacc[db], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// Q rows of this lane as the B operand of S^T = K Q^T, pre-scaled by
+// log2(e)/sqrt(128): lane holds Q[qpos][16 ks + 8 half .. +8] * c
+__device__ __forceinline__ void load_q(bf16x8 (&qreg)[8], const __bf16* qp, bool qvalid, int half) {
+  constexpr float c = kLog2e * 0.08838834764831845f;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    u32x4 x = qvalid ? *reinterpret_cast<const u32x4*>(qp + ks * 16 + half * 8) : u32x4{0, 0, 0, 0};
+    qreg[ks] = __builtin_bit_cast(bf16x8, x);
+  }
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qreg[ks][e] = (__bf16)((float)qreg[ks][e] * c);
+}
+
+// o = u / l in bf16 and lse = ln(sum_j exp(s_j / sqrt(d))) for this lane's row
+__device__ __forceinline__ void store_row(const f32x16 (&oacc)[4], float m, float lsum, __bf16* op, float* lse,
+                                          int half) {
+  const float inv = 1.f / lsum;
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      bf16x4 ov;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(oacc[db][i4 * 4 + e] * inv);
+      const int d = db * 32 + 8 * i4 + 4 * half;
+      *reinterpret_cast<bf16x4*>(op + d) = ov;
+    }
+  }
+  if (lse && half == 0) *lse = (m + __log2f(lsum)) * 0.6931471805599453f;
+}
+
+// --------------------------------------------------------------------------
+// Lock-step kernel.  PIPE = 0: one stage, loads then compute; PIPE = 2: one
+// stage, V(t) and K(t+1) loads overlap S(t) / softmax / P V(t); PIPE = R >= 3:
+// an (R-1)-stage ring, tile t+R-2 is issued while tile t is computed.
 template <int HPR, int PIPE>
 __global__ void __launch_bounds__(128 * HPR) prefill_bf16_kernel(Geom g, FwdBufs a, int xcd_run) {
   constexpr int NBUF = PIPE >= 3 ? PIPE - 1 : 1;
@@ -98,7 +259,6 @@ __global__ void __launch_bounds__(128 * HPR) prefill_bf16_kernel(Geom g, FwdBufs
   const int half = lane / 32, l32 = lane % 32;
   const int qpos = ri.r * kBlock + (wave % 2) * 32 + l32;
   const bool qvalid = qpos < ri.len;
-  const __bf16* q = (const __bf16*)a.q;
   const unsigned char* kbytes = (const unsigned char*)a.k;
   const unsigned char* vbytes = (const unsigned char*)a.v;
 
@@ -107,6 +267,11 @@ __global__ void __launch_bounds__(128 * HPR) prefill_bf16_kernel(Geom g, FwdBufs
   // with readlane so the loop issues no memory load (and no wait) for them
   const int jl0 = lane < ntiles ? a.col_idx[t_begin + lane] : 0;
   const int jl1 = lane + 64 < ntiles ? a.col_idx[t_begin + 64 + lane] : 0;
+  // Consume the loads here, on every path: the compiler's wait-count pass is
+  // path-insensitive, and a register that may still be pending at the loop
+  // header makes it wait for all vector loads (the tile prefetch included)
+  // inside the loop on every iteration.
+  asm volatile("" ::"v"(jl0), "v"(jl1));
   auto tile_id = [&](int it) {
     return it < 64 ? __builtin_amdgcn_readlane(jl0, it) : __builtin_amdgcn_readlane(jl1, it - 64);
   };
@@ -153,29 +318,17 @@ __global__ void __launch_bounds__(128 * HPR) prefill_bf16_kernel(Geom g, FwdBufs
     }
   }
 
-  // Q as the B operand of S^T = K Q^T: lane holds Q[qpos][16 ks + 8 half .. +8]
   bf16x8 qreg[8];
-  {
-    const __bf16* qp = q + q_offset(g, ri.s, head, ri.tok0, qvalid ? qpos : 0);
+  load_q(qreg, (const __bf16*)a.q + q_offset(g, ri.s, head, ri.tok0, qvalid ? qpos : 0), qvalid, half);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      u32x4 x = qvalid ? *reinterpret_cast<const u32x4*>(qp + ks * 16 + half * 8) : u32x4{0, 0, 0, 0};
-      qreg[ks] = __builtin_bit_cast(bf16x8, x);
-    }
-  }
+  for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(qreg[ks]));   // see the tile ids above
 
-  const float c2 = kLog2e * 0.08838834764831845f;   // log2(e) / sqrt(128)
-  // m is kept in raw score units; it is raised only when a row max grows by
-  // more than 8 / c2 (exp2 headroom 2^8), so most tiles skip the rescale.
-  const float grow = 8.0f / c2;
   float m = -INFINITY, lsum = 0.f;
   f32x16 oacc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
-
-  // per-lane transpose-read geometry: 16-lane group gi = lane / 16
-  const int gi = lane >> 4, li = lane & 15;
-  const int vh = gi >> 1, vdh = gi & 1;
+  f32x16 sacc[2];
+  bf16x8 pb[2][2];
 
   for (int it = 0; it < ntiles; ++it) {
     const int buf = NBUF > 1 ? it % NBUF : 0;
@@ -208,114 +361,185 @@ __global__ void __launch_bounds__(128 * HPR) prefill_bf16_kernel(Geom g, FwdBufs
       block_barrier();
     }
     const int j = tile_id(it);
-
-    // S^T[key][row] for keys kb*32 + (8*(i/4) + 4*half + i%4), row = l32
-    f32x16 sacc[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sacc[kb] = f32x16{};
-      const int key = kb * 32 + l32;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const int c = ks * 2 + half;
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(kt + key * 256 + ((c ^ ksw(key)) << 4));
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[ks], sacc[kb], 0, 0, 0);
-      }
-    }
+    s_tile(sacc, kt, qreg, m, l32, half);
     if (PIPE == 2 && it + 1 < ntiles) {
       block_barrier();          // every wave has read K(it): refill it with K(it+1)
       issue_k(it + 1, kt);
     }
-    if (j == ri.r || j * kBlock + kBlock > ri.len) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kpos = j * kBlock + kb * 32 + 8 * (i / 4) + 4 * half + (i % 4);
-          if (kpos > qpos || kpos >= ri.len) sacc[kb][i] = -INFINITY;
-        }
-      }
-    }
-    float mt = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sacc[kb][i]);
-    mt = max_xor32(mt);
-    if (__any(mt > m + grow)) {           // some row's max grew: move to the new max
-      const float mnew = fmaxf(m, mt);
-      const float msafe = mnew == -INFINITY ? 0.f : mnew;
-      const float alpha = __builtin_amdgcn_exp2f((m - msafe) * c2);
-      lsum *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-      m = mnew;
-    }
-    const float moff = -(m == -INFINITY ? 0.f : m) * c2;
-    float rs = 0.f;
-    bf16x8 pb[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c2, moff));
-        rs += p;
-        pb[kb][i / 8][i % 8] = (__bf16)p;
-      }
-    }
-    rs = sum_xor32(rs);
-    lsum += rs;
-
+    softmax_tile(sacc, pb, oacc, m, lsum, j == ri.r || j * kBlock + kBlock > ri.len, j * kBlock, qpos, ri.len,
+                 half);
     if (PIPE == 2) {
       // V(it) landed; K(it+1) may still be in flight
       if (it + 1 < ntiles) wait_vmcnt<HALF_LOADS>();
       else wait_vmcnt<0>();
       block_barrier();
     }
-    // O^T[d][row] += V^T[d][keys] P^T[keys][row]; k-slot (half, e) of step
-    // (kb, ks) is key kb*32 + 16 ks + 8 (e/4) + 4 half + e%4, matching the
-    // P^T values this lane holds in sacc[kb][8 ks + e].
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const int d = db * 32 + 16 * vdh + 4 * (li & 3);
-      const int chunk = d >> 3, h8 = (d >> 2) & 1;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int key0 = kb * 32 + 16 * ks + 4 * vh + (li >> 2);
-          const int key1 = key0 + 8;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (SA_LDS i16x4*)(vt + key0 * 256 + ((chunk ^ vsw(key0)) << 4) + h8 * 8));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (SA_LDS i16x4*)(vt + key1 * 256 + ((chunk ^ vsw(key1)) << 4) + h8 * 8));
-          const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kb][ks], oacc[db], 0, 0, 0);
-        }
-      }
-    }
+    pv_tile(oacc, pb, vt, lane);
     if (PIPE != 2) block_barrier();   // every wave is done with this stage before it is refilled
   }
 
-  if (qvalid) {
-    const float inv = 1.f / lsum;
-    __bf16* op = (__bf16*)a.o + q_offset(g, ri.s, head, ri.tok0, qpos);
+  if (qvalid)
+    store_row(oacc, m, lsum, (__bf16*)a.o + q_offset(g, ri.s, head, ri.tok0, qpos),
+              a.lse ? a.lse + lse_offset(g, ri.s, head, ri.tok0, qpos) : nullptr, half);
+}
+
+// --------------------------------------------------------------------------
+// Ping-pong bf16 prefill kernel for rows of four query heads (8 wavefronts).
+//
+// At ~200 VGPRs a SIMD holds two wavefronts, and in an 8-wavefront workgroup
+// they are waves w and w + 4 of the same row.  Run in lock step, both would
+// issue MFMAs at the same time and then both run the softmax on the vector ALU,
+// so the two units never overlap.  Here waves 0-3 (group 0) and 4-7 (group 1)
+// run half a tile apart: the tile loop is cut into slots separated by
+// barriers, and in every slot one group runs an MFMA phase while the other
+// runs a softmax phase.
+//   phases of one wavefront: S(0) X(0) M(0) X(1) M(1) ... X(n-1) M(n-1), where
+//     S(t) = K(t) Q^T (MFMA), X(t) = mask / max / exp / sum of tile t (VALU),
+//     M(t) = P(t) V(t) followed by S(t+1) (MFMA);
+//   group g runs phase p in slot p + g, slots 0 .. 2n+1.
+// K and V have separate NB-deep LDS rings.  Load round r = {K(r), V(r-1)}:
+// rounds 0 .. NB-1 are issued before the loop and round u+NB-1 right after the
+// barrier that opens slot 2u (u >= 1), when K(u-1) and V(u-2) have had their
+// last reads (slot 2u-1).  Round u is waited for before slot 2u, the first
+// slot that reads K(u) or V(u-1).
+template <int N>
+__device__ __forceinline__ void wait_vm_halves(int halves) {
+  // N = loads per half tile per wavefront; at most 7 half tiles in flight
+  switch (halves) {
+    case 7: wait_vmcnt<7 * N>(); break;
+    case 6: wait_vmcnt<6 * N>(); break;
+    case 5: wait_vmcnt<5 * N>(); break;
+    case 4: wait_vmcnt<4 * N>(); break;
+    case 3: wait_vmcnt<3 * N>(); break;
+    case 2: wait_vmcnt<2 * N>(); break;
+    case 1: wait_vmcnt<N>(); break;
+    default: wait_vmcnt<0>(); break;
+  }
+}
+
+template <int NB>
+__global__ void __launch_bounds__(512) prefill_bf16_pp_kernel(Geom g, FwdBufs a, int xcd_run) {
+  constexpr int NW = 8, D = 128;
+  constexpr int TILE = 64 * D * 2;
+  constexpr int HALF_LOADS = (TILE / 1024) / NW;   // 1 KB wave loads per K (or V) tile per wave
+  static_assert(NB >= 3 && NB <= 4, "ring depth");
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * NB * TILE];
+  unsigned char* const kring = lds;
+  unsigned char* const vring = lds + NB * TILE;
+
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int grp = wave >> 2;
+  const int64_t pos = xcd_schedule(blockIdx.x, g.rows, xcd_run);
+  const int64_t row = a.row_perm[g.rows - 1 - pos];   // longest rows first
+  const RowInfo ri = decode_row(g, row);
+  const int kvh = g.share ? ri.h : ri.h / g.group;
+  const int head = (g.share ? ri.h * g.group : ri.h) + wave / 2;
+  const int half = lane / 32, l32 = lane % 32;
+  const int qpos = ri.r * kBlock + (wave % 2) * 32 + l32;
+  const bool qvalid = qpos < ri.len;
+  const unsigned char* kbytes = (const unsigned char*)a.k;
+  const unsigned char* vbytes = (const unsigned char*)a.v;
+
+  const int t_begin = a.row_ptr[row], ntiles = a.row_ptr[row + 1] - t_begin;
+  const int jl0 = lane < ntiles ? a.col_idx[t_begin + lane] : 0;
+  const int jl1 = lane + 64 < ntiles ? a.col_idx[t_begin + 64 + lane] : 0;
+  asm volatile("" ::"v"(jl0), "v"(jl1));   // consumed on every path (see prefill_bf16_kernel)
+  auto tile_id = [&](int it) {
+    return it < 64 ? __builtin_amdgcn_readlane(jl0, it) : __builtin_amdgcn_readlane(jl1, it - 64);
+  };
+
+  const int sub = lane >> 4, cl = lane & 15;
+  auto issue_half = [&](int it, const unsigned char* src, unsigned char* dst, bool is_v) {
+    const int j = tile_id(it);
+    const int cnt = min(kBlock, ri.len - j * kBlock);
+    const int64_t off = kv_offset(g, ri.s, kvh, ri.tok0, j * kBlock) * 2;
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
+    for (int i = wave; i < 16; i += NW) {
+      const int key = 4 * i + sub;
+      const int kc = min(key, cnt - 1);      // rows past the end: any valid row (masked later)
+      const int sw = is_v ? vsw(key) : ksw(key);
+      load_lds16(src + off + kc * 256 + ((cl ^ sw) << 4), dst + i * 1024);
+    }
+  };
+  auto issue_round = [&](int r) {
+    if (r < ntiles) issue_half(r, kbytes, kring + (r % NB) * TILE, false);
+    if (r >= 1) issue_half(r - 1, vbytes, vring + ((r - 1) % NB) * TILE, true);
+  };
+  // half rounds issued after round u, when rounds 0 .. hi are out
+  auto younger_halves = [&](int u, int hi) {
+    if (hi <= u) return 0;
+    return 2 * (hi - u) - (hi == ntiles ? 1 : 0);
+  };
+  if (ntiles > 0) issue_round(0);
+
+  bf16x8 qreg[8];
+  load_q(qreg, (const __bf16*)a.q + q_offset(g, ri.s, head, ri.tok0, qvalid ? qpos : 0), qvalid, half);
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        bf16x4 ov;
+  for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(qreg[ks]));
+  if (ntiles > 0) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(oacc[db][i4 * 4 + e] * inv);
-        const int d = db * 32 + 8 * i4 + 4 * half;
-        *reinterpret_cast<bf16x4*>(op + d) = ov;
+    for (int r = 1; r < NB; ++r)
+      if (r <= ntiles) issue_round(r);
+  }
+
+  float m = -INFINITY, lsum = 0.f;
+  f32x16 oacc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
+  f32x16 sacc[2];
+  bf16x8 pb[2][2];
+
+  // Both groups run  M(u) | barrier | X(u) | barrier  for u = 0 .. n, with
+  // M(u) = P(u-1) then S(u); group 1 passes one barrier before its first
+  // M and group 0 one after its last X, which sets the half-tile offset.  In
+  // the global barrier count, group 0's M(u) follows barrier 2u and group 1's
+  // follows barrier 2u+1; round u is waited for before barrier 2u and round
+  // u+NB-1 issued right after it.
+  auto wait_round = [&](int u) {
+    const int hi = min(max(NB - 1, u + NB - 2), ntiles);
+    wait_vm_halves<HALF_LOADS>(younger_halves(u, hi));
+  };
+  auto issue_after = [&](int u) {   // right after barrier 2u
+    if (u >= 1 && u + NB - 1 <= ntiles) issue_round(u + NB - 1);
+  };
+  if (ntiles > 0) {
+    if (grp == 1) {
+      wait_round(0);
+      block_barrier();                               // barrier 0
+    }
+    for (int u = 0; u <= ntiles; ++u) {
+      if (grp == 0) {
+        wait_round(u);
+        block_barrier();                             // barrier 2u
+        issue_after(u);
+      } else {
+        block_barrier();                             // barrier 2u+1
+      }
+      if (u >= 1) pv_tile(oacc, pb, vring + ((u - 1) % NB) * TILE, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      if (u < ntiles) s_tile(sacc, kring + (u % NB) * TILE, qreg, m, l32, half);
+      if (grp == 0) {
+        block_barrier();                             // barrier 2u+1
+      } else if (u < ntiles) {
+        wait_round(u + 1);
+        block_barrier();                             // barrier 2u+2
+        issue_after(u + 1);
+      } else {
+        block_barrier();                             // barrier 2n+2
+      }
+      if (u < ntiles) {
+        const int j = tile_id(u);
+        softmax_tile(sacc, pb, oacc, m, lsum, j == ri.r || j * kBlock + kBlock > ri.len, j * kBlock, qpos,
+                     ri.len, half);
       }
     }
-    if (a.lse && half == 0)
-      a.lse[lse_offset(g, ri.s, head, ri.tok0, qpos)] = m * 0.08838834764831845f + logf(lsum);
+    if (grp == 0) block_barrier();                   // barrier 2n+2
   }
+
+  if (qvalid)
+    store_row(oacc, m, lsum, (__bf16*)a.o + q_offset(g, ri.s, head, ri.tok0, qpos),
+              a.lse ? a.lse + lse_offset(g, ri.s, head, ri.tok0, qpos) : nullptr, half);
 }
 
 // --------------------------------------------------------------------------
@@ -407,16 +631,19 @@ int launch_prefill(const Geom& g, int dtype, const FwdBufs& b, hipStream_t st) {
   if (dtype == SA_F32) return launch_f32(g, b, st);
   if (g.d != 128) return SA_ERR_UNSUPPORTED;
   dim3 grid((unsigned)g.rows);
-  // One LDS stage (32 KB) per workgroup: four MHA workgroups fit on a CU, so
-  // each SIMD runs two wavefronts from different workgroups whose softmax and
-  // MFMA phases interleave.  Measured on MI355X this beats a 2-4 stage ring
-  // (64-128 KB, fewer workgroups per CU) for both MHA and 4-head GQA rows; MHA
-  // rows gain a little more from overlapping V(t) / K(t+1) with compute.
-  const int run = 32;   // rows per XCD run
+  // One-head rows: one LDS stage (32 KB) per workgroup, so four workgroups fit
+  // on a CU and each SIMD runs two wavefronts of different rows; V(t) and
+  // K(t+1) loads overlap S(t) and the softmax.  Measured on MI355X this beats
+  // a 2-4 stage ring (64-128 KB, fewer workgroups per CU).  Runs of 128 rows
+  // per XCD keep one head's K/V (4 MB at n = 8192) in that XCD's L2.
+  // Four-head rows: the ping-pong kernel with 4-deep K and V rings (128 KB, one
+  // workgroup per CU); its two wavefronts per SIMD alternate MFMA and softmax
+  // phases.  Two-head rows: the lock-step kernel, one stage.
+  const int run = g.hpr == 1 ? 128 : 32;   // rows per XCD run
   switch (g.hpr) {
     case 1: prefill_bf16_kernel<1, 2><<<grid, 128, 0, st>>>(g, b, run); break;
     case 2: prefill_bf16_kernel<2, 0><<<grid, 256, 0, st>>>(g, b, run); break;
-    case 4: prefill_bf16_kernel<4, 0><<<grid, 512, 0, st>>>(g, b, run); break;
+    case 4: prefill_bf16_pp_kernel<4><<<grid, 512, 0, st>>>(g, b, run); break;
     default: return SA_ERR_UNSUPPORTED;
   }
   return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;

@@ -14,7 +14,7 @@ import torch
 import dynamic_block_sparse_amd as dbs
 from dynamic_block_sparse_amd import workloads as wk
 
-from parity import TOL, check_output, check_router, check_worklist, run_gpu, sample_rows
+from parity import LSE_TOL, TOL, check_output, check_router, check_worklist, run_gpu, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -39,6 +39,7 @@ def _full_check(w, inp, run, seqs=None, rows=None):
           f"lse max-abs {o['lse_max_abs']:.3e} over {o['n']} values", flush=True)
     assert o["max_abs"] <= mx
     assert o["mean_abs"] <= mean
+    assert o["lse_max_abs"] <= LSE_TOL[w.dtype]
 
 
 SMALL = [
