@@ -87,10 +87,14 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) de
     const int j = __builtin_amdgcn_readlane(jl, t);
     const int cnt = min(kBlock, ri.len - j * kBlock);
     const int64_t off = kv_offset(g, ri.s, kvh, 0, j * kBlock) * 2;
-    // K: A operand of S^T, key = 16 mb + lane % 16, d = 32 ks + 8 grp
-    u32x4 kr[4][4];
+    // K: A operand of S^T, key = 16 mb + lane % 16, d = 32 ks + 8 grp.  The
+    // tile's four 16-key blocks are fetched in two halves (the second after
+    // the first half's MFMAs are issued): at 3 wavefronts per SIMD the
+    // kernel has 168 VGPRs, and a whole tile of K operands would spill, and
+    // a scratch reload waits for every load in flight.
+    u32x4 kr[2][4];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
+    for (int mb = 0; mb < 2; ++mb) {
       const int key = min(16 * mb + hs, cnt - 1);   // rows past the end: any valid row (masked)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
@@ -106,12 +110,24 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) de
     // S^T[key = 16 mb + 4 grp + i][head = lane % 16]
     f32x4 sacc[4];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      sacc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int hb = 0; hb < 2; ++hb) {
+      if (hb == 1) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        sacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[mb][ks]), qb[ks],
-                                                          sacc[mb], 0, 0, 0);
+        for (int mb = 0; mb < 2; ++mb) {
+          const int key = min(16 * (mb + 2) + hs, cnt - 1);
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks)
+            kr[mb][ks] = *reinterpret_cast<const u32x4*>(kbytes + off + key * 256 + ks * 64 + grp * 16);
+        }
+      }
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        sacc[2 * hb + mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          sacc[2 * hb + mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[mb][ks]), qb[ks],
+                                                                    sacc[2 * hb + mb], 0, 0, 0);
+      }
     }
     float mt = -INFINITY;
 #pragma unroll

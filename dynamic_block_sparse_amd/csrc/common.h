@@ -125,21 +125,52 @@ template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
 
-// Wave-level reductions (64 lanes) via cross-lane shuffles.
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+// Wave-level reductions (64 lanes; all lanes active, every lane gets the
+// result).  Within each 16-lane row: DPP quad_perm [1,0,3,2] and [2,3,0,1]
+// (partners lane ^ 1, lane ^ 2), then row_half_mirror (lane i <- 7 - i of its
+// 8-lane half) and row_mirror (lane i <- 15 - i), after which every lane holds
+// its row's result; v_permlane16_swap / v_permlane32_swap then combine rows
+// (partners lane ^ 16, lane ^ 32).  All of it stays in the VALU, no LDS.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
 }
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+template <typename Op>
+__device__ __forceinline__ uint32_t row16_reduce(uint32_t x, Op op) {
+  x = op(x, dpp_u<0xB1>(x));
+  x = op(x, dpp_u<0x4E>(x));
+  x = op(x, dpp_u<0x141>(x));
+  x = op(x, dpp_u<0x140>(x));
+  return x;
 }
-__device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+template <typename Op>
+__device__ __forceinline__ uint32_t pair16(uint32_t x, Op op) {
+  const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return op(r[0], r[1]);
+}
+template <typename Op>
+__device__ __forceinline__ uint32_t pair32(uint32_t x, Op op) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return op(r[0], r[1]);
+}
+struct OpAddF { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return __float_as_uint(__uint_as_float(a) + __uint_as_float(b)); } };
+struct OpMaxF { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b))); } };
+struct OpAddI { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; } };
+struct OpMinU { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return min(a, b); } };
+struct OpMaxU { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return max(a, b); } };
+
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t x, Op op) {
+  return pair32(pair16(row16_reduce(x, op), op), op);
+}
+__device__ __forceinline__ float wave_max(float v) { return __uint_as_float(wave_reduce(__float_as_uint(v), OpMaxF{})); }
+__device__ __forceinline__ float wave_sum(float v) { return __uint_as_float(wave_reduce(__float_as_uint(v), OpAddF{})); }
+__device__ __forceinline__ int wave_sum_i(int v) { return (int)wave_reduce((uint32_t)v, OpAddI{}); }
+__device__ __forceinline__ uint32_t wave_min_u(uint32_t v) { return wave_reduce(v, OpMinU{}); }
+__device__ __forceinline__ uint32_t wave_max_u(uint32_t v) { return wave_reduce(v, OpMaxU{}); }
+// sum over each 32-lane half of the wave
+__device__ __forceinline__ float half_sum(float v) {
+  return __uint_as_float(pair16(row16_reduce(__float_as_uint(v), OpAddF{}), OpAddF{}));
 }
 
 __device__ __forceinline__ int wave_incl_scan_i(int v) {

@@ -11,8 +11,10 @@ int launch_cu_blocks(const int32_t* cu_seqlens, int32_t* cu_blocks, int batch, h
 int launch_summary(const Geom& g, int dtype, const void* k, float* summ, int slots,
                    hipStream_t st);
 size_t route_smem_bytes(const Geom& g, int qpool);
+// Candidate scores of every row: [rows, max_blocks] fp32 (workspace).
+size_t route_scores_bytes(const Geom& g);
 int launch_route(const Geom& g, const sa_route_cfg& rc, int dtype, const void* q,
-                 const float* summ, int32_t* J, hipStream_t st);
+                 const float* summ, float* scores, int32_t* J, hipStream_t st);
 
 struct WorklistBufs {
   const int32_t* J;

@@ -6,6 +6,8 @@
 // is a fixed branch.  [P2] §4: shared GQA routing averages over the head group.
 // [P1] (top-k of long candidate lists): select without materialising a sort,
 // with a stable rule for equal scores (lower block id first).
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -50,7 +52,7 @@ __global__ void __launch_bounds__(256) summary_kernel(Geom g, const T* __restric
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   const T* base = k + kv_offset(g, s, h, tok0, j * kBlock) + c * 8;
-  for (int t = ph; t < cnt; t += PH) {
+  auto add_row = [&](int t) {
     const T* p = base + (int64_t)t * D;
     if constexpr (sizeof(T) == 2) {
       u32x4 x = *reinterpret_cast<const u32x4*>(p);
@@ -68,11 +70,21 @@ __global__ void __launch_bounds__(256) summary_kernel(Geom g, const T* __restric
         acc[4 + i] += x1[i];
       }
     }
+  };
+  if (cnt == kBlock) {
+    // full block: every row's load is issued before the sums need them
+#pragma unroll
+    for (int t = 0; t < kBlock / PH; ++t) add_row(ph + t * PH);
+  } else {
+    for (int t = ph; t < cnt; t += PH) add_row(t);
   }
+  // sum the key phases: partners lane ^ 8 (D = 64 only), ^ 16, ^ 32
 #pragma unroll
-  for (int o = CH; o < kWave; o <<= 1) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] += __shfl_xor(acc[i], o, kWave);
+  for (int i = 0; i < 8; ++i) {
+    uint32_t u = __float_as_uint(acc[i]);
+    if constexpr (CH <= 8) u = OpAddF{}(u, dpp_u<0x128>(u));   // row_ror:8 = lane ^ 8 in a 16-lane row
+    u = pair32(pair16(u, OpAddF{}), OpAddF{});
+    acc[i] = __uint_as_float(u);
   }
   if (ph == 0) {
     const float inv = 1.f / (float)cnt;
@@ -88,105 +100,80 @@ __global__ void __launch_bounds__(256) summary_kernel(Geom g, const T* __restric
   }
 }
 
-// ---------------------------------------------------------------------------
-// Block-wide helpers for 256-thread workgroups.
-__device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = __lane_id();
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int t = __shfl_up(v, o, kWave);
-    if (lane >= o) v += t;
-  }
-  return v;
-}
-
-// Exclusive scan over the 256 threads; returns the prefix, *total = sum.
-__device__ __forceinline__ int block_excl_scan256(int v, int* sh /* >= 4 ints */, int* total) {
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  int inc = wave_incl_scan(v);
-  __syncthreads();
-  if (lane == kWave - 1) sh[wave] = inc;
-  __syncthreads();
-  int before = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    int x = sh[w];
-    before += (w < wave) ? x : 0;
-    tot += x;
-  }
-  *total = tot;
-  return before + inc - v;
-}
-
-__device__ __forceinline__ float block_max256(float v, float* sh) {
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  v = wave_max(v);
-  __syncthreads();
-  if (lane == 0) sh[wave] = v;
-  __syncthreads();
-  return fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
-}
-
 __device__ __forceinline__ uint32_t order_key(float x) {
   uint32_t u = __float_as_uint(x + 0.0f);   // -0 -> +0 so equal values share a key
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
 // ---------------------------------------------------------------------------
-// Routing: one 256-thread workgroup per worklist row.
-//   1. pool the row's queries (mean: one pooled vector over the row's query
-//      heads and valid queries; max: per-query scores, max per head, mean
-//      over heads)
-//   2. score every complete-history candidate block against the summaries
-//   3. pick the budget (top-k or Eq 7) and select the top D by
-//      (score desc, id asc) with an MSB-first radix select on order-preserving
-//      score keys, then emit the picks in ascending id order
-template <typename T, int D>
-__global__ void __launch_bounds__(256) route_kernel(Geom g, sa_route_cfg rc, const T* __restrict__ q,
-                                                    const float* __restrict__ summ,
-                                                    int32_t* __restrict__ J) {
+// Per-row routing context: candidates are the complete history blocks j < r
+// (decode: j < N-1) other than the forced ones; candidate i is block start + i.
+struct RouteRow {
+  RowInfo ri;
+  int kvh, h0, qt0, nq, cur, start, nc, nforced;
+  bool ff;
+};
+
+__device__ __forceinline__ RouteRow route_row(const Geom& g, const sa_route_cfg& rc, int64_t row) {
+  RouteRow w;
+  w.ri = decode_row(g, row);
+  w.kvh = g.share ? w.ri.h : w.ri.h / g.group;
+  w.h0 = g.share ? w.ri.h * g.group : w.ri.h;
+  if (g.mode == SA_DECODE) {
+    w.qt0 = 0;
+    w.nq = 1;
+  } else {
+    w.qt0 = w.ri.r * kBlock;
+    w.nq = min(kBlock, w.ri.len - w.qt0);
+  }
+  w.cur = w.ri.r;
+  w.ff = (rc.forced & SA_FORCE_FIRST) != 0;
+  const int n_hist = (g.mode == SA_DECODE) ? w.ri.nblk - 1 : w.ri.r;   // blocks j < current
+  w.start = (w.ff && n_hist > 0) ? 1 : 0;
+  w.nc = max(n_hist - w.start, 0);
+  w.nforced = 1 + ((w.ff && w.cur != 0) ? 1 : 0);
+  return w;
+}
+
+// Decode rows (few, with long histories) split their candidates into chunks
+// of kDecodeChunk, one workgroup each; prefill rows are many and take one.
+constexpr int kDecodeChunk = 512;
+
+// ---------------------------------------------------------------------------
+// Routing scores: one 256-thread workgroup per (worklist row, chunk of
+// `chunk` candidates).
+//   mean pool: one pooled vector over the row's query heads and valid
+//     queries, dotted with every candidate summary;
+//   max pool: per-query scores, max over the block's queries, mean over heads.
+// Scores land in scores[row * max_blocks + i] for candidate i.
+template <typename T, int D, int U>
+__global__ void __launch_bounds__(256) route_score_kernel(Geom g, sa_route_cfg rc, const T* __restrict__ q,
+                                                          const float* __restrict__ summ,
+                                                          float* __restrict__ scores, int chunk) {
   extern __shared__ float smem[];
-  float* sc = smem;                                  // [max_blocks] candidate scores
-  float* qbar = sc + ((g.max_blocks + 3) & ~3);      // [D]
-  float* red = qbar + D;                             // [16 * D] phase partials / max-pool rows
-  __shared__ int ishare[8];
-  __shared__ float fshare[4];
-  __shared__ int hist[256];
-  __shared__ uint32_t sel_state[2];
+  float* qbar = smem;          // [D]
+  float* red = qbar + D;       // [16 * D] phase partials / max-pool rows
 
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int64_t row = blockIdx.x;
-  const RowInfo ri = decode_row(g, row);
-  const int kvh = g.share ? ri.h : ri.h / g.group;
-  const int h0 = g.share ? ri.h * g.group : ri.h;
+  const RouteRow w = route_row(g, rc, row);
+  const int c0 = blockIdx.y * chunk, c1 = min(w.nc, c0 + chunk);
+  if (c0 >= c1) return;   // uniform: the whole workgroup leaves
   const int nh = g.hpr;
-  int qt0, nq;
-  if (g.mode == SA_DECODE) {
-    qt0 = 0;
-    nq = 1;
-  } else {
-    qt0 = ri.r * kBlock;
-    nq = min(kBlock, ri.len - qt0);
-  }
-  const int cur = ri.r;
-  const bool ff = (rc.forced & SA_FORCE_FIRST) != 0;
-  const int n_hist = (g.mode == SA_DECODE) ? ri.nblk - 1 : ri.r;   // blocks j < current
-  const int start = (ff && n_hist > 0) ? 1 : 0;
-  const int nc = max(n_hist - start, 0);
-  const int nforced = 1 + ((ff && cur != 0) ? 1 : 0);
-  const float* cbase = summ + sum_offset(g, ri.s, kvh, ri.blk0, 0);
+  const float* cbase = summ + sum_offset(g, w.ri.s, w.kvh, w.ri.blk0, 0);
+  float* srow = scores + row * (int64_t)g.max_blocks;
 
   if (rc.qpool == SA_POOL_MEAN) {
-    // ---- 1. mean pool over (head, query) pairs
+    // ---- mean pool over (head, query) pairs
     constexpr int CH = D / 8, PH = 256 / CH;
     const int c = tid % CH, ph = tid / CH;
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    const int items = nh * nq;
+    const int items = nh * w.nq;
     for (int it = ph; it < items; it += PH) {
-      const int hh = h0 + it / nq, t = it % nq;
-      const T* p = q + q_offset(g, ri.s, hh, ri.tok0, qt0 + t) + c * 8;
+      const int hh = w.h0 + it / w.nq, t = it % w.nq;
+      const T* p = q + q_offset(g, w.ri.s, hh, w.ri.tok0, w.qt0 + t) + c * 8;
       if constexpr (sizeof(T) == 2) {
         u32x4 x = *reinterpret_cast<const u32x4*>(p);
 #pragma unroll
@@ -213,146 +200,160 @@ __global__ void __launch_bounds__(256) route_kernel(Geom g, sa_route_cfg rc, con
       qbar[tid] = sacc / (float)items;
     }
     __syncthreads();
-    // ---- 2. scores: LPC lanes cooperate on one candidate (4 floats each)
+    // ---- scores: LPC lanes cooperate on one candidate (4 floats each).
+    // U candidates per lane group are loaded before any is reduced, so a
+    // wavefront keeps U x 1 KB of summary reads in flight (U = 16 for the
+    // long, HBM-resident decode histories; 8 for prefill rows, whose
+    // summaries are shared through L2 and whose candidate lists are short).
     constexpr int LPC = D / 4, CPS = kWave / LPC;
     const int cl = lane % LPC, cw = lane / LPC;
     const f32x4 qv = *reinterpret_cast<const f32x4*>(qbar + cl * 4);
-    for (int base = wave * CPS; base < nc; base += 4 * CPS) {
-      const int j = start + base + cw;
-      float part = 0.f;
-      if (base + cw < nc) {
-        const f32x4 cv = *reinterpret_cast<const f32x4*>(cbase + (int64_t)j * D + cl * 4);
-        part = qv[0] * cv[0] + qv[1] * cv[1] + qv[2] * cv[2] + qv[3] * cv[3];
+    for (int base = c0 + wave * CPS; base < c1; base += 4 * CPS * U) {
+      float part[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        // unconditional load of a clamped candidate: a guarded load would be
+        // waited for before the next one is issued
+        const int ci = base + u * 4 * CPS + cw;
+        const int cc = min(ci, c1 - 1);
+        const f32x4 cv = *reinterpret_cast<const f32x4*>(cbase + (int64_t)(w.start + cc) * D + cl * 4);
+        part[u] = (qv[0] * cv[0] + qv[1] * cv[1] + qv[2] * cv[2] + qv[3] * cv[3]) * (ci < c1 ? 1.f : 0.f);
       }
 #pragma unroll
-      for (int o = 1; o < LPC; o <<= 1) part += __shfl_xor(part, o, kWave);
-      if (cl == 0 && base + cw < nc) sc[base + cw] = part;
+      for (int u = 0; u < U; ++u) {
+        const int ci = base + u * 4 * CPS + cw;
+        static_assert(LPC == 32 || LPC == 16, "lanes per candidate");
+        float x = part[u];
+        x = LPC == 32 ? half_sum(x) : __uint_as_float(row16_reduce(__float_as_uint(x), OpAddF{}));
+        if (cl == 0 && ci < c1) srow[ci] = x;
+      }
     }
   } else {
-    // ---- max pool: per-query scores, max over the block's queries, mean over heads
-    for (int i = tid; i < nc; i += 256) sc[i] = 0.f;
+    // ---- max pool: per-query scores, max over the block's queries, mean over
+    // heads.  Each wavefront owns candidates c0 + wave, +4, ..., accumulated
+    // over heads in registers (lane 0).
     constexpr int LD = D + 1;
+    const int nmine = (c1 - c0 - wave + 3) / 4;
     for (int hh = 0; hh < nh; ++hh) {
       __syncthreads();
-      for (int e = tid; e < nq * D; e += 256) {
+      for (int e = tid; e < w.nq * D; e += 256) {
         const int t = e / D, dd = e % D;
-        red[t * LD + dd] = to_f32<T>(q[q_offset(g, ri.s, h0 + hh, ri.tok0, qt0 + t) + dd]);
+        red[t * LD + dd] = to_f32<T>(q[q_offset(g, w.ri.s, w.h0 + hh, w.ri.tok0, w.qt0 + t) + dd]);
       }
       __syncthreads();
-      for (int ci = wave; ci < nc; ci += 4) {
-        const float* cj = cbase + (int64_t)(start + ci) * D;
+      for (int k = 0; k < nmine; ++k) {
+        const int ci = c0 + wave + 4 * k;
+        const float* cj = cbase + (int64_t)(w.start + ci) * D;
         float dot = 0.f;
-        if (lane < nq) {
+        if (lane < w.nq) {
           for (int dd = 0; dd < D; ++dd) dot += red[lane * LD + dd] * cj[dd];
         } else {
           dot = -INFINITY;
         }
         dot = wave_max(dot);
-        if (lane == 0) sc[ci] += dot / (float)nh;
+        if (lane == 0) srow[ci] = (hh == 0 ? 0.f : srow[ci]) + dot / (float)nh;
       }
     }
   }
-  __syncthreads();
+}
 
-  // ---- 3. budget
+// ---------------------------------------------------------------------------
+// Selection: one wavefront per worklist row; the row's candidate scores sit
+// in registers as order-preserving keys (E per lane, candidate lane + 64 e).
+//   1. budget: top-k, or Eq 7's clipped count of scores >= max - tau_rel;
+//   2. the D-th largest key T, built bit by bit from the MSB as the largest
+//      value with #(key >= T) >= D (ballot counts, no LDS, no barriers);
+//   3. picks = keys > T plus the lowest-id keys == T, written in ascending id
+//      order from ballot prefix counts; forced blocks first, -1 padding last.
+// Empty key slots hold 0, which no threshold with a set bit counts.
+template <int E>
+__global__ void __launch_bounds__(64) route_select_kernel(Geom g, sa_route_cfg rc, const float* __restrict__ scores,
+                                                          int32_t* __restrict__ J) {
+  const int lane = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const RouteRow w = route_row(g, rc, row);
+  const float* srow = scores + row * (int64_t)g.max_blocks;
+  // Every load is issued unconditionally (clamped to a valid slot) and the
+  // guard applies to the value: a load under a per-slot branch is waited for
+  // before the next branch, which serialises E memory round trips.
+  uint32_t key[E];
+  float mx = -INFINITY;
+  const int last = max(w.nc - 1, 0);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = lane + 64 * e;
+    const float x = srow[min(i, last)];
+    const bool ok = i < w.nc;
+    key[e] = order_key(x) & (ok ? 0xffffffffu : 0u);   // masks, not a branch
+    mx = fmaxf(mx, ok ? x : -INFINITY);
+  }
+  // #(key >= x) over the row: lane counts in four independent chains, then
+  // one wave sum
+  auto count_ge = [&](uint32_t x) {
+    int c[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int e = 0; e < E; ++e) c[e & 3] += key[e] >= x ? 1 : 0;
+    return wave_sum_i((c[0] + c[1]) + (c[2] + c[3]));
+  };
+
   int kr = rc.k_b;
   if (rc.select == SA_SELECT_THRESHOLD) {
-    float m = -INFINITY;
-    for (int i = tid; i < nc; i += 256) m = fmaxf(m, sc[i]);
-    m = block_max256(m, fshare);
-    const float tau = m - rc.tau_rel;
-    int above = 0;
-    for (int i = tid; i < nc; i += 256) above += (sc[i] >= tau) ? 1 : 0;
-    int tot;
-    (void)block_excl_scan256(above, ishare, &tot);
-    const int count = nforced + (nc > 0 ? tot : 0);
-    kr = min(rc.k_b, max(rc.k_min, count));
+    mx = wave_max(mx);
+    const int above = w.nc > 0 ? count_ge(order_key(mx - rc.tau_rel)) : 0;
+    kr = min(rc.k_b, max(rc.k_min, w.nforced + above));
   }
-  const int dsel = min(max(kr - nforced, 0), nc);
-
-  // ---- radix select of the dsel-th largest key (all keys valid candidates)
+  const int dsel = min(max(kr - w.nforced, 0), w.nc);
+  const bool take_all = (dsel == w.nc);
   uint32_t thr = 0u;
   int take_eq = 0;
-  const bool take_all = (dsel == nc);
   if (!take_all && dsel > 0) {
-    uint32_t prefix = 0u, pmask = 0u;
-    int remaining = dsel;
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      for (int i = tid; i < 256; i += 256) hist[i] = 0;
-      __syncthreads();
-      for (int i = tid; i < nc; i += 256) {
-        const uint32_t key = order_key(sc[i]);
-        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
-      }
-      __syncthreads();
-      if (wave == 0) {
-        // lane l owns digits 255-4l .. 252-4l (descending)
-        int cnt[4], local = 0;
+    // T lies in [kmin, kmax]: the bits above their highest difference are
+    // common to every candidate key and need no search
+    uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          cnt[i] = hist[255 - 4 * lane - i];
-          local += cnt[i];
-        }
-        const int incl = wave_incl_scan(local);
-        int above = incl - local;     // keys with a larger digit
-        if (above < remaining && remaining <= incl) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if (above < remaining && remaining <= above + cnt[i]) {
-              sel_state[0] = (uint32_t)(255 - 4 * lane - i);
-              sel_state[1] = (uint32_t)(remaining - above);
-            }
-            above += cnt[i];
-          }
-        }
+    for (int e = 0; e < E; ++e) {
+      if (lane + 64 * e < w.nc) {
+        kmin = min(kmin, key[e]);
+        kmax = max(kmax, key[e]);
       }
-      __syncthreads();
-      prefix |= sel_state[0] << shift;
-      pmask |= 255u << shift;
-      remaining = (int)sel_state[1];
-      __syncthreads();
     }
-    thr = prefix;
-    take_eq = remaining;
+    kmin = wave_min_u(kmin);
+    kmax = wave_max_u(kmax);
+    const uint32_t diff = kmin ^ kmax;
+    const int top = diff ? 31 - __builtin_clz(diff) : -1;
+    uint32_t t = top < 0 ? kmax : top >= 31 ? 0u : (kmax & ~((2u << top) - 1u));
+    for (int bit = top; bit >= 0; --bit) {
+      const uint32_t cand = t | (1u << bit);
+      if (count_ge(cand) >= dsel) t = cand;
+    }
+    thr = t;
+    take_eq = dsel - (t == 0xffffffffu ? 0 : count_ge(t + 1u));
   }
 
-  // ---- emit forced blocks, picks (ascending id) and padding
   int32_t* jrow = J + row * rc.k_b;
-  if (tid == 0) {
-    int w = 0;
-    if (ff && cur != 0) jrow[w++] = 0;
-    jrow[w++] = cur;
+  if (lane == 0) {
+    int k = 0;
+    if (w.ff && w.cur != 0) jrow[k++] = 0;
+    jrow[k++] = w.cur;
   }
   if (dsel > 0) {
-    const int chunk = (nc + 255) / 256;
-    const int c0 = min(tid * chunk, nc), c1 = min(c0 + chunk, nc);
-    // rank of this thread's first equal-to-threshold key among all equal keys
-    int n_eq = 0;
-    if (!take_all)
-      for (int i = c0; i < c1; ++i) n_eq += (order_key(sc[i]) == thr) ? 1 : 0;
-    int tot;
-    const int eq_base = block_excl_scan256(n_eq, ishare, &tot);
-    int n_take = 0;
-    {
-      int e = eq_base;
-      for (int i = c0; i < c1; ++i) {
-        const uint32_t key = order_key(sc[i]);
-        const bool tk = take_all || key > thr || (key == thr && e++ < take_eq);
-        n_take += tk ? 1 : 0;
-      }
-    }
-    int pos = block_excl_scan256(n_take, ishare + 4, &tot);
-    {
-      int e = eq_base;
-      for (int i = c0; i < c1; ++i) {
-        const uint32_t key = order_key(sc[i]);
-        const bool tk = take_all || key > thr || (key == thr && e++ < take_eq);
-        if (tk) jrow[nforced + pos++] = start + i;
-      }
+    const uint64_t below = (1ull << lane) - 1ull;
+    int pos = 0, eq_seen = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int i = lane + 64 * e;
+      const bool valid = i < w.nc;
+      const bool eq = !take_all && valid && key[e] == thr;
+      const uint64_t beq = __ballot(eq);
+      const int eq_rank = eq_seen + __popcll(beq & below);
+      const bool take = valid && (take_all || key[e] > thr || (eq && eq_rank < take_eq));
+      const uint64_t bt = __ballot(take);
+      if (take) jrow[w.nforced + pos + __popcll(bt & below)] = w.start + i;
+      pos += __popcll(bt);
+      eq_seen += __popcll(beq);
     }
   }
-  for (int i = nforced + dsel + tid; i < rc.k_b; i += 256) jrow[i] = -1;
+  for (int i = w.nforced + dsel + lane; i < rc.k_b; i += 64) jrow[i] = -1;
 }
 
 // ---------------------------------------------------------------------------
@@ -375,29 +376,44 @@ int launch_summary(const Geom& g, int dtype, const void* k, float* summ, int slo
 }
 
 size_t route_smem_bytes(const Geom& g, int qpool) {
-  const size_t sc = (size_t)((g.max_blocks + 3) & ~3) * 4;
   const size_t qb = (size_t)g.d * 4;
   const size_t mean_red = (size_t)(256 / (g.d / 8)) * g.d * 4;   // phase partials
   const size_t max_red = (size_t)kBlock * (g.d + 1) * 4;         // one head's query rows
-  return sc + qb + (qpool == SA_POOL_MAX ? max_red : mean_red);
+  return qb + (qpool == SA_POOL_MAX ? max_red : mean_red);
 }
 
+size_t route_scores_bytes(const Geom& g) { return (size_t)g.rows * g.max_blocks * sizeof(float); }
+
 int launch_route(const Geom& g, const sa_route_cfg& rc, int dtype, const void* q,
-                 const float* summ, int32_t* J, hipStream_t st) {
+                 const float* summ, float* scores, int32_t* J, hipStream_t st) {
   if (g.rows <= 0) return SA_OK;
   const size_t smem = route_smem_bytes(g, rc.qpool);
-  dim3 grid((unsigned)g.rows);
+  const int chunk = g.mode == SA_DECODE ? kDecodeChunk : std::max(g.max_blocks, 1);
+  const int chunks = (std::max(g.max_blocks, 1) + chunk - 1) / chunk;
+  dim3 grid((unsigned)g.rows, (unsigned)chunks);
+  const bool dec = g.mode == SA_DECODE;
+#define SA_SCORE(T, D)                                                                     \
+  (dec ? route_score_kernel<T, D, 16><<<grid, 256, smem, st>>>(g, rc, (const T*)q, summ, scores, chunk) \
+       : route_score_kernel<T, D, 8><<<grid, 256, smem, st>>>(g, rc, (const T*)q, summ, scores, chunk))
   if (dtype == SA_BF16) {
-    if (g.d == 128)
-      route_kernel<__bf16, 128><<<grid, 256, smem, st>>>(g, rc, (const __bf16*)q, summ, J);
-    else
-      route_kernel<__bf16, 64><<<grid, 256, smem, st>>>(g, rc, (const __bf16*)q, summ, J);
+    if (g.d == 128) SA_SCORE(__bf16, 128);
+    else SA_SCORE(__bf16, 64);
   } else {
-    if (g.d == 128)
-      route_kernel<float, 128><<<grid, 256, smem, st>>>(g, rc, (const float*)q, summ, J);
-    else
-      route_kernel<float, 64><<<grid, 256, smem, st>>>(g, rc, (const float*)q, summ, J);
+    if (g.d == 128) SA_SCORE(float, 128);
+    else SA_SCORE(float, 64);
   }
+#undef SA_SCORE
+  if (hipGetLastError() != hipSuccess) return SA_ERR_HIP;
+  // keys per lane: the smallest power of two with 64 E >= max_blocks
+  dim3 sgrid((unsigned)g.rows);
+  const int mb = std::max(g.max_blocks, 1);
+  if (mb <= 128) route_select_kernel<2><<<sgrid, 64, 0, st>>>(g, rc, scores, J);
+  else if (mb <= 256) route_select_kernel<4><<<sgrid, 64, 0, st>>>(g, rc, scores, J);
+  else if (mb <= 512) route_select_kernel<8><<<sgrid, 64, 0, st>>>(g, rc, scores, J);
+  else if (mb <= 1024) route_select_kernel<16><<<sgrid, 64, 0, st>>>(g, rc, scores, J);
+  else if (mb <= 2048) route_select_kernel<32><<<sgrid, 64, 0, st>>>(g, rc, scores, J);
+  else if (mb <= 4096) route_select_kernel<64><<<sgrid, 64, 0, st>>>(g, rc, scores, J);
+  else route_select_kernel<128><<<sgrid, 64, 0, st>>>(g, rc, scores, J);
   return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 

@@ -10,7 +10,7 @@ namespace sa {
 namespace {
 
 constexpr int kMaxWidth = 128;        // k_b + forced blocks per row
-constexpr int kMaxRouteBlocks = 8192; // candidate scores kept in LDS by the router
+constexpr int kMaxRouteBlocks = 8192; // candidates per row the selection keeps in registers (128 per lane)
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -144,7 +144,9 @@ int resolve_splits(const Plan& pl, int requested) {
 
 size_t ws_size(const Plan& pl, int which, int splits) {
   size_t sz = ws_cu_blocks(pl);
-  if (which == 1) {
+  if (which == 0) {
+    sz += align_up(route_scores_bytes(pl.g));
+  } else if (which == 1) {
     sz += align_up((size_t)pl.g.rows * kMaxWidth * sizeof(int32_t));
     sz += align_up((size_t)pl.g.rows * sizeof(int32_t));
   } else if (which == 2 && pl.g.mode == SA_DECODE) {
@@ -214,7 +216,8 @@ int sparse_attn_route(const sa_problem* p, const sa_route_cfg* rc, const void* q
   if (!summaries_in) {
     if ((st = launch_summary(pl.g, p->dtype, k, summaries, (int)pl.kv_slots, hs)) != SA_OK) return st;
   }
-  return launch_route(pl.g, *rc, p->dtype, q, summaries, J, hs);
+  float* scores = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(ws) + ws_cu_blocks(pl));
+  return launch_route(pl.g, *rc, p->dtype, q, summaries, scores, J, hs);
 }
 
 int sparse_attn_build_worklist(const sa_problem* p, const sa_route_cfg* rc, const int32_t* J,

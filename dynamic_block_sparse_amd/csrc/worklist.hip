@@ -95,49 +95,87 @@ __global__ void __launch_bounds__(64) wl_rows_kernel(Geom g, sa_route_cfg rc, in
     atomicOr(err, (er ? SA_WL_ERR_RANGE : 0) | (ea ? SA_WL_ERR_ACAUSAL : 0));
 }
 
+// Row pointers and the bucket order in one 1024-thread workgroup.  Thread t
+// owns a contiguous chunk of rows; the row-length sum and the per-bucket row
+// counts of every chunk are scanned together (wave scans, then a scan of the
+// 16 wave totals in LDS), so the whole scan costs two barriers.
 __global__ void __launch_bounds__(1024) wl_scan_kernel(int64_t rows, int n_buckets,
                                                        const int32_t* __restrict__ tmp_len,
                                                        int32_t* __restrict__ row_ptr,
                                                        int32_t* __restrict__ row_perm,
                                                        int32_t* __restrict__ bucket_ptr) {
-  __shared__ int sh[16];
-  __shared__ int bucket_base[kMaxBuckets + 1];
-  const int tid = threadIdx.x;
+  constexpr int K = kMaxBuckets + 1;   // [0] length sum, [1 + b] rows in bucket b
+  constexpr int NW = 1024 / kWave;
+  __shared__ int wtot[NW][K];
+  __shared__ int total[K];
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int64_t chunk = (rows + 1023) / 1024;
   const int64_t r0 = min((int64_t)tid * chunk, rows), r1 = min(r0 + chunk, rows);
-  int sum = 0;
-  int cnt[kMaxBuckets];
+  int v[K];
 #pragma unroll
-  for (int b = 0; b < kMaxBuckets; ++b) cnt[b] = 0;
+  for (int k = 0; k < K; ++k) v[k] = 0;
   for (int64_t r = r0; r < r1; ++r) {
     const int len = tmp_len[r];
-    sum += len;
+    v[0] += len;
     const int bk = bucket_of(len);
 #pragma unroll
-    for (int b = 0; b < kMaxBuckets; ++b) cnt[b] += (b == bk) ? 1 : 0;
+    for (int b = 0; b < kMaxBuckets; ++b) v[1 + b] += (b == bk) ? 1 : 0;
   }
-  int total;
-  int run = block_excl_scan<1024>(sum, sh, &total);
+  // inclusive wave scans of all K values
+  int inc[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) inc[k] = v[k];
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int t = __shfl_up(inc[k], o, kWave);
+      if (lane >= o) inc[k] += t;
+    }
+  }
+  if (lane == kWave - 1) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) wtot[wave][k] = inc[k];
+  }
+  __syncthreads();
+  // thread k turns column k of the wave totals into exclusive wave prefixes
+  if (tid < K) {
+    int acc = 0;
+    for (int w = 0; w < NW; ++w) {
+      const int x = wtot[w][tid];
+      wtot[w][tid] = acc;
+      acc += x;
+    }
+    total[tid] = acc;
+  }
+  __syncthreads();
+  int excl[K], tot[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    excl[k] = wtot[wave][k] + inc[k] - v[k];
+    tot[k] = total[k];
+  }
+  // bucket b starts after all rows of buckets < b
+  int base[kMaxBuckets];
+  {
+    int acc = 0;
+#pragma unroll
+    for (int b = 0; b < kMaxBuckets; ++b) {
+      base[b] = acc;
+      acc += (b < n_buckets) ? tot[1 + b] : 0;
+    }
+    if (tid == 0) {
+#pragma unroll
+      for (int b = 0; b < kMaxBuckets; ++b)
+        if (b < n_buckets) bucket_ptr[b] = base[b];
+      bucket_ptr[n_buckets] = acc;
+      row_ptr[rows] = tot[0];
+    }
+  }
+  int run = excl[0];
   int rank[kMaxBuckets];
 #pragma unroll
-  for (int b = 0; b < kMaxBuckets; ++b) {
-    int tb;
-    rank[b] = block_excl_scan<1024>(cnt[b], sh, &tb);
-    if (tid == 0) bucket_base[b] = tb;   // per-bucket totals for now
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int acc = 0;
-    for (int b = 0; b < n_buckets; ++b) {
-      const int c = bucket_base[b];
-      bucket_base[b] = acc;
-      bucket_ptr[b] = acc;
-      acc += c;
-    }
-    bucket_ptr[n_buckets] = acc;
-    row_ptr[rows] = total;
-  }
-  __syncthreads();
+  for (int b = 0; b < kMaxBuckets; ++b) rank[b] = base[b] + excl[1 + b];
   for (int64_t r = r0; r < r1; ++r) {
     const int len = tmp_len[r];
     row_ptr[r] = run;
@@ -147,7 +185,7 @@ __global__ void __launch_bounds__(1024) wl_scan_kernel(int64_t rows, int n_bucke
 #pragma unroll
     for (int b = 0; b < kMaxBuckets; ++b) {
       if (b == bk) {
-        pos = bucket_base[b] + rank[b];
+        pos = rank[b];
         rank[b] += 1;
       }
     }

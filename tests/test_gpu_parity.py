@@ -123,6 +123,54 @@ def test_worklist_adversarial_J(dev):
     assert ref["err"] == dbs.SA_WL_ERR_RANGE | dbs.SA_WL_ERR_ACAUSAL
 
 
+def _oracle_J(w, inp):
+    from oracle import problem as oprob
+    qs, ks, _vs = wk.per_sequence(inp)
+    j_rows, scores = oprob.route(qs, ks, inp.lengths, w.block, w.mode, w.qpool, w.share_gqa, w.select,
+                                 w.k_b, w.k_min, w.tau_rel, w.forced_first)
+    return np.stack([np.asarray(j) for j in j_rows]), scores
+
+
+@pytest.mark.parametrize("pattern", ["all", "even", "pairs"])
+def test_router_exact_ties(dev, pattern):
+    """Exactly equal scores: copies of one key block have bit-identical
+    summaries, so their scores tie exactly on both sides and the selection must
+    take the lowest block ids, row for row ([P2] selection with ties broken by
+    the lower id)."""
+    w = wk.PREFILL_MHA.replace(name=f"router_ties_{pattern}", heads_q=3, heads_kv=3, seqlen=2048, k_b=6)
+    inp = wk.make_inputs(w, dev)
+    kb = inp.k.view(1, 3, 32, 64, 128)
+    if pattern == "all":        # every block equal: picks are blocks 0, 1, 2, ...
+        kb[:, :, 1:] = kb[:, :, :1].clone()
+    elif pattern == "even":     # even blocks tie with each other, odd ones are random
+        kb[:, :, 2::2] = kb[:, :, :1].clone()
+    else:                       # blocks 2m and 2m+1 are equal
+        kb[:, :, 1::2] = kb[:, :, 0::2].clone()
+    run = run_gpu(w, inp)
+    J_ref, scores = _oracle_J(w, inp)
+    checked = 0
+    for i, (g_all, cands, forced) in enumerate(scores):
+        cands = sorted(cands)
+        g = np.sort(np.asarray(g_all, dtype=np.float64)[cands])[::-1]
+        d = int(np.sum(np.asarray(J_ref[i]) >= 0)) - len(forced)   # picks among the candidates
+        if 0 < d < len(g):
+            gap = g[d - 1] - g[d]
+            if gap != 0.0 and gap <= 1e-5 * max(abs(g[d - 1]), 1e-30):
+                continue   # a near tie that fp32 may order either way
+        got, ref = run.J[i], np.asarray(J_ref[i])
+        # the same picks (the oracle lists them by score, the library ascending)
+        assert sorted(got[got >= 0].tolist()) == sorted(ref[ref >= 0].tolist()), (i, got, ref)
+        # layout: forced blocks, then the picks ascending, then -1 padding
+        nf = len(forced)
+        picks = got[nf:][got[nf:] >= 0]
+        assert sorted(got[:nf].tolist()) == sorted(forced) and np.all(np.diff(picks) > 0), (i, got)
+        assert np.all(got[nf + len(picks):] == -1), (i, got)
+        checked += 1
+    assert checked >= len(scores) // 2
+    o = check_output(w, inp, run, list(range(run.J.shape[0])))
+    assert o["max_abs"] <= TOL["bf16"][0]
+
+
 def test_run_to_run_deterministic(dev):
     w = wk.PREFILL_GQA.replace(name="determinism", heads_q=8, heads_kv=2, seqlen=2048, k_b=8)
     inp = wk.make_inputs(w, dev)
