@@ -171,23 +171,46 @@ __global__ void __launch_bounds__(256) route_score_kernel(Geom g, sa_route_cfg r
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
     const int items = nh * w.nq;
-    for (int it = ph; it < items; it += PH) {
-      const int hh = w.h0 + it / w.nq, t = it % w.nq;
-      const T* p = q + q_offset(g, w.ri.s, hh, w.ri.tok0, w.qt0 + t) + c * 8;
+    // UP items per thread are loaded before any is added (clamped to a
+    // valid item, weight 0 past the end), so a row's pooled query costs one
+    // memory round trip per UP items rather than one per item
+    constexpr int UP = 8;
+    for (int it0 = ph; it0 < items; it0 += PH * UP) {
       if constexpr (sizeof(T) == 2) {
-        u32x4 x = *reinterpret_cast<const u32x4*>(p);
+        u32x4 x[UP];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[2 * i] += bf16_lo(x[i]);
-          acc[2 * i + 1] += bf16_hi(x[i]);
+        for (int u = 0; u < UP; ++u) {
+          const int it = min(it0 + u * PH, items - 1);
+          const int hh = w.h0 + it / w.nq, t = it % w.nq;
+          x[u] = *reinterpret_cast<const u32x4*>(q + q_offset(g, w.ri.s, hh, w.ri.tok0, w.qt0 + t) + c * 8);
+        }
+#pragma unroll
+        for (int u = 0; u < UP; ++u) {
+          const float wgt = it0 + u * PH < items ? 1.f : 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[2 * i] += wgt * bf16_lo(x[u][i]);
+            acc[2 * i + 1] += wgt * bf16_hi(x[u][i]);
+          }
         }
       } else {
-        f32x4 x0 = *reinterpret_cast<const f32x4*>(p);
-        f32x4 x1 = *reinterpret_cast<const f32x4*>(p + 4);
+        f32x4 x0[UP], x1[UP];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[i] += x0[i];
-          acc[4 + i] += x1[i];
+        for (int u = 0; u < UP; ++u) {
+          const int it = min(it0 + u * PH, items - 1);
+          const int hh = w.h0 + it / w.nq, t = it % w.nq;
+          const T* p = q + q_offset(g, w.ri.s, hh, w.ri.tok0, w.qt0 + t) + c * 8;
+          x0[u] = *reinterpret_cast<const f32x4*>(p);
+          x1[u] = *reinterpret_cast<const f32x4*>(p + 4);
+        }
+#pragma unroll
+        for (int u = 0; u < UP; ++u) {
+          const float wgt = it0 + u * PH < items ? 1.f : 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[i] += wgt * x0[u][i];
+            acc[4 + i] += wgt * x1[u][i];
+          }
         }
       }
     }
