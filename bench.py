@@ -199,6 +199,8 @@ def main():
     ap.add_argument("--decode-splits", type=int, default=0)
     ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all",
                     help="profiling aid: time one setting only (the JSON line then lacks the other)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="profiling aid: time eager steps only (value then comes from eager steps)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="profiling aid: run a plain device copy of this many MiB (5 times) first, "
                          "the known-size reference for HBM byte counters")
@@ -232,7 +234,7 @@ def main():
     st = Stepper(dbs, w, inp)
     log("timing prefill steps")
     eager_ms, stage, fwd_all = timed(st, args.steps, args.warmup)
-    ms = graph_timed(st, args.steps, args.warmup)
+    ms = eager_ms if args.no_graph else graph_timed(st, args.steps, args.warmup)
     visits = st.tile_visits()
     flops = visits * 4 * w.block * w.block * w.head_dim
     fwd_ms = stage[2]
@@ -258,8 +260,9 @@ def main():
                      "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_for("prefill_bf16_kernel")},
-        "step": "HIP graph replay of route + worklist + fwd; eager_ms_per_step: the same step "
-                "launched call by call, stages_ms: its per-call split",
+        "step": ("eager steps (--no-graph)" if args.no_graph else
+                 "HIP graph replay of route + worklist + fwd") +
+                "; eager_ms_per_step: the step launched call by call, stages_ms: its per-call split",
         "eager_ms_per_step": round(eager_ms, 5),
         "stages_ms": {"route": round(stage[0], 5), "worklist": round(stage[1], 5),
                       "fwd": round(stage[2], 5), "fwd_p10": round(fwd_all[len(fwd_all) // 10], 5),
@@ -279,7 +282,7 @@ def run_decode(args, dbs, wk, dev, out, inp, w):
         sd = Stepper(dbs, wd, inp_d, summaries_in=True, num_splits=args.decode_splits)
         log("timing decode steps")
         eager_msd, stage_d, _ = timed(sd, max(args.steps // 2, 10), args.warmup)
-        msd = graph_timed(sd, max(args.steps // 2, 10), args.warmup)
+        msd = eager_msd if args.no_graph else graph_timed(sd, max(args.steps // 2, 10), args.warmup)
         nnz = int(sd.wl.row_ptr[sd.sz.rows].item())
         kv_bytes = nnz * wd.block * wd.head_dim * 2 * 2
         qo_bytes = 2 * wd.batch * wd.heads_q * wd.head_dim * 2
