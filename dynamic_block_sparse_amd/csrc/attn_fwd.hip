@@ -20,6 +20,7 @@
 //     16-byte / 8-byte units so the MFMA operand reads are bank-conflict free;
 //   * tiles are visited in the worklist's ascending address order ([P2] §1.2).
 // fp32 path: a plain SIMT kernel (one lane per query row), exact-fp32 softmax.
+#include <algorithm>
 #include <utility>
 
 #include "common.h"
@@ -251,136 +252,141 @@ __global__ void __launch_bounds__(128 * HPR) prefill_bf16_kernel(Geom g, FwdBufs
 
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int64_t pos = xcd_schedule(blockIdx.x, g.rows, xcd_run);
-  const int64_t row = a.row_perm[g.rows - 1 - pos];   // longest rows first
-  const RowInfo ri = decode_row(g, row);
-  const int kvh = g.share ? ri.h : ri.h / g.group;
-  const int head = (g.share ? ri.h * g.group : ri.h) + wave / 2;
-  const int half = lane / 32, l32 = lane % 32;
-  const int qpos = ri.r * kBlock + (wave % 2) * 32 + l32;
-  const bool qvalid = qpos < ri.len;
-  const unsigned char* kbytes = (const unsigned char*)a.k;
-  const unsigned char* vbytes = (const unsigned char*)a.v;
+  // Workgroup b takes worklist positions b, b + G, b + 2G, ... (G = gridDim.x;
+  // G = rows unless the launch is persistent, see prefill_grid).
+  for (int64_t vb = blockIdx.x; vb < g.rows; vb += gridDim.x) {
+    if (vb != blockIdx.x) block_barrier();   // the previous row's LDS reads are done
+    const int64_t pos = xcd_schedule(vb, g.rows, xcd_run);
+    const int64_t row = a.row_perm[g.rows - 1 - pos];   // longest rows first
+    const RowInfo ri = decode_row(g, row);
+    const int kvh = g.share ? ri.h : ri.h / g.group;
+    const int head = (g.share ? ri.h * g.group : ri.h) + wave / 2;
+    const int half = lane / 32, l32 = lane % 32;
+    const int qpos = ri.r * kBlock + (wave % 2) * 32 + l32;
+    const bool qvalid = qpos < ri.len;
+    const unsigned char* kbytes = (const unsigned char*)a.k;
+    const unsigned char* vbytes = (const unsigned char*)a.v;
 
-  const int t_begin = a.row_ptr[row], ntiles = a.row_ptr[row + 1] - t_begin;
-  // the row's tile ids, one per lane (a row holds at most 128 tiles); read back
-  // with readlane so the loop issues no memory load (and no wait) for them
-  const int jl0 = lane < ntiles ? a.col_idx[t_begin + lane] : 0;
-  const int jl1 = lane + 64 < ntiles ? a.col_idx[t_begin + 64 + lane] : 0;
-  // Consume the loads here, on every path: the compiler's wait-count pass is
-  // path-insensitive, and a register that may still be pending at the loop
-  // header makes it wait for all vector loads (the tile prefetch included)
-  // inside the loop on every iteration.
-  asm volatile("" ::"v"(jl0), "v"(jl1));
-  auto tile_id = [&](int it) {
-    return it < 64 ? __builtin_amdgcn_readlane(jl0, it) : __builtin_amdgcn_readlane(jl1, it - 64);
-  };
+    const int t_begin = a.row_ptr[row], ntiles = a.row_ptr[row + 1] - t_begin;
+    // the row's tile ids, one per lane (a row holds at most 128 tiles); read back
+    // with readlane so the loop issues no memory load (and no wait) for them
+    const int jl0 = lane < ntiles ? a.col_idx[t_begin + lane] : 0;
+    const int jl1 = lane + 64 < ntiles ? a.col_idx[t_begin + 64 + lane] : 0;
+    // Consume the loads here, on every path: the compiler's wait-count pass is
+    // path-insensitive, and a register that may still be pending at the loop
+    // header makes it wait for all vector loads (the tile prefetch included)
+    // inside the loop on every iteration.
+    asm volatile("" ::"v"(jl0), "v"(jl1));
+    auto tile_id = [&](int it) {
+      return it < 64 ? __builtin_amdgcn_readlane(jl0, it) : __builtin_amdgcn_readlane(jl1, it - 64);
+    };
 
-  // 16-byte global->LDS loads of tile `it`: K into kt, V into vt
-  const int sub = lane >> 4, cl = lane & 15;
-  auto tile_off = [&](int it, int* cnt) {
-    const int j = tile_id(it);
-    *cnt = min(kBlock, ri.len - j * kBlock);
-    return kv_offset(g, ri.s, kvh, ri.tok0, j * kBlock) * 2;
-  };
-  auto issue_k = [&](int it, unsigned char* kt) {
-    int cnt;
-    const int64_t off = tile_off(it, &cnt);
-#pragma unroll
-    for (int i = wave; i < 16; i += NW) {
-      const int key = 4 * i + sub;
-      const int kc = min(key, cnt - 1);      // rows past the end: any valid row (masked later)
-      load_lds16(kbytes + off + kc * 256 + ((cl ^ ksw(key)) << 4), kt + i * 1024);
-    }
-  };
-  auto issue_v = [&](int it, unsigned char* vt) {
-    int cnt;
-    const int64_t off = tile_off(it, &cnt);
-#pragma unroll
-    for (int i = wave; i < 16; i += NW) {
-      const int key = 4 * i + sub;
-      const int kc = min(key, cnt - 1);
-      load_lds16(vbytes + off + kc * 256 + ((cl ^ vsw(key)) << 4), vt + i * 1024);
-    }
-  };
-  auto issue = [&](int it, int buf) {
-    issue_k(it, lds + buf * 2 * TILE);
-    issue_v(it, lds + buf * 2 * TILE + TILE);
-  };
-  if (ntiles > 0) {
-    if (PIPE == 2) {
-      issue_k(0, lds);
-    } else {
-#pragma unroll
-      for (int p = 0; p < NBUF - 1; ++p)
-        if (p < ntiles) issue(p, p);
-      if (NBUF == 1) issue(0, 0);
-    }
-  }
-
-  bf16x8 qreg[8];
-  load_q(qreg, (const __bf16*)a.q + q_offset(g, ri.s, head, ri.tok0, qvalid ? qpos : 0), qvalid, half);
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(qreg[ks]));   // see the tile ids above
-
-  float m = -INFINITY, lsum = 0.f;
-  f32x16 oacc[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
-  f32x16 sacc[2];
-  bf16x8 pb[2][2];
-
-  for (int it = 0; it < ntiles; ++it) {
-    const int buf = NBUF > 1 ? it % NBUF : 0;
-    unsigned char* kt = lds + buf * 2 * TILE;
-    unsigned char* vt = kt + TILE;
-    if (PIPE == 2) {
-      // K(it) landed (only it is outstanding); every wave is past P V(it-1)
-      wait_vmcnt<0>();
-      block_barrier();
-      issue_v(it, vt);
-    } else if (NBUF > 1) {
-      // the ring slot of tile it+NBUF-1 was last read at iteration it-1,
-      // which ended with a barrier; keep NBUF-1 tiles in flight
-      const int nxt = it + NBUF - 1;
-      if (nxt < ntiles) {
-        issue(nxt, nxt % NBUF);
-        wait_vmcnt<(NBUF - 1) * LOADS>();
-      } else {
-        // no new issue: tiles it+1 .. min(it+NBUF-2, ntiles-1) may stay in flight
-        const int younger = min(NBUF - 2, ntiles - 1 - it);
-        if (younger >= 3) wait_vmcnt<3 * LOADS>();
-        else if (younger == 2) wait_vmcnt<2 * LOADS>();
-        else if (younger == 1) wait_vmcnt<LOADS>();
-        else wait_vmcnt<0>();
+    // 16-byte global->LDS loads of tile `it`: K into kt, V into vt
+    const int sub = lane >> 4, cl = lane & 15;
+    auto tile_off = [&](int it, int* cnt) {
+      const int j = tile_id(it);
+      *cnt = min(kBlock, ri.len - j * kBlock);
+      return kv_offset(g, ri.s, kvh, ri.tok0, j * kBlock) * 2;
+    };
+    auto issue_k = [&](int it, unsigned char* kt) {
+      int cnt;
+      const int64_t off = tile_off(it, &cnt);
+  #pragma unroll
+      for (int i = wave; i < 16; i += NW) {
+        const int key = 4 * i + sub;
+        const int kc = min(key, cnt - 1);      // rows past the end: any valid row (masked later)
+        load_lds16(kbytes + off + kc * 256 + ((cl ^ ksw(key)) << 4), kt + i * 1024);
       }
-      block_barrier();
-    } else {
-      if (it > 0) issue(it, 0);   // the previous iteration ended with a barrier
-      wait_vmcnt<0>();
-      block_barrier();
+    };
+    auto issue_v = [&](int it, unsigned char* vt) {
+      int cnt;
+      const int64_t off = tile_off(it, &cnt);
+  #pragma unroll
+      for (int i = wave; i < 16; i += NW) {
+        const int key = 4 * i + sub;
+        const int kc = min(key, cnt - 1);
+        load_lds16(vbytes + off + kc * 256 + ((cl ^ vsw(key)) << 4), vt + i * 1024);
+      }
+    };
+    auto issue = [&](int it, int buf) {
+      issue_k(it, lds + buf * 2 * TILE);
+      issue_v(it, lds + buf * 2 * TILE + TILE);
+    };
+    if (ntiles > 0) {
+      if (PIPE == 2) {
+        issue_k(0, lds);
+      } else {
+  #pragma unroll
+        for (int p = 0; p < NBUF - 1; ++p)
+          if (p < ntiles) issue(p, p);
+        if (NBUF == 1) issue(0, 0);
+      }
     }
-    const int j = tile_id(it);
-    s_tile(sacc, kt, qreg, m, l32, half);
-    if (PIPE == 2 && it + 1 < ntiles) {
-      block_barrier();          // every wave has read K(it): refill it with K(it+1)
-      issue_k(it + 1, kt);
-    }
-    softmax_tile(sacc, pb, oacc, m, lsum, j == ri.r || j * kBlock + kBlock > ri.len, j * kBlock, qpos, ri.len,
-                 half);
-    if (PIPE == 2) {
-      // V(it) landed; K(it+1) may still be in flight
-      if (it + 1 < ntiles) wait_vmcnt<HALF_LOADS>();
-      else wait_vmcnt<0>();
-      block_barrier();
-    }
-    pv_tile(oacc, pb, vt, lane);
-    if (PIPE != 2) block_barrier();   // every wave is done with this stage before it is refilled
-  }
 
-  if (qvalid)
-    store_row(oacc, m, lsum, (__bf16*)a.o + q_offset(g, ri.s, head, ri.tok0, qpos),
-              a.lse ? a.lse + lse_offset(g, ri.s, head, ri.tok0, qpos) : nullptr, half);
+    bf16x8 qreg[8];
+    load_q(qreg, (const __bf16*)a.q + q_offset(g, ri.s, head, ri.tok0, qvalid ? qpos : 0), qvalid, half);
+  #pragma unroll
+    for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(qreg[ks]));   // see the tile ids above
+
+    float m = -INFINITY, lsum = 0.f;
+    f32x16 oacc[4];
+  #pragma unroll
+    for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
+    f32x16 sacc[2];
+    bf16x8 pb[2][2];
+
+    for (int it = 0; it < ntiles; ++it) {
+      const int buf = NBUF > 1 ? it % NBUF : 0;
+      unsigned char* kt = lds + buf * 2 * TILE;
+      unsigned char* vt = kt + TILE;
+      if (PIPE == 2) {
+        // K(it) landed (only it is outstanding); every wave is past P V(it-1)
+        wait_vmcnt<0>();
+        block_barrier();
+        issue_v(it, vt);
+      } else if (NBUF > 1) {
+        // the ring slot of tile it+NBUF-1 was last read at iteration it-1,
+        // which ended with a barrier; keep NBUF-1 tiles in flight
+        const int nxt = it + NBUF - 1;
+        if (nxt < ntiles) {
+          issue(nxt, nxt % NBUF);
+          wait_vmcnt<(NBUF - 1) * LOADS>();
+        } else {
+          // no new issue: tiles it+1 .. min(it+NBUF-2, ntiles-1) may stay in flight
+          const int younger = min(NBUF - 2, ntiles - 1 - it);
+          if (younger >= 3) wait_vmcnt<3 * LOADS>();
+          else if (younger == 2) wait_vmcnt<2 * LOADS>();
+          else if (younger == 1) wait_vmcnt<LOADS>();
+          else wait_vmcnt<0>();
+        }
+        block_barrier();
+      } else {
+        if (it > 0) issue(it, 0);   // the previous iteration ended with a barrier
+        wait_vmcnt<0>();
+        block_barrier();
+      }
+      const int j = tile_id(it);
+      s_tile(sacc, kt, qreg, m, l32, half);
+      if (PIPE == 2 && it + 1 < ntiles) {
+        block_barrier();          // every wave has read K(it): refill it with K(it+1)
+        issue_k(it + 1, kt);
+      }
+      softmax_tile(sacc, pb, oacc, m, lsum, j == ri.r || j * kBlock + kBlock > ri.len, j * kBlock, qpos, ri.len,
+                   half);
+      if (PIPE == 2) {
+        // V(it) landed; K(it+1) may still be in flight
+        if (it + 1 < ntiles) wait_vmcnt<HALF_LOADS>();
+        else wait_vmcnt<0>();
+        block_barrier();
+      }
+      pv_tile(oacc, pb, vt, lane);
+      if (PIPE != 2) block_barrier();   // every wave is done with this stage before it is refilled
+    }
+
+    if (qvalid)
+      store_row(oacc, m, lsum, (__bf16*)a.o + q_offset(g, ri.s, head, ri.tok0, qpos),
+                a.lse ? a.lse + lse_offset(g, ri.s, head, ri.tok0, qpos) : nullptr, half);
+  }
 }
 
 // --------------------------------------------------------------------------
@@ -626,11 +632,29 @@ int launch_f32(const Geom& g, const FwdBufs& b, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 
+// Grid for `rows` worklist rows.  With few generations of workgroups (rows
+// <= 4 x the co-resident slots) the run ends with a tail of staggered late
+// starts, so the grid is the slots (at least 8, a multiple of 8 so position v
+// stays on XCD v % 8) and each workgroup loops over its rows.  With many
+// generations the dispatcher's first-come assignment balances the CUs better
+// than a fixed share does, and the grid is one workgroup per row.
+template <typename K>
+unsigned prefill_grid(K kernel, int threads, int64_t rows) {
+  int dev = 0, cus = 0, per = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, 0) != hipSuccess) {
+    return (unsigned)rows;
+  }
+  int64_t slots = (int64_t)std::max(per, 1) * std::max(cus, 1);
+  slots = std::max<int64_t>(8, slots / 8 * 8);
+  return (unsigned)(rows <= 4 * slots ? std::min(rows, slots) : rows);
+}
+
 int launch_prefill(const Geom& g, int dtype, const FwdBufs& b, hipStream_t st) {
   if (g.rows <= 0) return SA_OK;
   if (dtype == SA_F32) return launch_f32(g, b, st);
   if (g.d != 128) return SA_ERR_UNSUPPORTED;
-  dim3 grid((unsigned)g.rows);
   // One-head rows: one LDS stage (32 KB) per workgroup, so four workgroups fit
   // on a CU and each SIMD runs two wavefronts of different rows; V(t) and
   // K(t+1) loads overlap S(t) and the softmax.  Measured on MI355X this beats
@@ -639,11 +663,26 @@ int launch_prefill(const Geom& g, int dtype, const FwdBufs& b, hipStream_t st) {
   // Four-head rows: the ping-pong kernel with 4-deep K and V rings (128 KB, one
   // workgroup per CU); its two wavefronts per SIMD alternate MFMA and softmax
   // phases.  Two-head rows: the lock-step kernel, one stage.
+  // The lock-step kernel's grid comes from prefill_grid (persistent when the
+  // rows fill few generations).
   const int run = g.hpr == 1 ? 128 : 32;   // rows per XCD run
   switch (g.hpr) {
-    case 1: prefill_bf16_kernel<1, 2><<<grid, 128, 0, st>>>(g, b, run); break;
-    case 2: prefill_bf16_kernel<2, 0><<<grid, 256, 0, st>>>(g, b, run); break;
-    case 4: prefill_bf16_pp_kernel<4><<<grid, 512, 0, st>>>(g, b, run); break;
+    case 1: {
+      auto k = prefill_bf16_kernel<1, 2>;
+      k<<<prefill_grid(k, 128, g.rows), 128, 0, st>>>(g, b, run);
+      break;
+    }
+    case 2: {
+      auto k = prefill_bf16_kernel<2, 0>;
+      k<<<prefill_grid(k, 256, g.rows), 256, 0, st>>>(g, b, run);
+      break;
+    }
+    case 4:
+      // one workgroup per row: the outer row loop of the persistent form
+      // costs this kernel ~14 % in code generation, and with one workgroup
+      // per CU its rows always fill many generations
+      prefill_bf16_pp_kernel<4><<<(unsigned)g.rows, 512, 0, st>>>(g, b, run);
+      break;
     default: return SA_ERR_UNSUPPORTED;
   }
   return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
