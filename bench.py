@@ -9,16 +9,19 @@ already resident in HBM:
 on the 8192-token MHA prefill setting (B=1, H=16, n=8192, d=128, b=64,
 k_b=16, bf16, planted relevance).  `value` is the selected-tile FLOPs of the
 step (4*b*b*d per (query head, tile) visit of the worklist) divided by the
-whole step's time, in TFLOP/s.  The attention kernel alone is reported in
-`roofline` against the bf16 dense MFMA peak; routing and worklist times are
-reported separately in `stages_ms`.  The split-KV decode setting (64 x
-131072-token caches, Hq=32, Hkv=8, k_b=64) is timed too and reported under
-`decode` as KV GB/s against the HBM peak.
+step's time, the step replayed as one HIP graph, in TFLOP/s.  The attention
+call alone is reported in `roofline` against the bf16 dense MFMA peak, timed
+as the median call over steps that each start with the 256 MB last-level
+cache flushed (a 512 MB buffer rewritten outside the events); every call's
+median, p10 and p90 are in `stages_ms`, warm (back to back) and flushed.  The
+split-KV decode setting (64 x 131072-token caches, Hq=32, Hkv=8, k_b=64) is
+timed the same way and reported under `decode` as KV GB/s against the HBM peak.
 
 The fp64 CPU oracle is timed on a bounded sample of the same prefill input
 (`cpu_baseline`): a reported baseline, not a target.
 
     python bench.py [--steps K] [--warmup W] [--no-decode] [--no-cpu]
+    python bench.py --workload NAME     # another bf16 setting, same measurements
 """
 from __future__ import annotations
 
@@ -36,6 +39,7 @@ METRIC = "sparse-attn fwd TFLOP/s on selected tiles (% MFMA peak); decode KV GB/
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+FLUSH_BYTES = 512 << 20        # twice the 256 MB last-level (MALL) cache
 
 
 def log(msg):
@@ -105,13 +109,34 @@ class Stepper:
         if ev is not None:
             ev[3].record()
 
+    def fwd_kernel_name(self):
+        """The attention kernel the library picks: by query heads per worklist row."""
+        hpr = self.w.group if self.w.share_gqa else 1
+        return {1: "prefill_bf16_kernel<1,2>", 2: "prefill_bf16_kernel<2,0>",
+                4: "prefill_bf16_pp_kernel<4>"}.get(hpr, f"heads per row {hpr}")
+
+    def worklist_stats(self):
+        """Rows per length bucket and the tiles per row (max and mean)."""
+        rp = self.wl.row_ptr[:self.sz.rows + 1].cpu()
+        lens = (rp[1:] - rp[:-1]).double()
+        bp = self.wl.bucket_ptr.cpu().tolist()
+        return {"bucket_rows": [bp[i + 1] - bp[i] for i in range(len(bp) - 1)],
+                "tiles_per_row_max": int(lens.max().item()),
+                "tiles_per_row_mean": round(float(lens.mean().item()), 3)}
+
     def tile_visits(self):
         """Sum over rows of unique tiles times the query heads each row serves."""
         nnz = int(self.wl.row_ptr[self.sz.rows].item())
         return nnz * (self.w.group if self.w.share_gqa else 1)
 
 
-def timed(stepper, steps, warmup):
+def timed(stepper, steps, warmup, flush=None):
+    """Eager steps, each call bracketed by events on the current stream.
+
+    With `flush` (a device buffer larger than the 256 MB last-level cache) the
+    buffer is rewritten before every step, outside the events, so no step
+    finds the previous step's K/V in cache; the mean over the loop then
+    includes the flushes and only the per-call times are meaningful."""
     import torch
     for _ in range(warmup):
         stepper.step()
@@ -121,13 +146,22 @@ def timed(stepper, steps, warmup):
     torch.cuda.synchronize()
     start.record()
     for i in range(steps):
+        if flush is not None:
+            flush.add_(1)
         stepper.step(evs[i])
     end.record()
     torch.cuda.synchronize()
     total = start.elapsed_time(end)
-    stage = [sum(e[k].elapsed_time(e[k + 1]) for e in evs) / steps for k in range(3)]
-    fwd_all = sorted(e[2].elapsed_time(e[3]) for e in evs)
-    return total / steps, stage, fwd_all
+    per_call = [[e[k].elapsed_time(e[k + 1]) for e in evs] for k in range(3)]
+    return total / steps, per_call
+
+
+def spread(xs):
+    """Mean, median, p10 and p90 of a list of times (ms)."""
+    ys = sorted(xs)
+    n = len(ys)
+    return {"mean": round(sum(ys) / n, 5), "median": round(ys[n // 2], 5),
+            "p10": round(ys[n // 10], 5), "p90": round(ys[(n * 9) // 10], 5)}
 
 
 def graph_timed(stepper, steps, warmup):
@@ -188,7 +222,102 @@ def cpu_baseline(w, inp, heads):
                 seconds=round(t3 - t0, 3))
 
 
+def prefill_flops(st, w):
+    """Physical selected-tile FLOPs (4*b*b*d per visit) and the causal-effective
+    count in which each diagonal tile holds only its b*(b+1)/2 unmasked pairs."""
+    visits = st.tile_visits()
+    per = 4 * w.block * w.block * w.head_dim
+    diag = st.sz.rows * (w.group if w.share_gqa else 1)
+    eff = (visits - diag) * per + diag * 4 * (w.block * (w.block + 1) // 2) * w.head_dim
+    return visits, visits * per, eff
+
+
+def measure_prefill(args, dbs, w, inp, flush):
+    import torch
+    st = Stepper(dbs, w, inp)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    st.step()
+    torch.cuda.synchronize()
+    first_ms = (time.perf_counter() - t0) * 1e3
+    log(f"timing {w.name}: warm eager steps")
+    eager_ms, warm = timed(st, args.steps, args.warmup)
+    log(f"timing {w.name}: steps with the last-level cache flushed before each")
+    _, cold = timed(st, args.steps, 2, flush)
+    ms = eager_ms if args.no_graph else graph_timed(st, args.steps, args.warmup)
+    visits, flops, eff = prefill_flops(st, w)
+    fwd_ms = spread(cold[2])["median"]
+    achieved = flops / (fwd_ms * 1e-3) / 1e12
+    rec = {
+        "value": round(flops / (ms * 1e-3) / 1e12, 3),
+        "ms_per_step": round(ms, 5),
+        "config": {"workload": w.name, "batch": w.batch, "heads_q": w.heads_q, "heads_kv": w.heads_kv,
+                   "seqlen": w.seqlen or f"varlen {w.varlen_min}..{w.varlen_max}",
+                   "head_dim": w.head_dim, "block": w.block, "k_b": w.k_b, "select": w.select,
+                   "qpool": w.qpool, "tile_visits": visits, "selected_tile_flops": flops,
+                   "causal_effective_flops": eff},
+        "roofline": {"bound": "mfma", "kernel": st.fwd_kernel_name(),
+                     "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_for("prefill_bf16_kernel") if w is args.headline else None,
+                     "time": "median fwd call, last-level cache flushed before each step"},
+        "step": ("eager steps (--no-graph)" if args.no_graph else
+                 "HIP graph replay of route + worklist + fwd") +
+                "; eager_ms_per_step: the step launched call by call",
+        "eager_ms_per_step": round(eager_ms, 5),
+        "first_step_ms": round(first_ms, 3),
+        "stages_ms": {"warm": {k: spread(v) for k, v in zip(("route", "worklist", "fwd"), warm)},
+                      "cache_flushed": {k: spread(v) for k, v in zip(("route", "worklist", "fwd"), cold)}},
+        "effective_tflops": round(eff / (fwd_ms * 1e-3) / 1e12, 3),
+        "worklist_err": int(st.wl.err.item()),
+    }
+    if w.varlen or w.select == "threshold":
+        rec["worklist"] = st.worklist_stats()
+    del st
+    return rec
+
+
+def measure_decode(args, dbs, wd, dev, flush):
+    import torch
+    log(f"generating {wd.name}")
+    inp_d = wk_make(wd, dev)
+    sd = Stepper(dbs, wd, inp_d, summaries_in=True, num_splits=args.decode_splits)
+    steps = max(args.steps // 2, 10)
+    log(f"timing {wd.name}: warm eager steps")
+    eager_msd, warm = timed(sd, steps, args.warmup)
+    log(f"timing {wd.name}: steps with the last-level cache flushed before each")
+    _, cold = timed(sd, steps, 2, flush)
+    msd = eager_msd if args.no_graph else graph_timed(sd, steps, args.warmup)
+    nnz = int(sd.wl.row_ptr[sd.sz.rows].item())
+    kv_bytes = nnz * wd.block * wd.head_dim * 2 * 2
+    qo_bytes = 2 * wd.batch * wd.heads_q * wd.head_dim * 2
+    fwd_ms = spread(cold[2])["median"]
+    gbs = (kv_bytes + qo_bytes) / (fwd_ms * 1e-3) / 1e9
+    route_bytes = wd.batch * wd.heads_kv * (wd.seqlen // wd.block) * wd.head_dim * 4
+    rec = {
+        "workload": wd.name, "ms_per_step": round(msd, 5), "eager_ms_per_step": round(eager_msd, 5),
+        "stages_ms": {"warm": {k: spread(v) for k, v in zip(("route", "worklist", "fwd"), warm)},
+                      "cache_flushed": {k: spread(v) for k, v in zip(("route", "worklist", "fwd"), cold)}},
+        "kv_bytes": kv_bytes, "kv_gbs": round(gbs, 1),
+        "roofline": {"bound": "hbm", "kernel": "decode_split_kernel<4> + decode_merge_kernel",
+                     "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": traffic_for("decode_split_kernel"),
+                     "time": "median fwd call, last-level cache flushed before each step"},
+        "route_summary_gbs": round(route_bytes / (spread(cold[0])["median"] * 1e-3) / 1e9, 1),
+    }
+    del sd, inp_d
+    torch.cuda.empty_cache()
+    return rec
+
+
+def wk_make(w, dev):
+    from dynamic_block_sparse_amd import workloads as wk
+    return wk.make_inputs(w, dev)
+
+
 def main():
+    from dynamic_block_sparse_amd import workloads as wk
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
@@ -197,6 +326,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=16)
     ap.add_argument("--decode-splits", type=int, default=0)
+    ap.add_argument("--workload", choices=[w.name for w in wk.ALL if w.dtype == "bf16"],
+                    default=wk.PREFILL_MHA.name,
+                    help="the prefill setting timed for the JSON line (default: the 8192-token MHA "
+                         "setting); the others reproduce the per-setting measurements")
     ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all",
                     help="profiling aid: time one setting only (the JSON line then lacks the other)")
     ap.add_argument("--no-graph", action="store_true",
@@ -212,7 +345,6 @@ def main():
 
     import torch
     import dynamic_block_sparse_amd as dbs
-    from dynamic_block_sparse_amd import workloads as wk
 
     dev = torch.device("cuda:0")
     dbs.load_library()
@@ -225,83 +357,38 @@ def main():
         torch.cuda.synchronize()
         del a, b
         log(f"copy calibration: 5 copies of {args.copy_calibration} MiB")
-    w = wk.PREFILL_MHA
-    out = {}
-    if args.only == "decode":
-        return run_decode(args, dbs, wk, dev, out, None, w)
-    log(f"generating {w.name}")
-    inp = wk.make_inputs(w, dev)
-    st = Stepper(dbs, w, inp)
-    log("timing prefill steps")
-    eager_ms, stage, fwd_all = timed(st, args.steps, args.warmup)
-    ms = eager_ms if args.no_graph else graph_timed(st, args.steps, args.warmup)
-    visits = st.tile_visits()
-    flops = visits * 4 * w.block * w.block * w.head_dim
-    fwd_ms = stage[2]
-    achieved = flops / (fwd_ms * 1e-3) / 1e12
-    err = int(st.wl.err.item())
-    out.update({
-        "metric": METRIC,
-        "value": round(flops / (ms * 1e-3) / 1e12, 3),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) Q/K/V with planted relevance; no dataset)",
-        "config": {"workload": w.name, "batch": w.batch, "heads_q": w.heads_q, "heads_kv": w.heads_kv,
-                   "seqlen": w.seqlen, "head_dim": w.head_dim, "block": w.block, "k_b": w.k_b,
-                   "qpool": w.qpool, "tile_visits": visits, "selected_tile_flops": flops},
-        "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel<1>",
-                     "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_for("prefill_bf16_kernel")},
-        "step": ("eager steps (--no-graph)" if args.no_graph else
-                 "HIP graph replay of route + worklist + fwd") +
-                "; eager_ms_per_step: the step launched call by call, stages_ms: its per-call split",
-        "eager_ms_per_step": round(eager_ms, 5),
-        "stages_ms": {"route": round(stage[0], 5), "worklist": round(stage[1], 5),
-                      "fwd": round(stage[2], 5), "fwd_p10": round(fwd_all[len(fwd_all) // 10], 5),
-                      "fwd_p90": round(fwd_all[(len(fwd_all) * 9) // 10], 5)},
-        "worklist_err": err,
-    })
-    del st
-    run_decode(args, dbs, wk, dev, out, inp, w)
-
-
-def run_decode(args, dbs, wk, dev, out, inp, w):
-    import torch
+    # 512 MB rewritten between timed steps: twice the last-level cache
+    flush = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    args.headline = wk.PREFILL_MHA
+    w = wk.BY_NAME[args.workload]
+    if w.mode == "decode":
+        args.only = "decode"
+    out = {"metric": METRIC}
+    inp = None
+    if args.only != "decode":
+        if w is not wk.PREFILL_MHA:
+            args.headline = w
+        log(f"generating {w.name}")
+        inp = wk.make_inputs(w, dev)
+        rec = measure_prefill(args, dbs, w, inp, flush)
+        out.update({"value": rec.pop("value"), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+                    "warmup": args.warmup, "ms_per_step": rec.pop("ms_per_step"),
+                    "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+                    "data": "synthetic (seeded N(0,1) Q/K/V with planted relevance; no dataset)"})
+        out.update(rec)
     if not args.no_decode and args.only != "prefill":
-        wd = wk.DECODE
-        log(f"generating {wd.name}")
-        inp_d = wk.make_inputs(wd, dev)
-        sd = Stepper(dbs, wd, inp_d, summaries_in=True, num_splits=args.decode_splits)
-        log("timing decode steps")
-        eager_msd, stage_d, _ = timed(sd, max(args.steps // 2, 10), args.warmup)
-        msd = eager_msd if args.no_graph else graph_timed(sd, max(args.steps // 2, 10), args.warmup)
-        nnz = int(sd.wl.row_ptr[sd.sz.rows].item())
-        kv_bytes = nnz * wd.block * wd.head_dim * 2 * 2
-        qo_bytes = 2 * wd.batch * wd.heads_q * wd.head_dim * 2
-        gbs = (kv_bytes + qo_bytes) / (stage_d[2] * 1e-3) / 1e9
-        route_bytes = wd.batch * wd.heads_kv * (wd.seqlen // wd.block) * wd.head_dim * 4
-        out["decode"] = {
-            "workload": wd.name, "ms_per_step": round(msd, 5), "eager_ms_per_step": round(eager_msd, 5),
-            "stages_ms": {"route": round(stage_d[0], 5), "worklist": round(stage_d[1], 5),
-                          "fwd": round(stage_d[2], 5)},
-            "kv_bytes": kv_bytes, "kv_gbs": round(gbs, 1),
-            "roofline": {"bound": "hbm", "kernel": "decode_split_kernel<4> + decode_merge_kernel",
-                         "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "traffic": traffic_for("decode_split_kernel")},
-            "route_summary_gbs": round(route_bytes / (stage_d[0] * 1e-3) / 1e9, 1),
-        }
-        del sd, inp_d
-        torch.cuda.empty_cache()
-    if not args.no_cpu and inp is not None:
+        wd = w if w.mode == "decode" else wk.DECODE
+        rec = measure_decode(args, dbs, wd, dev, flush)
+        if args.only == "decode":
+            out.update({"value": rec["kv_gbs"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+                        "warmup": args.warmup, "ms_per_step": rec["ms_per_step"],
+                        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+                        "dtype": "bf16", "data": "synthetic (seeded N(0,1) Q/K/V; no dataset)",
+                        "config": {"workload": wd.name}})
+        out["decode"] = rec
+    del flush
+    torch.cuda.empty_cache()
+    if not args.no_cpu and inp is not None and w is wk.PREFILL_MHA:
         log(f"timing the oracle on {args.cpu_heads} heads")
         out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_heads)
     print(json.dumps(out), flush=True)
