@@ -96,25 +96,6 @@ __device__ __forceinline__ int64_t xcd_schedule(int64_t b, int64_t rows, int G) 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 constexpr float kGrow = 8.0f;
 
-// S^T[key][row] = K Q^T for the 64 keys of the K tile at kt, accumulated onto
-// the reference offset
-__device__ __forceinline__ void s_tile(f32x16 (&sacc)[2], const unsigned char* kt, const bf16x8 (&qreg)[8],
-                                       float m, int l32, int half) {
-  const float init = m == -INFINITY ? 0.f : -m;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sacc[kb][i] = init;
-    const int key = kb * 32 + l32;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const int c = ks * 2 + half;
-      const bf16x8 av = *reinterpret_cast<const bf16x8*>(kt + key * 256 + ((c ^ ksw(key)) << 4));
-      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[ks], sacc[kb], 0, 0, 0);
-    }
-  }
-}
-
 // Mask, row maximum, lazy rescale, P = exp2(S - m) in bf16 and the row sum of
 // those bf16 weights ([P2] §1.2 Eq 3-5).  `kbase` is the tile's first key
 // position; `masked` says whether any key of the tile can be masked for this
@@ -176,31 +157,78 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&sacc)[2], bf16x8 (&pb)[2][
   lsum += sum_xor32((r[0] + r[1]) + (r[2] + r[3]));
 }
 
-// O^T[d][row] += V^T[d][keys] P^T[keys][row] for the V tile at vt; V^T
-// operands come from LDS transpose reads of the row-major V tile
-__device__ __forceinline__ void pv_tile(f32x16 (&oacc)[4], const bf16x8 (&pb)[2][2], const unsigned char* vt,
-                                        int lane) {
-  const int gi = lane >> 4, li = lane & 15;
-  const int vh = gi >> 1, vdh = gi & 1;
-#pragma unroll
-  for (int db = 0; db < 4; ++db) {
-    const int d = db * 32 + 16 * vdh + 4 * (li & 3);
-    const int chunk = d >> 3, h8 = (d >> 2) & 1;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int key0 = kb * 32 + 16 * ks + 4 * vh + (li >> 2);
-        const int key1 = key0 + 8;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (SA_LDS i16x4*)(vt + key0 * 256 + ((chunk ^ vsw(key0)) << 4) + h8 * 8));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (SA_LDS i16x4*)(vt + key1 * 256 + ((chunk ^ vsw(key1)) << 4) + h8 * 8));
-        const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kb][ks], oacc[db], 0, 0, 0);
-      }
+// LDS reads behind operand i of an MFMA phase (two transpose reads for a V^T
+// operand, one read for a K operand) and behind operands 0 .. n-1
+template <int NPV, int N>
+constexpr int mfma_reads(int i) { return i >= N ? 0 : i < NPV ? 2 : 1; }
+template <int NPV, int N>
+constexpr int mfma_reads_before(int n) {
+  int r = 0;
+  for (int i = 0; i < n; ++i) r += mfma_reads<NPV, N>(i);
+  return r;
+}
+
+// One MFMA phase: O^T += V^T P^T for the V tile at vt (when PV), then
+// S^T = K Q^T onto the reference offset -m for the K tile at kt (when S): 16 +
+// 16 MFMAs whose LDS operands are read DEPTH MFMAs ahead of use.  Left to
+// itself the compiler reads each operand right before its MFMA into the same
+// few registers, so nearly every MFMA waits out a full LDS latency; here the
+// read for MFMA i + DEPTH is issued right after MFMA i (scheduling groups pin
+// that order).  V^T operands come from LDS transpose reads of the row-major V
+// tile.  Each accumulator sees its MFMAs in the order (kb, ks).
+template <bool PV, bool S, int DEPTH>
+__device__ __forceinline__ void mfma_phase(f32x16 (&oacc)[4], const bf16x8 (&pb)[2][2], const unsigned char* vt,
+                                           f32x16 (&sacc)[2], const unsigned char* kt, const bf16x8 (&qreg)[8],
+                                           float m, int lane) {
+  constexpr int NPV = PV ? 16 : 0, NS = S ? 16 : 0, N = NPV + NS;
+  const int l32 = lane & 31, half = lane >> 5;
+  const int gi = lane >> 4, li = lane & 15, vh = gi >> 1, vdh = gi & 1;
+  // operand i < NPV: V^T block (kb, ks, db) = (i >> 3, (i >> 2) & 1, i & 3);
+  // operand NPV + j: K block (ks, kb) = (j >> 1, j & 1)
+  auto operand = [&](int i) -> bf16x8 {
+    if (i < NPV) {
+      const int kb = i >> 3, ks = (i >> 2) & 1, db = i & 3;
+      const int d = db * 32 + 16 * vdh + 4 * (li & 3);
+      const int chunk = d >> 3, h8 = (d >> 2) & 1;
+      const int key0 = kb * 32 + 16 * ks + 4 * vh + (li >> 2), key1 = key0 + 8;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (SA_LDS i16x4*)(vt + key0 * 256 + ((chunk ^ vsw(key0)) << 4) + h8 * 8));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (SA_LDS i16x4*)(vt + key1 * 256 + ((chunk ^ vsw(key1)) << 4) + h8 * 8));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
-  }
+    const int j = i - NPV, ks = j >> 1, kb = j & 1;
+    const int key = kb * 32 + l32, c = ks * 2 + half;
+    return *reinterpret_cast<const bf16x8*>(kt + key * 256 + ((c ^ ksw(key)) << 4));
+  };
+  constexpr int kMfma = 0x008, kDsRead = 0x100;   // scheduling-group masks
+  bf16x8 buf[DEPTH];
+#pragma unroll
+  for (int i = 0; i < DEPTH; ++i)
+    if (i < N) buf[i] = operand(i);
+  __builtin_amdgcn_sched_group_barrier(kDsRead, mfma_reads_before<NPV, N>(DEPTH), 0);
+  auto step = [&]<int I>() {
+    const bf16x8 av = buf[I % DEPTH];
+    if constexpr (I + DEPTH < N) buf[I % DEPTH] = operand(I + DEPTH);
+    if constexpr (I < NPV) {
+      constexpr int kb = I >> 3, ks = (I >> 2) & 1, db = I & 3;
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kb][ks], oacc[db], 0, 0, 0);
+    } else {
+      constexpr int ks = (I - NPV) >> 1, kb = (I - NPV) & 1;
+      if constexpr (ks == 0) {   // the accumulator starts at the reference offset
+        const float init = m == -INFINITY ? 0.f : -m;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[kb][i] = init;
+      }
+      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[ks], sacc[kb], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+    if constexpr (mfma_reads<NPV, N>(I + DEPTH) > 0)
+      __builtin_amdgcn_sched_group_barrier(kDsRead, mfma_reads<NPV, N>(I + DEPTH), 0);
+  };
+  [&]<int... Is>(std::integer_sequence<int, Is...>) {
+    (step.template operator()<Is>(), ...);
+  }(std::make_integer_sequence<int, N>{});
 }
 
 // Q rows of this lane as the B operand of S^T = K Q^T, pre-scaled by
@@ -248,6 +276,7 @@ __global__ void __launch_bounds__(128 * HPR) prefill_bf16_kernel(Geom g, FwdBufs
   constexpr int TILE = 64 * D * 2;          // bytes of one K (or V) tile
   constexpr int LOADS = 2 * (TILE / 1024) / NW;   // 1 KB wave loads per tile per wave
   constexpr int HALF_LOADS = LOADS / 2;           // of K or of V alone
+  constexpr int kDepth = 6;                       // MFMAs of lead for the LDS operand reads
   __shared__ __attribute__((aligned(1024))) unsigned char lds[NBUF * 2 * TILE];
 
   const int tid = threadIdx.x, lane = tid % kWave;
@@ -366,7 +395,7 @@ __global__ void __launch_bounds__(128 * HPR) prefill_bf16_kernel(Geom g, FwdBufs
         block_barrier();
       }
       const int j = tile_id(it);
-      s_tile(sacc, kt, qreg, m, l32, half);
+      mfma_phase<false, true, kDepth>(oacc, pb, vt, sacc, kt, qreg, m, lane);
       if (PIPE == 2 && it + 1 < ntiles) {
         block_barrier();          // every wave has read K(it): refill it with K(it+1)
         issue_k(it + 1, kt);
@@ -379,7 +408,7 @@ __global__ void __launch_bounds__(128 * HPR) prefill_bf16_kernel(Geom g, FwdBufs
         else wait_vmcnt<0>();
         block_barrier();
       }
-      pv_tile(oacc, pb, vt, lane);
+      mfma_phase<true, false, kDepth>(oacc, pb, vt, sacc, kt, qreg, m, lane);
       if (PIPE != 2) block_barrier();   // every wave is done with this stage before it is refilled
     }
 
@@ -429,6 +458,7 @@ __global__ void __launch_bounds__(512) prefill_bf16_pp_kernel(Geom g, FwdBufs a,
   constexpr int TILE = 64 * D * 2;
   constexpr int HALF_LOADS = (TILE / 1024) / NW;   // 1 KB wave loads per K (or V) tile per wave
   static_assert(NB >= 3 && NB <= 4, "ring depth");
+  constexpr int kDepth = 6;   // MFMAs of lead for the LDS operand reads
   __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * NB * TILE];
   unsigned char* const kring = lds;
   unsigned char* const vring = lds + NB * TILE;
@@ -522,9 +552,13 @@ __global__ void __launch_bounds__(512) prefill_bf16_pp_kernel(Geom g, FwdBufs a,
       } else {
         block_barrier();                             // barrier 2u+1
       }
-      if (u >= 1) pv_tile(oacc, pb, vring + ((u - 1) % NB) * TILE, lane);
-      __builtin_amdgcn_sched_barrier(0);
-      if (u < ntiles) s_tile(sacc, kring + (u % NB) * TILE, qreg, m, l32, half);
+      {
+        const unsigned char* vt = vring + ((u + NB - 1) % NB) * TILE;   // V(u-1)
+        const unsigned char* kt = kring + (u % NB) * TILE;              // K(u)
+        if (u >= 1) mfma_phase<true, false, kDepth>(oacc, pb, vt, sacc, kt, qreg, m, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        if (u < ntiles) mfma_phase<false, true, kDepth>(oacc, pb, vt, sacc, kt, qreg, m, lane);
+      }
       if (grp == 0) {
         block_barrier();                             // barrier 2u+1
       } else if (u < ntiles) {
