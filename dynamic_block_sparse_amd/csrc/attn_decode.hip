@@ -26,8 +26,10 @@ namespace sa {
 
 constexpr float kLog2eD = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kFusedSplits = 8;   // up to this many splits merge inside one workgroup
 
 size_t decode_partials_bytes(const Geom& g, int splits) {
+  if (splits <= kFusedSplits) return 0;   // states merge in LDS
   return (size_t)g.rows * splits * g.hpr * (g.d + 2) * sizeof(float);
 }
 
@@ -46,14 +48,20 @@ __device__ __forceinline__ void dec_wait_vmcnt() {
 // V rows: the 8 rows two 16-lane groups read together map to 16 distinct slots
 __device__ __forceinline__ int dec_vsw(int key) { return (key & 7) << 1; }
 
+// Partial state of one split of a row, per lane: oacc[db][i] = u of head
+// slot lane % 16 at d = 16 db + 4 (lane / 16) + i; m, l of that head slot.
+struct DecodePartial {
+  f32x4 oacc[8];
+  float m, l;
+};
+
+// Stream tiles [tb, te) of split sp of `row` (one wavefront; vt = its 16 KB
+// of LDS for the V tile) and return its unnormalised state.
 template <int G>
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) decode_split_kernel(Geom g, FwdBufs a, int splits) {
+__device__ __forceinline__ void decode_split(const Geom& g, const FwdBufs& a, int64_t row, int sp, int splits,
+                                             unsigned char* vt, DecodePartial& out) {
   constexpr int D = 128;
-  __shared__ __attribute__((aligned(1024))) unsigned char vt[64 * D * 2];
-  const int lane = threadIdx.x;
-  const int64_t item = blockIdx.x;
-  const int64_t row = item / splits;
-  const int sp = (int)(item % splits);
+  const int lane = threadIdx.x % kWave;
   const RowInfo ri = decode_row(g, row);
   const int kvh = g.share ? ri.h : ri.h / g.group;
   const int h0 = g.share ? ri.h * g.group : ri.h;
@@ -187,53 +195,123 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) de
     // the next tile's V loads overwrite vt: every transpose read above has
     // returned (the MFMAs consumed them), so no further wait is needed
   }
-  float* part = a.part + ((int64_t)row * splits + sp) * G * (D + 2);
+#pragma unroll
+  for (int db = 0; db < 8; ++db) out.oacc[db] = oacc[db];
+  out.m = m;
+  out.l = l;
+}
+
+// Write a lane's share of a split state: slot hs < G of `dst`, laid out as
+// [head][D + 2] floats (u[0..D), m, l).
+template <int G>
+__device__ __forceinline__ void store_partial(float* dst, const DecodePartial& st, int lane) {
+  constexpr int D = 128;
+  const int hs = lane & 15, grp = lane >> 4;
   if (hs < G) {
-    float* ph = part + hs * (D + 2);
+    float* ph = dst + hs * (D + 2);
 #pragma unroll
     for (int db = 0; db < 8; ++db)
-      *reinterpret_cast<f32x4*>(ph + 16 * db + 4 * grp) = oacc[db];
+      *reinterpret_cast<f32x4*>(ph + 16 * db + 4 * grp) = st.oacc[db];
     if (grp == 0) {
-      ph[D] = m;
-      ph[D + 1] = l;
+      ph[D] = st.m;
+      ph[D + 1] = st.l;
     }
+  }
+}
+
+// Eq 3-5 merge of `splits` states of one head (stride between splits:
+// `sstride` floats) for d = 2 e, 2 e + 1; writes o (and lse when e == 0).
+__device__ __forceinline__ void merge_states(const Geom& g, const FwdBufs& a, const RowInfo& ri, int head,
+                                             const float* base, int64_t sstride, int splits, int e) {
+  constexpr int D = 128;
+  float mx = -INFINITY;
+  for (int s = 0; s < splits; ++s) mx = fmaxf(mx, base[s * sstride + D]);
+  const float msafe = mx == -INFINITY ? 0.f : mx;
+  float L = 0.f, u0 = 0.f, u1 = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    const float* ps = base + s * sstride;
+    const float ms = ps[D];
+    if (ms == -INFINITY) continue;
+    const float w = exp2f(ms - msafe);
+    L += w * ps[D + 1];
+    u0 += w * ps[2 * e];
+    u1 += w * ps[2 * e + 1];
+  }
+  const float inv = 1.f / L;
+  __bf16* op = (__bf16*)a.o + q_offset(g, ri.s, head, 0, 0);
+  op[2 * e] = (__bf16)(u0 * inv);
+  op[2 * e + 1] = (__bf16)(u1 * inv);
+  if (a.lse && e == 0) a.lse[lse_offset(g, ri.s, head, 0, 0)] = msafe * kLn2 + logf(L);
+}
+
+// One wavefront per (row, split); partial states go to the workspace and
+// decode_merge_kernel combines them.  Used for more than kFusedSplits splits.
+template <int G>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) decode_split_kernel(Geom g, FwdBufs a, int splits) {
+  constexpr int D = 128;
+  __shared__ __attribute__((aligned(1024))) unsigned char vt[64 * D * 2];
+  const int64_t row = blockIdx.x / splits;
+  const int sp = (int)(blockIdx.x % splits);
+  DecodePartial st;
+  decode_split<G>(g, a, row, sp, splits, vt, st);
+  store_partial<G>(a.part + ((int64_t)row * splits + sp) * G * (D + 2), st, threadIdx.x);
+}
+
+// One workgroup per row, one wavefront per split (splits <= kFusedSplits),
+// each with its own 16 KB LDS slice for V tiles.  The split states meet in
+// LDS (each wavefront overwrites its own slice once its tiles are done) and
+// the workgroup merges them: no workspace round trip and no second launch.
+template <int G>
+__global__ void __launch_bounds__(64 * kFusedSplits) __attribute__((amdgpu_waves_per_eu(3)))
+decode_fused_kernel(Geom g, FwdBufs a) {
+  constexpr int D = 128, SLICE = 64 * D * 2;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char dyn_lds[];
+  const int splits = blockDim.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
+  const int64_t row = blockIdx.x;
+  unsigned char* slice = dyn_lds + wave * SLICE;
+  DecodePartial st;
+  decode_split<G>(g, a, row, wave, splits, slice, st);
+  store_partial<G>(reinterpret_cast<float*>(slice), st, lane);
+  __syncthreads();
+  const RowInfo ri = decode_row(g, row);
+  const int h0 = g.share ? ri.h * g.group : ri.h;
+  for (int item = threadIdx.x; item < G * (D / 2); item += blockDim.x) {
+    const int hh = item / (D / 2), e = item % (D / 2);
+    merge_states(g, a, ri, h0 + hh, reinterpret_cast<const float*>(dyn_lds) + hh * (D + 2), SLICE / 4, splits, e);
   }
 }
 
 // Merge the split partials of one (row, head) with Eq 3-5 and normalise.
 __global__ void __launch_bounds__(64) decode_merge_kernel(Geom g, FwdBufs a, int splits) {
   constexpr int D = 128;
-  const int lane = threadIdx.x;
   const int64_t row = blockIdx.x;
   const int hh = blockIdx.y;
   const RowInfo ri = decode_row(g, row);
   const int head = (g.share ? ri.h * g.group : ri.h) + hh;
   const int G = g.hpr;
   const float* base = a.part + (int64_t)row * splits * G * (D + 2) + hh * (D + 2);
-  float mx = -INFINITY;
-  for (int s = 0; s < splits; ++s) mx = fmaxf(mx, base[(int64_t)s * G * (D + 2) + D]);
-  const float msafe = mx == -INFINITY ? 0.f : mx;
-  float L = 0.f, u0 = 0.f, u1 = 0.f;
-  for (int s = 0; s < splits; ++s) {
-    const float* ps = base + (int64_t)s * G * (D + 2);
-    const float ms = ps[D];
-    if (ms == -INFINITY) continue;
-    const float w = exp2f(ms - msafe);
-    L += w * ps[D + 1];
-    u0 += w * ps[2 * lane];
-    u1 += w * ps[2 * lane + 1];
-  }
-  const float inv = 1.f / L;
-  __bf16* op = (__bf16*)a.o + q_offset(g, ri.s, head, 0, 0);
-  op[2 * lane] = (__bf16)(u0 * inv);
-  op[2 * lane + 1] = (__bf16)(u1 * inv);
-  if (a.lse && lane == 0) a.lse[lse_offset(g, ri.s, head, 0, 0)] = msafe * kLn2 + logf(L);
+  merge_states(g, a, ri, head, base, (int64_t)G * (D + 2), splits, threadIdx.x);
 }
 
 int launch_decode(const Geom& g, int dtype, const FwdBufs& b, int splits, hipStream_t st) {
   if (g.rows <= 0) return SA_OK;
   if (dtype == SA_F32) return launch_prefill(g, dtype, b, st);   // SIMT kernel handles decode
   if (g.d != 128) return SA_ERR_UNSUPPORTED;
+  if (splits <= kFusedSplits) {
+    const unsigned threads = (unsigned)(64 * splits);
+    const size_t lds = (size_t)splits * 64 * 128 * 2;
+    const unsigned rows = (unsigned)g.rows;
+    switch (g.hpr) {
+      case 1: decode_fused_kernel<1><<<rows, threads, lds, st>>>(g, b); break;
+      case 2: decode_fused_kernel<2><<<rows, threads, lds, st>>>(g, b); break;
+      case 4: decode_fused_kernel<4><<<rows, threads, lds, st>>>(g, b); break;
+      case 8: decode_fused_kernel<8><<<rows, threads, lds, st>>>(g, b); break;
+      case 16: decode_fused_kernel<16><<<rows, threads, lds, st>>>(g, b); break;
+      default: return SA_ERR_UNSUPPORTED;
+    }
+    return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
+  }
   const unsigned items = (unsigned)(g.rows * splits);
   switch (g.hpr) {
     case 1: decode_split_kernel<1><<<items, 64, 0, st>>>(g, b, splits); break;

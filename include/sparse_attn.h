@@ -180,7 +180,8 @@ int sparse_attn_build_worklist(const sa_problem* p, const sa_route_cfg* rc, cons
  *   cached position of the listed blocks; the row's tiles are cut into
  *   num_splits groups (0 = library's choice; raised to at least
  *   ceil((k_b + forced) / 64)) whose partial (m, l, u) states are merged with
- *   Eq 3-5.  Accumulation and softmax are fp32; bf16 inputs use
+ *   Eq 3-5: inside one workgroup for up to 8 groups (no workspace), through
+ *   fp32 states in the workspace and a second kernel for more.  Accumulation and softmax are fp32; bf16 inputs use
  *   bf16 matrix-core products with P rounded to bf16 before P V. */
 int sparse_attn_fwd(const sa_problem* p, const sa_route_cfg* rc, const int32_t* row_ptr,
                     const int32_t* col_idx, const int32_t* row_perm, const void* q,

@@ -75,8 +75,9 @@ def test_small_varlen_threshold(dev):
     _full_check(w, inp, run)
 
 
-@pytest.mark.parametrize("splits", [1, 2, 3, 8])
+@pytest.mark.parametrize("splits", [1, 2, 3, 8, 16])
 def test_small_decode_splits(dev, splits):
+    """Up to 8 splits merge inside one workgroup; 16 takes the workspace + merge-kernel path."""
     w = wk.DECODE.replace(name=f"decode_small_s{splits}", batch=3, heads_q=8, heads_kv=2, seqlen=1000,
                           k_b=8)
     print(f"case {w.name}", flush=True)
