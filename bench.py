@@ -299,10 +299,10 @@ def measure_decode(args, dbs, wd, dev, flush):
         "stages_ms": {"warm": {k: spread(v) for k, v in zip(("route", "worklist", "fwd"), warm)},
                       "cache_flushed": {k: spread(v) for k, v in zip(("route", "worklist", "fwd"), cold)}},
         "kv_bytes": kv_bytes, "kv_gbs": round(gbs, 1),
-        "roofline": {"bound": "hbm", "kernel": "decode_split_kernel<4> + decode_merge_kernel",
+        "roofline": {"bound": "hbm", "kernel": "decode_fused_kernel<4> (4 splits merged in LDS)",
                      "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4),
-                     "traffic": traffic_for("decode_split_kernel"),
+                     "traffic": traffic_for("decode_fused_kernel"),
                      "time": "median fwd call, last-level cache flushed before each step"},
         "route_summary_gbs": round(route_bytes / (spread(cold[0])["median"] * 1e-3) / 1e9, 1),
     }
