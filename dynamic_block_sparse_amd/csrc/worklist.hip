@@ -7,14 +7,16 @@
 // waits on a host-side dedup; int32 ids.  [P2] Eq 7 and [P3] "from index
 // output to worklist": rows are grouped into capacity buckets 4, 8, 16, ...
 //
-// Three launches, no atomics on the output (bit-exact, run-to-run stable):
+// Two launches, no atomics on the output (bit-exact, run-to-run stable):
 //   1. rows:    one wavefront per row: validate, add forced ids, LSD radix
 //               sort with 1-bit ballot splits through LDS, drop duplicates,
 //               write the row's unique ids and its length to workspace
-//   2. scan:    one 1024-thread workgroup: row_ptr (exclusive scan of the
-//               lengths), per-bucket counts -> bucket_ptr, and the stable
-//               (bucket, row) order -> row_perm
-//   3. scatter: copy each row's ids to col_idx[row_ptr[row] ..]
+//   2. finish:  one workgroup per 256 rows: row_ptr (exclusive scan of the
+//               lengths), per-bucket counts -> bucket_ptr, the stable
+//               (bucket, row) order -> row_perm, and the copy of each row's
+//               ids to col_idx[row_ptr[row] ..].  Every workgroup reads all
+//               row lengths (4 bytes a row) for the totals and for what
+//               precedes its chunk, so none waits for another.
 #include "common.h"
 #include "kernels.h"
 
@@ -95,116 +97,124 @@ __global__ void __launch_bounds__(64) wl_rows_kernel(Geom g, sa_route_cfg rc, in
     atomicOr(err, (er ? SA_WL_ERR_RANGE : 0) | (ea ? SA_WL_ERR_ACAUSAL : 0));
 }
 
-// Row pointers and the bucket order in one 1024-thread workgroup.  Thread t
-// owns a contiguous chunk of rows; the row-length sum and the per-bucket row
-// counts of every chunk are scanned together (wave scans, then a scan of the
-// 16 wave totals in LDS), so the whole scan costs two barriers.
-__global__ void __launch_bounds__(1024) wl_scan_kernel(int64_t rows, int n_buckets,
-                                                       const int32_t* __restrict__ tmp_len,
-                                                       int32_t* __restrict__ row_ptr,
-                                                       int32_t* __restrict__ row_perm,
-                                                       int32_t* __restrict__ bucket_ptr) {
+// Step 2 for rows c0 .. c0 + 255 (c0 = 256 * block).  Thread t first sums,
+// over every row and over the rows before c0, the length and one count per
+// bucket; then owns row c0 + t: its row pointer and its slot in the bucket
+// order come from those prefixes plus an exclusive scan inside the chunk.
+__global__ void __launch_bounds__(256) wl_finish_kernel(int64_t rows, int n_buckets,
+                                                        const int32_t* __restrict__ tmp_cols,
+                                                        const int32_t* __restrict__ tmp_len,
+                                                        int32_t* __restrict__ row_ptr,
+                                                        int32_t* __restrict__ col_idx,
+                                                        int32_t* __restrict__ row_perm,
+                                                        int32_t* __restrict__ bucket_ptr) {
   constexpr int K = kMaxBuckets + 1;   // [0] length sum, [1 + b] rows in bucket b
-  constexpr int NW = 1024 / kWave;
+  constexpr int NT = 256, NW = NT / kWave;
+  __shared__ int red[NW][2 * K];
   __shared__ int wtot[NW][K];
-  __shared__ int total[K];
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-  const int64_t chunk = (rows + 1023) / 1024;
-  const int64_t r0 = min((int64_t)tid * chunk, rows), r1 = min(r0 + chunk, rows);
-  int v[K];
+  const int64_t c0 = (int64_t)blockIdx.x * NT;
+  // ---- totals over all rows and over the rows before this chunk
+  int all[K], pre[K];
 #pragma unroll
-  for (int k = 0; k < K; ++k) v[k] = 0;
-  for (int64_t r = r0; r < r1; ++r) {
-    const int len = tmp_len[r];
-    v[0] += len;
-    const int bk = bucket_of(len);
+  for (int k = 0; k < K; ++k) all[k] = pre[k] = 0;
+  // UP lengths per thread are loaded before any is used (clamped to the last
+  // row, weight 0 past the end): one memory round trip per UP rows
+  constexpr int UP = 8;
+  for (int64_t r0 = tid; r0 < rows; r0 += (int64_t)NT * UP) {
+    int lens[UP];
 #pragma unroll
-    for (int b = 0; b < kMaxBuckets; ++b) v[1 + b] += (b == bk) ? 1 : 0;
-  }
-  // inclusive wave scans of all K values
-  int inc[K];
+    for (int u = 0; u < UP; ++u) lens[u] = tmp_len[min(r0 + (int64_t)u * NT, rows - 1)];
 #pragma unroll
-  for (int k = 0; k < K; ++k) inc[k] = v[k];
+    for (int u = 0; u < UP; ++u) {
+      const int64_t r = r0 + (int64_t)u * NT;
+      const int in_all = r < rows ? 1 : 0, in_pre = r < c0 ? 1 : 0;
+      const int len = lens[u] * in_all;
+      const int bk = bucket_of(lens[u]);
+      all[0] += len;
+      pre[0] += in_pre * len;
 #pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const int t = __shfl_up(inc[k], o, kWave);
-      if (lane >= o) inc[k] += t;
+      for (int b = 0; b < kMaxBuckets; ++b) {
+        const int one = (b == bk ? 1 : 0) * in_all;
+        all[1 + b] += one;
+        pre[1 + b] += in_pre * one;
+      }
     }
   }
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    all[k] = wave_sum_i(all[k]);
+    pre[k] = wave_sum_i(pre[k]);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      red[wave][k] = all[k];
+      red[wave][K + k] = pre[k];
+    }
+  }
+  // ---- this thread's row and the exclusive scan of the chunk
+  const int64_t r = c0 + tid;
+  const bool valid = r < rows;
+  const int len = valid ? tmp_len[r] : 0;
+  const int bk = valid ? bucket_of(len) : -1;
+  int v[K], inc[K];
+  v[0] = len;
+#pragma unroll
+  for (int b = 0; b < kMaxBuckets; ++b) v[1 + b] = b == bk ? 1 : 0;
+#pragma unroll
+  for (int k = 0; k < K; ++k) inc[k] = wave_incl_scan_i(v[k]);
   if (lane == kWave - 1) {
 #pragma unroll
     for (int k = 0; k < K; ++k) wtot[wave][k] = inc[k];
   }
   __syncthreads();
-  // thread k turns column k of the wave totals into exclusive wave prefixes
-  if (tid < K) {
-    int acc = 0;
-    for (int w = 0; w < NW; ++w) {
-      const int x = wtot[w][tid];
-      wtot[w][tid] = acc;
-      acc += x;
-    }
-    total[tid] = acc;
-  }
-  __syncthreads();
-  int excl[K], tot[K];
+  int tot[K], before[K], excl[K];
 #pragma unroll
   for (int k = 0; k < K; ++k) {
-    excl[k] = wtot[wave][k] + inc[k] - v[k];
-    tot[k] = total[k];
+    int t = 0, p = 0, w0 = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      t += red[w][k];
+      p += red[w][K + k];
+      w0 += w < wave ? wtot[w][k] : 0;
+    }
+    tot[k] = t;
+    before[k] = p;
+    excl[k] = w0 + inc[k] - v[k];
   }
   // bucket b starts after all rows of buckets < b
-  int base[kMaxBuckets];
-  {
-    int acc = 0;
+  int base_acc = 0, pos = 0;
 #pragma unroll
-    for (int b = 0; b < kMaxBuckets; ++b) {
-      base[b] = acc;
-      acc += (b < n_buckets) ? tot[1 + b] : 0;
-    }
-    if (tid == 0) {
-#pragma unroll
-      for (int b = 0; b < kMaxBuckets; ++b)
-        if (b < n_buckets) bucket_ptr[b] = base[b];
-      bucket_ptr[n_buckets] = acc;
-      row_ptr[rows] = tot[0];
-    }
+  for (int b = 0; b < kMaxBuckets; ++b) {
+    if (b == bk) pos = base_acc + before[1 + b] + excl[1 + b];
+    if (blockIdx.x == 0 && tid == 0 && b < n_buckets) bucket_ptr[b] = base_acc;
+    base_acc += b < n_buckets ? tot[1 + b] : 0;
   }
-  int run = excl[0];
-  int rank[kMaxBuckets];
-#pragma unroll
-  for (int b = 0; b < kMaxBuckets; ++b) rank[b] = base[b] + excl[1 + b];
-  for (int64_t r = r0; r < r1; ++r) {
-    const int len = tmp_len[r];
-    row_ptr[r] = run;
-    run += len;
-    const int bk = bucket_of(len);
-    int pos = 0;
-#pragma unroll
-    for (int b = 0; b < kMaxBuckets; ++b) {
-      if (b == bk) {
-        pos = rank[b];
-        rank[b] += 1;
-      }
-    }
+  if (blockIdx.x == 0 && tid == 0) {
+    bucket_ptr[n_buckets] = base_acc;
+    row_ptr[rows] = tot[0];
+  }
+  if (valid) {
+    row_ptr[r] = before[0] + excl[0];
     row_perm[pos] = (int32_t)r;
   }
-}
-
-__global__ void __launch_bounds__(256) wl_scatter_kernel(int64_t rows,
-                                                         const int32_t* __restrict__ tmp_cols,
-                                                         const int32_t* __restrict__ tmp_len,
-                                                         const int32_t* __restrict__ row_ptr,
-                                                         int32_t* __restrict__ col_idx) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
-  const int lane = threadIdx.x % kWave;
-  if (row >= rows) return;
-  const int n = tmp_len[row];
-  const int32_t* src = tmp_cols + row * kWidthPad;
-  int32_t* dst = col_idx + row_ptr[row];
-  for (int i = lane; i < n; i += kWave) dst[i] = src[i];
+  // ---- copy this row's ids to col_idx[row_ptr[r] ..]: 16-byte loads of the
+  // row's workspace slots (512-byte aligned), 4-byte stores (row_ptr is not)
+  if (valid) {
+    const int32_t* src = tmp_cols + r * kWidthPad;
+    int32_t* dst = col_idx + before[0] + excl[0];
+    for (int i = 0; i < len; i += 16) {
+      u32x4 x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[u] = *reinterpret_cast<const u32x4*>(src + i + 4 * u);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (i + 4 * u + e < len) dst[i + 4 * u + e] = (int32_t)x[u][e];
+    }
+  }
 }
 
 __global__ void __launch_bounds__(1024) cu_blocks_kernel(const int32_t* __restrict__ cu_seqlens,
@@ -241,11 +251,9 @@ int launch_worklist(const Geom& g, const sa_route_cfg& rc, int width_max, int n_
   while ((1 << nbits) < g.max_blocks) ++nbits;
   wl_rows_kernel<<<(unsigned)g.rows, 64, 0, st>>>(g, rc, nbits, b.J, b.tmp_cols, b.tmp_len, b.err);
   if (hipGetLastError() != hipSuccess) return SA_ERR_HIP;
-  wl_scan_kernel<<<1, 1024, 0, st>>>(g.rows, n_buckets, b.tmp_len, b.row_ptr, b.row_perm,
-                                     b.bucket_ptr);
-  if (hipGetLastError() != hipSuccess) return SA_ERR_HIP;
-  wl_scatter_kernel<<<(unsigned)((g.rows + 3) / 4), 256, 0, st>>>(g.rows, b.tmp_cols, b.tmp_len,
-                                                                  b.row_ptr, b.col_idx);
+  wl_finish_kernel<<<(unsigned)((g.rows + 255) / 256), 256, 0, st>>>(g.rows, n_buckets, b.tmp_cols, b.tmp_len,
+                                                                     b.row_ptr, b.col_idx, b.row_perm,
+                                                                     b.bucket_ptr);
   return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 
