@@ -11,7 +11,7 @@
 //   1. rows:    one wavefront per row: validate, add forced ids, LSD radix
 //               sort with 1-bit ballot splits through LDS, drop duplicates,
 //               write the row's unique ids and its length to workspace
-//   2. finish:  one workgroup per 256 rows: row_ptr (exclusive scan of the
+//   2. finish:  one workgroup per 64 or 256 rows: row_ptr (exclusive scan of the
 //               lengths), per-bucket counts -> bucket_ptr, the stable
 //               (bucket, row) order -> row_perm, and the copy of each row's
 //               ids to col_idx[row_ptr[row] ..].  Every workgroup reads all
@@ -97,11 +97,15 @@ __global__ void __launch_bounds__(64) wl_rows_kernel(Geom g, sa_route_cfg rc, in
     atomicOr(err, (er ? SA_WL_ERR_RANGE : 0) | (ea ? SA_WL_ERR_ACAUSAL : 0));
 }
 
-// Step 2 for rows c0 .. c0 + 255 (c0 = 256 * block).  Thread t first sums,
+// Step 2 for rows c0 .. c0 + NT - 1 (c0 = NT * block).  Thread t first sums,
 // over every row and over the rows before c0, the length and one count per
 // bucket; then owns row c0 + t: its row pointer and its slot in the bucket
 // order come from those prefixes plus an exclusive scan inside the chunk.
-__global__ void __launch_bounds__(256) wl_finish_kernel(int64_t rows, int n_buckets,
+// NT = 64 for up to 1024 rows (more, smaller workgroups: decode's 512 rows
+// 18 us vs 27 us in two 256-thread ones), else 256 (fewer passes over the row
+// lengths per workgroup).
+template <int NT>
+__global__ void __launch_bounds__(NT) wl_finish_kernel(int64_t rows, int n_buckets,
                                                         const int32_t* __restrict__ tmp_cols,
                                                         const int32_t* __restrict__ tmp_len,
                                                         int32_t* __restrict__ row_ptr,
@@ -109,7 +113,7 @@ __global__ void __launch_bounds__(256) wl_finish_kernel(int64_t rows, int n_buck
                                                         int32_t* __restrict__ row_perm,
                                                         int32_t* __restrict__ bucket_ptr) {
   constexpr int K = kMaxBuckets + 1;   // [0] length sum, [1 + b] rows in bucket b
-  constexpr int NT = 256, NW = NT / kWave;
+  constexpr int NW = NT / kWave;
   __shared__ int red[NW][2 * K];
   __shared__ int wtot[NW][K];
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
@@ -200,19 +204,24 @@ __global__ void __launch_bounds__(256) wl_finish_kernel(int64_t rows, int n_buck
     row_perm[pos] = (int32_t)r;
   }
   // ---- copy this row's ids to col_idx[row_ptr[r] ..]: 16-byte loads of the
-  // row's workspace slots (512-byte aligned), 4-byte stores (row_ptr is not)
+  // row's workspace slots (512-byte aligned) in two halves of 64 slots, each
+  // loaded whole before any store (one memory round trip per half), 4-byte
+  // stores (row_ptr is not aligned)
   if (valid) {
     const int32_t* src = tmp_cols + r * kWidthPad;
     int32_t* dst = col_idx + before[0] + excl[0];
-    for (int i = 0; i < len; i += 16) {
-      u32x4 x[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) x[u] = *reinterpret_cast<const u32x4*>(src + i + 4 * u);
+    for (int hf = 0; hf < kWidthPad / 64; ++hf) {
+      if (64 * hf < len) {
+        u32x4 x[16];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < 16; ++u) x[u] = *reinterpret_cast<const u32x4*>(src + 64 * hf + 4 * u);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (i + 4 * u + e < len) dst[i + 4 * u + e] = (int32_t)x[u][e];
+        for (int u = 0; u < 16; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (64 * hf + 4 * u + e < len) dst[64 * hf + 4 * u + e] = (int32_t)x[u][e];
+      }
     }
   }
 }
@@ -251,9 +260,14 @@ int launch_worklist(const Geom& g, const sa_route_cfg& rc, int width_max, int n_
   while ((1 << nbits) < g.max_blocks) ++nbits;
   wl_rows_kernel<<<(unsigned)g.rows, 64, 0, st>>>(g, rc, nbits, b.J, b.tmp_cols, b.tmp_len, b.err);
   if (hipGetLastError() != hipSuccess) return SA_ERR_HIP;
-  wl_finish_kernel<<<(unsigned)((g.rows + 255) / 256), 256, 0, st>>>(g.rows, n_buckets, b.tmp_cols, b.tmp_len,
-                                                                     b.row_ptr, b.col_idx, b.row_perm,
-                                                                     b.bucket_ptr);
+  if (g.rows <= 1024)
+    wl_finish_kernel<64><<<(unsigned)((g.rows + 63) / 64), 64, 0, st>>>(g.rows, n_buckets, b.tmp_cols, b.tmp_len,
+                                                                       b.row_ptr, b.col_idx, b.row_perm,
+                                                                       b.bucket_ptr);
+  else
+    wl_finish_kernel<256><<<(unsigned)((g.rows + 255) / 256), 256, 0, st>>>(g.rows, n_buckets, b.tmp_cols,
+                                                                          b.tmp_len, b.row_ptr, b.col_idx,
+                                                                          b.row_perm, b.bucket_ptr);
   return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 
