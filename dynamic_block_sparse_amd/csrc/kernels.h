@@ -8,13 +8,20 @@ namespace sa {
 // Block offsets of a packed batch: cu_blocks[s] = sum_{s' < s} ceil(len_s' / b).
 int launch_cu_blocks(const int32_t* cu_seqlens, int32_t* cu_blocks, int batch, hipStream_t st);
 
-int launch_summary(const Geom& g, int dtype, const void* k, float* summ, int slots,
-                   hipStream_t st);
+// Block summaries of k; with qbar (prefill, mean pooling) the same pass also
+// writes each route row's pooled query, [rows, d] fp32.
+int launch_summary(const Geom& g, int dtype, const void* k, float* summ, int slots, const void* q,
+                   float* qbar, hipStream_t st);
 size_t route_smem_bytes(const Geom& g, int qpool);
 // Candidate scores of every row: [rows, max_blocks] fp32 (workspace).
 size_t route_scores_bytes(const Geom& g);
+// Pooled queries written by the summary pass: [rows, d] fp32 (workspace;
+// prefill with mean pooling only, else 0).
+size_t route_qbar_bytes(const Geom& g, int qpool);
+// qbar: pooled queries from launch_summary (prefill rows are then scored in
+// tiles), or null to pool inside the per-row score kernel.
 int launch_route(const Geom& g, const sa_route_cfg& rc, int dtype, const void* q,
-                 const float* summ, float* scores, int32_t* J, hipStream_t st);
+                 const float* summ, const float* qbar, float* scores, int32_t* J, hipStream_t st);
 
 struct WorklistBufs {
   const int32_t* J;

@@ -13,20 +13,34 @@
 
 namespace sa {
 
+// Route row of (sequence s, routing head h, query block r): the inverse of
+// decode_row for prefill rows.
+__device__ __forceinline__ int64_t prefill_row_index(const Geom& g, int s, int h, int r, int blk0, int nblk) {
+  if (g.varlen) return (int64_t)g.hr * blk0 + (int64_t)h * nblk + r;
+  return ((int64_t)s * g.hr + h) * nblk + r;
+}
+
 // ---------------------------------------------------------------------------
 // Block summaries.  One wavefront per (sequence, kv head, key block): lanes own
 // an 8-element column chunk and a key phase, so every load is a 16-byte (bf16)
 // or 32-byte (fp32) piece of a contiguous 64 x d tile; phases are summed with
 // cross-lane shuffles.  Padding tokens past the sequence end never enter the
 // sum, and a partial block divides by its own count.
+// With `qbar`, grid rows hkv .. hkv + hr - 1 pool the queries the same way in
+// the same pass ([P2] Eq 6 mean pooling): the wavefront of (sequence, routing
+// head h, query block r) averages the block's valid queries over the row's
+// query heads (the KV head's group when routing is shared) and writes the
+// route row's pooled vector to qbar[row][0 .. d).
 template <typename T, int D>
 __global__ void __launch_bounds__(256) summary_kernel(Geom g, const T* __restrict__ k,
-                                                      float* __restrict__ summ, int slots) {
+                                                      float* __restrict__ summ, int slots,
+                                                      const T* __restrict__ q, float* __restrict__ qbar) {
   constexpr int CH = D / 8;        // column chunks per row
   constexpr int PH = kWave / CH;   // key phases per wave
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int slot = blockIdx.x * 4 + wave;
-  const int h = blockIdx.y;
+  const bool pool_q = (int)blockIdx.y >= g.hkv;
+  const int h = pool_q ? (int)blockIdx.y - g.hkv : (int)blockIdx.y;
   if (slot >= slots) return;
   int s, j, tok0 = 0, blk0 = 0, len;
   if (g.varlen) {
@@ -51,7 +65,10 @@ __global__ void __launch_bounds__(256) summary_kernel(Geom g, const T* __restric
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  const T* base = k + kv_offset(g, s, h, tok0, j * kBlock) + c * 8;
+  const int nh = pool_q ? g.hpr : 1;   // query heads pooled into the row
+  const int h0 = g.share ? h * g.group : h;
+  const T* base = pool_q ? q + q_offset(g, s, h0, tok0, j * kBlock) + c * 8
+                         : k + kv_offset(g, s, h, tok0, j * kBlock) + c * 8;
   auto add_row = [&](int t) {
     const T* p = base + (int64_t)t * D;
     if constexpr (sizeof(T) == 2) {
@@ -71,12 +88,15 @@ __global__ void __launch_bounds__(256) summary_kernel(Geom g, const T* __restric
       }
     }
   };
-  if (cnt == kBlock) {
-    // full block: every row's load is issued before the sums need them
+  for (int hh = 0; hh < nh; ++hh) {
+    if (cnt == kBlock) {
+      // full block: every row's load is issued before the sums need them
 #pragma unroll
-    for (int t = 0; t < kBlock / PH; ++t) add_row(ph + t * PH);
-  } else {
-    for (int t = ph; t < cnt; t += PH) add_row(t);
+      for (int t = 0; t < kBlock / PH; ++t) add_row(ph + t * PH);
+    } else {
+      for (int t = ph; t < cnt; t += PH) add_row(t);
+    }
+    base += g.q_head;   // next query head of the group (only read when pooling queries)
   }
   // sum the key phases: partners lane ^ 8 (D = 64 only), ^ 16, ^ 32
 #pragma unroll
@@ -87,8 +107,10 @@ __global__ void __launch_bounds__(256) summary_kernel(Geom g, const T* __restric
     acc[i] = __uint_as_float(u);
   }
   if (ph == 0) {
-    const float inv = 1.f / (float)cnt;
-    float* out = summ + sum_offset(g, s, h, blk0, j) + c * 8;
+    const float inv = 1.f / (float)(cnt * nh);
+    const int nblk = g.varlen ? g.cu_blocks[s + 1] - blk0 : ceil_div(g.n, kBlock);
+    float* out = pool_q ? qbar + prefill_row_index(g, s, h, j, blk0, nblk) * D + c * 8
+                        : summ + sum_offset(g, s, h, blk0, j) + c * 8;
     f32x4 o0, o1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -133,6 +155,102 @@ __device__ __forceinline__ RouteRow route_row(const Geom& g, const sa_route_cfg&
   w.nc = max(n_hist - w.start, 0);
   w.nforced = 1 + ((w.ff && w.cur != 0) ? 1 : 0);
   return w;
+}
+
+// ---------------------------------------------------------------------------
+// Prefill scores under mean pooling, as tiles of the product Qbar C^T of one
+// (sequence, routing head) ([P2] Eq 6: g_rj = qbar_r . c_j for j < r): a
+// workgroup takes kScoreRows query blocks x kScoreCols key blocks, stages
+// the pooled queries (from the summary pass) and the summaries in LDS (every
+// load issued before the first store), and each thread accumulates 2-8 dot
+// products in fp32.  16 x 32 tiles for short histories (more workgroups,
+// short FMA chains), 32 x 64 for long ones (fewer staged bytes per score).  Scored per row instead, every summary is read
+// once per later query block (O(N^2 d) reads from L2); here once per tile row.
+// Scores land in scores[row * max_blocks + (j - start_r)] for the row's
+// candidates j (start_r = 1 when block 0 is forced and r > 0).
+template <int D, int kScoreRows, int kScoreCols>
+__global__ void __launch_bounds__(256) route_score_tile_kernel(Geom g, sa_route_cfg rc,
+                                                               const float* __restrict__ qbar,
+                                                               const float* __restrict__ summ,
+                                                               float* __restrict__ scores) {
+  constexpr int LD = D + 4;   // row pitch in floats
+  constexpr int QV = kScoreRows * D / 4 / 256, CV = kScoreCols * D / 4 / 256;   // float4 per thread
+  __shared__ __attribute__((aligned(16))) float qs[kScoreRows * LD];
+  __shared__ __attribute__((aligned(16))) float cs[kScoreCols * LD];
+  const int s = blockIdx.z / g.hr, h = blockIdx.z % g.hr;
+  int blk0 = 0, nblk;
+  if (g.varlen) {
+    blk0 = g.cu_blocks[s];
+    nblk = g.cu_blocks[s + 1] - blk0;
+  } else {
+    nblk = ceil_div(g.n, kBlock);
+  }
+  const int r0 = blockIdx.x * kScoreRows, j0 = blockIdx.y * kScoreCols;
+  // candidates satisfy j < r <= r0 + kScoreRows - 1: tiles above the diagonal have none
+  if (r0 >= nblk || j0 > r0 + kScoreRows - 2) return;   // uniform
+  const int kvh = g.share ? h : h / g.group;
+  const int64_t row0 = prefill_row_index(g, s, h, 0, blk0, nblk);   // rows of (s, h) are row0 + r
+  const float* cbase = summ + sum_offset(g, s, kvh, blk0, 0);
+  const int tid = threadIdx.x;
+  // stage (rows past the end: clamped copies, never written out)
+  f32x4 qv4[QV], cv4[CV];
+#pragma unroll
+  for (int u = 0; u < QV; ++u) {
+    const int e = tid + 256 * u, rr = e / (D / 4), k4 = e % (D / 4);
+    qv4[u] = *reinterpret_cast<const f32x4*>(qbar + (row0 + min(r0 + rr, nblk - 1)) * D + 4 * k4);
+  }
+#pragma unroll
+  for (int u = 0; u < CV; ++u) {
+    const int e = tid + 256 * u, jj = e / (D / 4), k4 = e % (D / 4);
+    cv4[u] = *reinterpret_cast<const f32x4*>(cbase + (int64_t)min(j0 + jj, nblk - 1) * D + 4 * k4);
+  }
+#pragma unroll
+  for (int u = 0; u < QV; ++u) {
+    const int e = tid + 256 * u;
+    *reinterpret_cast<f32x4*>(qs + (e / (D / 4)) * LD + 4 * (e % (D / 4))) = qv4[u];
+  }
+#pragma unroll
+  for (int u = 0; u < CV; ++u) {
+    const int e = tid + 256 * u;
+    *reinterpret_cast<f32x4*>(cs + (e / (D / 4)) * LD + 4 * (e % (D / 4))) = cv4[u];
+  }
+  __syncthreads();
+  constexpr int RA = kScoreRows * kScoreCols / 256 >= 2 && kScoreRows >= 32 ? 2 : 1;   // rows per thread
+  constexpr int CB = kScoreRows * kScoreCols / 256 / RA;                              // columns per thread
+  constexpr int CG = kScoreCols / CB;                                                 // column groups
+  const int rg = tid / CG, cg = tid % CG;   // rows RA rg ..; columns CB cg ..
+  float acc[RA][CB];
+#pragma unroll
+  for (int a = 0; a < RA; ++a)
+#pragma unroll
+    for (int b = 0; b < CB; ++b) acc[a][b] = 0.f;
+#pragma unroll 4
+  for (int k = 0; k < D; k += 4) {
+    f32x4 qv[RA], cv[CB];
+#pragma unroll
+    for (int a = 0; a < RA; ++a) qv[a] = *reinterpret_cast<const f32x4*>(qs + (RA * rg + a) * LD + k);
+#pragma unroll
+    for (int b = 0; b < CB; ++b) cv[b] = *reinterpret_cast<const f32x4*>(cs + (CB * cg + b) * LD + k);
+#pragma unroll
+    for (int a = 0; a < RA; ++a)
+#pragma unroll
+      for (int b = 0; b < CB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[a][b] = __builtin_fmaf(qv[a][i], cv[b][i], acc[a][b]);
+  }
+  const bool ff = (rc.forced & SA_FORCE_FIRST) != 0;
+#pragma unroll
+  for (int a = 0; a < RA; ++a) {
+    const int r = r0 + RA * rg + a;
+    if (r >= nblk) continue;
+    const int start = (ff && r > 0) ? 1 : 0;
+    float* srow = scores + (row0 + r) * (int64_t)g.max_blocks;
+#pragma unroll
+    for (int b = 0; b < CB; ++b) {
+      const int j = j0 + CB * cg + b;
+      if (j >= start && j < r) srow[j - start] = acc[a][b];
+    }
+  }
 }
 
 // Decode rows (few, with long histories) split their candidates into chunks
@@ -382,20 +500,20 @@ __global__ void __launch_bounds__(64) route_select_kernel(Geom g, sa_route_cfg r
 }
 
 // ---------------------------------------------------------------------------
-int launch_summary(const Geom& g, int dtype, const void* k, float* summ, int slots,
-                   hipStream_t st) {
+int launch_summary(const Geom& g, int dtype, const void* k, float* summ, int slots, const void* q,
+                   float* qbar, hipStream_t st) {
   if (slots <= 0) return SA_OK;
-  dim3 grid((slots + 3) / 4, g.hkv);
+  dim3 grid((slots + 3) / 4, g.hkv + (qbar ? g.hr : 0));
   if (dtype == SA_BF16) {
     if (g.d == 128)
-      summary_kernel<__bf16, 128><<<grid, 256, 0, st>>>(g, (const __bf16*)k, summ, slots);
+      summary_kernel<__bf16, 128><<<grid, 256, 0, st>>>(g, (const __bf16*)k, summ, slots, (const __bf16*)q, qbar);
     else
-      summary_kernel<__bf16, 64><<<grid, 256, 0, st>>>(g, (const __bf16*)k, summ, slots);
+      summary_kernel<__bf16, 64><<<grid, 256, 0, st>>>(g, (const __bf16*)k, summ, slots, (const __bf16*)q, qbar);
   } else {
     if (g.d == 128)
-      summary_kernel<float, 128><<<grid, 256, 0, st>>>(g, (const float*)k, summ, slots);
+      summary_kernel<float, 128><<<grid, 256, 0, st>>>(g, (const float*)k, summ, slots, (const float*)q, qbar);
     else
-      summary_kernel<float, 64><<<grid, 256, 0, st>>>(g, (const float*)k, summ, slots);
+      summary_kernel<float, 64><<<grid, 256, 0, st>>>(g, (const float*)k, summ, slots, (const float*)q, qbar);
   }
   return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
@@ -408,11 +526,33 @@ size_t route_smem_bytes(const Geom& g, int qpool) {
 }
 
 size_t route_scores_bytes(const Geom& g) { return (size_t)g.rows * g.max_blocks * sizeof(float); }
+size_t route_qbar_bytes(const Geom& g, int qpool) {
+  return (g.mode == SA_PREFILL && qpool == SA_POOL_MEAN) ? (size_t)g.rows * g.d * sizeof(float) : 0;
+}
+
+int launch_select(const Geom& g, const sa_route_cfg& rc, const float* scores, int32_t* J, hipStream_t st);
 
 int launch_route(const Geom& g, const sa_route_cfg& rc, int dtype, const void* q,
-                 const float* summ, float* scores, int32_t* J, hipStream_t st) {
+                 const float* summ, const float* qbar, float* scores, int32_t* J, hipStream_t st) {
   if (g.rows <= 0) return SA_OK;
   const size_t smem = route_smem_bytes(g, rc.qpool);
+  const int mbk = std::max(g.max_blocks, 1);
+  if (g.mode == SA_PREFILL && rc.qpool == SA_POOL_MEAN && qbar && (int64_t)g.batch * g.hr <= 65535) {
+    // measured on MI355X: 16 x 32 tiles 6.0 us vs 7.9 for 32 x 64 at 128 blocks
+    // per sequence, 44 us vs 39 at 512
+    const bool small = mbk <= 256;
+    const int tr = small ? 16 : 32, tc = small ? 32 : 64;
+    dim3 tgrid((unsigned)((mbk + tr - 1) / tr), (unsigned)((mbk + tc - 1) / tc), (unsigned)(g.batch * g.hr));
+    if (g.d == 128) {
+      if (small) route_score_tile_kernel<128, 16, 32><<<tgrid, 256, 0, st>>>(g, rc, qbar, summ, scores);
+      else route_score_tile_kernel<128, 32, 64><<<tgrid, 256, 0, st>>>(g, rc, qbar, summ, scores);
+    } else {
+      if (small) route_score_tile_kernel<64, 16, 32><<<tgrid, 256, 0, st>>>(g, rc, qbar, summ, scores);
+      else route_score_tile_kernel<64, 32, 64><<<tgrid, 256, 0, st>>>(g, rc, qbar, summ, scores);
+    }
+    if (hipGetLastError() != hipSuccess) return SA_ERR_HIP;
+    return launch_select(g, rc, scores, J, st);
+  }
   const int chunk = g.mode == SA_DECODE ? kDecodeChunk : std::max(g.max_blocks, 1);
   const int chunks = (std::max(g.max_blocks, 1) + chunk - 1) / chunk;
   dim3 grid((unsigned)g.rows, (unsigned)chunks);
@@ -429,6 +569,10 @@ int launch_route(const Geom& g, const sa_route_cfg& rc, int dtype, const void* q
   }
 #undef SA_SCORE
   if (hipGetLastError() != hipSuccess) return SA_ERR_HIP;
+  return launch_select(g, rc, scores, J, st);
+}
+
+int launch_select(const Geom& g, const sa_route_cfg& rc, const float* scores, int32_t* J, hipStream_t st) {
   // keys per lane: the smallest power of two with 64 E >= max_blocks
   dim3 sgrid((unsigned)g.rows);
   const int mb = std::max(g.max_blocks, 1);

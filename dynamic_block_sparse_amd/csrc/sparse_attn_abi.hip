@@ -19,6 +19,7 @@ int popcount2(uint32_t f) { return (int)(f & 1u) + (int)((f >> 1) & 1u); }
 
 struct Plan {
   Geom g;
+  int qpool = SA_POOL_MEAN;
   int width_max = 0;
   int n_buckets = 0;
   int64_t kv_slots = 0;   // summary slots
@@ -113,6 +114,7 @@ int validate(const sa_problem* p, const sa_route_cfg* rc, Plan* out) {
   out->n_buckets = nbk;
   out->nnz_cap = g.rows * out->width_max;
   if (out->nnz_cap > INT32_MAX || g.rows > INT32_MAX) return SA_ERR_UNSUPPORTED;
+  out->qpool = rc->qpool;
   return SA_OK;
 }
 
@@ -146,6 +148,7 @@ size_t ws_size(const Plan& pl, int which, int splits) {
   size_t sz = ws_cu_blocks(pl);
   if (which == 0) {
     sz += align_up(route_scores_bytes(pl.g));
+    sz += align_up(route_qbar_bytes(pl.g, pl.qpool));
   } else if (which == 1) {
     sz += align_up((size_t)pl.g.rows * kMaxWidth * sizeof(int32_t));
     sz += align_up((size_t)pl.g.rows * sizeof(int32_t));
@@ -213,11 +216,16 @@ int sparse_attn_route(const sa_problem* p, const sa_route_cfg* rc, const void* q
   if (ws_bytes < ws_size(pl, 0, 1) || (ws_size(pl, 0, 1) && !ws)) return SA_ERR_WORKSPACE;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   if ((st = prep_cu_blocks(pl, ws, hs)) != SA_OK) return st;
+  unsigned char* w = reinterpret_cast<unsigned char*>(ws) + ws_cu_blocks(pl);
+  float* scores = reinterpret_cast<float*>(w);
+  // pooled queries come out of the summary pass when it runs here
+  float* qbar = nullptr;
+  if (!summaries_in && route_qbar_bytes(pl.g, pl.qpool) > 0)
+    qbar = reinterpret_cast<float*>(w + align_up(route_scores_bytes(pl.g)));
   if (!summaries_in) {
-    if ((st = launch_summary(pl.g, p->dtype, k, summaries, (int)pl.kv_slots, hs)) != SA_OK) return st;
+    if ((st = launch_summary(pl.g, p->dtype, k, summaries, (int)pl.kv_slots, q, qbar, hs)) != SA_OK) return st;
   }
-  float* scores = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(ws) + ws_cu_blocks(pl));
-  return launch_route(pl.g, *rc, p->dtype, q, summaries, scores, J, hs);
+  return launch_route(pl.g, *rc, p->dtype, q, summaries, qbar, scores, J, hs);
 }
 
 int sparse_attn_build_worklist(const sa_problem* p, const sa_route_cfg* rc, const int32_t* J,

@@ -150,8 +150,11 @@ size_t sparse_attn_workspace_size(const sa_problem* p, const sa_route_cfg* rc, i
  *   Scores are fp32; ties closer than fp32 rounding may order differently from
  *   an exact evaluation.
  *   ws          (device) sparse_attn_workspace_size(p, rc, 0, 0) bytes: the
- *               candidate scores of every row ([rows, max_blocks] fp32) and,
- *               for a packed batch, the per-sequence block offsets. */
+ *               candidate scores of every row ([rows, max_blocks] fp32); for
+ *               prefill with mean pooling, the pooled query of every row
+ *               ([rows, d] fp32, written by the summary pass when
+ *               summaries_in = 0); for a packed batch, the per-sequence block
+ *               offsets. */
 int sparse_attn_route(const sa_problem* p, const sa_route_cfg* rc, const void* q, const void* k,
                       float* summaries, int32_t summaries_in, int32_t* J, void* ws,
                       size_t ws_bytes, void* stream);
