@@ -46,6 +46,10 @@ SMALL = [
     wk.TINY_F32,
     wk.TINY_F32_DENSE,
     wk.TINY_F32.replace(name="tiny_f32_ragged_n500_d128_mean", seqlen=500, head_dim=128, qpool="mean", k_b=4),
+    # d = 64 mean pooling with block 0 forced: the pooled-query summary pass and
+    # the 16 x 32 score tiles with fp32 inputs
+    wk.TINY_F32.replace(name="tiny_f32_n2500_d64_mean_ff", batch=2, seqlen=2500, qpool="mean", k_b=6,
+                        forced_first=True),
     wk.PREFILL_MHA.replace(name="mha_small_h3_n1000_kb16", heads_q=3, heads_kv=3, seqlen=1000),
     wk.PREFILL_MHA.replace(name="mha_small_h2_n700_kb5_maxpool", heads_q=2, heads_kv=2, seqlen=700,
                            k_b=5, qpool="max"),
