@@ -36,11 +36,12 @@ constexpr float kLog2e = 1.4426950408889634f;
 // LDS per stage: K [64 keys][128 d] and V [64 keys][128 d], both row-major in
 // 16-byte chunks with an XOR swizzle on the chunk index, filled straight from
 // HBM with 16-byte global->LDS loads (no staging registers; the swizzle is
-// applied by permuting the per-lane source addresses).  NBUF = 2 double-
-// buffers the stages: the next tile's loads are in flight while the current
-// tile is computed.  V^T operands come from the LDS transpose read
-// (ds_read_b64_tr_b16): in each 16-lane group it returns, to lane i, the
-// i-th column of the 4 x 16 block that the group's lanes read row-wise.
+// applied by permuting the per-lane source addresses).  The lock-step kernel
+// keeps one stage and overlaps the next tile's K and this tile's V with the
+// products; the ping-pong kernel keeps 4-deep K and V rings.  V^T operands
+// come from the LDS transpose read (ds_read_b64_tr_b16): in each 16-lane group
+// it returns, to lane i, the i-th column of the 4 x 16 block that the group's
+// lanes read row-wise.
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 #define SA_LDS __attribute__((address_space(3)))
@@ -265,19 +266,17 @@ __device__ __forceinline__ void store_row(const f32x16 (&oacc)[4], float m, floa
 }
 
 // --------------------------------------------------------------------------
-// Lock-step kernel.  PIPE = 0: one stage, loads then compute; PIPE = 2: one
-// stage, V(t) and K(t+1) loads overlap S(t) / softmax / P V(t); PIPE = R >= 3:
-// an (R-1)-stage ring, tile t+R-2 is issued while tile t is computed.
+// Lock-step kernel, one LDS stage.  PIPE = 0: loads, then the tile's products;
+// PIPE = 2: V(t) and K(t+1) loads overlap S(t) / softmax / P V(t).
 template <int HPR, int PIPE>
 __global__ void __launch_bounds__(128 * HPR) prefill_bf16_kernel(Geom g, FwdBufs a, int xcd_run) {
-  constexpr int NBUF = PIPE >= 3 ? PIPE - 1 : 1;
+  static_assert(PIPE == 0 || PIPE == 2, "pipeline form");
   constexpr int D = 128;
   constexpr int NW = 2 * HPR;               // wavefronts: 2 per query head
   constexpr int TILE = 64 * D * 2;          // bytes of one K (or V) tile
-  constexpr int LOADS = 2 * (TILE / 1024) / NW;   // 1 KB wave loads per tile per wave
-  constexpr int HALF_LOADS = LOADS / 2;           // of K or of V alone
+  constexpr int HALF_LOADS = (TILE / 1024) / NW;  // 1 KB wave loads of a K (or V) tile per wave
   constexpr int kDepth = 6;                       // MFMAs of lead for the LDS operand reads
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[NBUF * 2 * TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * TILE];
 
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -337,19 +336,11 @@ __global__ void __launch_bounds__(128 * HPR) prefill_bf16_kernel(Geom g, FwdBufs
         load_lds16(vbytes + off + kc * 256 + ((cl ^ vsw(key)) << 4), vt + i * 1024);
       }
     };
-    auto issue = [&](int it, int buf) {
-      issue_k(it, lds + buf * 2 * TILE);
-      issue_v(it, lds + buf * 2 * TILE + TILE);
-    };
+    unsigned char* const kt = lds;
+    unsigned char* const vt = lds + TILE;
     if (ntiles > 0) {
-      if (PIPE == 2) {
-        issue_k(0, lds);
-      } else {
-  #pragma unroll
-        for (int p = 0; p < NBUF - 1; ++p)
-          if (p < ntiles) issue(p, p);
-        if (NBUF == 1) issue(0, 0);
-      }
+      issue_k(0, kt);
+      if (PIPE == 0) issue_v(0, vt);
     }
 
     bf16x8 qreg[8];
@@ -365,32 +356,16 @@ __global__ void __launch_bounds__(128 * HPR) prefill_bf16_kernel(Geom g, FwdBufs
     bf16x8 pb[2][2];
 
     for (int it = 0; it < ntiles; ++it) {
-      const int buf = NBUF > 1 ? it % NBUF : 0;
-      unsigned char* kt = lds + buf * 2 * TILE;
-      unsigned char* vt = kt + TILE;
       if (PIPE == 2) {
         // K(it) landed (only it is outstanding); every wave is past P V(it-1)
         wait_vmcnt<0>();
         block_barrier();
         issue_v(it, vt);
-      } else if (NBUF > 1) {
-        // the ring slot of tile it+NBUF-1 was last read at iteration it-1,
-        // which ended with a barrier; keep NBUF-1 tiles in flight
-        const int nxt = it + NBUF - 1;
-        if (nxt < ntiles) {
-          issue(nxt, nxt % NBUF);
-          wait_vmcnt<(NBUF - 1) * LOADS>();
-        } else {
-          // no new issue: tiles it+1 .. min(it+NBUF-2, ntiles-1) may stay in flight
-          const int younger = min(NBUF - 2, ntiles - 1 - it);
-          if (younger >= 3) wait_vmcnt<3 * LOADS>();
-          else if (younger == 2) wait_vmcnt<2 * LOADS>();
-          else if (younger == 1) wait_vmcnt<LOADS>();
-          else wait_vmcnt<0>();
-        }
-        block_barrier();
       } else {
-        if (it > 0) issue(it, 0);   // the previous iteration ended with a barrier
+        if (it > 0) {   // the previous iteration ended with a barrier
+          issue_k(it, kt);
+          issue_v(it, vt);
+        }
         wait_vmcnt<0>();
         block_barrier();
       }
