@@ -50,15 +50,27 @@ __device__ __forceinline__ int ksw(int key) { return key & 15; }
 // V rows: the four rows a transpose read touches land in distinct bank groups
 __device__ __forceinline__ int vsw(int key) { return ((key & 3) << 2) + ((key & 2)); }
 
-// 16-byte global->LDS load: lane l's 16 bytes land at lds_wave_base + 16 l.
+// 16-byte global->LDS load: lane l's 16 bytes, read from base + off (base a
+// wave-uniform address in SGPRs, off the lane's 32-bit byte offset), land at
+// lds_wave_base + 16 l.  The tile loops keep every lane's offset in a register
+// for the whole row, so a tile's loads take no vector address arithmetic.
 // Issued as inline assembly so that the compiler's wait-count insertion does
 // not treat every later LDS read as dependent on it (it would otherwise wait
 // for all loads, including the next tile's prefetch); the kernel waits for
 // these loads explicitly with wait_vmcnt before each barrier.
-__device__ __forceinline__ void load_lds16(const void* g, const unsigned char* lds_wave_base) {
+__device__ __forceinline__ void load_lds16_sv(const unsigned char* base, uint32_t off,
+                                              const unsigned char* lds_wave_base) {
   const uint32_t m0 = (uint32_t)(uintptr_t)(SA_LDS const unsigned char*)lds_wave_base;
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(g), "s"(m0) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(off), "s"(base), "s"(m0) : "memory", "m0");
+}
+
+// A wave-uniform pointer the compiler cannot prove uniform, moved to SGPRs.
+__device__ __forceinline__ const unsigned char* uniform_ptr(const unsigned char* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const unsigned char*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
@@ -102,7 +114,7 @@ constexpr float kGrow = 8.0f;
 // position; `masked` says whether any key of the tile can be masked for this
 // row (the diagonal block, or a block that runs past the sequence end).
 __device__ __forceinline__ void softmax_tile(f32x16 (&sacc)[2], bf16x8 (&pb)[2][2], f32x16 (&oacc)[4],
-                                             float& m, float& lsum, bool masked, int kbase, int qpos,
+                                             float& m, f32x16& negm, float& lsum, bool masked, int kbase, int qpos,
                                              int len, int half) {
   if (masked) {
 #pragma unroll
@@ -136,6 +148,8 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&sacc)[2], bf16x8 (&pb)[2][
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[kb][i] -= shift;
     m = (first ? 0.f : m) + shift;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) negm[i] = -m;
   }
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
@@ -155,7 +169,8 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&sacc)[2], bf16x8 (&pb)[2][
         pair[1] = pb[kb][h][2 * e + 1];
         r[e] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, r[e], false);
       }
-  lsum += sum_xor32((r[0] + r[1]) + (r[2] + r[3]));
+  // this lane's half of the row's keys; the two halves are added once, at the end
+  lsum += (r[0] + r[1]) + (r[2] + r[3]);
 }
 
 // LDS reads behind operand i of an MFMA phase (two transpose reads for a V^T
@@ -180,7 +195,7 @@ constexpr int mfma_reads_before(int n) {
 template <bool PV, bool S, int DEPTH>
 __device__ __forceinline__ void mfma_phase(f32x16 (&oacc)[4], const bf16x8 (&pb)[2][2], const unsigned char* vt,
                                            f32x16 (&sacc)[2], const unsigned char* kt, const bf16x8 (&qreg)[8],
-                                           float m, int lane) {
+                                           const f32x16& negm, int lane) {
   constexpr int NPV = PV ? 16 : 0, NS = S ? 16 : 0, N = NPV + NS;
   const int l32 = lane & 31, half = lane >> 5;
   const int gi = lane >> 4, li = lane & 15, vh = gi >> 1, vdh = gi & 1;
@@ -216,12 +231,8 @@ __device__ __forceinline__ void mfma_phase(f32x16 (&oacc)[4], const bf16x8 (&pb)
       oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kb][ks], oacc[db], 0, 0, 0);
     } else {
       constexpr int ks = (I - NPV) >> 1, kb = (I - NPV) & 1;
-      if constexpr (ks == 0) {   // the accumulator starts at the reference offset
-        const float init = m == -INFINITY ? 0.f : -m;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[kb][i] = init;
-      }
-      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[ks], sacc[kb], 0, 0, 0);
+      // the accumulator starts at the reference offset -m (0 before the first tile)
+      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[ks], ks == 0 ? negm : sacc[kb], 0, 0, 0);
     }
     __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
     if constexpr (mfma_reads<NPV, N>(I + DEPTH) > 0)
@@ -309,33 +320,43 @@ __global__ void __launch_bounds__(128 * HPR) prefill_bf16_kernel(Geom g, FwdBufs
       return it < 64 ? __builtin_amdgcn_readlane(jl0, it) : __builtin_amdgcn_readlane(jl1, it - 64);
     };
 
-    // 16-byte global->LDS loads of tile `it`: K into kt, V into vt
+    // 16-byte global->LDS loads of tile `it`: K into kt, V into vt.  Wave w
+    // loads the 1 KB slices w, w + NW, ... of a tile; in slice i lane (sub, cl)
+    // carries 16-byte chunk cl of key 4 i + sub to its swizzled slot.  The
+    // per-lane byte offsets of a full tile are fixed for the row.
+    constexpr int NLD = 16 / NW;
     const int sub = lane >> 4, cl = lane & 15;
-    auto tile_off = [&](int it, int* cnt) {
+    uint32_t koff[NLD], voff[NLD];
+  #pragma unroll
+    for (int ii = 0; ii < NLD; ++ii) {
+      const int key = 4 * (wave + NW * ii) + sub;
+      koff[ii] = key * 256 + ((cl ^ ksw(key)) << 4);
+      voff[ii] = key * 256 + ((cl ^ vsw(key)) << 4);
+    }
+    const int64_t kv_row = kv_offset(g, ri.s, kvh, ri.tok0, 0) * 2;
+    const unsigned char* const krow = uniform_ptr(kbytes + kv_row);
+    const unsigned char* const vrow = uniform_ptr(vbytes + kv_row);
+    const int len_u = __builtin_amdgcn_readfirstlane(ri.len);
+    auto issue = [&](int it, const unsigned char* src, const uint32_t (&off)[NLD], unsigned char* dst, bool is_v) {
       const int j = tile_id(it);
-      *cnt = min(kBlock, ri.len - j * kBlock);
-      return kv_offset(g, ri.s, kvh, ri.tok0, j * kBlock) * 2;
-    };
-    auto issue_k = [&](int it, unsigned char* kt) {
-      int cnt;
-      const int64_t off = tile_off(it, &cnt);
+      const unsigned char* base = src + (int64_t)j * TILE;
+      const int cnt = len_u - j * kBlock;
+      if (cnt >= kBlock) {
   #pragma unroll
-      for (int i = wave; i < 16; i += NW) {
-        const int key = 4 * i + sub;
-        const int kc = min(key, cnt - 1);      // rows past the end: any valid row (masked later)
-        load_lds16(kbytes + off + kc * 256 + ((cl ^ ksw(key)) << 4), kt + i * 1024);
+        for (int ii = 0; ii < NLD; ++ii) load_lds16_sv(base, off[ii], dst + (wave + NW * ii) * 1024);
+      } else {
+        asm volatile("");   // the sequence's last, partial block: a real branch
+  #pragma unroll
+        for (int ii = 0; ii < NLD; ++ii) {
+          const int key = 4 * (wave + NW * ii) + sub;
+          const int kc = min(key, cnt - 1);   // rows past the end: any valid row (masked later)
+          const uint32_t o = kc * 256 + ((cl ^ (is_v ? vsw(key) : ksw(key))) << 4);
+          load_lds16_sv(base, o, dst + (wave + NW * ii) * 1024);
+        }
       }
     };
-    auto issue_v = [&](int it, unsigned char* vt) {
-      int cnt;
-      const int64_t off = tile_off(it, &cnt);
-  #pragma unroll
-      for (int i = wave; i < 16; i += NW) {
-        const int key = 4 * i + sub;
-        const int kc = min(key, cnt - 1);
-        load_lds16(vbytes + off + kc * 256 + ((cl ^ vsw(key)) << 4), vt + i * 1024);
-      }
-    };
+    auto issue_k = [&](int it, unsigned char* kt) { issue(it, krow, koff, kt, false); };
+    auto issue_v = [&](int it, unsigned char* vt) { issue(it, vrow, voff, vt, true); };
     unsigned char* const kt = lds;
     unsigned char* const vt = lds + TILE;
     if (ntiles > 0) {
@@ -349,6 +370,7 @@ __global__ void __launch_bounds__(128 * HPR) prefill_bf16_kernel(Geom g, FwdBufs
     for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(qreg[ks]));   // see the tile ids above
 
     float m = -INFINITY, lsum = 0.f;
+    f32x16 negm = {};   // -m in every slot: the S^T accumulator's start (0 before the first tile)
     f32x16 oacc[4];
   #pragma unroll
     for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
@@ -370,12 +392,12 @@ __global__ void __launch_bounds__(128 * HPR) prefill_bf16_kernel(Geom g, FwdBufs
         block_barrier();
       }
       const int j = tile_id(it);
-      mfma_phase<false, true, kDepth>(oacc, pb, vt, sacc, kt, qreg, m, lane);
+      mfma_phase<false, true, kDepth>(oacc, pb, vt, sacc, kt, qreg, negm, lane);
       if (PIPE == 2 && it + 1 < ntiles) {
         block_barrier();          // every wave has read K(it): refill it with K(it+1)
         issue_k(it + 1, kt);
       }
-      softmax_tile(sacc, pb, oacc, m, lsum, j == ri.r || j * kBlock + kBlock > ri.len, j * kBlock, qpos, ri.len,
+      softmax_tile(sacc, pb, oacc, m, negm, lsum, j == ri.r || j * kBlock + kBlock > ri.len, j * kBlock, qpos, ri.len,
                    half);
       if (PIPE == 2) {
         // V(it) landed; K(it+1) may still be in flight
@@ -383,10 +405,11 @@ __global__ void __launch_bounds__(128 * HPR) prefill_bf16_kernel(Geom g, FwdBufs
         else wait_vmcnt<0>();
         block_barrier();
       }
-      mfma_phase<true, false, kDepth>(oacc, pb, vt, sacc, kt, qreg, m, lane);
+      mfma_phase<true, false, kDepth>(oacc, pb, vt, sacc, kt, qreg, negm, lane);
       if (PIPE != 2) block_barrier();   // every wave is done with this stage before it is refilled
     }
 
+    lsum = sum_xor32(lsum);
     if (qvalid)
       store_row(oacc, m, lsum, (__bf16*)a.o + q_offset(g, ri.s, head, ri.tok0, qpos),
                 a.lse ? a.lse + lse_offset(g, ri.s, head, ri.tok0, qpos) : nullptr, half);
@@ -460,22 +483,43 @@ __global__ void __launch_bounds__(512) prefill_bf16_pp_kernel(Geom g, FwdBufs a,
     return it < 64 ? __builtin_amdgcn_readlane(jl0, it) : __builtin_amdgcn_readlane(jl1, it - 64);
   };
 
+  // per-lane byte offsets of this wave's 1 KB slices of a full tile (see
+  // prefill_bf16_kernel)
+  constexpr int NLD = 16 / NW;
   const int sub = lane >> 4, cl = lane & 15;
+  uint32_t koff[NLD], voff[NLD];
+#pragma unroll
+  for (int ii = 0; ii < NLD; ++ii) {
+    const int key = 4 * (wave + NW * ii) + sub;
+    koff[ii] = key * 256 + ((cl ^ ksw(key)) << 4);
+    voff[ii] = key * 256 + ((cl ^ vsw(key)) << 4);
+  }
+  const int64_t kv_row = kv_offset(g, ri.s, kvh, ri.tok0, 0) * 2;
+  const unsigned char* const krow = uniform_ptr(kbytes + kv_row);
+  const unsigned char* const vrow = uniform_ptr(vbytes + kv_row);
+  const int len_u = __builtin_amdgcn_readfirstlane(ri.len);
   auto issue_half = [&](int it, const unsigned char* src, unsigned char* dst, bool is_v) {
     const int j = tile_id(it);
-    const int cnt = min(kBlock, ri.len - j * kBlock);
-    const int64_t off = kv_offset(g, ri.s, kvh, ri.tok0, j * kBlock) * 2;
+    const unsigned char* base = src + (int64_t)j * TILE;
+    const int cnt = len_u - j * kBlock;
+    if (cnt >= kBlock) {
 #pragma unroll
-    for (int i = wave; i < 16; i += NW) {
-      const int key = 4 * i + sub;
-      const int kc = min(key, cnt - 1);      // rows past the end: any valid row (masked later)
-      const int sw = is_v ? vsw(key) : ksw(key);
-      load_lds16(src + off + kc * 256 + ((cl ^ sw) << 4), dst + i * 1024);
+      for (int ii = 0; ii < NLD; ++ii)
+        load_lds16_sv(base, is_v ? voff[ii] : koff[ii], dst + (wave + NW * ii) * 1024);
+    } else {
+      asm volatile("");   // the sequence's last, partial block: a real branch
+#pragma unroll
+      for (int ii = 0; ii < NLD; ++ii) {
+        const int key = 4 * (wave + NW * ii) + sub;
+        const int kc = min(key, cnt - 1);   // rows past the end: any valid row (masked later)
+        const uint32_t o = kc * 256 + ((cl ^ (is_v ? vsw(key) : ksw(key))) << 4);
+        load_lds16_sv(base, o, dst + (wave + NW * ii) * 1024);
+      }
     }
   };
   auto issue_round = [&](int r) {
-    if (r < ntiles) issue_half(r, kbytes, kring + (r % NB) * TILE, false);
-    if (r >= 1) issue_half(r - 1, vbytes, vring + ((r - 1) % NB) * TILE, true);
+    if (r < ntiles) issue_half(r, krow, kring + (r % NB) * TILE, false);
+    if (r >= 1) issue_half(r - 1, vrow, vring + ((r - 1) % NB) * TILE, true);
   };
   // half rounds issued after round u, when rounds 0 .. hi are out
   auto younger_halves = [&](int u, int hi) {
@@ -495,6 +539,7 @@ __global__ void __launch_bounds__(512) prefill_bf16_pp_kernel(Geom g, FwdBufs a,
   }
 
   float m = -INFINITY, lsum = 0.f;
+  f32x16 negm = {};   // -m in every slot: the S^T accumulator's start (0 before the first tile)
   f32x16 oacc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
@@ -530,9 +575,9 @@ __global__ void __launch_bounds__(512) prefill_bf16_pp_kernel(Geom g, FwdBufs a,
       {
         const unsigned char* vt = vring + ((u + NB - 1) % NB) * TILE;   // V(u-1)
         const unsigned char* kt = kring + (u % NB) * TILE;              // K(u)
-        if (u >= 1) mfma_phase<true, false, kDepth>(oacc, pb, vt, sacc, kt, qreg, m, lane);
+        if (u >= 1) mfma_phase<true, false, kDepth>(oacc, pb, vt, sacc, kt, qreg, negm, lane);
         __builtin_amdgcn_sched_barrier(0);
-        if (u < ntiles) mfma_phase<false, true, kDepth>(oacc, pb, vt, sacc, kt, qreg, m, lane);
+        if (u < ntiles) mfma_phase<false, true, kDepth>(oacc, pb, vt, sacc, kt, qreg, negm, lane);
       }
       if (grp == 0) {
         block_barrier();                             // barrier 2u+1
@@ -545,13 +590,14 @@ __global__ void __launch_bounds__(512) prefill_bf16_pp_kernel(Geom g, FwdBufs a,
       }
       if (u < ntiles) {
         const int j = tile_id(u);
-        softmax_tile(sacc, pb, oacc, m, lsum, j == ri.r || j * kBlock + kBlock > ri.len, j * kBlock, qpos,
+        softmax_tile(sacc, pb, oacc, m, negm, lsum, j == ri.r || j * kBlock + kBlock > ri.len, j * kBlock, qpos,
                      ri.len, half);
       }
     }
     if (grp == 0) block_barrier();                   // barrier 2n+2
   }
 
+  lsum = sum_xor32(lsum);
   if (qvalid)
     store_row(oacc, m, lsum, (__bf16*)a.o + q_offset(g, ri.s, head, ri.tok0, qpos),
               a.lse ? a.lse + lse_offset(g, ri.s, head, ri.tok0, qpos) : nullptr, half);
