@@ -36,7 +36,8 @@ SA_SELECT_TOPK, SA_SELECT_THRESHOLD = 0, 1
 SA_FORCE_CURRENT, SA_FORCE_FIRST = 1, 2
 
 EXPORTED = ["sparse_attn_sizes", "sparse_attn_workspace_size", "sparse_attn_route",
-            "sparse_attn_build_worklist", "sparse_attn_fwd", "sparse_attn_status_string"]
+            "sparse_attn_build_worklist", "sparse_attn_fwd", "sparse_attn_append_kv",
+            "sparse_attn_status_string"]
 
 
 class SAError(RuntimeError):
@@ -51,7 +52,8 @@ class _Problem(ctypes.Structure):
                 ("block", ctypes.c_int32), ("seqlen", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("mode", ctypes.c_int32),
                 ("cu_seqlens", ctypes.c_void_p), ("total_tokens", ctypes.c_int32),
-                ("total_blocks", ctypes.c_int32), ("max_blocks", ctypes.c_int32)]
+                ("total_blocks", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
+                ("kv_capacity", ctypes.c_int32)]
 
 
 class _RouteCfg(ctypes.Structure):
@@ -77,6 +79,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sparse_attn_sizes.argtypes = [P, R, ctypes.POINTER(i64), ctypes.POINTER(i32),
                                       ctypes.POINTER(i64), ctypes.POINTER(i32), ctypes.POINTER(i64)]
     lib.sparse_attn_sizes.restype = ctypes.c_int
+    lib.sparse_attn_append_kv.argtypes = [P, i32, vp, vp, vp, vp, vp, vp]
+    lib.sparse_attn_append_kv.restype = ctypes.c_int
     lib.sparse_attn_workspace_size.argtypes = [P, R, i32, i32]
     lib.sparse_attn_workspace_size.restype = sz
     lib.sparse_attn_route.argtypes = [P, R, vp, vp, vp, i32, vp, vp, sz, vp]
@@ -111,14 +115,16 @@ class Problem:
     block: int = 64
     cu_seqlens: Optional[torch.Tensor] = None   # int32 [batch+1] on the device
     lengths: Optional[list] = None              # host copy of the varlen lengths
+    kv_capacity: int = 0         # decode: allocated cache tokens (0 = seqlen)
 
     @staticmethod
     def fixed(batch, heads_q, heads_kv, head_dim, seqlen, dtype="bf16"):
         return Problem(batch, heads_q, heads_kv, head_dim, seqlen, dtype, "prefill")
 
     @staticmethod
-    def decode(batch, heads_q, heads_kv, head_dim, cache_len, dtype="bf16"):
-        return Problem(batch, heads_q, heads_kv, head_dim, cache_len, dtype, "decode")
+    def decode(batch, heads_q, heads_kv, head_dim, cache_len, dtype="bf16", kv_capacity=0):
+        return Problem(batch, heads_q, heads_kv, head_dim, cache_len, dtype, "decode",
+                       kv_capacity=kv_capacity)
 
     @staticmethod
     def varlen(lengths, heads_q, heads_kv, head_dim, cu_seqlens, dtype="bf16"):
@@ -131,6 +137,7 @@ class Problem:
         p.block, p.seqlen = self.block, self.seqlen
         p.dtype = SA_BF16 if self.dtype == "bf16" else SA_F32
         p.mode = SA_DECODE if self.mode == "decode" else SA_PREFILL
+        p.kv_capacity = self.kv_capacity
         if self.cu_seqlens is not None:
             p.cu_seqlens = self.cu_seqlens.data_ptr()
             nb = [-(-int(x) // self.block) for x in self.lengths]
@@ -212,7 +219,8 @@ def summaries_shape(prob: Problem):
     if prob.cu_seqlens is not None:
         nb = sum(-(-int(x) // prob.block) for x in prob.lengths)
         return (prob.heads_kv, nb, prob.head_dim)
-    nb = -(-prob.seqlen // prob.block)
+    n = prob.kv_capacity if (prob.mode == "decode" and prob.kv_capacity) else prob.seqlen
+    nb = -(-n // prob.block)
     return (prob.batch, prob.heads_kv, nb, prob.head_dim)
 
 
@@ -284,6 +292,29 @@ def fwd(prob: Problem, cfg: RouteConfig, wl: Worklist, q, k, v, o=None, lse=None
         ctypes.byref(p), ctypes.byref(c), _ptr(wl.row_ptr), _ptr(wl.col_idx), _ptr(wl.row_perm),
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), num_splits, _ptr(ws), wsb, _stream(dev)))
     return o, lse
+
+
+def append_kv(prob: Problem, k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
+              v_cache: torch.Tensor, summaries: torch.Tensor):
+    """sparse_attn_append_kv: writes k_new / v_new [S, Hkv, n, d] into rows
+    [prob.seqlen, prob.seqlen + n) of the caches [S, Hkv, kv_capacity, d] and
+    updates the fp32 summaries of the blocks they land in (in place).  The
+    caller advances prob.seqlen by n afterwards."""
+    dt = torch.bfloat16 if prob.dtype == "bf16" else torch.float32
+    cap = prob.kv_capacity
+    shape_c = (prob.batch, prob.heads_kv, cap, prob.head_dim)
+    n = k_new.shape[2] if k_new.dim() == 4 else -1
+    shape_n = (prob.batch, prob.heads_kv, n, prob.head_dim)
+    for name, t, shp, tdt in (("k_new", k_new, shape_n, dt), ("v_new", v_new, shape_n, dt),
+                              ("k_cache", k_cache, shape_c, dt), ("v_cache", v_cache, shape_c, dt),
+                              ("summaries", summaries, summaries_shape(prob), torch.float32)):
+        if tuple(t.shape) != shp or t.dtype != tdt or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"append_kv: {name} must be a contiguous {tdt} device tensor of shape {shp}, "
+                             f"got {tuple(t.shape)} {t.dtype}")
+    p = prob.to_c()
+    _check("sparse_attn_append_kv", load_library().sparse_attn_append_kv(
+        ctypes.byref(p), n, _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(summaries),
+        _stream(k_cache.device)))
 
 
 def problem_for(w, inp) -> Problem:

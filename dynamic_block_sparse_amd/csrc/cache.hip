@@ -1,0 +1,101 @@
+// Decode-cache append: new K/V rows go into the cache, and the summaries of
+// the blocks they land in are updated in place.
+//
+// [P2] §3.1 (summaries are cache state) and Eq 11: block j's summary is the
+// running mean of its r_j valid keys, kept with the KV cache and updated as
+// keys arrive instead of being rebuilt by a scan over the history.  A chunk of
+// n new keys of block j turns c_j into (r_j c_j + sum of the new keys) /
+// (r_j + n); a block that had no valid key (r_j = 0) starts from the new keys.
+//
+// One wavefront per (sequence, KV head, touched block).  Each lane owns E =
+// d / 64 adjacent columns: it copies those columns of the block's new K and V
+// rows (so a row moves as one coalesced 128- or 256-byte burst per tensor),
+// sums the new keys of its columns in fp32 in token order, and writes the
+// updated summary.  Rows are handled four at a time so their loads are in
+// flight together.
+#include "common.h"
+#include "kernels.h"
+
+namespace sa {
+
+template <typename T, int E>
+__global__ void __launch_bounds__(64) append_kv_kernel(AppendGeom g, const T* __restrict__ k_new,
+                                                       const T* __restrict__ v_new, T* __restrict__ k_cache,
+                                                       T* __restrict__ v_cache, float* __restrict__ summ) {
+  constexpr int D = 64 * E;
+  const int lane = threadIdx.x;
+  const int s = (int)blockIdx.x / g.hkv, h = (int)blockIdx.x % g.hkv;
+  const int j = g.len0 / kBlock + (int)blockIdx.y;   // block that receives tokens [t0, t1)
+  const int lo = j * kBlock;
+  const int t0 = max(lo, g.len0), t1 = min(lo + kBlock, g.len0 + g.n_new);
+  const int r_old = max(0, min(lo + kBlock, g.len0) - lo);   // valid keys before the append
+  const int col = lane * E;
+  const T* kn = k_new + (int64_t)s * g.new_seq + (int64_t)h * g.new_head + col;
+  const T* vn = v_new + (int64_t)s * g.new_seq + (int64_t)h * g.new_head + col;
+  T* kd = k_cache + (int64_t)s * g.cache_seq + (int64_t)h * g.cache_head + col;
+  T* vd = v_cache + (int64_t)s * g.cache_seq + (int64_t)h * g.cache_head + col;
+
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  constexpr int U = 4;
+  int t = t0;
+  for (; t + U <= t1; t += U) {
+    T kx[U][E], vx[U][E];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        kx[u][e] = kn[(int64_t)(t + u - g.len0) * D + e];
+        vx[u][e] = vn[(int64_t)(t + u - g.len0) * D + e];
+      }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        kd[(int64_t)(t + u) * D + e] = kx[u][e];
+        vd[(int64_t)(t + u) * D + e] = vx[u][e];
+        acc[e] += (float)kx[u][e];
+      }
+  }
+  for (; t < t1; ++t) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const T kx = kn[(int64_t)(t - g.len0) * D + e];
+      const T vx = vn[(int64_t)(t - g.len0) * D + e];
+      kd[(int64_t)t * D + e] = kx;
+      vd[(int64_t)t * D + e] = vx;
+      acc[e] += (float)kx;
+    }
+  }
+  float* c = summ + ((int64_t)s * g.sum_seq + (int64_t)h * g.sum_head + j) * D + col;
+  const float inv = 1.f / (float)(r_old + t1 - t0);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const float sum = r_old > 0 ? fmaf((float)r_old, c[e], acc[e]) : acc[e];
+    c[e] = sum * inv;
+  }
+}
+
+int launch_append_kv(const AppendGeom& g, int dtype, int n_seq, int touched, const void* k_new,
+                     const void* v_new, void* k_cache, void* v_cache, float* summ, hipStream_t st) {
+  const dim3 grid((unsigned)(n_seq * g.hkv), (unsigned)touched);
+  if (dtype == SA_BF16) {
+    if (g.d == 128)
+      append_kv_kernel<__bf16, 2><<<grid, 64, 0, st>>>(g, (const __bf16*)k_new, (const __bf16*)v_new,
+                                                       (__bf16*)k_cache, (__bf16*)v_cache, summ);
+    else
+      append_kv_kernel<__bf16, 1><<<grid, 64, 0, st>>>(g, (const __bf16*)k_new, (const __bf16*)v_new,
+                                                       (__bf16*)k_cache, (__bf16*)v_cache, summ);
+  } else {
+    if (g.d == 128)
+      append_kv_kernel<float, 2><<<grid, 64, 0, st>>>(g, (const float*)k_new, (const float*)v_new,
+                                                      (float*)k_cache, (float*)v_cache, summ);
+    else
+      append_kv_kernel<float, 1><<<grid, 64, 0, st>>>(g, (const float*)k_new, (const float*)v_new,
+                                                      (float*)k_cache, (float*)v_cache, summ);
+  }
+  return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
+
+}  // namespace sa

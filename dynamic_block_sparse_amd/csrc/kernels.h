@@ -42,4 +42,15 @@ int launch_prefill(const Geom& g, int dtype, const FwdBufs& b, hipStream_t st);
 int launch_decode(const Geom& g, int dtype, const FwdBufs& b, int splits, hipStream_t st);
 size_t decode_partials_bytes(const Geom& g, int splits);
 
+// Decode-cache append: rows [len0, len0 + n_new) of every (sequence, KV head)
+// and the Eq 11 update of the summaries of the blocks they land in.
+struct AppendGeom {
+  int hkv, d, len0, n_new;
+  int64_t cache_seq, cache_head;   // element strides of the K/V cache
+  int64_t new_seq, new_head;       // element strides of the new rows
+  int64_t sum_seq, sum_head;       // summary strides in blocks
+};
+int launch_append_kv(const AppendGeom& g, int dtype, int n_seq, int touched, const void* k_new,
+                     const void* v_new, void* k_cache, void* v_cache, float* summ, hipStream_t st);
+
 }  // namespace sa

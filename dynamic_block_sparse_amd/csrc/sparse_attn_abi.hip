@@ -59,19 +59,25 @@ int validate(const sa_problem* p, const sa_route_cfg* rc, Plan* out) {
   if (p->mode == SA_DECODE) {
     if (p->cu_seqlens || p->seqlen < 1) return SA_ERR_INVALID_ARG;
     g.n = p->seqlen;
+    // the cache may hold room beyond the valid length: strides follow the capacity
+    const int cap = p->kv_capacity > 0 ? p->kv_capacity : p->seqlen;
+    if (p->kv_capacity < 0 || cap < g.n) return SA_ERR_INVALID_ARG;
     const int nb = (g.n + kBlock - 1) / kBlock;
+    const int nbc = (cap + kBlock - 1) / kBlock;
     g.max_blocks = nb;
     g.total_blocks = nb;
     g.rows = (int64_t)g.batch * g.hr;
     g.q_seq = (int64_t)g.hq * d;
     g.q_head = d;
-    g.kv_seq = (int64_t)g.hkv * g.n * d;
-    g.kv_head = (int64_t)g.n * d;
-    g.sum_seq = (int64_t)g.hkv * nb;
-    g.sum_head = nb;
+    g.kv_seq = (int64_t)g.hkv * cap * d;
+    g.kv_head = (int64_t)cap * d;
+    g.sum_seq = (int64_t)g.hkv * nbc;
+    g.sum_head = nbc;
     g.lse_seq = g.hq;
     g.lse_head = 1;
-    out->kv_slots = (int64_t)g.batch * nb;
+    out->kv_slots = (int64_t)g.batch * nbc;
+  } else if (p->kv_capacity != 0) {
+    return SA_ERR_INVALID_ARG;   // prefill has no cache capacity
   } else if (p->cu_seqlens) {
     if (p->seqlen != 0 || p->total_tokens < 1 || p->total_blocks < p->batch ||
         p->max_blocks < 1 || p->max_blocks > p->total_blocks)
@@ -171,6 +177,37 @@ int prep_cu_blocks(Plan& pl, void* ws, hipStream_t st) {
 using namespace sa;
 
 extern "C" {
+
+int sparse_attn_append_kv(const sa_problem* p, int32_t n_new, const void* k_new, const void* v_new,
+                          void* k_cache, void* v_cache, float* summaries, void* stream) {
+  using namespace sa;
+  if (!p || p->mode != SA_DECODE || p->cu_seqlens) return SA_ERR_INVALID_ARG;
+  if (p->batch < 1 || p->heads_q < 1 || p->heads_kv < 1 || p->heads_q % p->heads_kv != 0)
+    return SA_ERR_INVALID_ARG;
+  if (p->dtype != SA_F32 && p->dtype != SA_BF16) return SA_ERR_INVALID_ARG;
+  if (p->block != kBlock) return SA_ERR_UNSUPPORTED;
+  if (p->head_dim != 64 && p->head_dim != 128) return SA_ERR_UNSUPPORTED;
+  if (n_new < 0 || p->seqlen < 0 || p->kv_capacity < 1) return SA_ERR_INVALID_ARG;
+  if ((int64_t)p->seqlen + n_new > p->kv_capacity) return SA_ERR_INVALID_ARG;
+  if (n_new == 0) return SA_OK;
+  if (!k_new || !v_new || !k_cache || !v_cache || !summaries) return SA_ERR_INVALID_ARG;
+  const int touched = (p->seqlen + n_new - 1) / kBlock - p->seqlen / kBlock + 1;
+  if (touched > 65535 || (int64_t)p->batch * p->heads_kv > INT32_MAX) return SA_ERR_UNSUPPORTED;
+  const int64_t d = p->head_dim, cap = p->kv_capacity, nbc = (cap + kBlock - 1) / kBlock;
+  AppendGeom g;
+  g.hkv = p->heads_kv;
+  g.d = p->head_dim;
+  g.len0 = p->seqlen;
+  g.n_new = n_new;
+  g.cache_head = cap * d;
+  g.cache_seq = (int64_t)p->heads_kv * cap * d;
+  g.new_head = (int64_t)n_new * d;
+  g.new_seq = (int64_t)p->heads_kv * n_new * d;
+  g.sum_head = nbc;
+  g.sum_seq = (int64_t)p->heads_kv * nbc;
+  return launch_append_kv(g, p->dtype, p->batch, touched, k_new, v_new, k_cache, v_cache, summaries,
+                          reinterpret_cast<hipStream_t>(stream));
+}
 
 const char* sparse_attn_status_string(int status) {
   switch (status) {

@@ -7,6 +7,10 @@
  *   sparse_attn_build_worklist   J               -> sorted, deduplicated CSR worklist
  *   sparse_attn_fwd              Q, K, V, worklist -> O (and log-sum-exp)
  *
+ * and one for the decode cache that routing reads:
+ *
+ *   sparse_attn_append_kv        new K/V rows -> cache rows and block summaries
+ *
  * The method ([P2] "2.1 Coarse-grained selection: from content grouping to
  * dynamic sparse blocks", PaperTrace sparse-attention 2-1; [P3] "From index to
  * kernel", PaperTrace sparse-attention 5-1):
@@ -47,9 +51,11 @@
  *   fixed-length prefill   Q, O [B, Hq, n, d]      K, V [B, Hkv, n, d]
  *   packed varlen prefill  Q, O [Hq, T, d]         K, V [Hkv, T, d]
  *                          cu_seqlens [B + 1] int32 token offsets
- *   decode                 Q, O [S, Hq, d]         K, V [S, Hkv, L, d]
+ *   decode                 Q, O [S, Hq, d]         K, V [S, Hkv, C, d] (C = kv_capacity,
+ *                                                  of which the first L = seqlen are valid)
  *   log-sum-exp            same as Q without d, fp32
- *   summaries (fp32)       fixed / decode [B, Hkv, N, d];  varlen [Hkv, sum_s N_s, d]
+ *   summaries (fp32)       fixed [B, Hkv, N, d]; decode [S, Hkv, ceil(C / b), d];
+ *                          varlen [Hkv, sum_s N_s, d]
  *   J (int32)              rows x k_b, rows in (sequence, routing head, query
  *                          block) row-major order; decode has one row per
  *                          (sequence, routing head)
@@ -103,6 +109,11 @@ typedef struct sa_problem {
   int32_t total_tokens;   /* varlen: cu_seqlens[batch] (host-known); else ignored */
   int32_t total_blocks;   /* varlen: sum_s ceil(len_s / b) (host-known); else ignored */
   int32_t max_blocks;     /* varlen: max_s ceil(len_s / b) (host-known); else ignored */
+  int32_t kv_capacity;    /* decode: tokens allocated per (sequence, KV head) in the K/V
+                             cache, >= seqlen; 0 = seqlen.  K/V are [S, Hkv, kv_capacity, d]
+                             and summaries [S, Hkv, ceil(kv_capacity / b), d], of which the
+                             first seqlen tokens / ceil(seqlen / b) blocks are valid.
+                             Must be 0 for prefill. */
 } sa_problem;
 
 /* Routing settings (host struct). */
@@ -121,7 +132,8 @@ typedef struct sa_route_cfg {
  *   width_max  widest possible worklist row: k_b + number of forced bits
  *   nnz_cap    R * width_max: a col_idx capacity that can never overflow
  *   n_buckets  NB: buckets 4, 8, ..., 4 * 2^(NB-1) cover width_max
- *   kv_blocks  summary slots (B * N, or total_blocks for varlen)
+ *   kv_blocks  summary slots (B * N; decode S * ceil(kv_capacity / b); varlen
+ *              total_blocks)
  * Returns SA_OK or SA_ERR_INVALID_ARG / SA_ERR_UNSUPPORTED. */
 int sparse_attn_sizes(const sa_problem* p, const sa_route_cfg* rc, int64_t* rows,
                       int32_t* width_max, int64_t* nnz_cap, int32_t* n_buckets,
@@ -190,6 +202,32 @@ int sparse_attn_fwd(const sa_problem* p, const sa_route_cfg* rc, const int32_t* 
                     const int32_t* col_idx, const int32_t* row_perm, const void* q,
                     const void* k, const void* v, void* o, float* lse, int32_t num_splits,
                     void* ws, size_t ws_bytes, void* stream);
+
+/* Decode-cache append ([P2] §3.1 "summaries are cache state" and Eq 11: the
+ * summaries are kept with the KV cache and updated as keys arrive, not
+ * rebuilt by a scan over the history).
+ *   p           decode geometry (mode SA_DECODE): batch = S, heads_kv, head_dim,
+ *               dtype; seqlen = L0, the cached length of every sequence before
+ *               the call (0 allowed); kv_capacity >= L0 + n_new (required).
+ *               heads_q is not used but must be a valid multiple of heads_kv.
+ *   n_new       tokens appended to every sequence (0: nothing is enqueued)
+ *   k_new, v_new (device) [S, Hkv, n_new, d] rows to append, in order
+ *   k_cache, v_cache (device) [S, Hkv, kv_capacity, d]: rows [L0, L0 + n_new)
+ *               receive k_new / v_new; no other row is touched
+ *   summaries   (device, fp32) [S, Hkv, ceil(kv_capacity / b), d]: every block j
+ *               that receives a new token is updated in place to
+ *               (r_j * c_j + sum of its new keys) / (r_j + its new count), r_j =
+ *               valid keys of block j before the call (a block with r_j = 0
+ *               starts from its new keys); other blocks are not touched.
+ *               Summaries of blocks below ceil(L0 / b) must hold the means of
+ *               the cached keys (sparse_attn_route with summaries_in = 0 writes
+ *               them; this call keeps them).
+ *   Arithmetic is fp32 (sums of the new keys in token order).  Calls on one
+ *   stream apply in order; the caller advances seqlen by n_new afterwards.
+ *   Returns SA_ERR_INVALID_ARG for a non-decode problem, a negative n_new,
+ *   L0 + n_new > kv_capacity or a null pointer (when n_new > 0). */
+int sparse_attn_append_kv(const sa_problem* p, int32_t n_new, const void* k_new, const void* v_new,
+                          void* k_cache, void* v_cache, float* summaries, void* stream);
 
 /* Human-readable text for a status code (static string). */
 const char* sparse_attn_status_string(int status);

@@ -5,6 +5,7 @@ No call here reaches a kernel launch: every argument set either fails host
 validation or goes to the pure-host size queries.
 """
 import ctypes
+import dataclasses
 import os
 import re
 
@@ -116,3 +117,31 @@ def test_calls_validate_before_any_launch(lib):
     assert lib.sparse_attn_fwd(ctypes.byref(p64), C, 8, 8, 8, 8, 8, 8, 8, None, 0, None, 0, None) \
         == dbs.SA_ERR_UNSUPPORTED
     assert lib.sparse_attn_status_string(dbs.SA_ERR_HIP) == b"HIP launch failed"
+
+
+def test_decode_capacity_sizes_and_prefill_rejects_capacity(lib):
+    d = dbs.sizes(dbs.Problem.decode(4, 8, 2, 128, 1000, kv_capacity=1500), dbs.RouteConfig(k_b=8, share_gqa=True))
+    assert d.kv_blocks == 4 * 24            # summary slots follow the capacity: ceil(1500 / 64)
+    assert dbs.summaries_shape(dbs.Problem.decode(4, 8, 2, 128, 1000, kv_capacity=1500)) == (4, 2, 24, 128)
+    for bad in (dbs.Problem.decode(4, 8, 2, 128, 1000, kv_capacity=999),   # capacity below the length
+                dbs.Problem.decode(4, 8, 2, 128, 1000, kv_capacity=-1),
+                dataclasses.replace(_prob(), kv_capacity=9000)):            # prefill has no capacity
+        with pytest.raises(dbs.SAError) as e:
+            dbs.sizes(bad, dbs.RouteConfig(k_b=8, share_gqa=True))
+        assert e.value.status == dbs.SA_ERR_INVALID_ARG
+
+
+def test_append_kv_validates_before_any_launch(lib):
+    """Every bad argument returns a status on the host; n_new = 0 enqueues nothing."""
+    def call(prob, n, ptr=8):
+        p = prob.to_c()
+        return lib.sparse_attn_append_kv(ctypes.byref(p), n, ptr, ptr, ptr, ptr, ptr, None)
+    ok = dbs.Problem.decode(2, 4, 2, 128, 100, kv_capacity=200)
+    assert call(ok, 0) == dbs.SA_OK                                            # nothing to do
+    assert call(ok, 101) == dbs.SA_ERR_INVALID_ARG                             # past the capacity
+    assert call(ok, -1) == dbs.SA_ERR_INVALID_ARG
+    assert call(ok, 5, ptr=None) == dbs.SA_ERR_INVALID_ARG                     # null pointers
+    assert call(dbs.Problem.decode(2, 4, 2, 128, 100), 1) == dbs.SA_ERR_INVALID_ARG   # no capacity set
+    assert call(dataclasses.replace(_prob(), kv_capacity=9000), 1) == dbs.SA_ERR_INVALID_ARG  # prefill
+    assert call(dbs.Problem.decode(2, 4, 2, 96, 100, kv_capacity=200), 1) == dbs.SA_ERR_UNSUPPORTED
+    assert call(dbs.Problem.decode(2, 4, 3, 128, 100, kv_capacity=200), 1) == dbs.SA_ERR_INVALID_ARG
