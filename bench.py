@@ -308,7 +308,58 @@ def measure_decode(args, dbs, wd, dev, flush):
     }
     del sd, inp_d
     torch.cuda.empty_cache()
+    rec["append_kv"] = measure_append(args, dbs, wd, dev)
     return rec
+
+
+def measure_append(args, dbs, wd, dev):
+    """sparse_attn_append_kv at the decode shape (S sequences x Hkv heads, d):
+    one token per sequence (what a decode step appends) and a 64-token chunk,
+    into a cache with room past its 100 valid rows (the cost depends only on
+    the appended rows and the blocks they land in, not on the cache length).
+    Timed as a HIP graph of R back-to-back calls, so host-side argument
+    marshalling is not counted; per call = graph time / R."""
+    import torch
+    S, hkv, d, cap, len0 = wd.batch, wd.heads_kv, wd.head_dim, 256, 100
+    g = torch.Generator(device=dev).manual_seed(5)
+    kc = torch.randn((S, hkv, cap, d), generator=g, device=dev).to(torch.bfloat16)
+    vc = torch.randn((S, hkv, cap, d), generator=g, device=dev).to(torch.bfloat16)
+    prob = dbs.Problem.decode(S, wd.heads_q, hkv, d, len0, "bf16", kv_capacity=cap)
+    summ = torch.randn(dbs.summaries_shape(prob), generator=g, device=dev)
+    out = {}
+    for n in (1, 64):
+        kn = torch.randn((S, hkv, n, d), generator=g, device=dev).to(torch.bfloat16)
+        vn = torch.randn((S, hkv, n, d), generator=g, device=dev).to(torch.bfloat16)
+        R = 20
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            for _ in range(max(args.warmup, 1)):
+                dbs.append_kv(prob, kn, vn, kc, vc, summ)
+        torch.cuda.current_stream(dev).wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(R):
+                dbs.append_kv(prob, kn, vn, kc, vc, summ)
+        graph.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(max(args.steps // 5, 10)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) / R)
+        del graph
+        med = spread(ts)["median"]
+        touched = (len0 + n - 1) // 64 - len0 // 64 + 1
+        nbytes = S * hkv * (4 * n * d * 2 + 2 * touched * d * 4)   # K/V read + written, summaries read + written
+        out[f"{n}_tokens"] = {"median_us": round(med * 1e3, 2), "bytes": nbytes,
+                              "gbs": round(nbytes / (med * 1e-3) / 1e9, 1)}
+    del kc, vc, summ
+    torch.cuda.empty_cache()
+    return out
 
 
 def wk_make(w, dev):

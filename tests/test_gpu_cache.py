@@ -120,3 +120,36 @@ def test_append_rejects_past_capacity():
     new = torch.zeros((1, 2, 5, 128), dtype=torch.bfloat16, device=dev)
     with pytest.raises(dbs.SAError):
         dbs.append_kv(prob, new, new, kc, kc.clone(), summ)
+
+
+def test_append_graph_replay_matches_eager():
+    """The append captured in a HIP graph and replayed three times (state reset
+    by eager copies between replays) gives the eager call's cache and
+    summaries bit for bit."""
+    dev = torch.device("cuda:0")
+    S, hkv, d, cap, len0, n = 4, 2, 128, 300, 70, 90
+    print(f"append_kv graph replay S={S} hkv={hkv} cap={cap} len0={len0} n={n}", flush=True)
+    g = torch.Generator(device=dev).manual_seed(3)
+    k0 = torch.randn((S, hkv, cap, d), generator=g, device=dev).to(torch.bfloat16)
+    v0 = torch.randn((S, hkv, cap, d), generator=g, device=dev).to(torch.bfloat16)
+    prob = dbs.Problem.decode(S, 4, hkv, d, len0, "bf16", kv_capacity=cap)
+    s0 = torch.randn(dbs.summaries_shape(prob), generator=g, device=dev)
+    kn = torch.randn((S, hkv, n, d), generator=g, device=dev).to(torch.bfloat16)
+    vn = torch.randn((S, hkv, n, d), generator=g, device=dev).to(torch.bfloat16)
+    ke, ve, se = k0.clone(), v0.clone(), s0.clone()
+    dbs.append_kv(prob, kn, vn, ke, ve, se)
+    kc, vc, sc = k0.clone(), v0.clone(), s0.clone()
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        dbs.append_kv(prob, kn, vn, kc, vc, sc)      # warm-up outside the capture
+    torch.cuda.current_stream(dev).wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dbs.append_kv(prob, kn, vn, kc, vc, sc)
+    for _ in range(3):
+        kc.copy_(k0); vc.copy_(v0); sc.copy_(s0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(kc, ke) and torch.equal(vc, ve) and torch.equal(sc, se)
