@@ -277,6 +277,49 @@ def measure_prefill(args, dbs, w, inp, flush):
     return rec
 
 
+def measure_dense(args, dbs, w, inp, flush, sparse_fwd_ms):
+    """The same causal attention done densely, for the sparse/dense crossover:
+    this library's prefill kernel on a worklist with every causal tile (k_b =
+    127, the widest row the worklist takes: all blocks of every query block
+    except one of the last), and torch's flash-attention SDPA (causal, bf16) on
+    the same tensors, forced to the flash backend.  Each call timed after the
+    last-level cache flush; medians in ms."""
+    import torch
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    n_q = -(-w.seqlen // w.block)
+    wdn = w.replace(name=w.name + "_dense", k_b=min(n_q, 127))
+    st = Stepper(dbs, wdn, inp)
+    st.route()
+    st.worklist()
+    visits = st.tile_visits()
+    ours, flash = [], []
+    reps = max(args.steps // 5, 10)
+    with sdpa_kernel(SDPBackend.FLASH_ATTENTION):
+        for i in range(reps + 2):
+            for fn, acc in ((st.fwd, ours),
+                            (lambda: torch.nn.functional.scaled_dot_product_attention(
+                                inp.q, inp.k, inp.v, is_causal=True), flash)):
+                flush.add_(1.0)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                torch.cuda.synchronize()
+                if i >= 2:
+                    acc.append(e0.elapsed_time(e1))
+    ours_ms, flash_ms = spread(ours)["median"], spread(flash)["median"]
+    causal = 4 * w.head_dim * w.heads_q * w.batch * w.seqlen * (w.seqlen + 1) // 2
+    del st
+    return {"ours_dense_fwd_ms": ours_ms, "ours_dense_tile_visits": visits,
+            "ours_dense_tflops_tiles": round(visits * 4 * w.block ** 2 * w.head_dim / (ours_ms * 1e-3) / 1e12, 1),
+            "torch_flash_sdpa_ms": flash_ms,
+            "torch_flash_sdpa_tflops_causal": round(causal / (flash_ms * 1e-3) / 1e12, 1),
+            "sparse_fwd_ms": sparse_fwd_ms,
+            "sparse_speedup_vs_flash": round(flash_ms / sparse_fwd_ms, 2),
+            "sparse_speedup_vs_ours_dense": round(ours_ms / sparse_fwd_ms, 2),
+            "note": "k_b=127 dense worklist: every causal tile except one of the last query block"}
+
+
 def measure_decode(args, dbs, wd, dev, flush):
     import torch
     log(f"generating {wd.name}")
@@ -375,6 +418,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip the dense comparison (this library's kernel on a full causal "
+                         "worklist, and torch flash-attention SDPA)")
     ap.add_argument("--cpu-heads", type=int, default=16)
     ap.add_argument("--decode-splits", type=int, default=0)
     ap.add_argument("--workload", choices=[w.name for w in wk.ALL if w.dtype == "bf16"],
@@ -427,6 +473,10 @@ def main():
                     "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
                     "data": "synthetic (seeded N(0,1) Q/K/V with planted relevance; no dataset)"})
         out.update(rec)
+        if not args.no_dense:
+            log(f"timing dense causal attention on {w.name}")
+            out["dense"] = measure_dense(args, dbs, w, inp, flush,
+                                         out["stages_ms"]["cache_flushed"]["fwd"]["median"])
     if not args.no_decode and args.only != "prefill":
         wd = w if w.mode == "decode" else wk.DECODE
         rec = measure_decode(args, dbs, wd, dev, flush)
