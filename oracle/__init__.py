@@ -23,8 +23,9 @@ Modules:
   counting   physical-work counts (Eq 8 / Eq 9 style)
   problem    whole-problem drivers (row order, per-sequence routing, sampled rows)
   cache      decode-cache maintenance: append K/V rows, Eq (11) summary update
+  quality    router quality: Eq (10) coverage of the dense attention, recall
 
 Parity status of each function is stated in its docstring; conventions that
 no page value fixes are marked "parity unpinned".
 """
-from . import routing, worklist, attention, counting, problem, cache  # noqa: F401
+from . import routing, worklist, attention, counting, problem, cache, quality  # noqa: F401
