@@ -103,59 +103,19 @@ __device__ __forceinline__ int64_t xcd_schedule(int64_t b, int64_t rows, int G) 
 // running reference m: Q is pre-scaled by log2(e)/sqrt(d) when it is loaded,
 // and the S^T accumulator starts at -m instead of 0 (m = -inf before a row's
 // first tile, when it starts at 0).  The softmax then needs one exp2 per
-// score and no multiply-add.  m moves only when a row maximum exceeds it by
-// more than kGrow (exp2 headroom 2^8), so most tiles skip the rescale of O.
+// score and no multiply-add.  m is set by a row's first tile and moves only
+// when a later tile's weights outgrow it (see softmax_tile), so most tiles
+// take no row maximum and skip the rescale of O.
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-constexpr float kGrow = 8.0f;
 
-// Mask, row maximum, lazy rescale, P = exp2(S - m) in bf16 and the row sum of
-// those bf16 weights ([P2] §1.2 Eq 3-5).  `kbase` is the tile's first key
-// position; `masked` says whether any key of the tile can be masked for this
-// row (the diagonal block, or a block that runs past the sequence end).
-__device__ __forceinline__ void softmax_tile(f32x16 (&sacc)[2], bf16x8 (&pb)[2][2], f32x16 (&oacc)[4],
-                                             float& m, f32x16& negm, float& lsum, bool masked, int kbase, int qpos,
-                                             int len, int half) {
-  if (masked) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int kpos = kbase + kb * 32 + 8 * (i / 4) + 4 * half + (i % 4);
-        if (kpos > qpos || kpos >= len) sacc[kb][i] = -INFINITY;
-      }
-    }
-  }
-  float m0 = -INFINITY, m1 = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    m0 = fmaxf(m0, sacc[0][i]);
-    m1 = fmaxf(m1, sacc[1][i]);
-  }
-  const float mt = max_xor32(fmaxf(m0, m1));   // row maximum, relative to m
-  if (__any(m == -INFINITY || mt > kGrow)) {
-    asm volatile("");   // a real branch: the rescale is rare, never speculate it
-    const bool first = m == -INFINITY;
-    const float shift = first ? mt : fmaxf(mt, 0.f);
-    const float alpha = first ? 0.f : __builtin_amdgcn_exp2f(-shift);
-    lsum *= alpha;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[kb][i] -= shift;
-    m = (first ? 0.f : m) + shift;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) negm[i] = -m;
-  }
+// P = exp2(S) in bf16 for the tile's scores (already offset by the row's
+// reference m) and this lane's sum of those bf16 weights, the ones P V uses.
+__device__ __forceinline__ float exp_tile(const f32x16 (&sacc)[2], bf16x8 (&pb)[2][2]) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) pb[kb][i / 8][i % 8] = (__bf16)__builtin_amdgcn_exp2f(sacc[kb][i]);
-  // the normaliser sums the bf16 weights that P V actually uses
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   float r[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -169,8 +129,78 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&sacc)[2], bf16x8 (&pb)[2][
         pair[1] = pb[kb][h][2 * e + 1];
         r[e] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, r[e], false);
       }
+  return (r[0] + r[1]) + (r[2] + r[3]);
+}
+
+// Row maximum of the tile's scores (both half-waves hold halves of a row).
+__device__ __forceinline__ float tile_max(const f32x16 (&sacc)[2]) {
+  float m0 = -INFINITY, m1 = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    m0 = fmaxf(m0, sacc[0][i]);
+    m1 = fmaxf(m1, sacc[1][i]);
+  }
+  return max_xor32(fmaxf(m0, m1));
+}
+
+// Mask, P = exp2(S - m) in bf16 and the row sum of those weights, with the
+// online-softmax reference m of [P2] §1.2 Eq 3-5.  Eq 3-5 give the same u / l
+// for any reference that keeps the weights finite, so m need not track the
+// running maximum: the row's first tile sets m to its maximum, and later tiles
+// exponentiate against the current m without a maximum.  A lane's partial row
+// sum bounds every weight it holds, so while it stays <= 2^16 no score rose
+// more than 16 (log2 units) above m; otherwise (also on inf) a rare branch
+// takes the row maximum, rescales u and l by 2^-shift, moves m and recomputes
+// P.  Weights stay <= 2^16, far from fp32 and bf16 overflow.  `kbase` is the
+// tile's first key position; `masked` says whether any key of the tile can be
+// masked for this row (the diagonal block, or one that runs past the end).
+constexpr float kBigSum = 65536.0f;
+
+__device__ __forceinline__ void softmax_tile(f32x16 (&sacc)[2], bf16x8 (&pb)[2][2], f32x16 (&oacc)[4],
+                                             float& m, f32x16& negm, float& lsum, bool masked, int kbase, int qpos,
+                                             int len, int half) {
+  if (masked) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kpos = kbase + kb * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+        if (kpos > qpos || kpos >= len) sacc[kb][i] = -INFINITY;
+      }
+    }
+  }
+  if (__any(m == -INFINITY)) {   // the row's first tile (every lane of the wave starts its row together)
+    asm volatile("");
+    const float mt = tile_max(sacc);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[kb][i] -= mt;
+    m = mt;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) negm[i] = -m;
+  }
+  float rs = exp_tile(sacc, pb);
+  if (__any(!(rs <= kBigSum))) {
+    asm volatile("");   // a real branch: the rescale is rare, never speculate it
+    const float shift = fmaxf(tile_max(sacc), 0.f);
+    const float alpha = __builtin_amdgcn_exp2f(-shift);
+    lsum *= alpha;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[kb][i] -= shift;
+    m += shift;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) negm[i] = -m;
+    rs = exp_tile(sacc, pb);
+  }
   // this lane's half of the row's keys; the two halves are added once, at the end
-  lsum += (r[0] + r[1]) + (r[2] + r[3]);
+  lsum += rs;
 }
 
 // LDS reads behind operand i of an MFMA phase (two transpose reads for a V^T

@@ -230,3 +230,59 @@ def test_full_decode(dev):
     run = run_gpu(w, inp)
     seqs = [0, 17, 63]
     _full_check(w, inp, run, seqs=seqs, rows=sample_rows(w, inp, seqs=seqs))
+
+
+# ---------------------------------------------------------------------------
+# Scores that keep rising from tile to tile: the bf16 kernels set a row's
+# softmax reference m from its first tile and re-reference only when a later
+# tile's weights would exceed 2^16 (scores more than 16 log2 units above m).
+# Key block j carries 12 j u (u a unit vector, queries ~u), so scores climb
+# ~1.5 log2 units per block and the re-reference fires, repeatedly, in every
+# row past block ~11; k_b = 16 at n = 1024 keeps every causal block.
+RISING = [(2, 2), (4, 2), (8, 2)]   # (Hq, Hkv): 1-, 2- and 4-head rows, one per bf16 kernel
+
+
+@pytest.mark.parametrize("hq,hkv", RISING, ids=lambda x: str(x))
+def test_rising_scores_rereference(dev, hq, hkv):
+    from oracle import attention as oatt
+    n, d, b = 1024, 128, 64
+    print(f"rising scores hq={hq} hkv={hkv} n={n}", flush=True)
+    g = torch.Generator().manual_seed(17)
+    u = torch.nn.functional.normalize(torch.randn((hkv, d), generator=g), dim=1)
+    grp = hq // hkv
+    q = (u.repeat_interleave(grp, 0)[:, None, :] + 0.3 * torch.randn((hq, n, d), generator=g))[None]
+    scale = 12.0 * (torch.arange(n) // b).float()
+    k = (scale[None, :, None] * u[:, None, :] + torch.randn((hkv, n, d), generator=g))[None]
+    v = torch.randn((1, hkv, n, d), generator=g)
+    q, k, v = (x.to(torch.bfloat16) for x in (q, k, v))
+    prob = dbs.Problem.fixed(1, hq, hkv, d, n, "bf16")
+    cfg = dbs.RouteConfig(k_b=16, share_gqa=hkv < hq)
+    J, _ = dbs.route(prob, cfg, q.to(dev), k.to(dev))
+    wl = dbs.build_worklist(prob, cfg, J)
+    o, lse = dbs.fwd(prob, cfg, wl, q.to(dev), k.to(dev), v.to(dev))
+    torch.cuda.synchronize()
+    rp, ci = wl.row_ptr.cpu().numpy(), wl.col_idx.cpu().numpy()
+    rows_per_head = n // b
+    qn, kn, vn = (x[0].double().numpy() for x in (q, k, v))
+    on, ln = o[0].float().cpu().numpy(), lse[0].cpu().numpy()
+    fired, errs, lerr = 0, [], 0.0
+    for h in range(hq):
+        kvh = h // grp
+        route_h = kvh if hkv < hq else h
+        for r in range(rows_per_head):
+            row = route_h * rows_per_head + r
+            assert ci[rp[row]:rp[row + 1]].tolist() == list(range(r + 1))   # every causal block
+            pos = np.arange(r * b, (r + 1) * b)
+            ref = oatt.masked_attention(qn[h, pos], pos, kn[kvh], vn[kvh], n, b, list(range(r + 1)), True)
+            errs.append(np.abs(on[h, pos] - ref["o"]))
+            lerr = max(lerr, float(np.max(np.abs(ln[h, pos] - ref["lse"]) / np.maximum(1.0, np.abs(ref["lse"])))))
+            # does a later tile rise more than 16 log2 units above the first tile's maximum?
+            s2 = qn[h, pos] @ kn[kvh, :(r + 1) * b].T / np.sqrt(d) * np.log2(np.e)
+            s2 = np.where(np.arange((r + 1) * b)[None, :] <= pos[:, None], s2, -np.inf)
+            fired += int(np.sum(s2[:, b:].max(axis=1, initial=-np.inf) - s2[:, :b].max(axis=1) > 16.0))
+    e = np.concatenate(errs)
+    print(f"rising scores: max-abs {e.max():.3e} mean-abs {e.mean():.3e} lse rel {lerr:.2e}; "
+          f"query rows past the 2^16 bound: {fired}", flush=True)
+    assert fired > 100                      # the re-reference path is exercised
+    assert e.max() <= TOL["bf16"][0] and e.mean() <= TOL["bf16"][1]
+    assert lerr <= LSE_TOL["bf16"]
