@@ -33,14 +33,14 @@ def row_table(lengths, b: int, mode: str, route_heads: int):
     return rows
 
 
-def row_meta(lengths, b: int, mode: str, route_heads: int, forced_first: bool):
+def row_meta(lengths, b: int, mode: str, route_heads: int, forced_first: bool, window: int = 1):
     """(n_k, r, mode, F_r) per row, for the worklist builder."""
-    return [(n_k, r, mode, routing.forced_blocks(r, n_k, mode, forced_first))
+    return [(n_k, r, mode, routing.forced_blocks(r, n_k, mode, forced_first, window))
             for (_s, _h, r, n_k) in row_table(lengths, b, mode, route_heads)]
 
 
 def route(qs, ks, lengths, b, mode, qpool, share_gqa, select, k_b, k_min, tau_rel,
-          forced_first, seqs=None):
+          forced_first, seqs=None, window: int = 1):
     """J rows [R, k_b] plus per-row (g, C_r, F_r) for the chosen sequences.
 
     seqs: subset of sequence ids to route (others left as None rows).
@@ -58,7 +58,7 @@ def route(qs, ks, lengths, b, mode, qpool, share_gqa, select, k_b, k_min, tau_re
             continue
         J, sc = routing.route_sequence(qs[s], ks[s], length, b, mode, qpool, share_gqa,
                                        select, k_b, k_min, tau_rel, forced_first,
-                                       return_scores=True)
+                                       return_scores=True, window=window)
         for h in range(route_heads):
             for r in range(J.shape[1]):
                 rr = r if mode == "prefill" else routing.num_blocks(length, b) - 1
@@ -68,8 +68,8 @@ def route(qs, ks, lengths, b, mode, qpool, share_gqa, select, k_b, k_min, tau_re
     return j_rows, scores
 
 
-def worklist(j_rows, lengths, b, mode, route_heads, forced_first, width_max):
-    meta = row_meta(lengths, b, mode, route_heads, forced_first)
+def worklist(j_rows, lengths, b, mode, route_heads, forced_first, width_max, window: int = 1):
+    meta = row_meta(lengths, b, mode, route_heads, forced_first, window)
     return wl.build(np.asarray(j_rows, dtype=np.int64).reshape(len(meta), -1), meta, width_max)
 
 

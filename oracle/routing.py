@@ -18,6 +18,9 @@ boundary paragraph of [P2] §2.1, and [P2] §4.1:
 
 Readings where the pages are silent (parity unpinned; both sides follow them):
   * k_b is the total per-row budget including forced blocks.
+  * A local window of W blocks forces the current block and the W - 1 before
+    it; they are excluded from scoring like the current block ([P2] §3.2:
+    the local branch is fixed, the dynamic branch picks among the rest).
   * "query pool = max" is the max over per-query *scores*, not an elementwise
     max of query vectors ([P2] §3.2 warns the latter builds a vector that
     does not exist).
@@ -67,15 +70,19 @@ def incremental_summary(keys: np.ndarray) -> np.ndarray:
     return out
 
 
-def forced_blocks(r: int, n_blocks: int, mode: str, forced_first: bool) -> list[int]:
-    """Forced set F_r: the current block, plus block 0 when asked.
+def forced_blocks(r: int, n_blocks: int, mode: str, forced_first: bool, window: int = 1) -> list[int]:
+    """Forced set F_r: the local window ending at the current block, plus block 0 when asked.
 
     Prefill: the current block of query block r is r ([P2] §2.1 causal boundary).
     Decode: the current block is the last cached block n_blocks - 1.
-    The first-block (sink) branch is the global branch of [P2] §3.2's union.
+    [P2] §3.2 builds a row as the union of a local branch (the most recent
+    blocks), a global branch (the first block, a sink) and the dynamic top-k
+    branch; the local and global branches are fixed, never scored.  `window`
+    is the local branch's length in blocks, the current one included (1 = the
+    current block only).
     """
     cur = r if mode == "prefill" else n_blocks - 1
-    f = {cur}
+    f = set(range(max(cur - max(window, 1) + 1, 0), cur + 1))
     if forced_first:
         f.add(0)
     return sorted(f)
@@ -149,7 +156,7 @@ def select_row(g: np.ndarray, cands: list[int], forced: list[int], select: str,
 
 def route_sequence(q: np.ndarray, k: np.ndarray, length: int, b: int, mode: str,
                    qpool: str, share_gqa: bool, select: str, k_b: int, k_min: int,
-                   tau_rel: float, forced_first: bool, return_scores: bool = False):
+                   tau_rel: float, forced_first: bool, return_scores: bool = False, window: int = 1):
     """J for one sequence: [H_r, N_q, k_b] int64 (N_q = 1 in decode).
 
     q: [Hq, n_q_tokens, d] (prefill: n_q_tokens >= length; decode: 1 query);
@@ -185,7 +192,7 @@ def route_sequence(q: np.ndarray, k: np.ndarray, length: int, b: int, mode: str,
         g_rows = np.mean(np.stack(pooled), axis=0)                      # mean over the head group
         for r in range(n_rows):
             cur = r if mode == "prefill" else n_blk - 1
-            forced = forced_blocks(cur, n_blk, mode, forced_first)
+            forced = forced_blocks(cur, n_blk, mode, forced_first, window)
             cands = candidate_blocks(cur, n_blk, mode, forced)
             g = g_rows[r]
             J[hr, r] = select_row(g, cands, forced, select, k_b, k_min, tau_rel)

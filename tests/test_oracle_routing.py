@@ -145,3 +145,30 @@ def test_route_sequence_matches_row_by_row_definition(qpool, share):
             lo, hi = r * b, min((r + 1) * b, n)
             g = routing.pooled_scores([q[h, lo:hi] for h in heads], c, qpool)
             assert np.max(np.abs(g - sc[hr][r][0])) < 1e-12
+
+
+def test_local_window_forced_and_excluded():
+    # [P2] §3.2 union: local window (fixed) + sink (fixed) + dynamic top-k over the rest
+    assert routing.forced_blocks(10, 20, "prefill", False, window=4) == [7, 8, 9, 10]
+    assert routing.forced_blocks(10, 20, "prefill", True, window=4) == [0, 7, 8, 9, 10]
+    assert routing.forced_blocks(2, 20, "prefill", True, window=4) == [0, 1, 2]     # window clipped at 0
+    assert routing.forced_blocks(5, 12, "decode", False, window=3) == [9, 10, 11]   # decode: last blocks
+    assert routing.forced_blocks(10, 20, "prefill", False, window=1) == [10]
+    f = routing.forced_blocks(10, 20, "prefill", True, window=4)
+    assert routing.candidate_blocks(10, 20, "prefill", f) == [1, 2, 3, 4, 5, 6]
+    assert routing.candidate_blocks(5, 12, "decode", [9, 10, 11]) == list(range(9))
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_window_topk_equals_brute_force(seed):
+    rng = np.random.default_rng(100 + seed)
+    nb, r = 12, 11
+    g = rng.integers(-3, 4, size=nb).astype(np.float64)
+    forced = routing.forced_blocks(r, nb, "prefill", forced_first=bool(seed % 2), window=3)
+    cands = routing.candidate_blocks(r, nb, "prefill", forced)
+    assert not set(cands) & set(forced) and max(cands) == r - 3
+    for k_b in range(len(forced), len(forced) + len(cands) + 1):
+        row = routing.select_row(g, cands, forced, "topk", k_b, 4, 2.0)
+        picks = set(j for j in row if j >= 0) - set(forced)
+        d = min(max(k_b - len(forced), 0), len(cands))
+        assert picks == _brute_topd(g, cands, d)
