@@ -60,7 +60,7 @@ class _RouteCfg(ctypes.Structure):
     _fields_ = [("qpool", ctypes.c_int32), ("share_gqa", ctypes.c_int32),
                 ("select", ctypes.c_int32), ("k_b", ctypes.c_int32),
                 ("k_min", ctypes.c_int32), ("tau_rel", ctypes.c_float),
-                ("forced", ctypes.c_uint32)]
+                ("forced", ctypes.c_uint32), ("window", ctypes.c_int32)]
 
 
 _lib = None
@@ -158,6 +158,7 @@ class RouteConfig:
     k_min: int = 4
     tau_rel: float = 2.0
     force_first: bool = False
+    window: int = 1              # local branch: current block + window - 1 before it, forced
 
     def to_c(self) -> _RouteCfg:
         c = _RouteCfg()
@@ -166,6 +167,7 @@ class RouteConfig:
         c.select = SA_SELECT_THRESHOLD if self.select == "threshold" else SA_SELECT_TOPK
         c.k_b, c.k_min, c.tau_rel = self.k_b, self.k_min, self.tau_rel
         c.forced = SA_FORCE_CURRENT | (SA_FORCE_FIRST if self.force_first else 0)
+        c.window = self.window
         return c
 
 
@@ -328,4 +330,4 @@ def problem_for(w, inp) -> Problem:
 
 def config_for(w) -> RouteConfig:
     return RouteConfig(k_b=w.k_b, qpool=w.qpool, share_gqa=w.share_gqa, select=w.select,
-                       k_min=w.k_min, tau_rel=w.tau_rel, force_first=w.forced_first)
+                       k_min=w.k_min, tau_rel=w.tau_rel, force_first=w.forced_first, window=w.window)

@@ -130,9 +130,12 @@ __device__ __forceinline__ uint32_t order_key(float x) {
 // ---------------------------------------------------------------------------
 // Per-row routing context: candidates are the complete history blocks j < r
 // (decode: j < N-1) other than the forced ones; candidate i is block start + i.
+// Forced: the local window lo .. cur (lo = max(cur - W + 1, 0)) and, with
+// SA_FORCE_FIRST, block 0; the candidates are then the contiguous range
+// [start, lo) with start = 1 when block 0 is forced outside the window.
 struct RouteRow {
   RowInfo ri;
-  int kvh, h0, qt0, nq, cur, start, nc, nforced;
+  int kvh, h0, qt0, nq, cur, lo, start, nc, nforced;
   bool ff;
 };
 
@@ -148,12 +151,12 @@ __device__ __forceinline__ RouteRow route_row(const Geom& g, const sa_route_cfg&
     w.qt0 = w.ri.r * kBlock;
     w.nq = min(kBlock, w.ri.len - w.qt0);
   }
-  w.cur = w.ri.r;
+  w.cur = w.ri.r;   // decode: the last cached block
   w.ff = (rc.forced & SA_FORCE_FIRST) != 0;
-  const int n_hist = (g.mode == SA_DECODE) ? w.ri.nblk - 1 : w.ri.r;   // blocks j < current
-  w.start = (w.ff && n_hist > 0) ? 1 : 0;
-  w.nc = max(n_hist - w.start, 0);
-  w.nforced = 1 + ((w.ff && w.cur != 0) ? 1 : 0);
+  w.lo = max(w.cur - max(rc.window, 1) + 1, 0);   // first block of the local window
+  w.start = (w.ff && w.lo > 0) ? 1 : 0;
+  w.nc = max(w.lo - w.start, 0);
+  w.nforced = (w.cur - w.lo + 1) + ((w.ff && w.lo > 0) ? 1 : 0);
   return w;
 }
 
@@ -474,10 +477,11 @@ __global__ void __launch_bounds__(64) route_select_kernel(Geom g, sa_route_cfg r
   }
 
   int32_t* jrow = J + row * rc.k_b;
-  if (lane == 0) {
-    int k = 0;
-    if (w.ff && w.cur != 0) jrow[k++] = 0;
-    jrow[k++] = w.cur;
+  // forced ids: the sink (when outside the window), then the window ascending
+  if (lane <= w.cur - w.lo) {
+    const int k0 = (w.ff && w.lo > 0) ? 1 : 0;
+    if (lane == 0 && k0) jrow[0] = 0;
+    jrow[k0 + lane] = w.lo + lane;
   }
   if (dsel > 0) {
     const uint64_t below = (1ull << lane) - 1ull;

@@ -15,8 +15,6 @@ constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-int popcount2(uint32_t f) { return (int)(f & 1u) + (int)((f >> 1) & 1u); }
-
 struct Plan {
   Geom g;
   int qpool = SA_POOL_MEAN;
@@ -38,7 +36,9 @@ int validate(const sa_problem* p, const sa_route_cfg* rc, Plan* out) {
   if (rc->share_gqa != 0 && rc->share_gqa != 1) return SA_ERR_INVALID_ARG;
   if (rc->select != SA_SELECT_TOPK && rc->select != SA_SELECT_THRESHOLD) return SA_ERR_INVALID_ARG;
   if (!(rc->forced & SA_FORCE_CURRENT) || (rc->forced & ~3u)) return SA_ERR_INVALID_ARG;
-  const int nforced = popcount2(rc->forced);
+  if (rc->window < 0 || rc->window > kMaxWidth) return SA_ERR_INVALID_ARG;
+  // forced ids a row can add: the local window (current block included) and the sink
+  const int nforced = (rc->window > 1 ? rc->window : 1) + ((rc->forced & SA_FORCE_FIRST) ? 1 : 0);
   if (rc->k_b < nforced || rc->k_b + nforced > kMaxWidth) return SA_ERR_INVALID_ARG;
   if (rc->select == SA_SELECT_THRESHOLD &&
       (rc->k_min < 0 || !isfinite(rc->tau_rel) || rc->tau_rel < 0.f))

@@ -42,11 +42,12 @@ __global__ void __launch_bounds__(64) wl_rows_kernel(Geom g, sa_route_cfg rc, in
   const bool ff = (rc.forced & SA_FORCE_FIRST) != 0;
   int ebits = 0;
 
+  const int win = max(rc.window, 1);
   auto load_slot = [&](int p) -> uint32_t {
     int v;
     if (p < rc.k_b) v = J[row * rc.k_b + p];
-    else if (p == rc.k_b) v = ri.r;                 // forced current block
-    else if (p == rc.k_b + 1 && ff) v = 0;          // forced first block
+    else if (p < rc.k_b + win) v = max(ri.r - (p - rc.k_b), -1);   // forced window: r, r-1, ..
+    else if (p == rc.k_b + win && ff) v = 0;                         // forced first block
     else v = -1;
     if (v == -1) return sentinel;
     if (v < -1 || v >= ri.nblk) {

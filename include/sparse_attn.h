@@ -125,11 +125,14 @@ typedef struct sa_route_cfg {
   int32_t k_min;          /* threshold: lower clip of Eq 7 */
   float tau_rel;          /* threshold: tau_r = max_j g_rj - tau_rel */
   uint32_t forced;        /* SA_FORCE_* bits; SA_FORCE_CURRENT must be set */
+  int32_t window;         /* local branch: the current block and the window - 1 blocks before
+                             it are forced and never scored ([P2] §3.2 union of a local, a
+                             global and a dynamic branch); 0 or 1 = the current block only */
 } sa_route_cfg;
 
 /* Host-side sizes derived from the geometry (no device work).
  *   rows       worklist rows R (prefill: H_r * total blocks; decode: S * H_r)
- *   width_max  widest possible worklist row: k_b + number of forced bits
+ *   width_max  widest possible worklist row: k_b + max(window, 1) + (SA_FORCE_FIRST ? 1 : 0)
  *   nnz_cap    R * width_max: a col_idx capacity that can never overflow
  *   n_buckets  NB: buckets 4, 8, ..., 4 * 2^(NB-1) cover width_max
  *   kv_blocks  summary slots (B * N; decode S * ceil(kv_capacity / b); varlen
@@ -154,8 +157,9 @@ size_t sparse_attn_workspace_size(const sa_problem* p, const sa_route_cfg* rc, i
  *               here (decode keeps them with the KV cache) and k is not read.
  *   J           (device, int32) [rows, k_b]: forced blocks ascending, then the
  *               selected history blocks ascending, then -1 padding.
- *   Per row: candidates are the complete history blocks j < r (decode: j < N-1)
- *   that are not forced; score g_j = pool over the block's valid queries of
+ *   Per row: forced F = the window blocks max(r - W + 1, 0) .. r (W = max(window, 1);
+ *   decode: r = N - 1) plus block 0 with SA_FORCE_FIRST; candidates are the
+ *   complete history blocks j < r (decode: j < N-1) that are not forced; score g_j = pool over the block's valid queries of
  *   q . c_j (no 1/sqrt(d)), averaged over the row's query heads; keep the top
  *   D = min(max(K_r - |F|, 0), |C|) by (score desc, id asc), where K_r = k_b
  *   (top-k) or min(k_b, max(k_min, |F| + #{g_j >= max g - tau_rel})).

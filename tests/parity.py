@@ -59,7 +59,7 @@ def check_worklist(w, inp, run: GpuRun):
     """Bit-exact worklist equality against the oracle applied to the GPU's J."""
     sz = dbs.sizes(dbs.problem_for(w, inp), dbs.config_for(w))
     ref = oprob.worklist(run.J, inp.lengths, w.block, w.mode, w.route_heads, w.forced_first,
-                         sz.width_max)
+                         sz.width_max, window=w.window)
     for key in ("row_ptr", "col_idx", "row_perm", "bucket_ptr"):
         assert np.array_equal(np.asarray(run.wl[key], np.int64), ref[key]), key
     assert run.wl["err"] == ref["err"]
@@ -123,7 +123,7 @@ def check_router(w, inp, run: GpuRun, seqs=None):
     lengths = inp.lengths
     _j, scores = oprob.route(qs_full(qs, seqs, len(lengths)), qs_full(ks, seqs, len(lengths)),
                              lengths, w.block, w.mode, w.qpool, w.share_gqa, w.select, w.k_b,
-                             w.k_min, w.tau_rel, w.forced_first, seqs=seqs)
+                             w.k_min, w.tau_rel, w.forced_first, seqs=seqs, window=w.window)
     bad, ties, checked = [], 0, 0
     for i, sc in enumerate(scores):
         if sc is None:

@@ -145,3 +145,14 @@ def test_append_kv_validates_before_any_launch(lib):
     assert call(dataclasses.replace(_prob(), kv_capacity=9000), 1) == dbs.SA_ERR_INVALID_ARG  # prefill
     assert call(dbs.Problem.decode(2, 4, 2, 96, 100, kv_capacity=200), 1) == dbs.SA_ERR_UNSUPPORTED
     assert call(dbs.Problem.decode(2, 4, 3, 128, 100, kv_capacity=200), 1) == dbs.SA_ERR_INVALID_ARG
+
+
+def test_window_sizes_and_limits(lib):
+    s = dbs.sizes(_prob(), dbs.RouteConfig(k_b=16, window=4, force_first=True))
+    assert s.width_max == 16 + 4 + 1
+    for bad in (dbs.RouteConfig(k_b=16, window=-1),
+                dbs.RouteConfig(k_b=4, window=5),                  # k_b must cover the forced ids
+                dbs.RouteConfig(k_b=100, window=30)):              # row wider than 128 slots
+        with pytest.raises(dbs.SAError) as e:
+            dbs.sizes(_prob(), bad)
+        assert e.value.status == dbs.SA_ERR_INVALID_ARG

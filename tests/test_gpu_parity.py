@@ -58,6 +58,11 @@ SMALL = [
                            k_b=6, share_gqa=False, forced_first=False),
     wk.PREFILL_GQA.replace(name="gqa_small_g2_b1_hq4_hkv2_n900", batch=1, heads_q=4, heads_kv=2, seqlen=900,
                            k_b=7),
+    # local window of forced blocks ([P2] §3.2 union), alone and with the sink
+    wk.PREFILL_MHA.replace(name="mha_small_h2_n1000_kb12_win4", heads_q=2, heads_kv=2, seqlen=1000, k_b=12,
+                           window=4),
+    wk.PREFILL_GQA.replace(name="gqa_small_b1_hq8_hkv2_n1500_kb10_win3_first", batch=1, heads_q=8,
+                           heads_kv=2, seqlen=1500, k_b=10, window=3),
 ]
 
 
@@ -88,6 +93,21 @@ def test_small_decode_splits(dev, splits):
     inp = wk.make_inputs(w, dev)
     run = run_gpu(w, inp, num_splits=splits)
     _full_check(w, inp, run)
+
+
+def test_small_window_decode_and_varlen(dev):
+    """The forced local window in decode (the last W cached blocks) and with Eq 7 thresholds."""
+    w = wk.DECODE.replace(name="decode_small_win4", batch=3, heads_q=8, heads_kv=2, seqlen=1000, k_b=9,
+                          window=4)
+    print(f"case {w.name}", flush=True)
+    inp = wk.make_inputs(w, dev)
+    _full_check(w, inp, run_gpu(w, inp))
+    w = wk.VARLEN.replace(name="varlen_small_thresh_win2", heads_q=8, heads_kv=2, k_b=16, window=2)
+    lengths = [700, 1344, 64, 2000, 1]
+    print(f"case {w.name} lengths {lengths}", flush=True)
+    inp = wk.make_inputs(w, dev, lengths=lengths)
+    w = inp.w
+    _full_check(w, inp, run_gpu(w, inp))
 
 
 def test_decode_unshared_heads(dev):
