@@ -306,3 +306,23 @@ def test_rising_scores_rereference(dev, hq, hkv):
     assert fired > 100                      # the re-reference path is exercised
     assert e.max() <= TOL["bf16"][0] and e.mean() <= TOL["bf16"][1]
     assert lerr <= LSE_TOL["bf16"]
+
+
+# ---------------------------------------------------------------------------
+# Edge cases: one-token prefill, decode caches shorter than or equal to one
+# block, and the widest row the worklist takes (k_b = 127: 128 slots per row).
+EDGE = [
+    wk.PREFILL_MHA.replace(name="edge_mha_n1", heads_q=2, heads_kv=2, seqlen=1, k_b=4),
+    wk.TINY_F32.replace(name="edge_f32_n1_d64", seqlen=1, k_b=2),
+    wk.DECODE.replace(name="edge_decode_L1", batch=2, heads_q=8, heads_kv=2, seqlen=1, k_b=4),
+    wk.DECODE.replace(name="edge_decode_L5", batch=2, heads_q=8, heads_kv=2, seqlen=5, k_b=4),
+    wk.DECODE.replace(name="edge_decode_L64", batch=2, heads_q=8, heads_kv=2, seqlen=64, k_b=4),
+    wk.PREFILL_MHA.replace(name="edge_mha_h2_n8192_kb127_widest", heads_q=2, heads_kv=2, k_b=127),
+]
+
+
+@pytest.mark.parametrize("w", EDGE, ids=lambda w: w.name)
+def test_edge_cases(dev, w):
+    print(f"case {w.name}", flush=True)
+    inp = wk.make_inputs(w, dev)
+    _full_check(w, inp, run_gpu(w, inp))
