@@ -28,7 +28,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsparse_attn.so")
 
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = 0, 1, 2, 3, 4
-SA_WL_ERR_RANGE, SA_WL_ERR_ACAUSAL = 1, 2
+SA_WL_ERR_RANGE, SA_WL_ERR_ACAUSAL, SA_WL_ERR_PAGE = 1, 2, 4
 SA_F32, SA_BF16 = 0, 1
 SA_PREFILL, SA_DECODE = 0, 1
 SA_POOL_MEAN, SA_POOL_MAX = 0, 1
@@ -53,7 +53,8 @@ class _Problem(ctypes.Structure):
                 ("dtype", ctypes.c_int32), ("mode", ctypes.c_int32),
                 ("cu_seqlens", ctypes.c_void_p), ("total_tokens", ctypes.c_int32),
                 ("total_blocks", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
-                ("kv_capacity", ctypes.c_int32)]
+                ("kv_capacity", ctypes.c_int32), ("block_table", ctypes.c_void_p),
+                ("table_stride", ctypes.c_int32), ("pool_blocks", ctypes.c_int32)]
 
 
 class _RouteCfg(ctypes.Structure):
@@ -116,15 +117,18 @@ class Problem:
     cu_seqlens: Optional[torch.Tensor] = None   # int32 [batch+1] on the device
     lengths: Optional[list] = None              # host copy of the varlen lengths
     kv_capacity: int = 0         # decode: allocated cache tokens (0 = seqlen)
+    block_table: Optional[torch.Tensor] = None  # decode, paged: int32 [batch, stride] pages (device)
+    pool_blocks: int = 0         # paged: pages in the [pool, Hkv, b, d] K/V pool
 
     @staticmethod
     def fixed(batch, heads_q, heads_kv, head_dim, seqlen, dtype="bf16"):
         return Problem(batch, heads_q, heads_kv, head_dim, seqlen, dtype, "prefill")
 
     @staticmethod
-    def decode(batch, heads_q, heads_kv, head_dim, cache_len, dtype="bf16", kv_capacity=0):
+    def decode(batch, heads_q, heads_kv, head_dim, cache_len, dtype="bf16", kv_capacity=0,
+               block_table=None, pool_blocks=0):
         return Problem(batch, heads_q, heads_kv, head_dim, cache_len, dtype, "decode",
-                       kv_capacity=kv_capacity)
+                       kv_capacity=kv_capacity, block_table=block_table, pool_blocks=pool_blocks)
 
     @staticmethod
     def varlen(lengths, heads_q, heads_kv, head_dim, cu_seqlens, dtype="bf16"):
@@ -138,6 +142,10 @@ class Problem:
         p.dtype = SA_BF16 if self.dtype == "bf16" else SA_F32
         p.mode = SA_DECODE if self.mode == "decode" else SA_PREFILL
         p.kv_capacity = self.kv_capacity
+        if self.block_table is not None:
+            p.block_table = self.block_table.data_ptr()
+            p.table_stride = int(self.block_table.shape[1])
+            p.pool_blocks = self.pool_blocks
         if self.cu_seqlens is not None:
             p.cu_seqlens = self.cu_seqlens.data_ptr()
             nb = [-(-int(x) // self.block) for x in self.lengths]
@@ -305,6 +313,8 @@ def append_kv(prob: Problem, k_new: torch.Tensor, v_new: torch.Tensor, k_cache: 
     dt = torch.bfloat16 if prob.dtype == "bf16" else torch.float32
     cap = prob.kv_capacity
     shape_c = (prob.batch, prob.heads_kv, cap, prob.head_dim)
+    if prob.block_table is not None:
+        shape_c = (prob.pool_blocks, prob.heads_kv, prob.block, prob.head_dim)
     n = k_new.shape[2] if k_new.dim() == 4 else -1
     shape_n = (prob.batch, prob.heads_kv, n, prob.head_dim)
     for name, t, shp, tdt in (("k_new", k_new, shape_n, dt), ("v_new", v_new, shape_n, dt),

@@ -74,8 +74,10 @@ __device__ __forceinline__ void decode_split(const Geom& g, const FwdBufs& a, in
   const float c2 = kLog2eD / sqrtf((float)D);
   const int hs = lane & 15, grp = lane >> 4;
 
-  // tile ids of this split, one per lane (a split holds at most 64 tiles)
+  // tile ids of this split, one per lane (a split holds at most 64 tiles), and
+  // for a paged cache their pages, looked up once here rather than per tile
   const int jl = tb + lane < te ? a.col_idx[t0 + tb + lane] : 0;
+  const int pgl = g.block_table && tb + lane < te ? g.block_table[(int64_t)ri.s * g.table_stride + jl] : 0;
 
   // B operand of S^T = K Q^T: Q[head slot = lane % 16][d = 32 ks + 8 grp .. +8]
   bf16x8 qb[4];
@@ -94,7 +96,8 @@ __device__ __forceinline__ void decode_split(const Geom& g, const FwdBufs& a, in
   for (int t = 0; t < te - tb; ++t) {
     const int j = __builtin_amdgcn_readlane(jl, t);
     const int cnt = min(kBlock, ri.len - j * kBlock);
-    const int64_t off = kv_offset(g, ri.s, kvh, 0, j * kBlock) * 2;
+    const int64_t off = (g.block_table ? page_offset(g, __builtin_amdgcn_readlane(pgl, t), kvh)
+                                       : kv_offset(g, ri.s, kvh, 0, j * kBlock)) * 2;
     // K: A operand of S^T, key = 16 mb + lane % 16, d = 32 ks + 8 grp.  The
     // tile's four 16-key blocks are fetched in two halves (the second after
     // the first half's MFMAs are issued): at 3 wavefronts per SIMD the

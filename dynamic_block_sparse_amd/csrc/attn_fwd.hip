@@ -665,8 +665,8 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(Geom g, FwdBufs a) {
     const int j = a.col_idx[t];
     const int cnt = min(kBlock, ri.len - j * kBlock);
     __syncthreads();
-    const float* kb = k + kv_offset(g, ri.s, kvh, ri.tok0, j * kBlock);
-    const float* vb = v + kv_offset(g, ri.s, kvh, ri.tok0, j * kBlock);
+    const float* kb = k + kv_block_offset(g, ri.s, kvh, ri.tok0, j);
+    const float* vb = v + kv_block_offset(g, ri.s, kvh, ri.tok0, j);
     for (int e = lane; e < 64 * D; e += 64) {
       const int key = e / D, dd = e % D;
       ks[key][dd] = key < cnt ? kb[e] : 0.f;

@@ -7,6 +7,9 @@
 // n new keys of block j turns c_j into (r_j c_j + sum of the new keys) /
 // (r_j + n); a block that had no valid key (r_j = 0) starts from the new keys.
 //
+// A paged cache (a block table into a [pool, Hkv, b, d] pool) writes each
+// block's rows into its page.
+//
 // One wavefront per (sequence, KV head, touched block).  Each lane owns E =
 // d / 64 adjacent columns: it copies those columns of the block's new K and V
 // rows (so a row moves as one coalesced 128- or 256-byte burst per tensor),
@@ -32,8 +35,17 @@ __global__ void __launch_bounds__(64) append_kv_kernel(AppendGeom g, const T* __
   const int col = lane * E;
   const T* kn = k_new + (int64_t)s * g.new_seq + (int64_t)h * g.new_head + col;
   const T* vn = v_new + (int64_t)s * g.new_seq + (int64_t)h * g.new_head + col;
-  T* kd = k_cache + (int64_t)s * g.cache_seq + (int64_t)h * g.cache_head + col;
-  T* vd = v_cache + (int64_t)s * g.cache_seq + (int64_t)h * g.cache_head + col;
+  // destination rows: token t of the block sits at row t - lo of its page (paged
+  // cache, page id clamped into the pool) or at row t of the sequence's plane
+  int64_t dst0;
+  if (g.block_table) {
+    const int page = min(max(g.block_table[(int64_t)s * g.table_stride + j], 0), g.pool_blocks - 1);
+    dst0 = ((int64_t)page * g.hkv + h) * kBlock * D - (int64_t)lo * D;
+  } else {
+    dst0 = (int64_t)s * g.cache_seq + (int64_t)h * g.cache_head;
+  }
+  T* kd = k_cache + dst0 + col;
+  T* vd = v_cache + dst0 + col;
 
   float acc[E];
 #pragma unroll

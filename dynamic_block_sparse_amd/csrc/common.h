@@ -40,6 +40,10 @@ struct Geom {
   int64_t kv_seq, kv_head;     // element strides of K/V
   int64_t sum_seq, sum_head;   // summary strides in blocks (varlen: sum_seq = 0)
   int64_t lse_seq, lse_head;   // strides of the lse array in tokens
+  // paged decode cache: K/V are a pool [pool_blocks, hkv, b, d] and logical
+  // block j of sequence s lives in page block_table[s * table_stride + j]
+  const int32_t* block_table;  // device, or null for a contiguous cache
+  int table_stride, pool_blocks;
 };
 
 struct RowInfo {
@@ -106,6 +110,18 @@ __device__ __forceinline__ int64_t q_offset(const Geom& g, int s, int h, int tok
 }
 __device__ __forceinline__ int64_t kv_offset(const Geom& g, int s, int h, int tok0, int t) {
   return (int64_t)s * g.kv_seq + (int64_t)h * g.kv_head + (int64_t)(tok0 + t) * g.d;
+}
+// Element offset of the first token of logical block j of (sequence s, KV
+// head h).  A paged decode cache looks the page up in the block table; a page
+// id outside the pool is clamped into it, so nothing reads or writes outside
+// the pool (the worklist builder reports such ids, SA_WL_ERR_PAGE).
+__device__ __forceinline__ int64_t page_offset(const Geom& g, int page, int h) {
+  page = min(max(page, 0), g.pool_blocks - 1);
+  return ((int64_t)page * g.hkv + h) * kBlock * g.d;
+}
+__device__ __forceinline__ int64_t kv_block_offset(const Geom& g, int s, int h, int tok0, int j) {
+  if (g.block_table) return page_offset(g, g.block_table[(int64_t)s * g.table_stride + j], h);
+  return kv_offset(g, s, h, tok0, j * kBlock);
 }
 __device__ __forceinline__ int64_t sum_offset(const Geom& g, int s, int h, int blk0, int j) {
   return ((int64_t)s * g.sum_seq + (int64_t)h * g.sum_head + blk0 + j) * g.d;

@@ -49,6 +49,8 @@ struct AppendGeom {
   int64_t cache_seq, cache_head;   // element strides of the K/V cache
   int64_t new_seq, new_head;       // element strides of the new rows
   int64_t sum_seq, sum_head;       // summary strides in blocks
+  const int32_t* block_table;      // paged cache: [S, table_stride] pages of a [pool, hkv, b, d] pool
+  int table_stride, pool_blocks;
 };
 int launch_append_kv(const AppendGeom& g, int dtype, int n_seq, int touched, const void* k_new,
                      const void* v_new, void* k_cache, void* v_cache, float* summ, hipStream_t st);

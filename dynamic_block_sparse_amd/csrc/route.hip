@@ -68,7 +68,7 @@ __global__ void __launch_bounds__(256) summary_kernel(Geom g, const T* __restric
   const int nh = pool_q ? g.hpr : 1;   // query heads pooled into the row
   const int h0 = g.share ? h * g.group : h;
   const T* base = pool_q ? q + q_offset(g, s, h0, tok0, j * kBlock) + c * 8
-                         : k + kv_offset(g, s, h, tok0, j * kBlock) + c * 8;
+                         : k + kv_block_offset(g, s, h, tok0, j) + c * 8;
   auto add_row = [&](int t) {
     const T* p = base + (int64_t)t * D;
     if constexpr (sizeof(T) == 2) {

@@ -76,8 +76,14 @@ int validate(const sa_problem* p, const sa_route_cfg* rc, Plan* out) {
     g.lse_seq = g.hq;
     g.lse_head = 1;
     out->kv_slots = (int64_t)g.batch * nbc;
-  } else if (p->kv_capacity != 0) {
-    return SA_ERR_INVALID_ARG;   // prefill has no cache capacity
+    if (p->block_table) {   // paged cache: every logical block of the capacity has a table entry
+      if (p->table_stride < nbc || p->pool_blocks < 1) return SA_ERR_INVALID_ARG;
+      g.block_table = p->block_table;
+      g.table_stride = p->table_stride;
+      g.pool_blocks = p->pool_blocks;
+    }
+  } else if (p->kv_capacity != 0 || p->block_table) {
+    return SA_ERR_INVALID_ARG;   // prefill has no cache capacity and no block table
   } else if (p->cu_seqlens) {
     if (p->seqlen != 0 || p->total_tokens < 1 || p->total_blocks < p->batch ||
         p->max_blocks < 1 || p->max_blocks > p->total_blocks)
@@ -205,6 +211,10 @@ int sparse_attn_append_kv(const sa_problem* p, int32_t n_new, const void* k_new,
   g.new_seq = (int64_t)p->heads_kv * n_new * d;
   g.sum_head = nbc;
   g.sum_seq = (int64_t)p->heads_kv * nbc;
+  g.block_table = p->block_table;
+  g.table_stride = p->table_stride;
+  g.pool_blocks = p->pool_blocks;
+  if (p->block_table && (p->table_stride < nbc || p->pool_blocks < 1)) return SA_ERR_INVALID_ARG;
   return launch_append_kv(g, p->dtype, p->batch, touched, k_new, v_new, k_cache, v_cache, summaries,
                           reinterpret_cast<hipStream_t>(stream));
 }

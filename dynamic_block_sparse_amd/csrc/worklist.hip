@@ -58,6 +58,13 @@ __global__ void __launch_bounds__(64) wl_rows_kernel(Geom g, sa_route_cfg rc, in
       ebits |= SA_WL_ERR_ACAUSAL;
       return sentinel;
     }
+    if (g.block_table) {   // paged decode cache: the block's page must lie in the pool
+      const int page = g.block_table[(int64_t)ri.s * g.table_stride + v];
+      if (page < 0 || page >= g.pool_blocks) {
+        ebits |= SA_WL_ERR_PAGE;
+        return sentinel;
+      }
+    }
     return (uint32_t)v;
   };
   uint32_t k0 = load_slot(lane);
@@ -94,8 +101,9 @@ __global__ void __launch_bounds__(64) wl_rows_kernel(Geom g, sa_route_cfg rc, in
   // OR the row's error bits into the caller's word (one atomic per bad row)
   const uint64_t er = __ballot(ebits & SA_WL_ERR_RANGE);
   const uint64_t ea = __ballot(ebits & SA_WL_ERR_ACAUSAL);
-  if (lane == 0 && (er | ea))
-    atomicOr(err, (er ? SA_WL_ERR_RANGE : 0) | (ea ? SA_WL_ERR_ACAUSAL : 0));
+  const uint64_t ep = __ballot(ebits & SA_WL_ERR_PAGE);
+  if (lane == 0 && (er | ea | ep))
+    atomicOr(err, (er ? SA_WL_ERR_RANGE : 0) | (ea ? SA_WL_ERR_ACAUSAL : 0) | (ep ? SA_WL_ERR_PAGE : 0));
 }
 
 // Step 2 for rows c0 .. c0 + NT - 1 (c0 = NT * block).  Thread t first sums,

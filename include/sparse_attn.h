@@ -83,6 +83,7 @@ extern "C" {
 /* Device error bits written (OR-ed) into the worklist's `err` word. */
 #define SA_WL_ERR_RANGE 1      /* an id < -1 or >= the sequence's block count */
 #define SA_WL_ERR_ACAUSAL 2    /* prefill: an id after the row's query block */
+#define SA_WL_ERR_PAGE 4       /* paged decode cache: the block's page lies outside the pool */
 
 #define SA_F32 0
 #define SA_BF16 1
@@ -114,6 +115,17 @@ typedef struct sa_problem {
                              and summaries [S, Hkv, ceil(kv_capacity / b), d], of which the
                              first seqlen tokens / ceil(seqlen / b) blocks are valid.
                              Must be 0 for prefill. */
+  const int32_t* block_table; /* decode, optional (device): paged cache.  [batch, table_stride]
+                             int32: logical block j of sequence s lives in page
+                             block_table[s * table_stride + j] of a K/V pool
+                             [pool_blocks, heads_kv, b, d] (each (page, head) tile is one
+                             contiguous chunk).  Summaries stay per logical block.  NULL:
+                             the contiguous layout above.  Must be NULL for prefill. */
+  int32_t table_stride;   /* paged: entries per sequence, >= ceil(kv_capacity / b) */
+  int32_t pool_blocks;    /* paged: pages in the pool; a page id outside [0, pool_blocks)
+                             is reported by the worklist builder (SA_WL_ERR_PAGE, entry
+                             dropped) and clamped by every kernel that reads or writes
+                             the pool, so nothing touches memory outside it */
 } sa_problem;
 
 /* Routing settings (host struct). */

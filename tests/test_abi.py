@@ -156,3 +156,18 @@ def test_window_sizes_and_limits(lib):
         with pytest.raises(dbs.SAError) as e:
             dbs.sizes(_prob(), bad)
         assert e.value.status == dbs.SA_ERR_INVALID_ARG
+
+
+def test_block_table_validation(lib):
+    import torch
+    table = torch.zeros((4, 24), dtype=torch.int32)      # host memory: only the pointer is checked here
+    ok = dbs.Problem.decode(4, 8, 2, 128, 1000, kv_capacity=1500, block_table=table, pool_blocks=96)
+    assert dbs.sizes(ok, dbs.RouteConfig(k_b=8, share_gqa=True)).kv_blocks == 4 * 24
+    short = dbs.Problem.decode(4, 8, 2, 128, 1000, kv_capacity=1500, block_table=table[:, :20].contiguous(),
+                               pool_blocks=96)                               # stride < ceil(1500 / 64)
+    no_pool = dbs.Problem.decode(4, 8, 2, 128, 1000, kv_capacity=1500, block_table=table, pool_blocks=0)
+    prefill = dataclasses.replace(_prob(), block_table=table, pool_blocks=96)
+    for bad in (short, no_pool, prefill):
+        with pytest.raises(dbs.SAError) as e:
+            dbs.sizes(bad, dbs.RouteConfig(k_b=8, share_gqa=True))
+        assert e.value.status == dbs.SA_ERR_INVALID_ARG
