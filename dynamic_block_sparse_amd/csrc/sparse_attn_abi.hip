@@ -20,7 +20,8 @@ struct Plan {
   int qpool = SA_POOL_MEAN;
   int width_max = 0;
   int n_buckets = 0;
-  int64_t kv_slots = 0;   // summary slots
+  int64_t kv_slots = 0;   // summary slots allocated (a decode cache's capacity)
+  int64_t sum_valid = 0;  // summary slots of valid blocks: the summary pass's grid
   int64_t nnz_cap = 0;
 };
 
@@ -76,6 +77,7 @@ int validate(const sa_problem* p, const sa_route_cfg* rc, Plan* out) {
     g.lse_seq = g.hq;
     g.lse_head = 1;
     out->kv_slots = (int64_t)g.batch * nbc;
+    out->sum_valid = (int64_t)g.batch * nb;
     if (p->block_table) {   // paged cache: every logical block of the capacity has a table entry
       if (p->table_stride < nbc || p->pool_blocks < 1) return SA_ERR_INVALID_ARG;
       g.block_table = p->block_table;
@@ -103,6 +105,7 @@ int validate(const sa_problem* p, const sa_route_cfg* rc, Plan* out) {
     g.lse_seq = 0;
     g.lse_head = p->total_tokens;
     out->kv_slots = p->total_blocks;
+    out->sum_valid = p->total_blocks;
   } else {
     if (p->seqlen < 1) return SA_ERR_INVALID_ARG;
     g.n = p->seqlen;
@@ -119,6 +122,7 @@ int validate(const sa_problem* p, const sa_route_cfg* rc, Plan* out) {
     g.lse_seq = (int64_t)g.hq * g.n;
     g.lse_head = g.n;
     out->kv_slots = (int64_t)g.batch * nb;
+    out->sum_valid = out->kv_slots;
   }
   out->width_max = rc->k_b + nforced;
   int nbk = 1;
@@ -270,7 +274,9 @@ int sparse_attn_route(const sa_problem* p, const sa_route_cfg* rc, const void* q
   if (!summaries_in && route_qbar_bytes(pl.g, pl.qpool) > 0)
     qbar = reinterpret_cast<float*>(w + align_up(route_scores_bytes(pl.g)));
   if (!summaries_in) {
-    if ((st = launch_summary(pl.g, p->dtype, k, summaries, (int)pl.kv_slots, q, qbar, hs)) != SA_OK) return st;
+    // one wavefront per valid block: the summary kernel maps slot -> (sequence, block)
+    // over the valid blocks (slots of a cache's spare capacity are never written)
+    if ((st = launch_summary(pl.g, p->dtype, k, summaries, (int)pl.sum_valid, q, qbar, hs)) != SA_OK) return st;
   }
   return launch_route(pl.g, *rc, p->dtype, q, summaries, qbar, scores, J, hs);
 }

@@ -153,3 +153,33 @@ def test_append_graph_replay_matches_eager():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(kc, ke) and torch.equal(vc, ve) and torch.equal(sc, se)
+
+
+def test_summary_pass_stays_inside_a_cache_with_spare_capacity():
+    """Regression: with kv_capacity > seqlen the summary pass must launch one
+    wavefront per valid block only.  It once launched one per allocated slot,
+    mapped (sequence, block) over the valid blocks, and so read K and wrote
+    summaries past the last sequence.  Guard rows after the summaries buffer
+    must stay untouched and every valid block must match the oracle."""
+    dev = torch.device("cuda:0")
+    S, hq, hkv, d, L, cap = 3, 4, 2, 128, 100, 700
+    print(f"summary pass, capacity {cap} > length {L}", flush=True)
+    g = torch.Generator().manual_seed(9)
+    k = torch.randn((S + 8, hkv, cap, d), generator=g).to(torch.bfloat16).to(dev)   # rows past S: guard
+    q = torch.randn((S, hq, d), generator=g).to(torch.bfloat16).to(dev)
+    prob = dbs.Problem.decode(S, hq, hkv, d, L, "bf16", kv_capacity=cap)
+    shape = dbs.summaries_shape(prob)
+    big = torch.full((S + 8,) + tuple(shape[1:]), SENT_SUM, dtype=torch.float32, device=dev)
+    summ = big[:S]
+    dbs.route(prob, dbs.RouteConfig(k_b=2, share_gqa=True), q, k[:S], summaries=summ)
+    torch.cuda.synchronize()
+    assert bool((big[S:] == SENT_SUM).all().item()), "summary pass wrote past the last sequence"
+    nb = -(-L // B)
+    assert bool((summ[:, :, nb:] == SENT_SUM).all().item())
+    kh = k[:S].double().cpu().numpy()
+    sh = summ.double().cpu().numpy()
+    for s in range(S):
+        for h in range(hkv):
+            ref = ocache.summaries_after(kh[s, h], L, B)
+            assert np.max(np.abs(sh[s, h, :nb] - ref)) <= SUM_TOL
+
