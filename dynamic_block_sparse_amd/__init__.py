@@ -54,7 +54,8 @@ class _Problem(ctypes.Structure):
                 ("cu_seqlens", ctypes.c_void_p), ("total_tokens", ctypes.c_int32),
                 ("total_blocks", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
                 ("kv_capacity", ctypes.c_int32), ("block_table", ctypes.c_void_p),
-                ("table_stride", ctypes.c_int32), ("pool_blocks", ctypes.c_int32)]
+                ("table_stride", ctypes.c_int32), ("pool_blocks", ctypes.c_int32),
+                ("q_start", ctypes.c_int32)]
 
 
 class _RouteCfg(ctypes.Structure):
@@ -119,10 +120,12 @@ class Problem:
     kv_capacity: int = 0         # decode: allocated cache tokens (0 = seqlen)
     block_table: Optional[torch.Tensor] = None  # decode, paged: int32 [batch, stride] pages (device)
     pool_blocks: int = 0         # paged: pages in the [pool, Hkv, b, d] K/V pool
+    q_start: int = 0             # chunked prefill: first query token (multiple of block)
 
     @staticmethod
-    def fixed(batch, heads_q, heads_kv, head_dim, seqlen, dtype="bf16"):
-        return Problem(batch, heads_q, heads_kv, head_dim, seqlen, dtype, "prefill")
+    def fixed(batch, heads_q, heads_kv, head_dim, seqlen, dtype="bf16", kv_capacity=0, q_start=0):
+        return Problem(batch, heads_q, heads_kv, head_dim, seqlen, dtype, "prefill",
+                       kv_capacity=kv_capacity, q_start=q_start)
 
     @staticmethod
     def decode(batch, heads_q, heads_kv, head_dim, cache_len, dtype="bf16", kv_capacity=0,
@@ -142,6 +145,7 @@ class Problem:
         p.dtype = SA_BF16 if self.dtype == "bf16" else SA_F32
         p.mode = SA_DECODE if self.mode == "decode" else SA_PREFILL
         p.kv_capacity = self.kv_capacity
+        p.q_start = self.q_start
         if self.block_table is not None:
             p.block_table = self.block_table.data_ptr()
             p.table_stride = int(self.block_table.shape[1])
@@ -229,7 +233,7 @@ def summaries_shape(prob: Problem):
     if prob.cu_seqlens is not None:
         nb = sum(-(-int(x) // prob.block) for x in prob.lengths)
         return (prob.heads_kv, nb, prob.head_dim)
-    n = prob.kv_capacity if (prob.mode == "decode" and prob.kv_capacity) else prob.seqlen
+    n = prob.kv_capacity if prob.kv_capacity else prob.seqlen
     nb = -(-n // prob.block)
     return (prob.batch, prob.heads_kv, nb, prob.head_dim)
 

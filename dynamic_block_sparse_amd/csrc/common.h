@@ -44,6 +44,9 @@ struct Geom {
   // block j of sequence s lives in page block_table[s * table_stride + j]
   const int32_t* block_table;  // device, or null for a contiguous cache
   int table_stride, pool_blocks;
+  // chunked prefill: the queries are tokens [q_tok_off, n) of each sequence
+  // (Q, O and lse hold only those), their rows query blocks qblk0 .. N - 1
+  int qblk0, q_tok_off;
 };
 
 struct RowInfo {
@@ -75,11 +78,12 @@ __device__ __forceinline__ RowInfo decode_row(const Geom& g, int64_t row) {
   }
   if (!g.varlen) {
     int nb = ceil_div(g.n, kBlock);
-    int64_t per_seq = (int64_t)g.hr * nb;
+    const int nrows = nb - g.qblk0;   // query blocks with rows (all but a cached prefix)
+    int64_t per_seq = (int64_t)g.hr * nrows;
     ri.s = (int)(row / per_seq);
     int64_t rem = row - (int64_t)ri.s * per_seq;
-    ri.h = (int)(rem / nb);
-    ri.r = (int)(rem % nb);
+    ri.h = (int)(rem / nrows);
+    ri.r = g.qblk0 + (int)(rem % nrows);
     ri.len = g.n;
     ri.nblk = nb;
     ri.tok0 = 0;
@@ -105,8 +109,9 @@ __device__ __forceinline__ RowInfo decode_row(const Geom& g, int64_t row) {
   return ri;
 }
 
+// Q / O element offset of query token t (an absolute position in the sequence).
 __device__ __forceinline__ int64_t q_offset(const Geom& g, int s, int h, int tok0, int t) {
-  return (int64_t)s * g.q_seq + (int64_t)h * g.q_head + (int64_t)(tok0 + t) * g.d;
+  return (int64_t)s * g.q_seq + (int64_t)h * g.q_head + (int64_t)(tok0 + t - g.q_tok_off) * g.d;
 }
 __device__ __forceinline__ int64_t kv_offset(const Geom& g, int s, int h, int tok0, int t) {
   return (int64_t)s * g.kv_seq + (int64_t)h * g.kv_head + (int64_t)(tok0 + t) * g.d;
@@ -127,7 +132,7 @@ __device__ __forceinline__ int64_t sum_offset(const Geom& g, int s, int h, int b
   return ((int64_t)s * g.sum_seq + (int64_t)h * g.sum_head + blk0 + j) * g.d;
 }
 __device__ __forceinline__ int64_t lse_offset(const Geom& g, int s, int h, int tok0, int t) {
-  return (int64_t)s * g.lse_seq + (int64_t)h * g.lse_head + tok0 + t;
+  return (int64_t)s * g.lse_seq + (int64_t)h * g.lse_head + tok0 + t - g.q_tok_off;
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }

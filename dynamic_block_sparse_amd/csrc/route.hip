@@ -17,7 +17,7 @@ namespace sa {
 // decode_row for prefill rows.
 __device__ __forceinline__ int64_t prefill_row_index(const Geom& g, int s, int h, int r, int blk0, int nblk) {
   if (g.varlen) return (int64_t)g.hr * blk0 + (int64_t)h * nblk + r;
-  return ((int64_t)s * g.hr + h) * nblk + r;
+  return ((int64_t)s * g.hr + h) * (nblk - g.qblk0) + (r - g.qblk0);   // rows from query block qblk0
 }
 
 // ---------------------------------------------------------------------------
@@ -60,6 +60,7 @@ __global__ void __launch_bounds__(256) summary_kernel(Geom g, const T* __restric
     j = slot % nb;
     len = g.n;
   }
+  if (pool_q && j < g.qblk0) return;   // a cached prefix block has no queries (chunked prefill)
   const int cnt = min(kBlock, len - j * kBlock);
   const int c = lane % CH, ph = lane / CH;
   float acc[8];
@@ -188,11 +189,12 @@ __global__ void __launch_bounds__(256) route_score_tile_kernel(Geom g, sa_route_
   } else {
     nblk = ceil_div(g.n, kBlock);
   }
-  const int r0 = blockIdx.x * kScoreRows, j0 = blockIdx.y * kScoreCols;
+  const int r0 = g.qblk0 + blockIdx.x * kScoreRows, j0 = blockIdx.y * kScoreCols;
   // candidates satisfy j < r <= r0 + kScoreRows - 1: tiles above the diagonal have none
   if (r0 >= nblk || j0 > r0 + kScoreRows - 2) return;   // uniform
   const int kvh = g.share ? h : h / g.group;
-  const int64_t row0 = prefill_row_index(g, s, h, 0, blk0, nblk);   // rows of (s, h) are row0 + r
+  // rows of (s, h) are row0 + r for its query blocks r >= qblk0
+  const int64_t row0 = prefill_row_index(g, s, h, g.qblk0, blk0, nblk) - g.qblk0;
   const float* cbase = summ + sum_offset(g, s, kvh, blk0, 0);
   const int tid = threadIdx.x;
   // stage (rows past the end: clamped copies, never written out)
@@ -546,7 +548,8 @@ int launch_route(const Geom& g, const sa_route_cfg& rc, int dtype, const void* q
     // per sequence, 44 us vs 39 at 512
     const bool small = mbk <= 256;
     const int tr = small ? 16 : 32, tc = small ? 32 : 64;
-    dim3 tgrid((unsigned)((mbk + tr - 1) / tr), (unsigned)((mbk + tc - 1) / tc), (unsigned)(g.batch * g.hr));
+    dim3 tgrid((unsigned)((mbk - g.qblk0 + tr - 1) / tr), (unsigned)((mbk + tc - 1) / tc),
+               (unsigned)(g.batch * g.hr));
     if (g.d == 128) {
       if (small) route_score_tile_kernel<128, 16, 32><<<tgrid, 256, 0, st>>>(g, rc, qbar, summ, scores);
       else route_score_tile_kernel<128, 32, 64><<<tgrid, 256, 0, st>>>(g, rc, qbar, summ, scores);

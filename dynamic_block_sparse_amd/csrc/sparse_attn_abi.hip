@@ -58,7 +58,7 @@ int validate(const sa_problem* p, const sa_route_cfg* rc, Plan* out) {
   g.mode = p->mode;
   const int64_t d = g.d;
   if (p->mode == SA_DECODE) {
-    if (p->cu_seqlens || p->seqlen < 1) return SA_ERR_INVALID_ARG;
+    if (p->cu_seqlens || p->seqlen < 1 || p->q_start != 0) return SA_ERR_INVALID_ARG;
     g.n = p->seqlen;
     // the cache may hold room beyond the valid length: strides follow the capacity
     const int cap = p->kv_capacity > 0 ? p->kv_capacity : p->seqlen;
@@ -84,9 +84,10 @@ int validate(const sa_problem* p, const sa_route_cfg* rc, Plan* out) {
       g.table_stride = p->table_stride;
       g.pool_blocks = p->pool_blocks;
     }
-  } else if (p->kv_capacity != 0 || p->block_table) {
-    return SA_ERR_INVALID_ARG;   // prefill has no cache capacity and no block table
+  } else if (p->block_table) {
+    return SA_ERR_INVALID_ARG;   // a block table only pages a decode cache
   } else if (p->cu_seqlens) {
+    if (p->kv_capacity != 0 || p->q_start != 0) return SA_ERR_INVALID_ARG;   // packed: no cache, no chunk
     if (p->seqlen != 0 || p->total_tokens < 1 || p->total_blocks < p->batch ||
         p->max_blocks < 1 || p->max_blocks > p->total_blocks)
       return SA_ERR_INVALID_ARG;
@@ -109,20 +110,29 @@ int validate(const sa_problem* p, const sa_route_cfg* rc, Plan* out) {
   } else {
     if (p->seqlen < 1) return SA_ERR_INVALID_ARG;
     g.n = p->seqlen;
+    // chunked prefill: queries are tokens [q_start, n) (a whole number of blocks
+    // in), K/V the whole sequence in a cache of kv_capacity tokens
+    const int cap = p->kv_capacity > 0 ? p->kv_capacity : p->seqlen;
+    if (p->kv_capacity < 0 || cap < g.n) return SA_ERR_INVALID_ARG;
+    if (p->q_start < 0 || p->q_start % kBlock != 0 || p->q_start >= g.n) return SA_ERR_INVALID_ARG;
     const int nb = (g.n + kBlock - 1) / kBlock;
+    const int nbc = (cap + kBlock - 1) / kBlock;
+    const int nq = g.n - p->q_start;   // query tokens per sequence
+    g.qblk0 = p->q_start / kBlock;
+    g.q_tok_off = p->q_start;
     g.max_blocks = nb;
     g.total_blocks = nb;
-    g.rows = (int64_t)g.batch * g.hr * nb;
-    g.q_seq = (int64_t)g.hq * g.n * d;
-    g.q_head = (int64_t)g.n * d;
-    g.kv_seq = (int64_t)g.hkv * g.n * d;
-    g.kv_head = (int64_t)g.n * d;
-    g.sum_seq = (int64_t)g.hkv * nb;
-    g.sum_head = nb;
-    g.lse_seq = (int64_t)g.hq * g.n;
-    g.lse_head = g.n;
-    out->kv_slots = (int64_t)g.batch * nb;
-    out->sum_valid = out->kv_slots;
+    g.rows = (int64_t)g.batch * g.hr * (nb - g.qblk0);
+    g.q_seq = (int64_t)g.hq * nq * d;
+    g.q_head = (int64_t)nq * d;
+    g.kv_seq = (int64_t)g.hkv * cap * d;
+    g.kv_head = (int64_t)cap * d;
+    g.sum_seq = (int64_t)g.hkv * nbc;
+    g.sum_head = nbc;
+    g.lse_seq = (int64_t)g.hq * nq;
+    g.lse_head = nq;
+    out->kv_slots = (int64_t)g.batch * nbc;
+    out->sum_valid = (int64_t)g.batch * nb;
   }
   out->width_max = rc->k_b + nforced;
   int nbk = 1;
@@ -191,7 +201,7 @@ extern "C" {
 int sparse_attn_append_kv(const sa_problem* p, int32_t n_new, const void* k_new, const void* v_new,
                           void* k_cache, void* v_cache, float* summaries, void* stream) {
   using namespace sa;
-  if (!p || p->mode != SA_DECODE || p->cu_seqlens) return SA_ERR_INVALID_ARG;
+  if (!p || p->mode != SA_DECODE || p->cu_seqlens || p->q_start != 0) return SA_ERR_INVALID_ARG;
   if (p->batch < 1 || p->heads_q < 1 || p->heads_kv < 1 || p->heads_q % p->heads_kv != 0)
     return SA_ERR_INVALID_ARG;
   if (p->dtype != SA_F32 && p->dtype != SA_BF16) return SA_ERR_INVALID_ARG;

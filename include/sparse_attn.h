@@ -114,7 +114,8 @@ typedef struct sa_problem {
                              cache, >= seqlen; 0 = seqlen.  K/V are [S, Hkv, kv_capacity, d]
                              and summaries [S, Hkv, ceil(kv_capacity / b), d], of which the
                              first seqlen tokens / ceil(seqlen / b) blocks are valid.
-                             Must be 0 for prefill. */
+                             Fixed-length prefill may use it the same way (chunked prefill
+                             over a cache); must be 0 for packed varlen. */
   const int32_t* block_table; /* decode, optional (device): paged cache.  [batch, table_stride]
                              int32: logical block j of sequence s lives in page
                              block_table[s * table_stride + j] of a K/V pool
@@ -126,6 +127,13 @@ typedef struct sa_problem {
                              is reported by the worklist builder (SA_WL_ERR_PAGE, entry
                              dropped) and clamped by every kernel that reads or writes
                              the pool, so nothing touches memory outside it */
+  int32_t q_start;        /* fixed-length prefill, optional: chunked prefill.  The queries are
+                             tokens [q_start, seqlen) of each sequence (a multiple of b, < seqlen);
+                             Q, O and lse hold only those ([B, Hq, seqlen - q_start, d]) while
+                             K/V hold the whole sequence (kv_capacity may exceed seqlen, as for
+                             a decode cache).  Rows are query blocks q_start / b .. N - 1, routed
+                             against every earlier block with the usual causal rules.  0 = the
+                             whole sequence; must be 0 for packed varlen and decode. */
 } sa_problem;
 
 /* Routing settings (host struct). */
@@ -143,7 +151,8 @@ typedef struct sa_route_cfg {
 } sa_route_cfg;
 
 /* Host-side sizes derived from the geometry (no device work).
- *   rows       worklist rows R (prefill: H_r * total blocks; decode: S * H_r)
+ *   rows       worklist rows R (prefill: H_r * total blocks, or H_r * B * (N - q_start / b)
+ *              for chunked prefill; decode: S * H_r)
  *   width_max  widest possible worklist row: k_b + max(window, 1) + (SA_FORCE_FIRST ? 1 : 0)
  *   nnz_cap    R * width_max: a col_idx capacity that can never overflow
  *   n_buckets  NB: buckets 4, 8, ..., 4 * 2^(NB-1) cover width_max

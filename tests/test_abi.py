@@ -125,7 +125,7 @@ def test_decode_capacity_sizes_and_prefill_rejects_capacity(lib):
     assert dbs.summaries_shape(dbs.Problem.decode(4, 8, 2, 128, 1000, kv_capacity=1500)) == (4, 2, 24, 128)
     for bad in (dbs.Problem.decode(4, 8, 2, 128, 1000, kv_capacity=999),   # capacity below the length
                 dbs.Problem.decode(4, 8, 2, 128, 1000, kv_capacity=-1),
-                dataclasses.replace(_prob(), kv_capacity=9000)):            # prefill has no capacity
+                dataclasses.replace(_prob(), kv_capacity=8000)):            # prefill: below the length too
         with pytest.raises(dbs.SAError) as e:
             dbs.sizes(bad, dbs.RouteConfig(k_b=8, share_gqa=True))
         assert e.value.status == dbs.SA_ERR_INVALID_ARG
@@ -143,6 +143,7 @@ def test_append_kv_validates_before_any_launch(lib):
     assert call(ok, 5, ptr=None) == dbs.SA_ERR_INVALID_ARG                     # null pointers
     assert call(dbs.Problem.decode(2, 4, 2, 128, 100), 1) == dbs.SA_ERR_INVALID_ARG   # no capacity set
     assert call(dataclasses.replace(_prob(), kv_capacity=9000), 1) == dbs.SA_ERR_INVALID_ARG  # prefill
+    assert call(dataclasses.replace(ok, q_start=64), 1) == dbs.SA_ERR_INVALID_ARG            # decode: no chunk
     assert call(dbs.Problem.decode(2, 4, 2, 96, 100, kv_capacity=200), 1) == dbs.SA_ERR_UNSUPPORTED
     assert call(dbs.Problem.decode(2, 4, 3, 128, 100, kv_capacity=200), 1) == dbs.SA_ERR_INVALID_ARG
 
@@ -171,3 +172,20 @@ def test_block_table_validation(lib):
         with pytest.raises(dbs.SAError) as e:
             dbs.sizes(bad, dbs.RouteConfig(k_b=8, share_gqa=True))
         assert e.value.status == dbs.SA_ERR_INVALID_ARG
+
+
+def test_chunked_prefill_sizes_and_limits(lib):
+    cfg = dbs.RouteConfig(k_b=16)
+    p = dbs.Problem.fixed(2, 4, 4, 128, 1500, "bf16", kv_capacity=2048, q_start=960)
+    s = dbs.sizes(p, cfg)
+    assert s.rows == 2 * 4 * (24 - 15)        # query blocks 15 .. 23 of every (sequence, head)
+    assert s.kv_blocks == 2 * 32              # summary slots follow the capacity
+    assert dbs.summaries_shape(p) == (2, 4, 32, 128)
+    for bad in (dataclasses.replace(p, q_start=100),     # not a whole number of blocks
+                dataclasses.replace(p, q_start=1536),    # no query left
+                dataclasses.replace(p, q_start=-64),
+                dataclasses.replace(dbs.Problem.decode(2, 4, 4, 128, 1500), q_start=64)):
+        with pytest.raises(dbs.SAError) as e:
+            dbs.sizes(bad, cfg)
+        assert e.value.status == dbs.SA_ERR_INVALID_ARG
+
