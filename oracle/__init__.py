@@ -24,8 +24,9 @@ Modules:
   problem    whole-problem drivers (row order, per-sequence routing, sampled rows)
   cache      decode-cache maintenance: append K/V rows, Eq (11) summary update
   quality    router quality: Eq (10) coverage of the dense attention, recall
+  backward   gradients of the masked attention (autograd of the definition, fp64)
 
 Parity status of each function is stated in its docstring; conventions that
 no page value fixes are marked "parity unpinned".
 """
-from . import routing, worklist, attention, counting, problem, cache, quality  # noqa: F401
+from . import routing, worklist, attention, counting, problem, cache, quality, backward  # noqa: F401
