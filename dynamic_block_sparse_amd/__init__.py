@@ -37,7 +37,7 @@ SA_FORCE_CURRENT, SA_FORCE_FIRST = 1, 2
 
 EXPORTED = ["sparse_attn_sizes", "sparse_attn_workspace_size", "sparse_attn_route",
             "sparse_attn_build_worklist", "sparse_attn_fwd", "sparse_attn_append_kv",
-            "sparse_attn_status_string"]
+            "sparse_attn_bwd", "sparse_attn_status_string"]
 
 
 class SAError(RuntimeError):
@@ -83,6 +83,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sparse_attn_sizes.restype = ctypes.c_int
     lib.sparse_attn_append_kv.argtypes = [P, i32, vp, vp, vp, vp, vp, vp]
     lib.sparse_attn_append_kv.restype = ctypes.c_int
+    lib.sparse_attn_bwd.argtypes = [P, R, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.sparse_attn_bwd.restype = ctypes.c_int
     lib.sparse_attn_workspace_size.argtypes = [P, R, i32, i32]
     lib.sparse_attn_workspace_size.restype = sz
     lib.sparse_attn_route.argtypes = [P, R, vp, vp, vp, i32, vp, vp, sz, vp]
@@ -306,6 +308,23 @@ def fwd(prob: Problem, cfg: RouteConfig, wl: Worklist, q, k, v, o=None, lse=None
         ctypes.byref(p), ctypes.byref(c), _ptr(wl.row_ptr), _ptr(wl.col_idx), _ptr(wl.row_perm),
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), num_splits, _ptr(ws), wsb, _stream(dev)))
     return o, lse
+
+
+def bwd(prob: Problem, cfg: RouteConfig, wl: Worklist, q, k, v, o, lse, dout, dq=None, dk=None, dv=None,
+        workspace: Optional[torch.Tensor] = None):
+    """sparse_attn_bwd: returns (dQ, dK, dV) for the forward that produced o and lse."""
+    lib = load_library()
+    dev = q.device
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    p, c = prob.to_c(), cfg.to_c()
+    wsb = workspace_size(prob, cfg, 3)
+    ws = workspace if workspace is not None and workspace.numel() >= wsb else _workspace(wsb, dev)
+    _check("sparse_attn_bwd", lib.sparse_attn_bwd(
+        ctypes.byref(p), ctypes.byref(c), _ptr(wl.row_ptr), _ptr(wl.col_idx), _ptr(q), _ptr(k), _ptr(v),
+        _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), wsb, _stream(dev)))
+    return dq, dk, dv
 
 
 def append_kv(prob: Problem, k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsparse_attn.so")
 SOURCES = ["sparse_attn_abi.hip", "route.hip", "worklist.hip", "attn_fwd.hip", "attn_decode.hip",
-           "cache.hip"]
+           "cache.hip", "attn_bwd.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 

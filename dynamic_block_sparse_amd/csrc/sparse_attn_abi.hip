@@ -170,6 +170,11 @@ int resolve_splits(const Plan& pl, int requested) {
   return requested < min_splits(pl) ? min_splits(pl) : requested;
 }
 
+// Elements of one K (or V) tensor in the problem's layout.
+int64_t kv_elems(const Plan& pl) {
+  return pl.g.varlen ? (int64_t)pl.g.hkv * pl.g.kv_head : (int64_t)pl.g.batch * pl.g.kv_seq;
+}
+
 size_t ws_size(const Plan& pl, int which, int splits) {
   size_t sz = ws_cu_blocks(pl);
   if (which == 0) {
@@ -180,6 +185,8 @@ size_t ws_size(const Plan& pl, int which, int splits) {
     sz += align_up((size_t)pl.g.rows * sizeof(int32_t));
   } else if (which == 2 && pl.g.mode == SA_DECODE) {
     sz += align_up(decode_partials_bytes(pl.g, splits));
+  } else if (which == 3) {   // backward: fp32 dK and dV accumulators in the K / V layout
+    sz += 2 * align_up((size_t)kv_elems(pl) * sizeof(float));
   }
   return sz;
 }
@@ -197,6 +204,43 @@ int prep_cu_blocks(Plan& pl, void* ws, hipStream_t st) {
 using namespace sa;
 
 extern "C" {
+
+int sparse_attn_bwd(const sa_problem* p, const sa_route_cfg* rc, const int32_t* row_ptr,
+                    const int32_t* col_idx, const void* q, const void* k, const void* v, const void* o,
+                    const float* lse, const void* dout, void* dq, void* dk, void* dv, void* ws,
+                    size_t ws_bytes, void* stream) {
+  using namespace sa;
+  Plan pl;
+  int st = validate(p, rc, &pl);
+  if (st != SA_OK) return st;
+  if (p->mode != SA_PREFILL) return SA_ERR_UNSUPPORTED;
+  if (!row_ptr || !col_idx || !q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
+    return SA_ERR_INVALID_ARG;
+  if ((p->dtype == SA_BF16 && p->head_dim != 128) || (p->dtype == SA_F32 && p->head_dim != 64))
+    return SA_ERR_UNSUPPORTED;
+  if (pl.g.rows > 65535LL * 65535LL) return SA_ERR_UNSUPPORTED;
+  const size_t need = ws_size(pl, 3, 0);
+  if (ws_bytes < need || !ws) return SA_ERR_WORKSPACE;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if ((st = prep_cu_blocks(pl, ws, hs)) != SA_OK) return st;
+  unsigned char* w = reinterpret_cast<unsigned char*>(ws) + ws_cu_blocks(pl);
+  const int64_t n = kv_elems(pl);
+  BwdBufs b;
+  b.row_ptr = row_ptr;
+  b.col_idx = col_idx;
+  b.q = q;
+  b.k = k;
+  b.v = v;
+  b.o = o;
+  b.dout = dout;
+  b.lse = lse;
+  b.dq = dq;
+  b.dk = dk;
+  b.dv = dv;
+  b.dk_acc = reinterpret_cast<float*>(w);
+  b.dv_acc = reinterpret_cast<float*>(w + align_up((size_t)n * sizeof(float)));
+  return launch_bwd(pl.g, p->dtype, b, n, hs);
+}
 
 int sparse_attn_append_kv(const sa_problem* p, int32_t n_new, const void* k_new, const void* v_new,
                           void* k_cache, void* v_cache, float* summaries, void* stream) {
@@ -261,7 +305,7 @@ int sparse_attn_sizes(const sa_problem* p, const sa_route_cfg* rc, int64_t* rows
 size_t sparse_attn_workspace_size(const sa_problem* p, const sa_route_cfg* rc, int32_t which,
                                   int32_t num_splits) {
   Plan pl;
-  if (validate(p, rc, &pl) != SA_OK || which < 0 || which > 2) return 0;
+  if (validate(p, rc, &pl) != SA_OK || which < 0 || which > 3) return 0;
   return ws_size(pl, which, resolve_splits(pl, num_splits));
 }
 

@@ -11,6 +11,10 @@
  *
  *   sparse_attn_append_kv        new K/V rows -> cache rows and block summaries
  *
+ * and one for training:
+ *
+ *   sparse_attn_bwd              dO and the forward's worklist and lse -> dQ, dK, dV
+ *
  * The method ([P2] "2.1 Coarse-grained selection: from content grouping to
  * dynamic sparse blocks", PaperTrace sparse-attention 2-1; [P3] "From index to
  * kernel", PaperTrace sparse-attention 5-1):
@@ -164,7 +168,7 @@ int sparse_attn_sizes(const sa_problem* p, const sa_route_cfg* rc, int64_t* rows
                       int64_t* kv_blocks);
 
 /* Bytes of device workspace needed by call `which` (0 route, 1 worklist,
- * 2 fwd).  For fwd in decode mode `num_splits` is the split-KV group count
+ * 2 fwd, 3 bwd).  For fwd in decode mode `num_splits` is the split-KV group count
  * (0 = the library's choice, the same one sparse_attn_fwd makes).  Returns 0
  * for an invalid problem. */
 size_t sparse_attn_workspace_size(const sa_problem* p, const sa_route_cfg* rc, int32_t which,
@@ -227,6 +231,28 @@ int sparse_attn_fwd(const sa_problem* p, const sa_route_cfg* rc, const int32_t* 
                     const int32_t* col_idx, const int32_t* row_perm, const void* q,
                     const void* k, const void* v, void* o, float* lse, int32_t num_splits,
                     void* ws, size_t ws_bytes, void* stream);
+
+/* Backward pass of the prefill attention over the forward's worklist ([P2] §4
+ * training paragraph and [P3]: gradients reuse the forward's block selection).
+ *   row_ptr, col_idx  (device) the worklist the forward used (same problem and config)
+ *   q, k, v, o        (device) the forward's inputs and output
+ *   lse               (device, fp32) the forward's log-sum-exp (natural log)
+ *   dout              (device) dL/dO, layout and dtype of o
+ *   dq                (device, out) layout and dtype of q
+ *   dk, dv            (device, out) layout and dtype of k: every element is
+ *                     written (0 for keys no query attends)
+ *   With P_ip = exp(q_i . k_p / sqrt(d) - lse_i) over the keys query i attended,
+ *   D_i = dO_i . O_i and dS_ip = P_ip (dO_i . v_p - D_i):
+ *   dQ_i = sum_p dS_ip k_p / sqrt(d), dK_p = sum_i dS_ip q_i / sqrt(d),
+ *   dV_p = sum_i P_ip dO_i.  fp32 arithmetic; dK and dV are accumulated in fp32
+ *   (workspace) with atomics, so their summation order is not fixed.
+ *   Prefill only (fixed, packed varlen or chunked); bf16 with head_dim 128 or
+ *   fp32 with head_dim 64.
+ *   ws                (device) sparse_attn_workspace_size(p, rc, 3, 0) bytes. */
+int sparse_attn_bwd(const sa_problem* p, const sa_route_cfg* rc, const int32_t* row_ptr,
+                    const int32_t* col_idx, const void* q, const void* k, const void* v, const void* o,
+                    const float* lse, const void* dout, void* dq, void* dk, void* dv, void* ws,
+                    size_t ws_bytes, void* stream);
 
 /* Decode-cache append ([P2] §3.1 "summaries are cache state" and Eq 11: the
  * summaries are kept with the KV cache and updated as keys arrive, not

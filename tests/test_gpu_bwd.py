@@ -1,0 +1,159 @@
+"""GPU parity of the backward pass (sparse_attn_bwd) against the oracle's
+gradients ([P2] §4 training paragraph, [P3]: the backward reuses the
+forward's block selection).
+
+The forward runs on the GPU (route, worklist, fwd); its worklist is the block
+selection, which the forward parity tests already check bit for bit against
+the oracle.  For every worklist row the oracle differentiates the plain
+masked attention of that row's queries (fp64 autograd of the definition) over
+the row's blocks; dQ of those queries is the row's dq, and dK, dV of a key are
+the sums over every row (and, under shared GQA routing, every query head of
+the group) that attends it.
+
+Tolerances, per tensor with scale = max |reference|:
+  bf16  |err| <= 8e-3 |ref| + 4e-3 scale.  The kernel reads the same bf16
+        inputs the oracle sees and computes in fp32, so the error is the bf16
+        rounding of the result (<= 2^-9 |ref|, taken with a factor 4) plus
+        terms of order 2^-9 scale from the bf16 output O inside D_i = dO . O.
+  fp32  |err| <= 1e-4 |ref| + 2e-5 scale: fp32 accumulation over up to a few
+        thousand terms, in an order the atomics do not fix; the absolute part
+        covers the cancellation in dP - D near zeros of the gradient.
+"""
+import numpy as np
+import pytest
+import torch
+
+import dynamic_block_sparse_amd as dbs
+from oracle import backward as obwd
+from oracle import problem as oprob
+
+pytestmark = pytest.mark.gpu
+
+B = 64
+RTOL = {"bf16": (8e-3, 4e-3), "f32": (1e-4, 2e-5)}
+
+CASES = [
+    # name, dtype, d, lengths (None: fixed), batch, hq, hkv, n, q_start, cap, k_b, share, first, window
+    ("mha_bf16", "bf16", 128, None, 2, 2, 2, 700, 0, 0, 4, False, False, 1),
+    ("gqa_shared_sink_win2", "bf16", 128, None, 1, 8, 2, 600, 0, 0, 3, True, True, 2),
+    ("gqa_per_head", "bf16", 128, None, 1, 4, 2, 450, 0, 0, 3, False, False, 1),
+    ("varlen_f32_d64", "f32", 64, [300, 577, 64], 3, 2, 1, 0, 0, 0, 3, False, True, 1),
+    ("chunked_bf16", "bf16", 128, None, 1, 2, 2, 900, 512, 1024, 4, False, False, 1),
+]
+
+
+def _inputs(case, dev):
+    name, dtype, d, lengths, bsz, hq, hkv, n, q0, cap, k_b, share, first, window = case
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    g = torch.Generator().manual_seed(41)
+    cfg = dbs.RouteConfig(k_b=k_b, share_gqa=share, force_first=first, window=window)
+    if lengths is not None:
+        total = sum(lengths)
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int32)
+        q = torch.randn((hq, total, d), generator=g).to(tdt)
+        k = torch.randn((hkv, total, d), generator=g).to(tdt)
+        v = torch.randn((hkv, total, d), generator=g).to(tdt)
+        do = torch.randn((hq, total, d), generator=g).to(tdt)
+        prob = dbs.Problem.varlen(lengths, hq, hkv, d, cu.to(dev), dtype)
+        # per-sequence views [H, len, d] for the oracle, token offset of each sequence
+        views = [(int(cu[s]), lengths[s]) for s in range(bsz)]
+        q_in = q
+    else:
+        kvn = cap or n
+        q = torch.randn((bsz, hq, n, d), generator=g).to(tdt)
+        k = torch.randn((bsz, hkv, kvn, d), generator=g).to(tdt)
+        v = torch.randn((bsz, hkv, kvn, d), generator=g).to(tdt)
+        do = torch.randn((bsz, hq, n - q0, d), generator=g).to(tdt)
+        prob = dbs.Problem.fixed(bsz, hq, hkv, d, n, dtype, kv_capacity=cap, q_start=q0)
+        views = None
+        q_in = q[:, :, q0:].contiguous()
+    return prob, cfg, q, q_in, k, v, do, views
+
+
+def _seq(x, s, views):
+    """[H, len, d] of sequence s (fp64 numpy)."""
+    if views is None:
+        return x[s].double().numpy()
+    t0, ln = views[s]
+    return x[:, t0:t0 + ln].double().numpy()
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: c[0])
+def test_bwd_matches_oracle(case):
+    name, dtype, d, lengths, bsz, hq, hkv, n, q0, cap, k_b, share, first, window = case
+    dev = torch.device("cuda:0")
+    print(f"bwd {name}: dtype={dtype} d={d} batch={bsz} hq={hq} hkv={hkv} n={n} lengths={lengths} "
+          f"q_start={q0} cap={cap}", flush=True)
+    prob, cfg, q, q_in, k, v, do, views = _inputs(case, dev)
+    qd, kd, vd, dod = q_in.to(dev), k.to(dev), v.to(dev), do.to(dev)
+    J, _summ = dbs.route(prob, cfg, qd, kd)
+    wl = dbs.build_worklist(prob, cfg, J)
+    o, lse = dbs.fwd(prob, cfg, wl, qd, kd, vd)
+    dq, dk, dv = dbs.bwd(prob, cfg, wl, qd, kd, vd, o, lse, dod)
+    torch.cuda.synchronize()
+    assert int(wl.err.item()) == 0
+
+    lens = lengths if lengths is not None else [n] * bsz
+    hr = hkv if share else hq
+    group = hq // hkv
+    table = oprob.row_table(lens, B, "prefill", hr)
+    r0 = q0 // B
+    gpu_rows = [t for t in table if t[2] >= r0]
+    rp, ci = wl.row_ptr.cpu().numpy(), wl.col_idx.cpu().numpy()
+    assert J.shape[0] == len(gpu_rows)
+
+    ref_dq = np.zeros(dq.shape, dtype=np.float64)
+    ref_dk = np.zeros(dk.shape, dtype=np.float64)
+    ref_dv = np.zeros(dv.shape, dtype=np.float64)
+    seqs = {}
+    for i, (s, h, r, _nk) in enumerate(gpu_rows):
+        if s not in seqs:
+            seqs[s] = tuple(_seq(x, s, views) for x in (q, k, v))
+        qs, ks, vs = seqs[s]
+        length = lens[s]
+        toks = np.arange(r * B, min((r + 1) * B, length))
+        blocks = ci[rp[i]:rp[i + 1]].tolist()
+        heads = range(h * group, (h + 1) * group) if share else [h]
+        for hh in heads:
+            kvh = hh // group
+            if views is None:
+                dout = do[s, hh, toks - q0].double().numpy()
+            else:
+                dout = do[hh, views[s][0] + toks].double().numpy()
+            gq, gk, gv = obwd.masked_attention_grads(qs[hh, toks], toks, ks[kvh], vs[kvh], length, B, blocks,
+                                                     True, dout)
+            if views is None:
+                ref_dq[s, hh, toks - q0] = gq
+                ref_dk[s, kvh, :length] += gk
+                ref_dv[s, kvh, :length] += gv
+            else:
+                t0 = views[s][0]
+                ref_dq[hh, t0 + toks] = gq
+                ref_dk[kvh, t0:t0 + length] += gk
+                ref_dv[kvh, t0:t0 + length] += gv
+
+    rtol, stol = RTOL[dtype]
+    for label, got, ref in (("dq", dq, ref_dq), ("dk", dk, ref_dk), ("dv", dv, ref_dv)):
+        g64 = got.float().cpu().numpy().astype(np.float64)
+        scale = float(np.max(np.abs(ref)))
+        err = np.abs(g64 - ref)
+        bound = rtol * np.abs(ref) + stol * scale
+        worst = float(np.max(err - bound))
+        print(f"bwd {name} {label}: scale {scale:.3e} max-abs {err.max():.3e} mean-abs {err.mean():.3e}",
+              flush=True)
+        assert worst <= 0, (name, label, np.unravel_index(np.argmax(err - bound), err.shape))
+    # keys past the sequence end (capacity tail) get exactly zero
+    if cap:
+        assert not dk[:, :, n:].any() and not dv[:, :, n:].any()
+
+
+def test_bwd_rejects_decode_and_other_head_dims():
+    dev = torch.device("cuda:0")
+    prob = dbs.Problem.fixed(1, 2, 2, 64, 128, "bf16")
+    cfg = dbs.RouteConfig(k_b=2)
+    x = torch.zeros((1, 2, 128, 64), dtype=torch.bfloat16, device=dev)
+    J, _ = dbs.route(prob, cfg, x, x)
+    wl = dbs.build_worklist(prob, cfg, J)
+    lse = torch.zeros((1, 2, 128), dtype=torch.float32, device=dev)
+    with pytest.raises(dbs.SAError):
+        dbs.bwd(prob, cfg, wl, x, x, x, x, lse, x)
