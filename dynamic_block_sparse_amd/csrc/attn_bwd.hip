@@ -8,16 +8,24 @@
 //   dS_ip = P_ip (dO_i . v_p - D_i),
 //   dQ_i = c sum_p dS_ip k_p,  dK_p = c sum_i dS_ip q_i,  dV_p = sum_i P_ip dO_i.
 //
-// One wavefront per (worklist row, query head), one lane per query row
-// (fp32 arithmetic throughout).  Per listed tile the K, V tiles are staged in
-// LDS (in the input dtype, lossless), each lane forms its row of P and dS
-// over the tile's 64 keys, accumulates dQ in registers and writes P and dS
-// transposed to LDS; then lane t takes key t and reduces dV_t = sum_i P_it
-// dO_i and dK_t = c sum_i dS_it q_i over the row's 64 queries (Q and dO rows
-// staged once per row), in chunks of 32 columns, and adds them to fp32
-// accumulators with atomics: a key block is listed by many rows (and, with
-// shared GQA routing, by every query head of the group).  A last pass
-// converts the accumulators to the output dtype.
+// bf16 path (d = 128), two kernels on v_mfma_f32_32x32x16_bf16, no atomics:
+//   * dQ, one workgroup per (worklist row, query head), 2 wavefronts of 32
+//     query rows: Q and dO rows live in registers, each listed K/V tile is
+//     staged in LDS, S^T = K Q^T and dP^T = V dO^T give every lane one query
+//     row of P and dS, and dQ^T += K^T dS^T reads K^T with LDS transpose
+//     reads.  It also writes D_i, which the second kernel reads;
+//   * dK and dV, one workgroup per (key block, KV head), 2 wavefronts of 32
+//     keys: K and V of the block are staged once; the kernel walks every
+//     worklist row of the sequence whose list holds the block (binary search
+//     of the sorted lists, 64 rows per step, one row per lane), stages the
+//     row's Q and dO, forms S = Q K^T and dP = dO V^T with one key per lane,
+//     and accumulates dV^T += dO^T P and dK^T += Q^T dS in registers over all
+//     of them, so each key is written once.
+//   P and dS enter the second products as bf16 operands (as P does in the
+//   forward); everything else is fp32.
+// fp32 path (d = 64): a plain SIMT kernel, one lane per query row, with dK
+// and dV added into fp32 workspace accumulators by atomics (their summation
+// order is therefore not fixed) and converted by a last pass.
 #include <algorithm>
 
 #include "common.h"
@@ -39,8 +47,14 @@ __global__ void __launch_bounds__(256) bwd_convert_kernel(const float* __restric
     out[i] = (T)acc[i];
 }
 
+// fp32 SIMT kernel: one wavefront per (worklist row, query head), one lane per
+// query row.  Per listed tile the K, V tiles are staged in LDS, each lane forms
+// its row of P and dS over the tile's 64 keys, accumulates dQ in registers and
+// writes P and dS transposed to LDS; then lane t takes key t and reduces
+// dV_t = sum_i P_it dO_i and dK_t = c sum_i dS_it q_i over the row's 64
+// queries in chunks of 32 columns, and adds them to the accumulators.
 template <typename T, int D>
-__global__ void __launch_bounds__(64) attn_bwd_kernel(Geom g, BwdBufs a) {
+__global__ void __launch_bounds__(64) attn_bwd_simt_kernel(Geom g, BwdBufs a) {
   // row padding of the per-lane-row tiles (Q, dO): an odd number of dwords per
   // row, so the 64 lanes reading their own rows hit distinct banks
   constexpr int PAD = sizeof(T) == 2 ? 2 : 1;
@@ -139,24 +153,319 @@ __global__ void __launch_bounds__(64) attn_bwd_kernel(Geom g, BwdBufs a) {
   }
 }
 
-int launch_bwd(const Geom& g, int dtype, const BwdBufs& b, int64_t kv_elems, hipStream_t st) {
+// --------------------------------------------------------------------------
+// bf16 MFMA kernels (d = 128).  v_mfma_f32_32x32x16_bf16 layouts, lane =
+// 32 half + l32:  A operand = A[l32][8 half + e],  B operand = B[8 half +
+// e][l32],  accumulator element i = C[8 (i / 4) + 4 half + i % 4][l32].
+// A 32-row block of an accumulator converts in place into the B operand of a
+// product that contracts over those rows, in the order
+//   k-slot (half, e) of step ks = row 16 ks + 8 (e / 4) + 4 half + e % 4,
+// and the A operand of that product is read in the same order from a
+// row-major LDS tile with ds_read_b64_tr_b16 (tr8 below).
+//
+// LDS tiles are [64 rows][128 d] bf16 (256 bytes a row) in 16-byte chunks,
+// the chunk index XORed with a row swizzle: rsw for tiles read only by rows
+// (16-byte reads of one row per lane), tsw for tiles also read transposed.
+
+#define SA_LDS __attribute__((address_space(3)))
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ int rsw(int row) { return row & 15; }
+__device__ __forceinline__ int tsw(int row) { return ((row & 3) << 2) + (row & 2); }
+
+// 8 bf16 of tile row `row`, columns 8 c .. 8 c + 7
+template <bool TR>
+__device__ __forceinline__ bf16x8 row8(const unsigned char* t, int row, int c) {
+  return *reinterpret_cast<const bf16x8*>(t + row * 256 + ((c ^ (TR ? tsw(row) : rsw(row))) << 4));
+}
+
+// A operand of a product contracting over tile rows: lane (l32, half) gets
+// column db * 32 + l32 of the rows rb * 32 + 16 ks + 8 (e / 4) + 4 half + e % 4.
+// Each 16-lane group's transpose read returns, to lane i, column i of the
+// 4 x 16 block its lanes address row-wise.
+__device__ __forceinline__ bf16x8 tr8(const unsigned char* t, int rb, int ks, int db, int lane) {
+  const int gi = lane >> 4, li = lane & 15, vh = gi >> 1, vdh = gi & 1;
+  const int d = db * 32 + 16 * vdh + 4 * (li & 3);
+  const int chunk = d >> 3, h8 = (d >> 2) & 1;
+  const int r0 = rb * 32 + 16 * ks + 4 * vh + (li >> 2), r1 = r0 + 8;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (SA_LDS i16x4*)(t + r0 * 256 + ((chunk ^ tsw(r0)) << 4) + h8 * 8));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (SA_LDS i16x4*)(t + r1 * 256 + ((chunk ^ tsw(r1)) << 4) + h8 * 8));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Stage `rows` valid rows (the rest zero) of a [64][128] bf16 tile whose row
+// i starts at src + i * 128, by the workgroup's 128 threads.
+template <bool TR>
+__device__ __forceinline__ void stage_tile(unsigned char* t, const __bf16* src, int rows, int tid) {
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int c = it * 128 + tid, row = c >> 4, ch = c & 15;
+    const u32x4 x = row < rows ? *reinterpret_cast<const u32x4*>(src + row * 128 + ch * 8) : u32x4{0, 0, 0, 0};
+    *reinterpret_cast<u32x4*>(t + row * 256 + ((ch ^ (TR ? tsw(row) : rsw(row))) << 4)) = x;
+  }
+}
+
+// Rows of a 32-column accumulator block scaled and stored as bf16: lane owns
+// column l32 (one output row at dst) and writes its 16 elements as four runs
+// of 4 consecutive d.
+__device__ __forceinline__ void store_acc(const f32x16 (&acc)[4], float scale, __bf16* dst, int half) {
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      bf16x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[db][4 * gq + e] * scale);
+      *reinterpret_cast<bf16x4*>(dst + db * 32 + 8 * gq + 4 * half) = v;
+    }
+}
+
+__global__ void __launch_bounds__(128) bwd_dq_bf16_kernel(Geom g, BwdBufs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char kt[64 * 256], vt[64 * 256];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, half = lane >> 5;
+  const int64_t row = blockIdx.x;
+  const RowInfo ri = decode_row(g, row);
+  const int head = (g.share ? ri.h * g.group : ri.h) + (int)blockIdx.y;
+  const int kvh = head / g.group;
+  const int qpos = ri.r * kBlock + w * 32 + l32;
+  const bool qvalid = qpos < ri.len;
+  const float c = 0.08838834764831845f, cl2 = c * kLog2e;   // 1 / sqrt(128)
+  const __bf16* k = (const __bf16*)a.k;
+  const __bf16* v = (const __bf16*)a.v;
+
+  // this lane's query row as B operands: d = 16 ks + 8 half .. + 8
+  bf16x8 qreg[8], doreg[8];
+  float delta = 0.f, lse2 = 0.f;
+  {
+    const int64_t qo = q_offset(g, ri.s, head, ri.tok0, qvalid ? qpos : ri.r * kBlock);
+    const __bf16* qp = (const __bf16*)a.q + qo + half * 8;
+    const __bf16* dp = (const __bf16*)a.dout + qo + half * 8;
+    const __bf16* op = (const __bf16*)a.o + qo + half * 8;
+    float part = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const u32x4 z = {0, 0, 0, 0};
+      qreg[ks] = __builtin_bit_cast(bf16x8, qvalid ? *reinterpret_cast<const u32x4*>(qp + ks * 16) : z);
+      doreg[ks] = __builtin_bit_cast(bf16x8, qvalid ? *reinterpret_cast<const u32x4*>(dp + ks * 16) : z);
+      const bf16x8 ov = __builtin_bit_cast(bf16x8, qvalid ? *reinterpret_cast<const u32x4*>(op + ks * 16) : z);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part = fmaf((float)doreg[ks][e], (float)ov[e], part);
+    }
+    delta = part + __shfl_xor(part, 32);
+    if (qvalid) {
+      const int64_t lo = lse_offset(g, ri.s, head, ri.tok0, qpos);
+      lse2 = a.lse[lo] * kLog2e;
+      if (half == 0) a.delta[lo] = delta;
+    }
+  }
+  f32x16 dq[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dq[db][i] = 0.f;
+
+  for (int t = a.row_ptr[row]; t < a.row_ptr[row + 1]; ++t) {
+    const int j = a.col_idx[t];
+    const int cnt = min(kBlock, ri.len - j * kBlock);
+    const int64_t kb = kv_block_offset(g, ri.s, kvh, ri.tok0, j);
+    __syncthreads();   // the previous tile is no longer read
+    stage_tile<true>(kt, k + kb, cnt, tid);
+    stage_tile<false>(vt, v + kb, cnt, tid);
+    __syncthreads();
+    f32x16 sacc[2], dpacc[2];
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[b2][i] = dpacc[b2][i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2) {
+        sacc[b2] = mfma(row8<true>(kt, b2 * 32 + l32, 2 * ks + half), qreg[ks], sacc[b2]);
+        dpacc[b2] = mfma(row8<false>(vt, b2 * 32 + l32, 2 * ks + half), doreg[ks], dpacc[b2]);
+      }
+    // dS^T of this lane's query over the tile's keys, as B operands
+    bf16x8 dsb[2][2];
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kpos = j * kBlock + b2 * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+        const bool ok = qvalid && kpos <= qpos;
+        const float p = ok ? __builtin_amdgcn_exp2f(fmaf(sacc[b2][i], cl2, -lse2)) : 0.f;
+        dsb[b2][i / 8][i % 8] = (__bf16)(p * (dpacc[b2][i] - delta));
+      }
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) dq[db] = mfma(tr8(kt, b2, ks, db, lane), dsb[b2][ks], dq[db]);
+  }
+  if (qvalid) store_acc(dq, c, (__bf16*)a.dq + q_offset(g, ri.s, head, ri.tok0, qpos), half);
+}
+
+// Worklist row id of (sequence s, routing head h, query block r).
+__device__ __forceinline__ int64_t row_id(const Geom& g, int s, int h, int r, int blk0, int nb) {
+  if (!g.varlen) return ((int64_t)s * g.hr + h) * (nb - g.qblk0) + (r - g.qblk0);
+  return (int64_t)g.hr * blk0 + (int64_t)h * nb + r;
+}
+
+__global__ void __launch_bounds__(128) bwd_dkdv_bf16_kernel(Geom g, BwdBufs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char kt[64 * 256], vt[64 * 256], qt[64 * 256], dot[64 * 256];
+  __shared__ float lse_s[64], del_s[64];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, half = lane >> 5;
+  const int kvh = blockIdx.y;
+  // key block slot -> (sequence, block)
+  int s, j, len, tok0, blk0, nb;
+  if (!g.varlen) {
+    nb = ceil_div(g.n, kBlock);
+    s = (int)(blockIdx.x / (unsigned)nb);
+    j = (int)(blockIdx.x % (unsigned)nb);
+    len = g.n;
+    tok0 = 0;
+    blk0 = 0;
+  } else {
+    int lo = 0, hi = g.batch - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (g.cu_blocks[mid] <= (int)blockIdx.x) lo = mid; else hi = mid - 1;
+    }
+    s = lo;
+    blk0 = g.cu_blocks[s];
+    nb = g.cu_blocks[s + 1] - blk0;
+    j = (int)blockIdx.x - blk0;
+    tok0 = g.cu_seqlens[s];
+    len = g.cu_seqlens[s + 1] - tok0;
+  }
+  const int cnt = min(kBlock, len - j * kBlock);
+  const int64_t kb = kv_block_offset(g, s, kvh, tok0, j);
+  stage_tile<false>(kt, (const __bf16*)a.k + kb, cnt, tid);
+  stage_tile<false>(vt, (const __bf16*)a.v + kb, cnt, tid);
+  const float c = 0.08838834764831845f, cl2 = c * kLog2e;
+  const int key = w * 32 + l32, kpos = j * kBlock + key;
+
+  f32x16 dk[4], dv[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dk[db][i] = dv[db][i] = 0.f;
+
+  const int nrh = g.share ? 1 : g.group;   // routing heads whose rows may list this block
+  const int rfirst = max(j, g.qblk0);      // causal: only query blocks r >= j list block j
+  for (int hh = 0; hh < nrh; ++hh) {
+    const int hr = g.share ? kvh : kvh * g.group + hh;
+    for (int r0 = rfirst; r0 < nb; r0 += 64) {
+      // one candidate row per lane: does its (sorted) list hold block j?
+      const int r = r0 + lane;
+      bool has = false;
+      if (r < nb) {
+        const int64_t rw = row_id(g, s, hr, r, blk0, nb);
+        int lo = a.row_ptr[rw], hi = a.row_ptr[rw + 1] - 1;
+        while (lo <= hi) {
+          const int mid = (lo + hi) >> 1, cj = a.col_idx[mid];
+          if (cj == j) { has = true; break; }
+          if (cj < j) lo = mid + 1; else hi = mid - 1;
+        }
+      }
+      uint64_t m = __ballot(has);
+      while (m) {
+        const int rr = r0 + __builtin_ctzll(m);
+        m &= m - 1;
+        const int qrows = min(kBlock, len - rr * kBlock);
+        for (int gh = 0; gh < (g.share ? g.group : 1); ++gh) {
+          const int head = g.share ? kvh * g.group + gh : hr;
+          const int64_t qo = q_offset(g, s, head, tok0, rr * kBlock);
+          __syncthreads();   // the previous pair's tiles are no longer read
+          stage_tile<true>(qt, (const __bf16*)a.q + qo, qrows, tid);
+          stage_tile<true>(dot, (const __bf16*)a.dout + qo, qrows, tid);
+          if (tid < 64) {
+            const bool ok = tid < qrows;
+            const int64_t lo = ok ? lse_offset(g, s, head, tok0, rr * kBlock + tid) : 0;
+            lse_s[tid] = ok ? a.lse[lo] * kLog2e : 0.f;
+            del_s[tid] = ok ? a.delta[lo] : 0.f;
+          }
+          __syncthreads();
+          // S = Q K^T and dP = dO V^T for this wave's 32 keys (one per lane)
+          f32x16 sacc[2], dpacc[2];
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sacc[qb][i] = dpacc[qb][i] = 0.f;
+#pragma unroll
+          for (int ks = 0; ks < 8; ++ks) {
+            const bf16x8 kv = row8<false>(kt, key, 2 * ks + half);
+            const bf16x8 vv = row8<false>(vt, key, 2 * ks + half);
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+              sacc[qb] = mfma(row8<true>(qt, qb * 32 + l32, 2 * ks + half), kv, sacc[qb]);
+              dpacc[qb] = mfma(row8<true>(dot, qb * 32 + l32, 2 * ks + half), vv, dpacc[qb]);
+            }
+          }
+          bf16x8 pb[2][2], dsb[2][2];
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int q = qb * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+              const bool ok = q < qrows && kpos <= rr * kBlock + q;
+              const float p = ok ? __builtin_amdgcn_exp2f(fmaf(sacc[qb][i], cl2, -lse_s[q])) : 0.f;
+              pb[qb][i / 8][i % 8] = (__bf16)p;
+              dsb[qb][i / 8][i % 8] = (__bf16)(p * (dpacc[qb][i] - del_s[q]));
+            }
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+              for (int ks = 0; ks < 2; ++ks) {
+                dv[db] = mfma(tr8(dot, qb, ks, db, lane), pb[qb][ks], dv[db]);
+                dk[db] = mfma(tr8(qt, qb, ks, db, lane), dsb[qb][ks], dk[db]);
+              }
+        }
+      }
+    }
+  }
+  if (key < cnt) {
+    store_acc(dk, c, (__bf16*)a.dk + kb + (int64_t)key * 128, half);
+    store_acc(dv, 1.f, (__bf16*)a.dv + kb + (int64_t)key * 128, half);
+  }
+}
+
+__global__ void __launch_bounds__(256) bwd_zero_kernel(uint32_t* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0u;
+}
+
+int launch_bwd(const Geom& g, int dtype, const BwdBufs& b, int64_t kv_elems, int kv_tail, hipStream_t st) {
   const unsigned fill_grid = (unsigned)std::min<int64_t>((kv_elems + 255) / 256, 65536);
+  if (dtype == SA_BF16) {
+    // keys past the sequence end (capacity tail) are never attended: dK = dV = 0
+    if (kv_tail) {
+      const int64_t words = kv_elems / 2;
+      const unsigned zg = (unsigned)std::min<int64_t>((words + 255) / 256, 65536);
+      bwd_zero_kernel<<<zg, 256, 0, st>>>((uint32_t*)b.dk, words);
+      bwd_zero_kernel<<<zg, 256, 0, st>>>((uint32_t*)b.dv, words);
+    }
+    if (g.rows > 0) {
+      bwd_dq_bf16_kernel<<<dim3((unsigned)g.rows, (unsigned)g.hpr), 128, 0, st>>>(g, b);
+      const unsigned slots = g.varlen ? (unsigned)g.total_blocks : (unsigned)(g.batch * ((g.n + kBlock - 1) / kBlock));
+      bwd_dkdv_bf16_kernel<<<dim3(slots, (unsigned)g.hkv), 128, 0, st>>>(g, b);
+    }
+    return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
+  }
   bwd_fill_kernel<<<fill_grid, 256, 0, st>>>(b.dk_acc, kv_elems);
   bwd_fill_kernel<<<fill_grid, 256, 0, st>>>(b.dv_acc, kv_elems);
-  if (g.rows > 0) {
-    const dim3 grid((unsigned)g.rows, (unsigned)g.hpr);
-    if (dtype == SA_BF16)
-      attn_bwd_kernel<__bf16, 128><<<grid, 64, 0, st>>>(g, b);
-    else
-      attn_bwd_kernel<float, 64><<<grid, 64, 0, st>>>(g, b);
-  }
-  if (dtype == SA_BF16) {
-    bwd_convert_kernel<__bf16><<<fill_grid, 256, 0, st>>>(b.dk_acc, (__bf16*)b.dk, kv_elems);
-    bwd_convert_kernel<__bf16><<<fill_grid, 256, 0, st>>>(b.dv_acc, (__bf16*)b.dv, kv_elems);
-  } else {
-    bwd_convert_kernel<float><<<fill_grid, 256, 0, st>>>(b.dk_acc, (float*)b.dk, kv_elems);
-    bwd_convert_kernel<float><<<fill_grid, 256, 0, st>>>(b.dv_acc, (float*)b.dv, kv_elems);
-  }
+  if (g.rows > 0)
+    attn_bwd_simt_kernel<float, 64><<<dim3((unsigned)g.rows, (unsigned)g.hpr), 64, 0, st>>>(g, b);
+  bwd_convert_kernel<float><<<fill_grid, 256, 0, st>>>(b.dk_acc, (float*)b.dk, kv_elems);
+  bwd_convert_kernel<float><<<fill_grid, 256, 0, st>>>(b.dv_acc, (float*)b.dv, kv_elems);
   return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 

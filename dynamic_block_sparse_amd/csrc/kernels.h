@@ -42,16 +42,19 @@ int launch_prefill(const Geom& g, int dtype, const FwdBufs& b, hipStream_t st);
 int launch_decode(const Geom& g, int dtype, const FwdBufs& b, int splits, hipStream_t st);
 size_t decode_partials_bytes(const Geom& g, int splits);
 
-// Backward pass over a forward worklist (prefill): dQ, dK, dV.  dk_acc / dv_acc
-// are fp32 accumulators in the K / V layout (workspace), zeroed by the launch.
+// Backward pass over a forward worklist (prefill): dQ, dK, dV.  delta holds
+// D_i per query (lse layout, workspace); dk_acc / dv_acc are the fp32 path's
+// accumulators in the K / V layout (workspace), zeroed by the launch.
+// kv_tail: K/V hold keys past the sequence end (a cache's capacity), whose
+// gradients are zero.
 struct BwdBufs {
   const int32_t *row_ptr, *col_idx;
   const void *q, *k, *v, *o, *dout;
   const float* lse;
   void *dq, *dk, *dv;
-  float *dk_acc, *dv_acc;
+  float *delta, *dk_acc, *dv_acc;
 };
-int launch_bwd(const Geom& g, int dtype, const BwdBufs& b, int64_t kv_elems, hipStream_t st);
+int launch_bwd(const Geom& g, int dtype, const BwdBufs& b, int64_t kv_elems, int kv_tail, hipStream_t st);
 
 // Decode-cache append: rows [len0, len0 + n_new) of every (sequence, KV head)
 // and the Eq 11 update of the summaries of the blocks they land in.

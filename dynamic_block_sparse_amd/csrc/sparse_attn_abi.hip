@@ -23,6 +23,7 @@ struct Plan {
   int64_t kv_slots = 0;   // summary slots allocated (a decode cache's capacity)
   int64_t sum_valid = 0;  // summary slots of valid blocks: the summary pass's grid
   int64_t nnz_cap = 0;
+  int dtype = SA_BF16;
 };
 
 int validate(const sa_problem* p, const sa_route_cfg* rc, Plan* out) {
@@ -30,6 +31,7 @@ int validate(const sa_problem* p, const sa_route_cfg* rc, Plan* out) {
   if (p->batch < 1 || p->heads_q < 1 || p->heads_kv < 1 || p->heads_q % p->heads_kv != 0)
     return SA_ERR_INVALID_ARG;
   if (p->dtype != SA_F32 && p->dtype != SA_BF16) return SA_ERR_INVALID_ARG;
+  out->dtype = p->dtype;
   if (p->mode != SA_PREFILL && p->mode != SA_DECODE) return SA_ERR_INVALID_ARG;
   if (p->block != kBlock) return SA_ERR_UNSUPPORTED;
   if (p->head_dim != 64 && p->head_dim != 128) return SA_ERR_UNSUPPORTED;
@@ -175,6 +177,11 @@ int64_t kv_elems(const Plan& pl) {
   return pl.g.varlen ? (int64_t)pl.g.hkv * pl.g.kv_head : (int64_t)pl.g.batch * pl.g.kv_seq;
 }
 
+// Elements of the lse array (one per query token and head).
+int64_t lse_elems(const Plan& pl) {
+  return pl.g.varlen ? (int64_t)pl.g.hq * pl.g.lse_head : (int64_t)pl.g.batch * pl.g.lse_seq;
+}
+
 size_t ws_size(const Plan& pl, int which, int splits) {
   size_t sz = ws_cu_blocks(pl);
   if (which == 0) {
@@ -185,8 +192,9 @@ size_t ws_size(const Plan& pl, int which, int splits) {
     sz += align_up((size_t)pl.g.rows * sizeof(int32_t));
   } else if (which == 2 && pl.g.mode == SA_DECODE) {
     sz += align_up(decode_partials_bytes(pl.g, splits));
-  } else if (which == 3) {   // backward: fp32 dK and dV accumulators in the K / V layout
-    sz += 2 * align_up((size_t)kv_elems(pl) * sizeof(float));
+  } else if (which == 3) {   // backward: D_i per query (lse layout); fp32: dK, dV accumulators
+    sz += align_up((size_t)lse_elems(pl) * sizeof(float));
+    if (pl.dtype == SA_F32) sz += 2 * align_up((size_t)kv_elems(pl) * sizeof(float));
   }
   return sz;
 }
@@ -237,9 +245,12 @@ int sparse_attn_bwd(const sa_problem* p, const sa_route_cfg* rc, const int32_t* 
   b.dq = dq;
   b.dk = dk;
   b.dv = dv;
-  b.dk_acc = reinterpret_cast<float*>(w);
-  b.dv_acc = reinterpret_cast<float*>(w + align_up((size_t)n * sizeof(float)));
-  return launch_bwd(pl.g, p->dtype, b, n, hs);
+  b.delta = reinterpret_cast<float*>(w);
+  w += align_up((size_t)lse_elems(pl) * sizeof(float));
+  b.dk_acc = p->dtype == SA_F32 ? reinterpret_cast<float*>(w) : nullptr;
+  b.dv_acc = p->dtype == SA_F32 ? reinterpret_cast<float*>(w + align_up((size_t)n * sizeof(float))) : nullptr;
+  const int kv_tail = !pl.g.varlen && p->kv_capacity > p->seqlen;   // keys no query can attend
+  return launch_bwd(pl.g, p->dtype, b, n, kv_tail, hs);
 }
 
 int sparse_attn_append_kv(const sa_problem* p, int32_t n_new, const void* k_new, const void* v_new,
