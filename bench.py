@@ -274,8 +274,45 @@ def measure_prefill(args, dbs, w, inp, flush):
     }
     if w.varlen or w.select == "threshold":
         rec["worklist"] = st.worklist_stats()
+    if not args.no_bwd:
+        log(f"timing the backward pass on {w.name}")
+        rec["backward"] = measure_bwd(args, dbs, st, visits)
     del st
     return rec
+
+
+def measure_bwd(args, dbs, st, visits):
+    """sparse_attn_bwd over the step's worklist, output and lse with a seeded
+    dO: each call bracketed by events (warm), median over the calls.  FLOPs
+    are the five products per selected tile visit (S, dP, dQ, dK, dV: 10 b^2 d);
+    the two kernels execute S and dP twice each (16 b^2 d)."""
+    import torch
+    w, inp = st.w, st.inp
+    g = torch.Generator(device=inp.q.device).manual_seed(7)
+    dout = torch.randn(inp.q.shape, generator=g, device=inp.q.device).to(inp.q.dtype)
+    dq, dk, dv = torch.empty_like(inp.q), torch.empty_like(inp.k), torch.empty_like(inp.v)
+    ws = torch.empty(max(dbs.workspace_size(st.prob, st.cfg, 3), 1), dtype=torch.uint8, device=inp.q.device)
+    call = lambda: dbs.bwd(st.prob, st.cfg, st.wl, inp.q, inp.k, inp.v, st.o, st.lse, dout, dq=dq, dk=dk,
+                           dv=dv, workspace=ws)
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(max(args.steps // 10, 5)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    med = spread(ts)["median"]
+    flops = visits * 10 * w.block * w.block * w.head_dim
+    tf = flops / (med * 1e-3) / 1e12
+    del dout, dq, dk, dv, ws
+    return {"median_ms": round(med, 4), "algorithmic_flops": flops, "tflops": round(tf, 2),
+            "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "kernels": "bwd_dq_bf16_kernel + bwd_dkdv_bf16_kernel",
+            "time": "median call, warm (events on the current stream)"}
 
 
 def measure_dense(args, dbs, w, inp, flush, sparse_fwd_ms):
@@ -427,6 +464,7 @@ def main():
                          "worklist, and torch flash-attention SDPA); off by default so that the "
                          "attention kernel's launches in a profile of the default run are the "
                          "sparse ones only")
+    ap.add_argument("--no-bwd", action="store_true", help="skip timing the backward pass")
     ap.add_argument("--cpu-heads", type=int, default=16)
     ap.add_argument("--decode-splits", type=int, default=0)
     ap.add_argument("--workload", choices=[w.name for w in wk.ALL if w.dtype == "bf16"],

@@ -14,8 +14,8 @@
 //     staged in LDS, S^T = K Q^T and dP^T = V dO^T give every lane one query
 //     row of P and dS, and dQ^T += K^T dS^T reads K^T with LDS transpose
 //     reads.  It also writes D_i, which the second kernel reads;
-//   * dK and dV, one workgroup per (key block, KV head), 2 wavefronts of 32
-//     keys: K and V of the block are staged once; the kernel walks every
+//   * dK and dV, one workgroup per (key block, KV head), 4 wavefronts (2 key
+//     halves x 2 query halves): K and V of the block are staged once; the kernel walks every
 //     worklist row of the sequence whose list holds the block (binary search
 //     of the sorted lists, 64 rows per step, one row per lane), stages the
 //     row's Q and dO, forms S = Q K^T and dP = dO V^T with one key per lane,
@@ -201,12 +201,12 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 }
 
 // Stage `rows` valid rows (the rest zero) of a [64][128] bf16 tile whose row
-// i starts at src + i * 128, by the workgroup's 128 threads.
-template <bool TR>
+// i starts at src + i * 128, by the workgroup's NT threads.
+template <bool TR, int NT>
 __device__ __forceinline__ void stage_tile(unsigned char* t, const __bf16* src, int rows, int tid) {
 #pragma unroll
-  for (int it = 0; it < 8; ++it) {
-    const int c = it * 128 + tid, row = c >> 4, ch = c & 15;
+  for (int it = 0; it < 1024 / NT; ++it) {
+    const int c = it * NT + tid, row = c >> 4, ch = c & 15;
     const u32x4 x = row < rows ? *reinterpret_cast<const u32x4*>(src + row * 128 + ch * 8) : u32x4{0, 0, 0, 0};
     *reinterpret_cast<u32x4*>(t + row * 256 + ((ch ^ (TR ? tsw(row) : rsw(row))) << 4)) = x;
   }
@@ -276,8 +276,8 @@ __global__ void __launch_bounds__(128) bwd_dq_bf16_kernel(Geom g, BwdBufs a) {
     const int cnt = min(kBlock, ri.len - j * kBlock);
     const int64_t kb = kv_block_offset(g, ri.s, kvh, ri.tok0, j);
     __syncthreads();   // the previous tile is no longer read
-    stage_tile<true>(kt, k + kb, cnt, tid);
-    stage_tile<false>(vt, v + kb, cnt, tid);
+    stage_tile<true, 128>(kt, k + kb, cnt, tid);
+    stage_tile<false, 128>(vt, v + kb, cnt, tid);
     __syncthreads();
     f32x16 sacc[2], dpacc[2];
 #pragma unroll
@@ -318,10 +318,17 @@ __device__ __forceinline__ int64_t row_id(const Geom& g, int s, int h, int r, in
   return (int64_t)g.hr * blk0 + (int64_t)h * nb + r;
 }
 
-__global__ void __launch_bounds__(128) bwd_dkdv_bf16_kernel(Geom g, BwdBufs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char kt[64 * 256], vt[64 * 256], qt[64 * 256], dot[64 * 256];
+// 4 wavefronts: wave w owns keys 32 (w & 1) .. + 32 and the 32 query rows
+// 32 (w >> 1) .. + 32 of every staged row, so each wave forms one 32 x 32
+// block of S and dP per (row, head) and accumulates dK^T, dV^T of its keys
+// over its query half; the two query halves are added through LDS at the end.
+__global__ void __launch_bounds__(256) bwd_dkdv_bf16_kernel(Geom g, BwdBufs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char kt[64 * 256], vt[64 * 256], qd[2][64 * 256];
   __shared__ float lse_s[64], del_s[64];
+  unsigned char* qt = qd[0];
+  unsigned char* dot = qd[1];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, half = lane >> 5;
+  const int kh = w & 1, qh = w >> 1;
   const int kvh = blockIdx.y;
   // key block slot -> (sequence, block)
   int s, j, len, tok0, blk0, nb;
@@ -347,10 +354,10 @@ __global__ void __launch_bounds__(128) bwd_dkdv_bf16_kernel(Geom g, BwdBufs a) {
   }
   const int cnt = min(kBlock, len - j * kBlock);
   const int64_t kb = kv_block_offset(g, s, kvh, tok0, j);
-  stage_tile<false>(kt, (const __bf16*)a.k + kb, cnt, tid);
-  stage_tile<false>(vt, (const __bf16*)a.v + kb, cnt, tid);
+  stage_tile<false, 256>(kt, (const __bf16*)a.k + kb, cnt, tid);
+  stage_tile<false, 256>(vt, (const __bf16*)a.v + kb, cnt, tid);
   const float c = 0.08838834764831845f, cl2 = c * kLog2e;
-  const int key = w * 32 + l32, kpos = j * kBlock + key;
+  const int key = kh * 32 + l32, kpos = j * kBlock + key;
 
   f32x16 dk[4], dv[4];
 #pragma unroll
@@ -384,8 +391,8 @@ __global__ void __launch_bounds__(128) bwd_dkdv_bf16_kernel(Geom g, BwdBufs a) {
           const int head = g.share ? kvh * g.group + gh : hr;
           const int64_t qo = q_offset(g, s, head, tok0, rr * kBlock);
           __syncthreads();   // the previous pair's tiles are no longer read
-          stage_tile<true>(qt, (const __bf16*)a.q + qo, qrows, tid);
-          stage_tile<true>(dot, (const __bf16*)a.dout + qo, qrows, tid);
+          stage_tile<true, 256>(qt, (const __bf16*)a.q + qo, qrows, tid);
+          stage_tile<true, 256>(dot, (const __bf16*)a.dout + qo, qrows, tid);
           if (tid < 64) {
             const bool ok = tid < qrows;
             const int64_t lo = ok ? lse_offset(g, s, head, tok0, rr * kBlock + tid) : 0;
@@ -393,49 +400,57 @@ __global__ void __launch_bounds__(128) bwd_dkdv_bf16_kernel(Geom g, BwdBufs a) {
             del_s[tid] = ok ? a.delta[lo] : 0.f;
           }
           __syncthreads();
-          // S = Q K^T and dP = dO V^T for this wave's 32 keys (one per lane)
-          f32x16 sacc[2], dpacc[2];
+          // S = Q K^T and dP = dO V^T: this wave's 32 query rows x 32 keys (one key per lane)
+          f32x16 sacc, dpacc;
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sacc[qb][i] = dpacc[qb][i] = 0.f;
+          for (int i = 0; i < 16; ++i) sacc[i] = dpacc[i] = 0.f;
 #pragma unroll
           for (int ks = 0; ks < 8; ++ks) {
-            const bf16x8 kv = row8<false>(kt, key, 2 * ks + half);
-            const bf16x8 vv = row8<false>(vt, key, 2 * ks + half);
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-              sacc[qb] = mfma(row8<true>(qt, qb * 32 + l32, 2 * ks + half), kv, sacc[qb]);
-              dpacc[qb] = mfma(row8<true>(dot, qb * 32 + l32, 2 * ks + half), vv, dpacc[qb]);
-            }
+            sacc = mfma(row8<true>(qt, qh * 32 + l32, 2 * ks + half), row8<false>(kt, key, 2 * ks + half), sacc);
+            dpacc = mfma(row8<true>(dot, qh * 32 + l32, 2 * ks + half), row8<false>(vt, key, 2 * ks + half),
+                         dpacc);
           }
-          bf16x8 pb[2][2], dsb[2][2];
+          bf16x8 pb[2], dsb[2];
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int q = qb * 32 + 8 * (i / 4) + 4 * half + (i % 4);
-              const bool ok = q < qrows && kpos <= rr * kBlock + q;
-              const float p = ok ? __builtin_amdgcn_exp2f(fmaf(sacc[qb][i], cl2, -lse_s[q])) : 0.f;
-              pb[qb][i / 8][i % 8] = (__bf16)p;
-              dsb[qb][i / 8][i % 8] = (__bf16)(p * (dpacc[qb][i] - del_s[q]));
-            }
+          for (int i = 0; i < 16; ++i) {
+            const int q = qh * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+            const bool ok = q < qrows && kpos <= rr * kBlock + q;
+            const float p = ok ? __builtin_amdgcn_exp2f(fmaf(sacc[i], cl2, -lse_s[q])) : 0.f;
+            pb[i / 8][i % 8] = (__bf16)p;
+            dsb[i / 8][i % 8] = (__bf16)(p * (dpacc[i] - del_s[q]));
+          }
 #pragma unroll
           for (int db = 0; db < 4; ++db)
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-              for (int ks = 0; ks < 2; ++ks) {
-                dv[db] = mfma(tr8(dot, qb, ks, db, lane), pb[qb][ks], dv[db]);
-                dk[db] = mfma(tr8(qt, qb, ks, db, lane), dsb[qb][ks], dk[db]);
-              }
+            for (int ks = 0; ks < 2; ++ks) {
+              dv[db] = mfma(tr8(dot, qh, ks, db, lane), pb[ks], dv[db]);
+              dk[db] = mfma(tr8(qt, qh, ks, db, lane), dsb[ks], dk[db]);
+            }
         }
       }
     }
   }
-  if (key < cnt) {
-    store_acc(dk, c, (__bf16*)a.dk + kb + (int64_t)key * 128, half);
-    store_acc(dv, 1.f, (__bf16*)a.dv + kb + (int64_t)key * 128, half);
+  // add the query halves: waves 2, 3 hand their sums to waves 0, 1 through
+  // LDS (element-major, so the lanes of a store hit consecutive banks)
+  float* red = reinterpret_cast<float*>(&qd[0][0]);   // [64 elements][2 key halves][64 lanes]
+  const bool out = key < cnt;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    f32x16 (&acc)[4] = pass == 0 ? dk : dv;
+    __syncthreads();
+    if (qh == 1)
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) red[((db * 16 + i) * 2 + kh) * 64 + lane] = acc[db][i];
+    __syncthreads();
+    if (qh == 0) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[db][i] += red[((db * 16 + i) * 2 + kh) * 64 + lane];
+      if (out) store_acc(acc, pass == 0 ? c : 1.f, (__bf16*)(pass == 0 ? a.dk : a.dv) + kb + (int64_t)key * 128, half);
+    }
   }
 }
 
@@ -456,7 +471,7 @@ int launch_bwd(const Geom& g, int dtype, const BwdBufs& b, int64_t kv_elems, int
     if (g.rows > 0) {
       bwd_dq_bf16_kernel<<<dim3((unsigned)g.rows, (unsigned)g.hpr), 128, 0, st>>>(g, b);
       const unsigned slots = g.varlen ? (unsigned)g.total_blocks : (unsigned)(g.batch * ((g.n + kBlock - 1) / kBlock));
-      bwd_dkdv_bf16_kernel<<<dim3(slots, (unsigned)g.hkv), 128, 0, st>>>(g, b);
+      bwd_dkdv_bf16_kernel<<<dim3(slots, (unsigned)g.hkv), 256, 0, st>>>(g, b);
     }
     return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
   }
