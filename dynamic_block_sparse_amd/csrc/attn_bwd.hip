@@ -10,8 +10,9 @@
 //
 // bf16 path (d = 128), two kernels on v_mfma_f32_32x32x16_bf16, no atomics:
 //   * dQ, one workgroup per (worklist row, query head), 2 wavefronts of 32
-//     query rows: Q and dO rows live in registers, each listed K/V tile is
-//     staged in LDS, S^T = K Q^T and dP^T = V dO^T give every lane one query
+//     query rows: the row's Q and dO are staged in LDS once, each listed K/V
+//     tile is loaded into registers while the previous one is multiplied and
+//     then staged in LDS, S^T = K Q^T and dP^T = V dO^T give every lane one query
 //     row of P and dS, and dQ^T += K^T dS^T reads K^T with LDS transpose
 //     reads.  It also writes D_i, which the second kernel reads;
 //   * dK and dV, one workgroup per (key block, KV head), 4 wavefronts (2 key
@@ -227,8 +228,31 @@ __device__ __forceinline__ void store_acc(const f32x16 (&acc)[4], float scale, _
     }
 }
 
+// The next tile's K and V rows are loaded into registers while the current
+// tile is multiplied, and written to LDS after the next barrier.
+struct TileRegs {
+  u32x4 k[8], v[8];
+};
+__device__ __forceinline__ void load_tile_regs(TileRegs& t, const __bf16* k, const __bf16* v, int rows, int tid) {
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int c = it * 128 + tid, row = c >> 4, ch = c & 15;
+    const u32x4 z = {0, 0, 0, 0};
+    t.k[it] = row < rows ? *reinterpret_cast<const u32x4*>(k + row * 128 + ch * 8) : z;
+    t.v[it] = row < rows ? *reinterpret_cast<const u32x4*>(v + row * 128 + ch * 8) : z;
+  }
+}
+__device__ __forceinline__ void store_tile_regs(const TileRegs& t, unsigned char* kt, unsigned char* vt, int tid) {
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int c = it * 128 + tid, row = c >> 4, ch = c & 15;
+    *reinterpret_cast<u32x4*>(kt + row * 256 + ((ch ^ tsw(row)) << 4)) = t.k[it];
+    *reinterpret_cast<u32x4*>(vt + row * 256 + ((ch ^ rsw(row)) << 4)) = t.v[it];
+  }
+}
+
 __global__ void __launch_bounds__(128) bwd_dq_bf16_kernel(Geom g, BwdBufs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char kt[64 * 256], vt[64 * 256];
+  __shared__ __attribute__((aligned(16))) unsigned char kt[64 * 256], vt[64 * 256], qs[64 * 256], dos[64 * 256];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, half = lane >> 5;
   const int64_t row = blockIdx.x;
   const RowInfo ri = decode_row(g, row);
@@ -236,28 +260,37 @@ __global__ void __launch_bounds__(128) bwd_dq_bf16_kernel(Geom g, BwdBufs a) {
   const int kvh = head / g.group;
   const int qpos = ri.r * kBlock + w * 32 + l32;
   const bool qvalid = qpos < ri.len;
+  const int qrows = min(kBlock, ri.len - ri.r * kBlock);
   const float c = 0.08838834764831845f, cl2 = c * kLog2e;   // 1 / sqrt(128)
   const __bf16* k = (const __bf16*)a.k;
   const __bf16* v = (const __bf16*)a.v;
+  const int t0 = a.row_ptr[row], t1 = a.row_ptr[row + 1];
 
-  // this lane's query row as B operands: d = 16 ks + 8 half .. + 8
-  bf16x8 qreg[8], doreg[8];
+  // the first tile's loads go out before anything else
+  TileRegs nxt;
+  if (t0 < t1) {
+    const int j = a.col_idx[t0];
+    const int64_t kb = kv_block_offset(g, ri.s, kvh, ri.tok0, j);
+    load_tile_regs(nxt, k + kb, v + kb, min(kBlock, ri.len - j * kBlock), tid);
+  }
+  // the row's Q and dO (B operands, read by rows); D_i = dO_i . O_i
+  const int64_t qo0 = q_offset(g, ri.s, head, ri.tok0, ri.r * kBlock);
+  stage_tile<false, 128>(qs, (const __bf16*)a.q + qo0, qrows, tid);
+  stage_tile<false, 128>(dos, (const __bf16*)a.dout + qo0, qrows, tid);
   float delta = 0.f, lse2 = 0.f;
   {
-    const int64_t qo = q_offset(g, ri.s, head, ri.tok0, qvalid ? qpos : ri.r * kBlock);
-    const __bf16* qp = (const __bf16*)a.q + qo + half * 8;
-    const __bf16* dp = (const __bf16*)a.dout + qo + half * 8;
-    const __bf16* op = (const __bf16*)a.o + qo + half * 8;
+    const int64_t qo = qo0 + (int64_t)(w * 32 + l32) * 128 + half * 8;
+    const __bf16* dp = (const __bf16*)a.dout + qo;
+    const __bf16* op = (const __bf16*)a.o + qo;
     float part = 0.f;
+    if (qvalid)
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const u32x4 z = {0, 0, 0, 0};
-      qreg[ks] = __builtin_bit_cast(bf16x8, qvalid ? *reinterpret_cast<const u32x4*>(qp + ks * 16) : z);
-      doreg[ks] = __builtin_bit_cast(bf16x8, qvalid ? *reinterpret_cast<const u32x4*>(dp + ks * 16) : z);
-      const bf16x8 ov = __builtin_bit_cast(bf16x8, qvalid ? *reinterpret_cast<const u32x4*>(op + ks * 16) : z);
+      for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8 dv8 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(dp + ks * 16));
+        const bf16x8 ov8 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(op + ks * 16));
 #pragma unroll
-      for (int e = 0; e < 8; ++e) part = fmaf((float)doreg[ks][e], (float)ov[e], part);
-    }
+        for (int e = 0; e < 8; ++e) part = fmaf((float)dv8[e], (float)ov8[e], part);
+      }
     delta = part + __shfl_xor(part, 32);
     if (qvalid) {
       const int64_t lo = lse_offset(g, ri.s, head, ri.tok0, qpos);
@@ -271,26 +304,32 @@ __global__ void __launch_bounds__(128) bwd_dq_bf16_kernel(Geom g, BwdBufs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) dq[db][i] = 0.f;
 
-  for (int t = a.row_ptr[row]; t < a.row_ptr[row + 1]; ++t) {
+  const int qrow = w * 32 + l32;
+  for (int t = t0; t < t1; ++t) {
     const int j = a.col_idx[t];
-    const int cnt = min(kBlock, ri.len - j * kBlock);
-    const int64_t kb = kv_block_offset(g, ri.s, kvh, ri.tok0, j);
     __syncthreads();   // the previous tile is no longer read
-    stage_tile<true, 128>(kt, k + kb, cnt, tid);
-    stage_tile<false, 128>(vt, v + kb, cnt, tid);
+    store_tile_regs(nxt, kt, vt, tid);
     __syncthreads();
+    if (t + 1 < t1) {   // next tile in flight during this one's products
+      const int jn = a.col_idx[t + 1];
+      const int64_t kbn = kv_block_offset(g, ri.s, kvh, ri.tok0, jn);
+      load_tile_regs(nxt, k + kbn, v + kbn, min(kBlock, ri.len - jn * kBlock), tid);
+    }
     f32x16 sacc[2], dpacc[2];
 #pragma unroll
     for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[b2][i] = dpacc[b2][i] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8 qb = row8<false>(qs, qrow, 2 * ks + half);
+      const bf16x8 db8 = row8<false>(dos, qrow, 2 * ks + half);
 #pragma unroll
       for (int b2 = 0; b2 < 2; ++b2) {
-        sacc[b2] = mfma(row8<true>(kt, b2 * 32 + l32, 2 * ks + half), qreg[ks], sacc[b2]);
-        dpacc[b2] = mfma(row8<false>(vt, b2 * 32 + l32, 2 * ks + half), doreg[ks], dpacc[b2]);
+        sacc[b2] = mfma(row8<true>(kt, b2 * 32 + l32, 2 * ks + half), qb, sacc[b2]);
+        dpacc[b2] = mfma(row8<false>(vt, b2 * 32 + l32, 2 * ks + half), db8, dpacc[b2]);
       }
+    }
     // dS^T of this lane's query over the tile's keys, as B operands
     bf16x8 dsb[2][2];
 #pragma unroll
