@@ -8,7 +8,7 @@
 //   dS_ip = P_ip (dO_i . v_p - D_i),
 //   dQ_i = c sum_p dS_ip k_p,  dK_p = c sum_i dS_ip q_i,  dV_p = sum_i P_ip dO_i.
 //
-// bf16 path (d = 128), two kernels on v_mfma_f32_32x32x16_bf16, no atomics:
+// bf16 path (d = 128), two kernels on v_mfma_f32_32x32x16_bf16:
 //   * dQ, one workgroup per (worklist row, query head), 2 wavefronts of 32
 //     query rows: the row's Q and dO are staged in LDS once, each listed K/V
 //     tile is loaded into registers while the previous one is multiplied and
@@ -21,7 +21,11 @@
 //     of the sorted lists, 64 rows per step, one row per lane), stages the
 //     row's Q and dO, forms S = Q K^T and dP = dO V^T with one key per lane,
 //     and accumulates dV^T += dO^T P and dK^T += Q^T dS in registers over all
-//     of them, so each key is written once.
+//     of them, so each key is written once.  A key block listed by more
+//     (row, head) pairs than a target (a counting pass finds out) is shared
+//     by up to 8 workgroups, each taking an equal run of its pairs: they add
+//     their sums into fp32 accumulators with atomics and the last one to
+//     finish converts them (only such blocks' sums have no fixed order).
 //   P and dS enter the second products as bf16 operands (as P does in the
 //   forward); everything else is fp32.
 // fp32 path (d = 64): a plain SIMT kernel, one lane per query row, with dK
@@ -357,6 +361,63 @@ __device__ __forceinline__ int64_t row_id(const Geom& g, int s, int h, int r, in
   return (int64_t)g.hr * blk0 + (int64_t)h * nb + r;
 }
 
+// Key block slot x (of one KV head) -> sequence, block and the sequence's
+// length, first token, first block slot and block count.
+struct KeySlot {
+  int s, j, len, tok0, blk0, nb;
+};
+__device__ __forceinline__ KeySlot key_slot(const Geom& g, int x) {
+  KeySlot k;
+  if (!g.varlen) {
+    k.nb = ceil_div(g.n, kBlock);
+    k.s = x / k.nb;
+    k.j = x % k.nb;
+    k.len = g.n;
+    k.tok0 = 0;
+    k.blk0 = 0;
+  } else {
+    int lo = 0, hi = g.batch - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (g.cu_blocks[mid] <= x) lo = mid; else hi = mid - 1;
+    }
+    k.s = lo;
+    k.blk0 = g.cu_blocks[lo];
+    k.nb = g.cu_blocks[lo + 1] - k.blk0;
+    k.j = x - k.blk0;
+    k.tok0 = g.cu_seqlens[lo];
+    k.len = g.cu_seqlens[lo + 1] - k.tok0;
+  }
+  return k;
+}
+
+// (row, head) pairs per key block: one wavefront per worklist row, whose
+// lanes add the query heads the row serves to the blocks it lists.
+__global__ void __launch_bounds__(256) bwd_count_kernel(Geom g, BwdBufs a) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= g.rows) return;
+  const RowInfo ri = decode_row(g, row);
+  const int kvh = g.share ? ri.h : ri.h / g.group;
+  const int64_t slot0 = g.varlen ? (int64_t)ri.blk0 : (int64_t)ri.s * ri.nblk;
+  const int t1 = a.row_ptr[row + 1];
+  for (int t = a.row_ptr[row] + (int)(threadIdx.x & 63); t < t1; t += 64)
+    atomicAdd(a.kcount + (slot0 + a.col_idx[t]) * g.hkv + kvh, g.hpr);
+}
+
+// Workgroups that share a key block add into the fp32 accumulators: clear
+// those blocks' rows.
+__global__ void __launch_bounds__(256) bwd_split_clear_kernel(Geom g, BwdBufs a) {
+  const int kvh = blockIdx.y;
+  if (a.kcount[(int64_t)blockIdx.x * g.hkv + kvh] <= a.split_target) return;
+  const KeySlot ks = key_slot(g, (int)blockIdx.x);
+  const int cnt = min(kBlock, ks.len - ks.j * kBlock);
+  const int64_t kb = kv_block_offset(g, ks.s, kvh, ks.tok0, ks.j);
+  for (int e = threadIdx.x; e < cnt * 128; e += 256) {
+    a.dk_acc[kb + e] = 0.f;
+    a.dv_acc[kb + e] = 0.f;
+  }
+}
+
 // 4 wavefronts: wave w owns keys 32 (w & 1) .. + 32 and the 32 query rows
 // 32 (w >> 1) .. + 32 of every staged row, so each wave forms one 32 x 32
 // block of S and dP per (row, head) and accumulates dK^T, dV^T of its keys
@@ -369,28 +430,16 @@ __global__ void __launch_bounds__(256) bwd_dkdv_bf16_kernel(Geom g, BwdBufs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, half = lane >> 5;
   const int kh = w & 1, qh = w >> 1;
   const int kvh = blockIdx.y;
-  // key block slot -> (sequence, block)
-  int s, j, len, tok0, blk0, nb;
-  if (!g.varlen) {
-    nb = ceil_div(g.n, kBlock);
-    s = (int)(blockIdx.x / (unsigned)nb);
-    j = (int)(blockIdx.x % (unsigned)nb);
-    len = g.n;
-    tok0 = 0;
-    blk0 = 0;
-  } else {
-    int lo = 0, hi = g.batch - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (g.cu_blocks[mid] <= (int)blockIdx.x) lo = mid; else hi = mid - 1;
-    }
-    s = lo;
-    blk0 = g.cu_blocks[s];
-    nb = g.cu_blocks[s + 1] - blk0;
-    j = (int)blockIdx.x - blk0;
-    tok0 = g.cu_seqlens[s];
-    len = g.cu_seqlens[s + 1] - tok0;
-  }
+  // a key block listed by more than split_target (row, head) pairs is shared
+  // by nch workgroups, each taking an equal run of its pairs in visiting order
+  const int64_t kidx = (int64_t)blockIdx.x * g.hkv + kvh;
+  const int units = a.kcount[kidx];
+  const int nch = units > a.split_target ? min(a.max_chunks, (units + a.split_target - 1) / a.split_target) : 1;
+  if ((int)blockIdx.z >= nch) return;
+  const int ord_lo = (int)((int64_t)units * blockIdx.z / nch);
+  const int ord_hi = (int)((int64_t)units * (blockIdx.z + 1) / nch);
+  const KeySlot ksl = key_slot(g, (int)blockIdx.x);
+  const int s = ksl.s, j = ksl.j, len = ksl.len, tok0 = ksl.tok0, blk0 = ksl.blk0, nb = ksl.nb;
   const int cnt = min(kBlock, len - j * kBlock);
   const int64_t kb = kv_block_offset(g, s, kvh, tok0, j);
   stage_tile<false, 256>(kt, (const __bf16*)a.k + kb, cnt, tid);
@@ -405,10 +454,12 @@ __global__ void __launch_bounds__(256) bwd_dkdv_bf16_kernel(Geom g, BwdBufs a) {
     for (int i = 0; i < 16; ++i) dk[db][i] = dv[db][i] = 0.f;
 
   const int nrh = g.share ? 1 : g.group;   // routing heads whose rows may list this block
+  const int ngh = g.share ? g.group : 1;   // query heads per row
   const int rfirst = max(j, g.qblk0);      // causal: only query blocks r >= j list block j
-  for (int hh = 0; hh < nrh; ++hh) {
+  int ord = 0;                             // visiting-order index of the next pair
+  for (int hh = 0; hh < nrh && ord < ord_hi; ++hh) {
     const int hr = g.share ? kvh : kvh * g.group + hh;
-    for (int r0 = rfirst; r0 < nb; r0 += 64) {
+    for (int r0 = rfirst; r0 < nb && ord < ord_hi; r0 += 64) {
       // one candidate row per lane: does its (sorted) list hold block j?
       const int r = r0 + lane;
       bool has = false;
@@ -422,11 +473,17 @@ __global__ void __launch_bounds__(256) bwd_dkdv_bf16_kernel(Geom g, BwdBufs a) {
         }
       }
       uint64_t m = __ballot(has);
+      const int in_m = __popcll(m) * ngh;
+      if (ord + in_m <= ord_lo) {   // all before this workgroup's run
+        ord += in_m;
+        continue;
+      }
       while (m) {
         const int rr = r0 + __builtin_ctzll(m);
         m &= m - 1;
         const int qrows = min(kBlock, len - rr * kBlock);
-        for (int gh = 0; gh < (g.share ? g.group : 1); ++gh) {
+        for (int gh = 0; gh < ngh; ++gh, ++ord) {
+          if (ord < ord_lo || ord >= ord_hi) continue;
           const int head = g.share ? kvh * g.group + gh : hr;
           const int64_t qo = q_offset(g, s, head, tok0, rr * kBlock);
           __syncthreads();   // the previous pair's tiles are no longer read
@@ -488,8 +545,31 @@ __global__ void __launch_bounds__(256) bwd_dkdv_bf16_kernel(Geom g, BwdBufs a) {
       for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[db][i] += red[((db * 16 + i) * 2 + kh) * 64 + lane];
-      if (out) store_acc(acc, pass == 0 ? c : 1.f, (__bf16*)(pass == 0 ? a.dk : a.dv) + kb + (int64_t)key * 128, half);
+      if (nch == 1) {
+        if (out) store_acc(acc, pass == 0 ? c : 1.f, (__bf16*)(pass == 0 ? a.dk : a.dv) + kb + (int64_t)key * 128, half);
+      } else if (out) {   // shared block: add this run's sums into the fp32 accumulators
+        float* dst = (pass == 0 ? a.dk_acc : a.dv_acc) + kb + (int64_t)key * 128;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) atomicAdd(dst + db * 32 + 8 * (i / 4) + 4 * half + (i % 4), acc[db][i]);
+      }
     }
+  }
+  if (nch == 1) return;
+  // the last of the block's workgroups converts the accumulated sums
+  __shared__ int last;
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) last = atomicAdd(a.kdone + kidx, 1) == nch - 1;
+  __syncthreads();
+  if (!last) return;
+  __threadfence();
+  for (int e = tid; e < cnt * 128; e += 256) {
+    const float vk = __hip_atomic_load(a.dk_acc + kb + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float vv = __hip_atomic_load(a.dv_acc + kb + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    ((__bf16*)a.dk)[kb + e] = (__bf16)(vk * c);
+    ((__bf16*)a.dv)[kb + e] = (__bf16)vv;
   }
 }
 
@@ -508,9 +588,14 @@ int launch_bwd(const Geom& g, int dtype, const BwdBufs& b, int64_t kv_elems, int
       bwd_zero_kernel<<<zg, 256, 0, st>>>((uint32_t*)b.dv, words);
     }
     if (g.rows > 0) {
-      bwd_dq_bf16_kernel<<<dim3((unsigned)g.rows, (unsigned)g.hpr), 128, 0, st>>>(g, b);
       const unsigned slots = g.varlen ? (unsigned)g.total_blocks : (unsigned)(g.batch * ((g.n + kBlock - 1) / kBlock));
-      bwd_dkdv_bf16_kernel<<<dim3(slots, (unsigned)g.hkv), 256, 0, st>>>(g, b);
+      const int64_t counters = 2 * (int64_t)slots * g.hkv;   // kcount and kdone, adjacent
+      bwd_zero_kernel<<<(unsigned)std::min<int64_t>((counters + 255) / 256, 65536), 256, 0, st>>>(
+          (uint32_t*)b.kcount, counters);
+      bwd_count_kernel<<<(unsigned)((g.rows + 3) / 4), 256, 0, st>>>(g, b);
+      bwd_split_clear_kernel<<<dim3(slots, (unsigned)g.hkv), 256, 0, st>>>(g, b);
+      bwd_dq_bf16_kernel<<<dim3((unsigned)g.rows, (unsigned)g.hpr), 128, 0, st>>>(g, b);
+      bwd_dkdv_bf16_kernel<<<dim3(slots, (unsigned)g.hkv, (unsigned)b.max_chunks), 256, 0, st>>>(g, b);
     }
     return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
   }

@@ -53,6 +53,11 @@ struct BwdBufs {
   const float* lse;
   void *dq, *dk, *dv;
   float *delta, *dk_acc, *dv_acc;
+  // bf16: (row, head) pairs listing each key block and finished workgroups per
+  // key block, [key block slot][KV head]; key blocks with more pairs than
+  // split_target are shared by several workgroups that add into dk_acc / dv_acc
+  int *kcount, *kdone;
+  int split_target, max_chunks;
 };
 int launch_bwd(const Geom& g, int dtype, const BwdBufs& b, int64_t kv_elems, int kv_tail, hipStream_t st);
 

@@ -3,6 +3,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -177,6 +179,11 @@ int64_t kv_elems(const Plan& pl) {
   return pl.g.varlen ? (int64_t)pl.g.hkv * pl.g.kv_head : (int64_t)pl.g.batch * pl.g.kv_seq;
 }
 
+// Key block slots of one KV head (every sequence's blocks).
+int64_t key_slots(const Plan& pl) {
+  return pl.g.varlen ? (int64_t)pl.g.total_blocks : (int64_t)pl.g.batch * ((pl.g.n + kBlock - 1) / kBlock);
+}
+
 // Elements of the lse array (one per query token and head).
 int64_t lse_elems(const Plan& pl) {
   return pl.g.varlen ? (int64_t)pl.g.hq * pl.g.lse_head : (int64_t)pl.g.batch * pl.g.lse_seq;
@@ -192,9 +199,11 @@ size_t ws_size(const Plan& pl, int which, int splits) {
     sz += align_up((size_t)pl.g.rows * sizeof(int32_t));
   } else if (which == 2 && pl.g.mode == SA_DECODE) {
     sz += align_up(decode_partials_bytes(pl.g, splits));
-  } else if (which == 3) {   // backward: D_i per query (lse layout); fp32: dK, dV accumulators
+  } else if (which == 3) {   // backward: D_i per query (lse layout), dK and dV fp32 accumulators,
+                             // per key block pair counts and finished-workgroup counts
     sz += align_up((size_t)lse_elems(pl) * sizeof(float));
-    if (pl.dtype == SA_F32) sz += 2 * align_up((size_t)kv_elems(pl) * sizeof(float));
+    sz += 2 * align_up((size_t)kv_elems(pl) * sizeof(float));
+    sz += align_up((size_t)2 * key_slots(pl) * pl.g.hkv * sizeof(int));
   }
   return sz;
 }
@@ -247,8 +256,17 @@ int sparse_attn_bwd(const sa_problem* p, const sa_route_cfg* rc, const int32_t* 
   b.dv = dv;
   b.delta = reinterpret_cast<float*>(w);
   w += align_up((size_t)lse_elems(pl) * sizeof(float));
-  b.dk_acc = p->dtype == SA_F32 ? reinterpret_cast<float*>(w) : nullptr;
-  b.dv_acc = p->dtype == SA_F32 ? reinterpret_cast<float*>(w + align_up((size_t)n * sizeof(float))) : nullptr;
+  b.dk_acc = reinterpret_cast<float*>(w);
+  w += align_up((size_t)n * sizeof(float));
+  b.dv_acc = reinterpret_cast<float*>(w);
+  w += align_up((size_t)n * sizeof(float));
+  b.kcount = reinterpret_cast<int*>(w);
+  b.kdone = b.kcount + key_slots(pl) * pl.g.hkv;
+  // a workgroup takes at most split_target (row, head) pairs of a key block:
+  // an eighth of the most a block can have, at least 32, so at most 8 share one
+  const int max_units = pl.g.max_blocks * pl.g.group;
+  b.split_target = std::max(32, max_units / 8);
+  b.max_chunks = (max_units + b.split_target - 1) / b.split_target;
   const int kv_tail = !pl.g.varlen && p->kv_capacity > p->seqlen;   // keys no query can attend
   return launch_bwd(pl.g, p->dtype, b, n, kv_tail, hs);
 }

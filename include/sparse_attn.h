@@ -245,9 +245,11 @@ int sparse_attn_fwd(const sa_problem* p, const sa_route_cfg* rc, const int32_t* 
  *   D_i = dO_i . O_i and dS_ip = P_ip (dO_i . v_p - D_i):
  *   dQ_i = sum_p dS_ip k_p / sqrt(d), dK_p = sum_i dS_ip q_i / sqrt(d),
  *   dV_p = sum_i P_ip dO_i.  bf16: fp32 accumulation on the matrix cores with P
- *   and dS rounded to bf16 as operands, each output written once (repeatable
- *   bit for bit).  fp32: fp32 arithmetic, dK and dV accumulated in fp32
- *   workspace with atomics, so their summation order is not fixed.
+ *   and dS rounded to bf16 as operands; dQ is repeatable bit for bit, and so
+ *   are dK, dV except for key blocks listed by many (row, head) pairs, whose
+ *   work is shared by several workgroups that add in atomic order.  fp32:
+ *   fp32 arithmetic, dK and dV accumulated in fp32 workspace with atomics, so
+ *   their summation order is not fixed.
  *   Prefill only (fixed, packed varlen or chunked); bf16 with head_dim 128 or
  *   fp32 with head_dim 64.
  *   ws                (device) sparse_attn_workspace_size(p, rc, 3, 0) bytes. */

@@ -143,9 +143,14 @@ def test_bwd_matches_oracle(case):
         print(f"bwd {name} {label}: scale {scale:.3e} max-abs {err.max():.3e} mean-abs {err.mean():.3e}",
               flush=True)
         assert worst <= 0, (name, label, np.unravel_index(np.argmax(err - bound), err.shape))
-    if dtype == "bf16":   # no atomics: a second call repeats every bit
+    if dtype == "bf16":
+        # dQ has no atomics: a second call repeats every bit.  dK, dV of a key
+        # block shared by several workgroups are summed in atomic order, so
+        # they may differ in the last bf16 bit.
         dq2, dk2, dv2 = dbs.bwd(prob, cfg, wl, qd, kd, vd, o, lse, dod)
-        assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+        assert torch.equal(dq, dq2)
+        for a, b in ((dk, dk2), (dv, dv2)):
+            assert torch.allclose(a.float(), b.float(), rtol=2 ** -7, atol=1e-6)
     # keys past the sequence end (capacity tail) get exactly zero
     if cap:
         assert not dk[:, :, n:].any() and not dv[:, :, n:].any()
