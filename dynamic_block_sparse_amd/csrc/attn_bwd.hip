@@ -176,8 +176,13 @@ __global__ void __launch_bounds__(64) attn_bwd_simt_kernel(Geom g, BwdBufs a) {
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 
+// rsw: 16 consecutive rows read at one chunk land on 16 distinct chunk slots.
+// tsw keeps that (it is a bijection of row & 15) and also gives the four
+// consecutive rows of a transpose read, each touching an aligned chunk pair,
+// distinct pair slots whose partners (chunk + 2, read by the neighbouring
+// 16 lanes) are distinct too: (row & 3) selects the pair slot's high bits.
 __device__ __forceinline__ int rsw(int row) { return row & 15; }
-__device__ __forceinline__ int tsw(int row) { return ((row & 3) << 2) + (row & 2); }
+__device__ __forceinline__ int tsw(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 
 // 8 bf16 of tile row `row`, columns 8 c .. 8 c + 7
 template <bool TR>
