@@ -206,6 +206,8 @@ __device__ __forceinline__ bf16x8 tr8(const unsigned char* t, int rb, int ks, in
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+constexpr int kMfma = 0x008, kDsRead = 0x100;   // scheduling-group masks
+
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -329,15 +331,28 @@ __global__ void __launch_bounds__(128) bwd_dq_bf16_kernel(Geom g, BwdBufs a) {
     for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[b2][i] = dpacc[b2][i] = 0.f;
+    // the six LDS operands of step ks + 1 are read while step ks multiplies
+    bf16x8 op[2][6];
+    auto rd = [&](int ks, bf16x8 (&o)[6]) {
+      o[0] = row8<true>(kt, l32, 2 * ks + half);
+      o[1] = row8<true>(kt, 32 + l32, 2 * ks + half);
+      o[2] = row8<false>(vt, l32, 2 * ks + half);
+      o[3] = row8<false>(vt, 32 + l32, 2 * ks + half);
+      o[4] = row8<false>(qs, qrow, 2 * ks + half);
+      o[5] = row8<false>(dos, qrow, 2 * ks + half);
+    };
+    rd(0, op[0]);
+    __builtin_amdgcn_sched_group_barrier(kDsRead, 6, 0);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const bf16x8 qb = row8<false>(qs, qrow, 2 * ks + half);
-      const bf16x8 db8 = row8<false>(dos, qrow, 2 * ks + half);
-#pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2) {
-        sacc[b2] = mfma(row8<true>(kt, b2 * 32 + l32, 2 * ks + half), qb, sacc[b2]);
-        dpacc[b2] = mfma(row8<false>(vt, b2 * 32 + l32, 2 * ks + half), db8, dpacc[b2]);
-      }
+      if (ks + 1 < 8) rd(ks + 1, op[(ks + 1) & 1]);
+      const bf16x8(&o)[6] = op[ks & 1];
+      sacc[0] = mfma(o[0], o[4], sacc[0]);
+      sacc[1] = mfma(o[1], o[4], sacc[1]);
+      dpacc[0] = mfma(o[2], o[5], dpacc[0]);
+      dpacc[1] = mfma(o[3], o[5], dpacc[1]);
+      if (ks + 1 < 8) __builtin_amdgcn_sched_group_barrier(kDsRead, 6, 0);
+      __builtin_amdgcn_sched_group_barrier(kMfma, 4, 0);
     }
     // dS^T of this lane's query over the tile's keys, as B operands
     bf16x8 dsb[2][2];
@@ -350,12 +365,20 @@ __global__ void __launch_bounds__(128) bwd_dq_bf16_kernel(Geom g, BwdBufs a) {
         const float p = ok ? __builtin_amdgcn_exp2f(fmaf(sacc[b2][i], cl2, -lse2)) : 0.f;
         dsb[b2][i / 8][i % 8] = (__bf16)(p * (dpacc[b2][i] - delta));
       }
+    // dQ^T += K^T dS^T: the transpose reads run four MFMAs ahead
+    bf16x8 ta[4];
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int i = 0; i < 4; ++i) ta[i] = tr8(kt, (i >> 1) & 1, i & 1, i >> 2, lane);
+    __builtin_amdgcn_sched_group_barrier(kDsRead, 8, 0);
 #pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) dq[db] = mfma(tr8(kt, b2, ks, db, lane), dsb[b2][ks], dq[db]);
+    for (int i = 0; i < 16; ++i) {
+      const int db = i >> 2, b2 = (i >> 1) & 1, ks = i & 1;
+      const bf16x8 av = ta[i & 3];
+      if (i + 4 < 16) ta[i & 3] = tr8(kt, ((i + 4) >> 1) & 1, (i + 4) & 1, (i + 4) >> 2, lane);
+      dq[db] = mfma(av, dsb[b2][ks], dq[db]);
+      __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+      if (i + 4 < 16) __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+    }
   }
   if (qvalid) store_acc(dq, c, (__bf16*)a.dq + q_offset(g, ri.s, head, ri.tok0, qpos), half);
 }
