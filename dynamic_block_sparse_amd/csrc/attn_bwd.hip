@@ -446,17 +446,21 @@ __global__ void __launch_bounds__(256) bwd_split_clear_kernel(Geom g, BwdBufs a)
   }
 }
 
-// 4 wavefronts: wave w owns keys 32 (w & 1) .. + 32 and the 32 query rows
-// 32 (w >> 1) .. + 32 of every staged row, so each wave forms one 32 x 32
-// block of S and dP per (row, head) and accumulates dK^T, dV^T of its keys
-// over its query half; the two query halves are added through LDS at the end.
-__global__ void __launch_bounds__(256) bwd_dkdv_bf16_kernel(Geom g, BwdBufs a) {
+// NW = 4 or 8 wavefronts: wave w owns keys 32 (w & 1) .. + 32, the 32 query
+// rows 32 ((w >> 1) & 1) .. + 32 of every staged row and (NW = 8) one half of
+// the d columns of the accumulators, so each wave forms one 32 x 32 block of S
+// and dP per (row, head) (the two d halves form the same block) and
+// accumulates dK^T, dV^T of its keys and columns over its query half; the two
+// query halves are added through LDS at the end.
+template <int NW>
+__global__ void __launch_bounds__(64 * NW) bwd_dkdv_bf16_kernel(Geom g, BwdBufs a) {
+  constexpr int NT = 64 * NW, NDB = 16 / NW;   // threads; 32-column d blocks per wave
   __shared__ __attribute__((aligned(16))) unsigned char kt[64 * 256], vt[64 * 256], qd[2][64 * 256];
   __shared__ float lse_s[64], del_s[64];
   unsigned char* qt = qd[0];
   unsigned char* dot = qd[1];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, half = lane >> 5;
-  const int kh = w & 1, qh = w >> 1;
+  const int kh = w & 1, qh = (w >> 1) & 1, dh = w >> 2;
   const int kvh = blockIdx.y;
   // a key block listed by more than split_target (row, head) pairs is shared
   // by nch workgroups, each taking an equal run of its pairs in visiting order
@@ -470,14 +474,14 @@ __global__ void __launch_bounds__(256) bwd_dkdv_bf16_kernel(Geom g, BwdBufs a) {
   const int s = ksl.s, j = ksl.j, len = ksl.len, tok0 = ksl.tok0, blk0 = ksl.blk0, nb = ksl.nb;
   const int cnt = min(kBlock, len - j * kBlock);
   const int64_t kb = kv_block_offset(g, s, kvh, tok0, j);
-  stage_tile<false, 256>(kt, (const __bf16*)a.k + kb, cnt, tid);
-  stage_tile<false, 256>(vt, (const __bf16*)a.v + kb, cnt, tid);
+  stage_tile<false, NT>(kt, (const __bf16*)a.k + kb, cnt, tid);
+  stage_tile<false, NT>(vt, (const __bf16*)a.v + kb, cnt, tid);
   const float c = 0.08838834764831845f, cl2 = c * kLog2e;
   const int key = kh * 32 + l32, kpos = j * kBlock + key;
 
-  f32x16 dk[4], dv[4];
+  f32x16 dk[NDB], dv[NDB];
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) dk[db][i] = dv[db][i] = 0.f;
 
@@ -515,8 +519,8 @@ __global__ void __launch_bounds__(256) bwd_dkdv_bf16_kernel(Geom g, BwdBufs a) {
           const int head = g.share ? kvh * g.group + gh : hr;
           const int64_t qo = q_offset(g, s, head, tok0, rr * kBlock);
           __syncthreads();   // the previous pair's tiles are no longer read
-          stage_tile<true, 256>(qt, (const __bf16*)a.q + qo, qrows, tid);
-          stage_tile<true, 256>(dot, (const __bf16*)a.dout + qo, qrows, tid);
+          stage_tile<true, NT>(qt, (const __bf16*)a.q + qo, qrows, tid);
+          stage_tile<true, NT>(dot, (const __bf16*)a.dout + qo, qrows, tid);
           if (tid < 64) {
             const bool ok = tid < qrows;
             const int64_t lo = ok ? lse_offset(g, s, head, tok0, rr * kBlock + tid) : 0;
@@ -544,11 +548,11 @@ __global__ void __launch_bounds__(256) bwd_dkdv_bf16_kernel(Geom g, BwdBufs a) {
             dsb[i / 8][i % 8] = (__bf16)(p * (dpacc[i] - del_s[q]));
           }
 #pragma unroll
-          for (int db = 0; db < 4; ++db)
+          for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-              dv[db] = mfma(tr8(dot, qh, ks, db, lane), pb[ks], dv[db]);
-              dk[db] = mfma(tr8(qt, qh, ks, db, lane), dsb[ks], dk[db]);
+              dv[db] = mfma(tr8(dot, qh, ks, dh * NDB + db, lane), pb[ks], dv[db]);
+              dk[db] = mfma(tr8(qt, qh, ks, dh * NDB + db, lane), dsb[ks], dk[db]);
             }
         }
       }
@@ -556,31 +560,45 @@ __global__ void __launch_bounds__(256) bwd_dkdv_bf16_kernel(Geom g, BwdBufs a) {
   }
   // add the query halves: waves 2, 3 hand their sums to waves 0, 1 through
   // LDS (element-major, so the lanes of a store hit consecutive banks)
-  float* red = reinterpret_cast<float*>(&qd[0][0]);   // [64 elements][2 key halves][64 lanes]
+  // [16 NDB elements][2 key halves][NW / 4 d halves][64 lanes] = 32 KB
+  float* red = reinterpret_cast<float*>(&qd[0][0]);
+  auto ri = [&](int e) { return ((e * 2 + kh) * (NW / 4) + dh) * 64 + lane; };
   const bool out = key < cnt;
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
-    f32x16 (&acc)[4] = pass == 0 ? dk : dv;
+    f32x16 (&acc)[NDB] = pass == 0 ? dk : dv;
     __syncthreads();
     if (qh == 1)
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) red[((db * 16 + i) * 2 + kh) * 64 + lane] = acc[db][i];
+        for (int i = 0; i < 16; ++i) red[ri(db * 16 + i)] = acc[db][i];
     __syncthreads();
-    if (qh == 0) {
+    if (qh == 0 && out) {
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[db][i] += red[((db * 16 + i) * 2 + kh) * 64 + lane];
+        for (int i = 0; i < 16; ++i) acc[db][i] += red[ri(db * 16 + i)];
+      const int64_t row0 = kb + (int64_t)key * 128;
       if (nch == 1) {
-        if (out) store_acc(acc, pass == 0 ? c : 1.f, (__bf16*)(pass == 0 ? a.dk : a.dv) + kb + (int64_t)key * 128, half);
-      } else if (out) {   // shared block: add this run's sums into the fp32 accumulators
-        float* dst = (pass == 0 ? a.dk_acc : a.dv_acc) + kb + (int64_t)key * 128;
+        __bf16* dst = (__bf16*)(pass == 0 ? a.dk : a.dv) + row0;
+        const float sc = pass == 0 ? c : 1.f;
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) atomicAdd(dst + db * 32 + 8 * (i / 4) + 4 * half + (i % 4), acc[db][i]);
+          for (int gq = 0; gq < 4; ++gq) {
+            bf16x4 v4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(acc[db][4 * gq + e] * sc);
+            *reinterpret_cast<bf16x4*>(dst + (dh * NDB + db) * 32 + 8 * gq + 4 * half) = v4;
+          }
+      } else {   // shared block: add this run's sums into the fp32 accumulators
+        float* dst = (pass == 0 ? a.dk_acc : a.dv_acc) + row0;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            atomicAdd(dst + (dh * NDB + db) * 32 + 8 * (i / 4) + 4 * half + (i % 4), acc[db][i]);
       }
     }
   }
@@ -593,7 +611,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_bf16_kernel(Geom g, BwdBufs a) {
   __syncthreads();
   if (!last) return;
   __threadfence();
-  for (int e = tid; e < cnt * 128; e += 256) {
+  for (int e = tid; e < cnt * 128; e += NT) {
     const float vk = __hip_atomic_load(a.dk_acc + kb + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const float vv = __hip_atomic_load(a.dv_acc + kb + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     ((__bf16*)a.dk)[kb + e] = (__bf16)(vk * c);
@@ -623,7 +641,7 @@ int launch_bwd(const Geom& g, int dtype, const BwdBufs& b, int64_t kv_elems, int
       bwd_count_kernel<<<(unsigned)((g.rows + 3) / 4), 256, 0, st>>>(g, b);
       bwd_split_clear_kernel<<<dim3(slots, (unsigned)g.hkv), 256, 0, st>>>(g, b);
       bwd_dq_bf16_kernel<<<dim3((unsigned)g.rows, (unsigned)g.hpr), 128, 0, st>>>(g, b);
-      bwd_dkdv_bf16_kernel<<<dim3(slots, (unsigned)g.hkv, (unsigned)b.max_chunks), 256, 0, st>>>(g, b);
+      bwd_dkdv_bf16_kernel<4><<<dim3(slots, (unsigned)g.hkv, (unsigned)b.max_chunks), 256, 0, st>>>(g, b);
     }
     return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
   }
