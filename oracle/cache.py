@@ -33,16 +33,21 @@ import numpy as np
 from .routing import block_summaries, num_blocks
 
 
-def append_update(c_old: np.ndarray, r_old: int, new_keys: np.ndarray) -> np.ndarray:
+def append_update(c_old: np.ndarray, r_old: int, new_keys: np.ndarray, kpool: str = "mean") -> np.ndarray:
     """Summary of a block after `new_keys` join its r_old valid keys.
 
     [P2] §3.1 Eq 11 over a chunk: s = r_old * c_old + sum(new_keys),
     c_new = s / (r_old + len(new_keys)).  With r_old = 0 the old summary is
-    ignored (the block had no valid key).
+    ignored (the block had no valid key).  Max-pooled summaries (kpool
+    "max") keep the per-dimension maximum: c_new = max(c_old, max(new_keys)),
+    again ignoring c_old when r_old = 0.
     """
     n = new_keys.shape[0]
     if n == 0:
         return np.asarray(c_old, dtype=np.float64).copy()
+    if kpool == "max":
+        m = new_keys.astype(np.float64).max(axis=0)
+        return np.maximum(m, np.asarray(c_old, dtype=np.float64)) if r_old > 0 else m
     s = new_keys.astype(np.float64).sum(axis=0)
     if r_old > 0:
         s = s + r_old * np.asarray(c_old, dtype=np.float64)
@@ -57,7 +62,8 @@ def touched_blocks(len0: int, n_new: int, b: int) -> range:
 
 
 def append_kv(k_cache: np.ndarray, v_cache: np.ndarray, summaries: np.ndarray, len0: int,
-              k_new: np.ndarray, v_new: np.ndarray, b: int):
+              k_new: np.ndarray, v_new: np.ndarray, b: int,
+              kpool: str = "mean"):
     """Append n new rows to one (sequence, KV head) of a decode cache.
 
     k_cache, v_cache: [capacity, d]; summaries: [ceil(capacity / b), d] whose
@@ -75,14 +81,15 @@ def append_kv(k_cache: np.ndarray, v_cache: np.ndarray, summaries: np.ndarray, l
         lo, hi = j * b, (j + 1) * b
         r_old = max(0, min(hi, len0) - lo)                 # valid keys before the append
         t0, t1 = max(lo, len0), min(hi, len0 + n)          # new tokens inside block j
-        c2[j] = append_update(c2[j], r_old, k_new[t0 - len0:t1 - len0])
+        c2[j] = append_update(c2[j], r_old, k_new[t0 - len0:t1 - len0], kpool)
     return k2, v2, c2
 
 
-def summaries_after(k_cache: np.ndarray, length: int, b: int) -> np.ndarray:
+def summaries_after(k_cache: np.ndarray, length: int, b: int, kpool: str = "mean") -> np.ndarray:
     """What the summaries of a cache of `length` valid rows must equal: the
-    batch block means of [P2] Eq 6 (`routing.block_summaries`)."""
-    return block_summaries(k_cache, length, b)
+    batch block summaries of [P2] Eq 6 (`routing.block_summaries`, mean or
+    per-dimension max)."""
+    return block_summaries(k_cache, length, b, kpool)
 
 
 def blocks_after(length: int, b: int) -> int:

@@ -40,7 +40,7 @@ def row_meta(lengths, b: int, mode: str, route_heads: int, forced_first: bool, w
 
 
 def route(qs, ks, lengths, b, mode, qpool, share_gqa, select, k_b, k_min, tau_rel,
-          forced_first, seqs=None, window: int = 1):
+          forced_first, seqs=None, window: int = 1, kpool: str = "mean"):
     """J rows [R, k_b] plus per-row (g, C_r, F_r) for the chosen sequences.
 
     seqs: subset of sequence ids to route (others left as None rows).
@@ -58,7 +58,7 @@ def route(qs, ks, lengths, b, mode, qpool, share_gqa, select, k_b, k_min, tau_re
             continue
         J, sc = routing.route_sequence(qs[s], ks[s], length, b, mode, qpool, share_gqa,
                                        select, k_b, k_min, tau_rel, forced_first,
-                                       return_scores=True, window=window)
+                                       return_scores=True, window=window, kpool=kpool)
         for h in range(route_heads):
             for r in range(J.shape[1]):
                 rr = r if mode == "prefill" else routing.num_blocks(length, b) - 1

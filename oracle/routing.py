@@ -39,20 +39,28 @@ def num_blocks(length: int, b: int) -> int:
     return -(-length // b)
 
 
-def block_summaries(k: np.ndarray, length: int, b: int) -> np.ndarray:
-    """Mean-pooled key summaries c_j for one (sequence, KV head).
+def block_summaries(k: np.ndarray, length: int, b: int, kpool: str = "mean") -> np.ndarray:
+    """Key summaries c_j for one (sequence, KV head).
 
     k: [n_tokens >= length, d].  Block j covers tokens [j*b, min((j+1)*b, length));
-    padding past `length` never enters a summary ([P2] §4.1), and a partial
-    block divides by its own count (the r_j of [P2] §3.1 Eq 11).
-    Pinned: the incremental Eq 11 form and a hand-computed mean in tests.
+    padding past `length` never enters a summary ([P2] §4.1).
+    kpool "mean": the block mean of [P2] Eq 6; a partial block divides by its
+    own count (the r_j of [P2] §3.1 Eq 11).
+    kpool "max": the per-dimension maximum over the block's valid keys, the
+    max-pooled summary that [P2] §2.1 and §4 set against the mean (it keeps
+    each dimension's extreme, possibly taken from different keys).
+    Pinned: the incremental Eq 11 form, a hand-computed mean, and for max a
+    brute-force loop, a two-key fixture and an upper-bound property in tests.
     """
+    if kpool not in ("mean", "max"):
+        raise ValueError(kpool)
     n_blk = num_blocks(length, b)
     c = np.zeros((n_blk, k.shape[1]), dtype=np.float64)
     for j in range(n_blk):
         lo = j * b
         hi = min((j + 1) * b, length)
-        c[j] = k[lo:hi].astype(np.float64).sum(axis=0) / (hi - lo)
+        blk = k[lo:hi].astype(np.float64)
+        c[j] = blk.sum(axis=0) / (hi - lo) if kpool == "mean" else blk.max(axis=0)
     return c
 
 
@@ -156,7 +164,8 @@ def select_row(g: np.ndarray, cands: list[int], forced: list[int], select: str,
 
 def route_sequence(q: np.ndarray, k: np.ndarray, length: int, b: int, mode: str,
                    qpool: str, share_gqa: bool, select: str, k_b: int, k_min: int,
-                   tau_rel: float, forced_first: bool, return_scores: bool = False, window: int = 1):
+                   tau_rel: float, forced_first: bool, return_scores: bool = False, window: int = 1,
+                   kpool: str = "mean"):
     """J for one sequence: [H_r, N_q, k_b] int64 (N_q = 1 in decode).
 
     q: [Hq, n_q_tokens, d] (prefill: n_q_tokens >= length; decode: 1 query);
@@ -167,7 +176,7 @@ def route_sequence(q: np.ndarray, k: np.ndarray, length: int, b: int, mode: str,
     hq, hkv = q.shape[0], k.shape[0]
     group = hq // hkv
     n_blk = num_blocks(length, b)
-    summaries = [block_summaries(k[h], length, b) for h in range(hkv)]
+    summaries = [block_summaries(k[h], length, b, kpool) for h in range(hkv)]
     route_heads = hkv if share_gqa else hq
     n_rows = n_blk if mode == "prefill" else 1
     J = np.full((route_heads, n_rows, k_b), -1, dtype=np.int64)

@@ -67,3 +67,23 @@ def test_untouched_blocks_and_padding_unchanged():
     assert np.allclose(c2[2], (k[8] + k[9] + 2.0) / 4, atol=1e-14)
     assert np.array_equal(c2[3], np.ones(d))
     assert np.array_equal(k2[10:13], np.ones((3, d))) and np.array_equal(k2[13:], k[13:])
+
+
+def test_max_append_equals_batch_max_of_the_grown_block():
+    """Max-pooled summaries kept with the cache: appending chunks to a block
+    gives the per-dimension maximum of all its valid keys, as a batch max over
+    the grown cache does; a block with no valid key starts from the new keys."""
+    rng = np.random.default_rng(21)
+    b, d, cap = 8, 5, 40
+    k = rng.standard_normal((cap, d))
+    v = rng.standard_normal((cap, d))
+    length = 11
+    summ = np.full((cap // b, d), -7.0)             # stale values in untouched slots
+    summ[:2] = routing.block_summaries(k, length, b, "max")
+    for n_new in (1, 3, 7, 9):
+        kn = rng.standard_normal((n_new, d))
+        vn = rng.standard_normal((n_new, d))
+        k, v, summ = cache.append_kv(k, v, summ, length, kn, vn, b, kpool="max")
+        length += n_new
+        nb = cache.blocks_after(length, b)
+        assert np.array_equal(summ[:nb], cache.summaries_after(k, length, b, "max"))

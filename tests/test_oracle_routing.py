@@ -172,3 +172,67 @@ def test_window_topk_equals_brute_force(seed):
         picks = set(j for j in row if j >= 0) - set(forced)
         d = min(max(k_b - len(forced), 0), len(cands))
         assert picks == _brute_topd(g, cands, d)
+
+
+# --- max-pooled key summaries ([P2] §2.1 and §4: the per-dimension maximum
+# over a block's keys, set against the mean of Eq 6) ---
+
+def test_max_summary_brute_force_loops():
+    """Plain Python loops over tokens and dimensions, a ragged last block,
+    and padding past the length that must not enter."""
+    rng = np.random.default_rng(11)
+    b, n, d = 4, 10, 3
+    k = rng.standard_normal((n + 2, d))
+    k[n:] = 1e6                                    # padding rows
+    c = routing.block_summaries(k, n, b, "max")
+    assert c.shape == (3, d)
+    for j in range(3):
+        for e in range(d):
+            best = -np.inf
+            for t in range(j * b, min((j + 1) * b, n)):
+                if k[t, e] > best:
+                    best = k[t, e]
+            assert c[j, e] == best
+
+
+def test_max_summary_assembles_dimensions_from_different_keys():
+    """Two keys (1, 0) and (0, 1): the max-pooled summary is (1, 1), a
+    vector equal to neither key, while the mean is (0.5, 0.5)."""
+    k = np.array([[1.0, 0.0], [0.0, 1.0]])
+    assert np.array_equal(routing.block_summaries(k, 2, 2, "max")[0], [1.0, 1.0])
+    assert np.array_equal(routing.block_summaries(k, 2, 2, "mean")[0], [0.5, 0.5])
+
+
+def test_max_summary_bounds_every_key_score_for_nonnegative_queries():
+    """For a query with no negative component, q . c_max >= q . k_i for every
+    key of the block (the mean gives only q . c_mean <= max_i q . k_i)."""
+    rng = np.random.default_rng(12)
+    b, d = 8, 16
+    k = rng.standard_normal((5 * b, d))
+    cmax = routing.block_summaries(k, 5 * b, b, "max")
+    cmean = routing.block_summaries(k, 5 * b, b, "mean")
+    for _ in range(20):
+        q = np.abs(rng.standard_normal(d))
+        for j in range(5):
+            scores = k[j * b:(j + 1) * b] @ q
+            assert q @ cmax[j] >= scores.max() - 1e-12
+            assert q @ cmean[j] <= scores.max() + 1e-12
+
+
+def test_max_route_prefers_the_block_with_a_spike():
+    """One block holds a single key aligned with the queries among noise; with
+    max pooling it outranks a block whose keys are all mildly aligned but
+    whose per-dimension maxima are smaller."""
+    b, d = 4, 4
+    n = 5 * b
+    k = np.zeros((n, d))
+    k[0:b] = 0.0
+    k[b:2 * b] = [[0.5, 0.0, 0.0, 0.0]] * b        # block 1: every key mildly aligned
+    k[2 * b] = [2.0, 0.0, 0.0, 0.0]                # block 2: one spike, the rest opposite
+    k[2 * b + 1:3 * b] = [-1.0, 0.0, 0.0, 0.0]
+    q = np.zeros((1, n, d))
+    q[0, :, 0] = 1.0
+    for kpool, want in (("max", 2), ("mean", 1)):
+        J = routing.route_sequence(q, k[None], n, b, "prefill", "mean", False, "topk", 2, 1, 0.0,
+                                   False, kpool=kpool)
+        assert J[0, 4, 1] == want, (kpool, J[0, 4])
