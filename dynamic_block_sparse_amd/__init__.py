@@ -62,7 +62,8 @@ class _RouteCfg(ctypes.Structure):
     _fields_ = [("qpool", ctypes.c_int32), ("share_gqa", ctypes.c_int32),
                 ("select", ctypes.c_int32), ("k_b", ctypes.c_int32),
                 ("k_min", ctypes.c_int32), ("tau_rel", ctypes.c_float),
-                ("forced", ctypes.c_uint32), ("window", ctypes.c_int32)]
+                ("forced", ctypes.c_uint32), ("window", ctypes.c_int32),
+                ("kpool", ctypes.c_int32)]
 
 
 _lib = None
@@ -81,7 +82,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sparse_attn_sizes.argtypes = [P, R, ctypes.POINTER(i64), ctypes.POINTER(i32),
                                       ctypes.POINTER(i64), ctypes.POINTER(i32), ctypes.POINTER(i64)]
     lib.sparse_attn_sizes.restype = ctypes.c_int
-    lib.sparse_attn_append_kv.argtypes = [P, i32, vp, vp, vp, vp, vp, vp]
+    lib.sparse_attn_append_kv.argtypes = [P, i32, vp, vp, vp, vp, vp, i32, vp]
     lib.sparse_attn_append_kv.restype = ctypes.c_int
     lib.sparse_attn_bwd.argtypes = [P, R, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.sparse_attn_bwd.restype = ctypes.c_int
@@ -173,6 +174,7 @@ class RouteConfig:
     tau_rel: float = 2.0
     force_first: bool = False
     window: int = 1              # local branch: current block + window - 1 before it, forced
+    kpool: str = "mean"          # key summaries: "mean" (block mean) | "max" (per-dimension max)
 
     def to_c(self) -> _RouteCfg:
         c = _RouteCfg()
@@ -182,6 +184,7 @@ class RouteConfig:
         c.k_b, c.k_min, c.tau_rel = self.k_b, self.k_min, self.tau_rel
         c.forced = SA_FORCE_CURRENT | (SA_FORCE_FIRST if self.force_first else 0)
         c.window = self.window
+        c.kpool = SA_POOL_MAX if self.kpool == "max" else SA_POOL_MEAN
         return c
 
 
@@ -328,11 +331,12 @@ def bwd(prob: Problem, cfg: RouteConfig, wl: Worklist, q, k, v, o, lse, dout, dq
 
 
 def append_kv(prob: Problem, k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
-              v_cache: torch.Tensor, summaries: torch.Tensor):
+              v_cache: torch.Tensor, summaries: torch.Tensor, kpool: str = "mean"):
     """sparse_attn_append_kv: writes k_new / v_new [S, Hkv, n, d] into rows
     [prob.seqlen, prob.seqlen + n) of the caches [S, Hkv, kv_capacity, d] and
-    updates the fp32 summaries of the blocks they land in (in place).  The
-    caller advances prob.seqlen by n afterwards."""
+    updates the fp32 summaries of the blocks they land in (in place; block
+    means, or per-dimension maxima with kpool "max").  The caller advances
+    prob.seqlen by n afterwards."""
     dt = torch.bfloat16 if prob.dtype == "bf16" else torch.float32
     cap = prob.kv_capacity
     shape_c = (prob.batch, prob.heads_kv, cap, prob.head_dim)
@@ -349,7 +353,7 @@ def append_kv(prob: Problem, k_new: torch.Tensor, v_new: torch.Tensor, k_cache: 
     p = prob.to_c()
     _check("sparse_attn_append_kv", load_library().sparse_attn_append_kv(
         ctypes.byref(p), n, _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(summaries),
-        _stream(k_cache.device)))
+        SA_POOL_MAX if kpool == "max" else SA_POOL_MEAN, _stream(k_cache.device)))
 
 
 def problem_for(w, inp) -> Problem:
@@ -363,4 +367,5 @@ def problem_for(w, inp) -> Problem:
 
 def config_for(w) -> RouteConfig:
     return RouteConfig(k_b=w.k_b, qpool=w.qpool, share_gqa=w.share_gqa, select=w.select,
-                       k_min=w.k_min, tau_rel=w.tau_rel, force_first=w.forced_first, window=w.window)
+                       k_min=w.k_min, tau_rel=w.tau_rel, force_first=w.forced_first, window=w.window,
+                       kpool=w.kpool)

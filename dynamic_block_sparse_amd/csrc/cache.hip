@@ -6,6 +6,8 @@
 // keys arrive instead of being rebuilt by a scan over the history.  A chunk of
 // n new keys of block j turns c_j into (r_j c_j + sum of the new keys) /
 // (r_j + n); a block that had no valid key (r_j = 0) starts from the new keys.
+// Max-pooled summaries ([P2] §2.1, §4) take the per-dimension maximum with the
+// new keys instead.
 //
 // A paged cache (a block table into a [pool, Hkv, b, d] pool) writes each
 // block's rows into its page.
@@ -47,9 +49,10 @@ __global__ void __launch_bounds__(64) append_kv_kernel(AppendGeom g, const T* __
   T* kd = k_cache + dst0 + col;
   T* vd = v_cache + dst0 + col;
 
+  // block sums of the new keys, or their per-dimension maxima (max-pooled summaries)
   float acc[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  for (int e = 0; e < E; ++e) acc[e] = g.kmax ? -INFINITY : 0.f;
   constexpr int U = 4;
   int t = t0;
   for (; t + U <= t1; t += U) {
@@ -67,7 +70,7 @@ __global__ void __launch_bounds__(64) append_kv_kernel(AppendGeom g, const T* __
       for (int e = 0; e < E; ++e) {
         kd[(int64_t)(t + u) * D + e] = kx[u][e];
         vd[(int64_t)(t + u) * D + e] = vx[u][e];
-        acc[e] += (float)kx[u][e];
+        acc[e] = g.kmax ? fmaxf(acc[e], (float)kx[u][e]) : acc[e] + (float)kx[u][e];
       }
   }
   for (; t < t1; ++t) {
@@ -77,15 +80,19 @@ __global__ void __launch_bounds__(64) append_kv_kernel(AppendGeom g, const T* __
       const T vx = vn[(int64_t)(t - g.len0) * D + e];
       kd[(int64_t)t * D + e] = kx;
       vd[(int64_t)t * D + e] = vx;
-      acc[e] += (float)kx;
+      acc[e] = g.kmax ? fmaxf(acc[e], (float)kx) : acc[e] + (float)kx;
     }
   }
   float* c = summ + ((int64_t)s * g.sum_seq + (int64_t)h * g.sum_head + j) * D + col;
   const float inv = 1.f / (float)(r_old + t1 - t0);
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const float sum = r_old > 0 ? fmaf((float)r_old, c[e], acc[e]) : acc[e];
-    c[e] = sum * inv;
+    if (g.kmax) {
+      c[e] = r_old > 0 ? fmaxf(c[e], acc[e]) : acc[e];
+    } else {
+      const float sum = r_old > 0 ? fmaf((float)r_old, c[e], acc[e]) : acc[e];
+      c[e] = sum * inv;
+    }
   }
 }
 

@@ -11,7 +11,7 @@ int launch_cu_blocks(const int32_t* cu_seqlens, int32_t* cu_blocks, int batch, h
 // Block summaries of k; with qbar (prefill, mean pooling) the same pass also
 // writes each route row's pooled query, [rows, d] fp32.
 int launch_summary(const Geom& g, int dtype, const void* k, float* summ, int slots, const void* q,
-                   float* qbar, hipStream_t st);
+                   float* qbar, int kpool, hipStream_t st);
 size_t route_smem_bytes(const Geom& g, int qpool);
 // Candidate scores of every row: [rows, max_blocks] fp32 (workspace).
 size_t route_scores_bytes(const Geom& g);
@@ -65,6 +65,7 @@ int launch_bwd(const Geom& g, int dtype, const BwdBufs& b, int64_t kv_elems, int
 // and the Eq 11 update of the summaries of the blocks they land in.
 struct AppendGeom {
   int hkv, d, len0, n_new;
+  int kmax;                        // max-pooled summaries (else block means)
   int64_t cache_seq, cache_head;   // element strides of the K/V cache
   int64_t new_seq, new_head;       // element strides of the new rows
   int64_t sum_seq, sum_head;       // summary strides in blocks

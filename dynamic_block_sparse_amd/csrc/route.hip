@@ -34,7 +34,8 @@ __device__ __forceinline__ int64_t prefill_row_index(const Geom& g, int s, int h
 template <typename T, int D>
 __global__ void __launch_bounds__(256) summary_kernel(Geom g, const T* __restrict__ k,
                                                       float* __restrict__ summ, int slots,
-                                                      const T* __restrict__ q, float* __restrict__ qbar) {
+                                                      const T* __restrict__ q, float* __restrict__ qbar,
+                                                      int kpool) {
   constexpr int CH = D / 8;        // column chunks per row
   constexpr int PH = kWave / CH;   // key phases per wave
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
@@ -63,31 +64,37 @@ __global__ void __launch_bounds__(256) summary_kernel(Geom g, const T* __restric
   if (pool_q && j < g.qblk0) return;   // a cached prefix block has no queries (chunked prefill)
   const int cnt = min(kBlock, len - j * kBlock);
   const int c = lane % CH, ph = lane / CH;
+  // max-pooled key summaries keep each dimension's maximum over the block's
+  // valid keys; block means (and pooled queries) sum and divide
+  const bool kmax = !pool_q && kpool == SA_POOL_MAX;
   float acc[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  for (int i = 0; i < 8; ++i) acc[i] = kmax ? -INFINITY : 0.f;
   const int nh = pool_q ? g.hpr : 1;   // query heads pooled into the row
   const int h0 = g.share ? h * g.group : h;
   const T* base = pool_q ? q + q_offset(g, s, h0, tok0, j * kBlock) + c * 8
                          : k + kv_block_offset(g, s, h, tok0, j) + c * 8;
   auto add_row = [&](int t) {
     const T* p = base + (int64_t)t * D;
+    float x[8];
     if constexpr (sizeof(T) == 2) {
-      u32x4 x = *reinterpret_cast<const u32x4*>(p);
+      u32x4 u = *reinterpret_cast<const u32x4*>(p);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        acc[2 * i] += bf16_lo(x[i]);
-        acc[2 * i + 1] += bf16_hi(x[i]);
+        x[2 * i] = bf16_lo(u[i]);
+        x[2 * i + 1] = bf16_hi(u[i]);
       }
     } else {
       f32x4 x0 = *reinterpret_cast<const f32x4*>(p);
       f32x4 x1 = *reinterpret_cast<const f32x4*>(p + 4);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        acc[i] += x0[i];
-        acc[4 + i] += x1[i];
+        x[i] = x0[i];
+        x[4 + i] = x1[i];
       }
     }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = kmax ? fmaxf(acc[i], x[i]) : acc[i] + x[i];
   };
   for (int hh = 0; hh < nh; ++hh) {
     if (cnt == kBlock) {
@@ -99,16 +106,22 @@ __global__ void __launch_bounds__(256) summary_kernel(Geom g, const T* __restric
     }
     base += g.q_head;   // next query head of the group (only read when pooling queries)
   }
-  // sum the key phases: partners lane ^ 8 (D = 64 only), ^ 16, ^ 32
+  // combine the key phases: partners lane ^ 8 (D = 64 only), ^ 16, ^ 32
+  auto combine = [&](auto op) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    uint32_t u = __float_as_uint(acc[i]);
-    if constexpr (CH <= 8) u = OpAddF{}(u, dpp_u<0x128>(u));   // row_ror:8 = lane ^ 8 in a 16-lane row
-    u = pair32(pair16(u, OpAddF{}), OpAddF{});
-    acc[i] = __uint_as_float(u);
-  }
+    for (int i = 0; i < 8; ++i) {
+      uint32_t u = __float_as_uint(acc[i]);
+      if constexpr (CH <= 8) u = op(u, dpp_u<0x128>(u));   // row_ror:8 = lane ^ 8 in a 16-lane row
+      u = pair32(pair16(u, op), op);
+      acc[i] = __uint_as_float(u);
+    }
+  };
+  if (kmax)
+    combine(OpMaxF{});
+  else
+    combine(OpAddF{});
   if (ph == 0) {
-    const float inv = 1.f / (float)(cnt * nh);
+    const float inv = kmax ? 1.f : 1.f / (float)(cnt * nh);
     const int nblk = g.varlen ? g.cu_blocks[s + 1] - blk0 : ceil_div(g.n, kBlock);
     float* out = pool_q ? qbar + prefill_row_index(g, s, h, j, blk0, nblk) * D + c * 8
                         : summ + sum_offset(g, s, h, blk0, j) + c * 8;
@@ -507,19 +520,23 @@ __global__ void __launch_bounds__(64) route_select_kernel(Geom g, sa_route_cfg r
 
 // ---------------------------------------------------------------------------
 int launch_summary(const Geom& g, int dtype, const void* k, float* summ, int slots, const void* q,
-                   float* qbar, hipStream_t st) {
+                   float* qbar, int kpool, hipStream_t st) {
   if (slots <= 0) return SA_OK;
   dim3 grid((slots + 3) / 4, g.hkv + (qbar ? g.hr : 0));
   if (dtype == SA_BF16) {
     if (g.d == 128)
-      summary_kernel<__bf16, 128><<<grid, 256, 0, st>>>(g, (const __bf16*)k, summ, slots, (const __bf16*)q, qbar);
+      summary_kernel<__bf16, 128><<<grid, 256, 0, st>>>(g, (const __bf16*)k, summ, slots, (const __bf16*)q, qbar,
+                                                       kpool);
     else
-      summary_kernel<__bf16, 64><<<grid, 256, 0, st>>>(g, (const __bf16*)k, summ, slots, (const __bf16*)q, qbar);
+      summary_kernel<__bf16, 64><<<grid, 256, 0, st>>>(g, (const __bf16*)k, summ, slots, (const __bf16*)q, qbar,
+                                                       kpool);
   } else {
     if (g.d == 128)
-      summary_kernel<float, 128><<<grid, 256, 0, st>>>(g, (const float*)k, summ, slots, (const float*)q, qbar);
+      summary_kernel<float, 128><<<grid, 256, 0, st>>>(g, (const float*)k, summ, slots, (const float*)q, qbar,
+                                                      kpool);
     else
-      summary_kernel<float, 64><<<grid, 256, 0, st>>>(g, (const float*)k, summ, slots, (const float*)q, qbar);
+      summary_kernel<float, 64><<<grid, 256, 0, st>>>(g, (const float*)k, summ, slots, (const float*)q, qbar,
+                                                      kpool);
   }
   return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
 }

@@ -38,6 +38,7 @@ int validate(const sa_problem* p, const sa_route_cfg* rc, Plan* out) {
   if (p->block != kBlock) return SA_ERR_UNSUPPORTED;
   if (p->head_dim != 64 && p->head_dim != 128) return SA_ERR_UNSUPPORTED;
   if (rc->qpool != SA_POOL_MEAN && rc->qpool != SA_POOL_MAX) return SA_ERR_INVALID_ARG;
+  if (rc->kpool != SA_POOL_MEAN && rc->kpool != SA_POOL_MAX) return SA_ERR_INVALID_ARG;
   if (rc->share_gqa != 0 && rc->share_gqa != 1) return SA_ERR_INVALID_ARG;
   if (rc->select != SA_SELECT_TOPK && rc->select != SA_SELECT_THRESHOLD) return SA_ERR_INVALID_ARG;
   if (!(rc->forced & SA_FORCE_CURRENT) || (rc->forced & ~3u)) return SA_ERR_INVALID_ARG;
@@ -272,9 +273,10 @@ int sparse_attn_bwd(const sa_problem* p, const sa_route_cfg* rc, const int32_t* 
 }
 
 int sparse_attn_append_kv(const sa_problem* p, int32_t n_new, const void* k_new, const void* v_new,
-                          void* k_cache, void* v_cache, float* summaries, void* stream) {
+                          void* k_cache, void* v_cache, float* summaries, int32_t kpool, void* stream) {
   using namespace sa;
   if (!p || p->mode != SA_DECODE || p->cu_seqlens || p->q_start != 0) return SA_ERR_INVALID_ARG;
+  if (kpool != SA_POOL_MEAN && kpool != SA_POOL_MAX) return SA_ERR_INVALID_ARG;
   if (p->batch < 1 || p->heads_q < 1 || p->heads_kv < 1 || p->heads_q % p->heads_kv != 0)
     return SA_ERR_INVALID_ARG;
   if (p->dtype != SA_F32 && p->dtype != SA_BF16) return SA_ERR_INVALID_ARG;
@@ -301,6 +303,7 @@ int sparse_attn_append_kv(const sa_problem* p, int32_t n_new, const void* k_new,
   g.block_table = p->block_table;
   g.table_stride = p->table_stride;
   g.pool_blocks = p->pool_blocks;
+  g.kmax = kpool == SA_POOL_MAX;
   if (p->block_table && (p->table_stride < nbc || p->pool_blocks < 1)) return SA_ERR_INVALID_ARG;
   return launch_append_kv(g, p->dtype, p->batch, touched, k_new, v_new, k_cache, v_cache, summaries,
                           reinterpret_cast<hipStream_t>(stream));
@@ -359,7 +362,8 @@ int sparse_attn_route(const sa_problem* p, const sa_route_cfg* rc, const void* q
   if (!summaries_in) {
     // one wavefront per valid block: the summary kernel maps slot -> (sequence, block)
     // over the valid blocks (slots of a cache's spare capacity are never written)
-    if ((st = launch_summary(pl.g, p->dtype, k, summaries, (int)pl.sum_valid, q, qbar, hs)) != SA_OK) return st;
+    if ((st = launch_summary(pl.g, p->dtype, k, summaries, (int)pl.sum_valid, q, qbar, rc->kpool, hs)) != SA_OK)
+      return st;
   }
   return launch_route(pl.g, *rc, p->dtype, q, summaries, qbar, scores, J, hs);
 }

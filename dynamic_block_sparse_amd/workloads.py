@@ -59,6 +59,7 @@ class Workload:
     tau_rel: float = 2.0
     forced_first: bool = False  # force block 0 in addition to the current block
     window: int = 1             # forced local window in blocks, the current block included
+    kpool: str = "mean"         # key summaries: block mean (Eq 6) or per-dimension max
     plant_scope: str = "none"   # "none" | "head" | "kv" | "seq"
     plant_blocks: int = 0
     plant_alpha: float = 0.0

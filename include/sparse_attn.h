@@ -152,6 +152,10 @@ typedef struct sa_route_cfg {
   int32_t window;         /* local branch: the current block and the window - 1 blocks before
                              it are forced and never scored ([P2] §3.2 union of a local, a
                              global and a dynamic branch); 0 or 1 = the current block only */
+  int32_t kpool;          /* key summaries: SA_POOL_MEAN (the block mean of [P2] Eq 6) or
+                             SA_POOL_MAX (per-dimension maximum over the block's valid keys,
+                             [P2] §2.1 and §4); stored summaries must have been built the
+                             same way */
 } sa_route_cfg;
 
 /* Host-side sizes derived from the geometry (no device work).
@@ -277,12 +281,16 @@ int sparse_attn_bwd(const sa_problem* p, const sa_route_cfg* rc, const int32_t* 
  *               Summaries of blocks below ceil(L0 / b) must hold the means of
  *               the cached keys (sparse_attn_route with summaries_in = 0 writes
  *               them; this call keeps them).
+ *   kpool       SA_POOL_MEAN: the update above.  SA_POOL_MAX (max-pooled
+ *               summaries): c_j <- max(c_j, per-dimension max of its new keys),
+ *               or that max alone when r_j = 0.
  *   Arithmetic is fp32 (sums of the new keys in token order).  Calls on one
  *   stream apply in order; the caller advances seqlen by n_new afterwards.
  *   Returns SA_ERR_INVALID_ARG for a non-decode problem, a negative n_new,
- *   L0 + n_new > kv_capacity or a null pointer (when n_new > 0). */
+ *   L0 + n_new > kv_capacity, an unknown kpool or a null pointer (when
+ *   n_new > 0). */
 int sparse_attn_append_kv(const sa_problem* p, int32_t n_new, const void* k_new, const void* v_new,
-                          void* k_cache, void* v_cache, float* summaries, void* stream);
+                          void* k_cache, void* v_cache, float* summaries, int32_t kpool, void* stream);
 
 /* Human-readable text for a status code (static string). */
 const char* sparse_attn_status_string(int status);

@@ -133,9 +133,9 @@ def test_decode_capacity_sizes_and_prefill_rejects_capacity(lib):
 
 def test_append_kv_validates_before_any_launch(lib):
     """Every bad argument returns a status on the host; n_new = 0 enqueues nothing."""
-    def call(prob, n, ptr=8):
+    def call(prob, n, ptr=8, kpool=dbs.SA_POOL_MEAN):
         p = prob.to_c()
-        return lib.sparse_attn_append_kv(ctypes.byref(p), n, ptr, ptr, ptr, ptr, ptr, None)
+        return lib.sparse_attn_append_kv(ctypes.byref(p), n, ptr, ptr, ptr, ptr, ptr, kpool, None)
     ok = dbs.Problem.decode(2, 4, 2, 128, 100, kv_capacity=200)
     assert call(ok, 0) == dbs.SA_OK                                            # nothing to do
     assert call(ok, 101) == dbs.SA_ERR_INVALID_ARG                             # past the capacity
@@ -146,6 +146,15 @@ def test_append_kv_validates_before_any_launch(lib):
     assert call(dataclasses.replace(ok, q_start=64), 1) == dbs.SA_ERR_INVALID_ARG            # decode: no chunk
     assert call(dbs.Problem.decode(2, 4, 2, 96, 100, kv_capacity=200), 1) == dbs.SA_ERR_UNSUPPORTED
     assert call(dbs.Problem.decode(2, 4, 3, 128, 100, kv_capacity=200), 1) == dbs.SA_ERR_INVALID_ARG
+    assert call(ok, 1, kpool=2) == dbs.SA_ERR_INVALID_ARG                      # unknown key pooling
+
+
+def test_route_cfg_kpool_validated(lib):
+    assert dbs.sizes(_prob(), dbs.RouteConfig(k_b=8, kpool="max")).rows > 0
+    c = dbs.RouteConfig(k_b=8).to_c()
+    c.kpool = 5
+    p = _prob().to_c()
+    assert lib.sparse_attn_workspace_size(ctypes.byref(p), ctypes.byref(c), 0, 0) == 0
 
 
 def test_window_sizes_and_limits(lib):
