@@ -198,3 +198,24 @@ def test_chunked_prefill_sizes_and_limits(lib):
             dbs.sizes(bad, cfg)
         assert e.value.status == dbs.SA_ERR_INVALID_ARG
 
+
+
+def test_bwd_validates_before_any_launch(lib):
+    """sparse_attn_bwd returns its status on the host for a decode problem, an
+    unsupported head_dim / dtype pair, null pointers and a short workspace."""
+    cfg = dbs.RouteConfig(k_b=8).to_c()
+
+    def call(prob, ws_bytes=1 << 40, ptr=8):
+        p = prob.to_c()
+        # row_ptr, col_idx, q, k, v, o, lse, dout, dq, dk, dv, ws
+        return lib.sparse_attn_bwd(ctypes.byref(p), ctypes.byref(cfg), *([ptr] * 12), ws_bytes, None)
+    ok = _prob()
+    need = lib.sparse_attn_workspace_size(ctypes.byref(ok.to_c()), ctypes.byref(cfg), 3, 0)
+    # D per query (16 heads x 8192 tokens), dK and dV accumulators, two counters per key block and head
+    assert need >= 16 * 8192 * 4 + 2 * 16 * 8192 * 128 * 4 + 2 * 128 * 16 * 4
+    assert lib.sparse_attn_workspace_size(ctypes.byref(ok.to_c()), ctypes.byref(cfg), 4, 0) == 0
+    assert call(dbs.Problem.decode(2, 4, 2, 128, 100)) == dbs.SA_ERR_UNSUPPORTED
+    assert call(_prob(head_dim=64)) == dbs.SA_ERR_UNSUPPORTED           # bf16 needs d = 128
+    assert call(_prob(dtype="f32")) == dbs.SA_ERR_UNSUPPORTED           # fp32 needs d = 64
+    assert call(ok, ptr=None) == dbs.SA_ERR_INVALID_ARG
+    assert call(ok, ws_bytes=need - 1) == dbs.SA_ERR_WORKSPACE
