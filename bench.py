@@ -285,7 +285,7 @@ def measure_bwd(args, dbs, st, visits):
     """sparse_attn_bwd over the step's worklist, output and lse with a seeded
     dO: each call bracketed by events (warm), median over the calls.  FLOPs
     are the five products per selected tile visit (S, dP, dQ, dK, dV: 10 b^2 d);
-    the two kernels execute S and dP twice each (16 b^2 d)."""
+    the two kernels form S and dP in both, so they execute 14 b^2 d."""
     import torch
     w, inp = st.w, st.inp
     g = torch.Generator(device=inp.q.device).manual_seed(7)
