@@ -40,6 +40,8 @@ CASES = [
     ("gqa_per_head", "bf16", 128, None, 1, 4, 2, 450, 0, 0, 3, False, False, 1),
     ("varlen_f32_d64", "f32", 64, [300, 577, 64], 3, 2, 1, 0, 0, 0, 3, False, True, 1),
     ("chunked_bf16", "bf16", 128, None, 1, 2, 2, 900, 512, 1024, 4, False, False, 1),
+    ("varlen_bf16_gqa", "bf16", 128, [300, 577, 64, 1000], 4, 8, 2, 0, 0, 0, 4, True, True, 2),
+    ("varlen_bf16_per_head", "bf16", 128, [700, 130], 2, 4, 2, 0, 0, 0, 3, False, False, 1),
 ]
 
 
