@@ -141,3 +141,40 @@ def test_max_key_summaries_decode_and_append():
             assert np.array_equal(sg2[s, h, :nb2].astype(np.float64), c2[:nb2]), (s, h)
             assert np.array_equal(c2[:nb2], ocache.summaries_after(
                 torch.cat([k[s, h, :L], kn[s, h]]).double().numpy(), L + n, B, "max"))
+
+
+def test_max_key_summaries_packed_varlen():
+    """Packed varlen prefill: each sequence's summary slots (from its first
+    block slot on) hold the per-dimension maxima of its own keys, ragged and
+    one-block sequences included; router rows match the oracle's scores."""
+    dev = torch.device("cuda:0")
+    lengths, hq, hkv, d = [300, 64, 577], 4, 2, 128
+    print(f"max key summaries varlen: lengths={lengths}", flush=True)
+    g = torch.Generator().manual_seed(53)
+    total = sum(lengths)
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    q = torch.randn((hq, total, d), generator=g).to(torch.bfloat16)
+    k = torch.randn((hkv, total, d), generator=g).to(torch.bfloat16)
+    prob = dbs.Problem.varlen(lengths, hq, hkv, d, torch.tensor(cu, dtype=torch.int32, device=dev), "bf16")
+    cfg = dbs.RouteConfig(k_b=4, share_gqa=True, kpool="max")
+    J, summ = dbs.route(prob, cfg, q.to(dev), k.to(dev))
+    wl = dbs.build_worklist(prob, cfg, J)
+    torch.cuda.synchronize()
+    assert int(wl.err.item()) == 0
+    sg = summ.cpu().numpy()
+    blk0 = 0
+    qs, ks = [], []
+    for s, ln in enumerate(lengths):
+        nb = -(-ln // B)
+        for h in range(hkv):
+            want = orout.block_summaries(k[h, cu[s]:cu[s] + ln].double().numpy(), ln, B, "max")
+            assert np.array_equal(sg[h, blk0:blk0 + nb].astype(np.float64), want), (s, h)
+        blk0 += nb
+        qs.append(q[:, cu[s]:cu[s] + ln].double().numpy())
+        ks.append(k[:, cu[s]:cu[s] + ln].double().numpy())
+    _j, scores = oprob.route(qs, ks, lengths, B, "prefill", "mean", True, "topk", 4, 4, 2.0, False, kpool="max")
+    rule = types.SimpleNamespace(select="topk", k_b=4)
+    Jh = J.cpu().numpy()
+    for i in range(Jh.shape[0]):
+        ok, _nd = check_router_row(Jh[i], scores[i], rule)
+        assert ok, (i, Jh[i])
