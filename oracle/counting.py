@@ -8,8 +8,11 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
                                 triangle, unique tiles only)
   effective pairs               pairs a query actually attends (diagonal tile
                                 counts its lower triangle only)
-  tile FLOPs                    4 * b_q * b_k * d per (query head, tile) visit:
-                                QK^T and PV, 2 FLOPs per multiply-add
+
+Pinned in tests: dense_causal_pairs and physical_pairs against the values the
+page prints (Eq 8, Eq 9 and the deduplicated total); effective_pairs_prefill
+against Eq 8 with every causal block listed and the closed form N b (b + 1) / 2
+with the diagonal alone.
 """
 from __future__ import annotations
 
@@ -22,10 +25,6 @@ def dense_causal_pairs(n: int) -> int:
 
 def physical_pairs(row_lengths, b_q: int, b_k: int) -> int:
     return int(np.sum(np.asarray(row_lengths, dtype=np.int64))) * b_q * b_k
-
-
-def tile_flops(tile_visits: int, b_q: int, b_k: int, d: int) -> int:
-    return 4 * b_q * b_k * d * int(tile_visits)
 
 
 def effective_pairs_prefill(rows, length: int, b: int) -> int:

@@ -7,6 +7,12 @@ the order of J's leading dimensions [B, H, N_q, k_b] in [P2]'s opening
 paragraph, with sequences of a packed batch concatenated.  In decode each
 (sequence, routing head) is one row whose current block is the last one.
 
+Pinned (tests/test_oracle_problem.py): row_table against a hand-written row
+list for ragged sequences (prefill and decode); the decode branch of
+attention_rows against torch's fp64 SDPA over all cached keys (partial last
+blocks, mixed cache lengths) and against plain loops on a sparse block list;
+a packed ragged batch against its sequences done one at a time.
+
 Inputs are per-sequence float64 arrays:
   qs[s]  [Hq, n_q_tokens, d]   (decode: n_q_tokens = 1)
   ks[s], vs[s]  [Hkv, n_k_tokens, d]
