@@ -214,6 +214,80 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _dtype_of(prob: Problem) -> torch.dtype:
+    return torch.bfloat16 if prob.dtype == "bf16" else torch.float32
+
+
+def q_shape(prob: Problem):
+    """Q / O / dO shape: fixed [B, Hq, n - q_start, d], packed [Hq, T, d], decode [S, Hq, d]."""
+    if prob.mode == "decode":
+        return (prob.batch, prob.heads_q, prob.head_dim)
+    if prob.cu_seqlens is not None:
+        return (prob.heads_q, int(sum(prob.lengths)), prob.head_dim)
+    return (prob.batch, prob.heads_q, prob.seqlen - prob.q_start, prob.head_dim)
+
+
+def kv_shape(prob: Problem):
+    """K / V shape: fixed and decode [B, Hkv, kv_capacity or n, d], packed [Hkv, T, d],
+    paged decode pool [pool_blocks, Hkv, b, d]."""
+    if prob.block_table is not None:
+        return (prob.pool_blocks, prob.heads_kv, prob.block, prob.head_dim)
+    if prob.cu_seqlens is not None:
+        return (prob.heads_kv, int(sum(prob.lengths)), prob.head_dim)
+    return (prob.batch, prob.heads_kv, prob.kv_capacity or prob.seqlen, prob.head_dim)
+
+
+def _require(call: str, name: str, t, shape, dtype, device=None, min_numel: bool = False):
+    """Raise ValueError unless t is a contiguous `dtype` tensor of `shape` (or,
+    with min_numel, a 1-D one holding at least shape[0] elements).  Checked
+    before anything is enqueued: the kernels index these buffers from the
+    geometry alone.  Where the tensors live is checked once all of them have
+    passed (_on_device)."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{call}: {name} must be a torch.Tensor, got {type(t).__name__}")
+    ok_shape = (t.dim() == 1 and t.numel() >= shape[0]) if min_numel else tuple(t.shape) == tuple(shape)
+    want = f"at least {shape[0]} elements (1-D)" if min_numel else f"shape {tuple(shape)}"
+    if not ok_shape or t.dtype != dtype:
+        raise ValueError(f"{call}: {name} must be {dtype} with {want}, got {t.dtype} {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{call}: {name} must be contiguous (strides {t.stride()})")
+
+
+def _on_device(call: str, device, **tensors):
+    """Raise ValueError unless every given tensor is a GPU tensor on `device`."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{call}: {name} must be a GPU tensor, got device {t.device}")
+        if t.device != device:
+            raise ValueError(f"{call}: {name} is on {t.device}, expected {device}")
+
+
+def _require_problem(call: str, prob: Problem, device):
+    """The device tables a Problem carries: cu_seqlens [B + 1] and block_table [B, stride], int32."""
+    if prob.cu_seqlens is not None:
+        if prob.lengths is None or len(prob.lengths) != prob.batch:
+            raise ValueError(f"{call}: a packed problem needs the host lengths of its {prob.batch} sequences")
+        _require(call, "cu_seqlens", prob.cu_seqlens, (prob.batch + 1,), torch.int32, device)
+    if prob.block_table is not None:
+        bt = prob.block_table
+        if bt.dim() != 2 or bt.shape[0] != prob.batch:
+            raise ValueError(f"{call}: block_table must be [batch, stride], got {tuple(bt.shape)}")
+        _require(call, "block_table", bt, tuple(bt.shape), torch.int32, device)
+
+
+def _require_worklist(call: str, prob: Problem, cfg: RouteConfig, wl: "Worklist", device, full: bool = True):
+    sz = sizes(prob, cfg)
+    _require(call, "row_ptr", wl.row_ptr, (sz.rows + 1,), torch.int32, device)
+    _require(call, "col_idx", wl.col_idx, (max(sz.nnz_cap, 1),), torch.int32, device, min_numel=True)
+    if full:
+        _require(call, "row_perm", wl.row_perm, (max(sz.rows, 1),), torch.int32, device, min_numel=True)
+        _require(call, "bucket_ptr", wl.bucket_ptr, (sz.n_buckets + 1,), torch.int32, device)
+        _require(call, "err", wl.err, (1,), torch.int32, device)
+    return sz
+
+
 def sizes(prob: Problem, cfg: RouteConfig) -> Sizes:
     lib = load_library()
     r, nnz, kv = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
@@ -234,6 +308,17 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
 
 
+def _use_workspace(call: str, workspace: Optional[torch.Tensor], nbytes: int, device) -> torch.Tensor:
+    """The caller's workspace when it is a big enough device buffer on `device`, else a new one."""
+    if workspace is None:
+        return _workspace(nbytes, device)
+    if not workspace.is_cuda or workspace.device != device or not workspace.is_contiguous():
+        raise ValueError(f"{call}: workspace must be a contiguous tensor on {device}")
+    if workspace.numel() * workspace.element_size() < nbytes:
+        return _workspace(nbytes, device)
+    return workspace
+
+
 def summaries_shape(prob: Problem):
     if prob.cu_seqlens is not None:
         nb = sum(-(-int(x) // prob.block) for x in prob.lengths)
@@ -248,14 +333,25 @@ def route(prob: Problem, cfg: RouteConfig, q: torch.Tensor, k: Optional[torch.Te
           J: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
     """sparse_attn_route: returns (J int32 [rows, k_b], fp32 summaries)."""
     lib = load_library()
+    _require("route", "q", q, q_shape(prob), _dtype_of(prob))
     dev = q.device
+    _require_problem("route", prob, dev)
+    if not summaries_in:
+        _require("route", "k", k, kv_shape(prob), _dtype_of(prob), dev)
+    elif summaries is None:
+        raise ValueError("route: summaries_in needs the stored summaries")
     if summaries is None:
         summaries = torch.empty(summaries_shape(prob), dtype=torch.float32, device=dev)
+    _require("route", "summaries", summaries, summaries_shape(prob), torch.float32, dev)
+    rows = sizes(prob, cfg).rows
     if J is None:
-        J = torch.empty((sizes(prob, cfg).rows, cfg.k_b), dtype=torch.int32, device=dev)
+        J = torch.empty((rows, cfg.k_b), dtype=torch.int32, device=dev)
+    _require("route", "J", J, (rows, cfg.k_b), torch.int32, dev)
+    _on_device("route", dev, q=q, k=None if summaries_in else k, summaries=summaries, J=J,
+               cu_seqlens=prob.cu_seqlens, block_table=prob.block_table)
     p, c = prob.to_c(), cfg.to_c()
     wsb = workspace_size(prob, cfg, 0)
-    ws = workspace if workspace is not None and workspace.numel() >= wsb else _workspace(wsb, dev)
+    ws = _use_workspace("route", workspace, wsb, dev)
     _check("sparse_attn_route", lib.sparse_attn_route(
         ctypes.byref(p), ctypes.byref(c), _ptr(q), _ptr(k), _ptr(summaries), int(summaries_in),
         _ptr(J), _ptr(ws), wsb, _stream(dev)))
@@ -275,7 +371,10 @@ def build_worklist(prob: Problem, cfg: RouteConfig, J: torch.Tensor, out: Option
                    workspace: Optional[torch.Tensor] = None) -> Worklist:
     """sparse_attn_build_worklist: returns the CSR worklist (device tensors)."""
     lib = load_library()
+    rows = sizes(prob, cfg).rows
+    _require("build_worklist", "J", J, (rows, cfg.k_b), torch.int32)
     dev = J.device
+    _require_problem("build_worklist", prob, dev)
     if out is None:
         sz = sizes(prob, cfg)
         out = Worklist(row_ptr=torch.empty(sz.rows + 1, dtype=torch.int32, device=dev),
@@ -284,10 +383,14 @@ def build_worklist(prob: Problem, cfg: RouteConfig, J: torch.Tensor, out: Option
                        bucket_ptr=torch.empty(sz.n_buckets + 1, dtype=torch.int32, device=dev),
                        err=torch.zeros(1, dtype=torch.int32, device=dev))
     else:
-        out.err.zero_()
+        _require_worklist("build_worklist", prob, cfg, out, dev)
+    _on_device("build_worklist", dev, J=J, row_ptr=out.row_ptr, col_idx=out.col_idx, row_perm=out.row_perm,
+               bucket_ptr=out.bucket_ptr, err=out.err, cu_seqlens=prob.cu_seqlens,
+               block_table=prob.block_table)
+    out.err.zero_()
     p, c = prob.to_c(), cfg.to_c()
     wsb = workspace_size(prob, cfg, 1)
-    ws = workspace if workspace is not None and workspace.numel() >= wsb else _workspace(wsb, dev)
+    ws = _use_workspace("build_worklist", workspace, wsb, dev)
     _check("sparse_attn_build_worklist", lib.sparse_attn_build_worklist(
         ctypes.byref(p), ctypes.byref(c), _ptr(J), _ptr(out.row_ptr), _ptr(out.col_idx),
         out.col_idx.numel(), _ptr(out.row_perm), _ptr(out.bucket_ptr), _ptr(out.err),
@@ -299,14 +402,26 @@ def fwd(prob: Problem, cfg: RouteConfig, wl: Worklist, q, k, v, o=None, lse=None
         want_lse: bool = True, num_splits: int = 0, workspace: Optional[torch.Tensor] = None):
     """sparse_attn_fwd: returns (O, LSE or None)."""
     lib = load_library()
+    dt, qs, kvs = _dtype_of(prob), q_shape(prob), kv_shape(prob)
+    _require("fwd", "q", q, qs, dt)
     dev = q.device
+    _require_problem("fwd", prob, dev)
+    _require("fwd", "k", k, kvs, dt, dev)
+    _require("fwd", "v", v, kvs, dt, dev)
+    _require_worklist("fwd", prob, cfg, wl, dev, full=False)
+    _require("fwd", "row_perm", wl.row_perm, (max(sizes(prob, cfg).rows, 1),), torch.int32, dev, min_numel=True)
     if o is None:
         o = torch.empty_like(q)
+    _require("fwd", "o", o, qs, dt, dev)
     if lse is None and want_lse:
         lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
+    if lse is not None:
+        _require("fwd", "lse", lse, qs[:-1], torch.float32, dev)
+    _on_device("fwd", dev, q=q, k=k, v=v, o=o, lse=lse, row_ptr=wl.row_ptr, col_idx=wl.col_idx,
+               row_perm=wl.row_perm, cu_seqlens=prob.cu_seqlens, block_table=prob.block_table)
     p, c = prob.to_c(), cfg.to_c()
     wsb = workspace_size(prob, cfg, 2, num_splits)
-    ws = workspace if workspace is not None and workspace.numel() >= wsb else _workspace(wsb, dev)
+    ws = _use_workspace("fwd", workspace, wsb, dev)
     _check("sparse_attn_fwd", lib.sparse_attn_fwd(
         ctypes.byref(p), ctypes.byref(c), _ptr(wl.row_ptr), _ptr(wl.col_idx), _ptr(wl.row_perm),
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), num_splits, _ptr(ws), wsb, _stream(dev)))
@@ -317,13 +432,24 @@ def bwd(prob: Problem, cfg: RouteConfig, wl: Worklist, q, k, v, o, lse, dout, dq
         workspace: Optional[torch.Tensor] = None):
     """sparse_attn_bwd: returns (dQ, dK, dV) for the forward that produced o and lse."""
     lib = load_library()
+    dt, qs, kvs = _dtype_of(prob), q_shape(prob), kv_shape(prob)
+    _require("bwd", "q", q, qs, dt)
     dev = q.device
+    _require_problem("bwd", prob, dev)
+    for name, t, shp, tdt in (("k", k, kvs, dt), ("v", v, kvs, dt), ("o", o, qs, dt),
+                              ("lse", lse, qs[:-1], torch.float32), ("dout", dout, qs, dt)):
+        _require("bwd", name, t, shp, tdt, dev)
+    _require_worklist("bwd", prob, cfg, wl, dev, full=False)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    for name, t, shp in (("dq", dq, qs), ("dk", dk, kvs), ("dv", dv, kvs)):
+        _require("bwd", name, t, shp, dt, dev)
+    _on_device("bwd", dev, q=q, k=k, v=v, o=o, lse=lse, dout=dout, dq=dq, dk=dk, dv=dv, row_ptr=wl.row_ptr,
+               col_idx=wl.col_idx, cu_seqlens=prob.cu_seqlens)
     p, c = prob.to_c(), cfg.to_c()
     wsb = workspace_size(prob, cfg, 3)
-    ws = workspace if workspace is not None and workspace.numel() >= wsb else _workspace(wsb, dev)
+    ws = _use_workspace("bwd", workspace, wsb, dev)
     _check("sparse_attn_bwd", lib.sparse_attn_bwd(
         ctypes.byref(p), ctypes.byref(c), _ptr(wl.row_ptr), _ptr(wl.col_idx), _ptr(q), _ptr(k), _ptr(v),
         _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), wsb, _stream(dev)))
