@@ -6,22 +6,27 @@ already resident in HBM:
 
     sparse_attn_route -> sparse_attn_build_worklist -> sparse_attn_fwd
 
-on the 8192-token MHA prefill setting (B=1, H=16, n=8192, d=128, b=64,
-k_b=16, bf16, planted relevance).  `value` is the selected-tile FLOPs of the
-step (4*b*b*d per (query head, tile) visit of the worklist) divided by the
-step's time, the step replayed as one HIP graph, in TFLOP/s.  The attention
-call alone is reported in `roofline` against the bf16 dense MFMA peak, timed
-as the median call over steps that each start with the 256 MB last-level
-cache flushed (a 512 MB buffer rewritten outside the events); every call's
-median, p10 and p90 are in `stages_ms`, warm (back to back) and flushed.  The
-split-KV decode setting (64 x 131072-token caches, Hq=32, Hkv=8, k_b=64) is
-timed the same way and reported under `decode` as KV GB/s against the HBM peak.
+The JSON line's `value` is the step on the packed variable-length setting, the
+largest prefill workload that fits one GPU (8 sequences of 2K-64K tokens drawn
+from a seed, Hq=32, Hkv=8, d=128, b=64, Eq 7 threshold routing with k_max=64,
+bf16, planted relevance): selected-tile FLOPs of the step (4*b*b*d per (query
+head, tile) visit of the worklist) divided by the step's time, the step
+replayed as one HIP graph, in TFLOP/s.  The attention kernel alone is reported
+in `roofline` against the bf16 dense MFMA peak: its mean launch time over every
+timed call (events on the stream the library launches on), warm and after a
+last-level cache flush (a 512 MB buffer rewritten outside the events).
 
-The fp64 CPU oracle is timed on a bounded sample of the same prefill input
-(`cpu_baseline`): a reported baseline, not a target.
+The other settings are timed the same way and reported under `settings`, each
+with its own `roofline`: the 8192-token MHA prefill (B=1, H=16, k_b=16), the
+32768-token GQA prefill (B=2, Hq=32, Hkv=8, k_b=32, sink forced) and split-KV
+decode (64 x 131072-token caches, Hq=32, Hkv=8, k_b=64) as KV GB/s against the
+HBM peak.  The backward pass is timed on the prefill settings.
 
-    python bench.py [--steps K] [--warmup W] [--no-decode] [--no-cpu]
-    python bench.py --workload NAME     # another bf16 setting, same measurements
+The fp64 CPU oracle is timed on a bounded, seeded sample of the headline
+setting (`cpu_baseline`): a reported baseline, not a target.
+
+    python bench.py [--steps K] [--warmup W] [--no-decode] [--no-cpu] [--no-bwd]
+    python bench.py --workload NAME     # time one setting only (it becomes the headline)
     python bench.py --dense             # adds the dense causal comparison (`dense`)
 """
 from __future__ import annotations
@@ -52,12 +57,14 @@ def source_sha(rel):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def traffic_for(kernel_key):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if still current."""
+def traffic_for(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload`, from committed rocprofv3
+    counter runs (profiles/traffic.json, keyed "kernel|workload"), or None when
+    that pair was never measured or the kernel's source changed since."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     with open(TRAFFIC_FILE) as f:
-        rec = json.load(f).get(kernel_key)
+        rec = json.load(f).get(f"{kernel}|{workload}")
     if not rec or rec.get("source_sha256") != source_sha(rec["source"]):
         return None
     return rec["bytes_per_launch"]
@@ -191,36 +198,76 @@ def graph_timed(stepper, steps, warmup):
     return start.elapsed_time(end) / steps
 
 
-def cpu_baseline(w, inp, heads):
-    """The fp64 oracle on `heads` heads of the prefill input: route, worklist, attention."""
-    import numpy as np
-    from oracle import problem as oprob
+def _host_info():
+    """Threads numpy's BLAS uses, the BLAS library, and the host CPU model."""
+    import numpy  # noqa: F401  (loads the BLAS so threadpoolctl can see it)
+    cores, blas = len(os.sched_getaffinity(0)), "unknown"
     try:
         from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:   # threadpoolctl absent: report the affinity mask
-        cores = len(os.sched_getaffinity(0))
-    q = inp.q[0, :heads].double().cpu().numpy()
-    k = inp.k[0, :heads].double().cpu().numpy()
-    v = inp.v[0, :heads].double().cpu().numpy()
-    lengths = [w.seqlen]
+        pools = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if pools:
+            cores = max(p.get("num_threads", 1) for p in pools)
+            blas = ", ".join(f"{p.get('internal_api')} {p.get('version')} ({p.get('threading_layer')})"
+                             for p in pools)
+    except Exception:   # threadpoolctl absent: the affinity mask
+        pass
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next(line.split(":", 1)[1].strip() for line in f if line.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
+    return int(cores), blas, model
+
+
+def cpu_baseline(w, inp, n_blocks, seed=0):
+    """The fp64 oracle as it stands, on a bounded seeded sample of the prefill input.
+
+    Sample: the shortest sequence of the batch, routed and worklisted whole
+    (every routing head and query block), and the masked attention of the rows
+    of `n_blocks` of its query blocks (blocks 0, 1, N-1 and seeded random ones;
+    0 = all of them) for every routing head.  The rate counts the selected-tile FLOPs of the
+    attended rows against the attention time plus their share (by rows) of
+    the routing and worklist time."""
+    import numpy as np
+    from oracle import problem as oprob
+    from dynamic_block_sparse_amd import workloads as wk
+    cores, blas, model = _host_info()
+    s = int(np.argmin(inp.lengths))
+    L = inp.lengths[s]
+    q, k, v = (x[0] for x in wk.per_sequence_subset(inp, [s]))
     t0 = time.perf_counter()
-    J, _ = oprob.route([q], [k], lengths, w.block, w.mode, w.qpool, w.share_gqa, w.select, w.k_b,
-                       w.k_min, w.tau_rel, w.forced_first)
+    J, _ = oprob.route([q], [k], [L], w.block, w.mode, w.qpool, w.share_gqa, w.select, w.k_b,
+                       w.k_min, w.tau_rel, w.forced_first, window=w.window, kpool=w.kpool)
     t1 = time.perf_counter()
-    wl = oprob.worklist(J, lengths, w.block, w.mode, heads, w.forced_first, w.k_b + 1)
+    wl = oprob.worklist(J, [L], w.block, w.mode, w.route_heads, w.forced_first,
+                        w.k_b + max(w.window, 1) + int(w.forced_first), window=w.window)
     t2 = time.perf_counter()
-    rows = list(range(len(J)))
+    nq = -(-L // w.block)
+    rng = np.random.default_rng(seed)
+    n_blocks = nq if n_blocks <= 0 else min(n_blocks, nq)
+    pick = {0, 1, nq - 1} if n_blocks >= 3 else set(range(n_blocks))
+    while len(pick) < n_blocks:
+        pick.add(int(rng.integers(0, nq)))
+    table = oprob.row_table([L], w.block, w.mode, w.route_heads)
+    rows = [i for i, (_s, _h, r, _n) in enumerate(table) if r in pick]
     blocks = {i: wl["col_idx"][wl["row_ptr"][i]:wl["row_ptr"][i + 1]].tolist() for i in rows}
-    oprob.attention_rows([q], [k], [v], lengths, w.block, w.mode, w.share_gqa, rows, blocks)
     t3 = time.perf_counter()
-    flops = int(wl["row_ptr"][-1]) * 4 * w.block * w.block * w.head_dim
-    return dict(value=round(flops / (t3 - t0) / 1e12, 6), unit="TFLOP/s", cores=int(cores),
-                kind="oracle",
-                sample=f"{heads} of {w.heads_q} heads of the prefill input, all {len(rows) // heads} "
-                       f"query blocks: route {t1 - t0:.2f}s, worklist {t2 - t1:.2f}s, "
-                       f"masked attention {t3 - t2:.2f}s ({flops / 1e9:.2f} GFLOP of selected tiles)",
-                seconds=round(t3 - t0, 3))
+    oprob.attention_rows([q], [k], [v], [L], w.block, w.mode, w.share_gqa, rows, blocks)
+    t4 = time.perf_counter()
+    hpr = w.group if w.share_gqa else 1
+    tiles = sum(len(blocks[i]) for i in rows)
+    flops = tiles * hpr * 4 * w.block * w.block * w.head_dim
+    share = len(rows) / len(table)
+    secs = (t4 - t3) + share * (t2 - t0)
+    return dict(value=round(flops / secs / 1e12, 6), unit="TFLOP/s", cores=cores, kind="oracle",
+                sample=(f"sequence {s} of {w.name} ({L} tokens, the batch's shortest): routed and "
+                        f"worklisted whole ({len(table)} rows: route {t1 - t0:.2f}s, worklist {t2 - t1:.2f}s), "
+                        f"masked attention of the {len(rows)} rows of {len(pick)} query blocks x "
+                        f"{w.route_heads} routing heads x {hpr} query heads ({t4 - t3:.2f}s, "
+                        f"{flops / 1e9:.2f} GFLOP of selected tiles); rate = those FLOPs / (attention "
+                        f"time + {share:.3f} of the route and worklist time)"),
+                seconds=round(t4 - t0, 3), cpu_model=model, blas=blas)
 
 
 def prefill_flops(st, w):
@@ -247,8 +294,12 @@ def measure_prefill(args, dbs, w, inp, flush):
     _, cold = timed(st, args.steps, 2, flush)
     ms = eager_ms if args.no_graph else graph_timed(st, args.steps, args.warmup)
     visits, flops, eff = prefill_flops(st, w)
-    fwd_ms = spread(cold[2])["median"]
+    # the attention kernel's mean launch time over every timed call, warm and
+    # after a flush (what a kernel trace of the same run averages)
+    fwd_calls = warm[2] + cold[2]
+    fwd_ms = sum(fwd_calls) / len(fwd_calls)
     achieved = flops / (fwd_ms * 1e-3) / 1e12
+    kernel = st.fwd_kernel_name()
     rec = {
         "value": round(flops / (ms * 1e-3) / 1e12, 3),
         "ms_per_step": round(ms, 5),
@@ -257,11 +308,16 @@ def measure_prefill(args, dbs, w, inp, flush):
                    "head_dim": w.head_dim, "block": w.block, "k_b": w.k_b, "select": w.select,
                    "qpool": w.qpool, "tile_visits": visits, "selected_tile_flops": flops,
                    "causal_effective_flops": eff},
-        "roofline": {"bound": "mfma", "kernel": st.fwd_kernel_name(),
+        "roofline": {"bound": "mfma", "kernel": kernel,
                      "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_for("prefill_bf16_kernel") if w is args.headline else None,
-                     "time": "median fwd call, last-level cache flushed before each step"},
+                     "traffic": traffic_for(kernel, w.name),
+                     "algorithmic_flops_per_launch": flops,
+                     "mean_launch_ms": round(fwd_ms, 5),
+                     "time": (f"mean of the {len(fwd_calls)} timed sparse_attn_fwd calls (warm, and after a "
+                              f"last-level cache flush), events on the launch stream; one attention launch "
+                              f"per call" + (" plus the 2 us block-offset kernel of a packed batch"
+                                             if w.varlen else ""))},
         "step": ("eager steps (--no-graph)" if args.no_graph else
                  "HIP graph replay of route + worklist + fwd") +
                 "; eager_ms_per_step: the step launched call by call",
@@ -270,6 +326,7 @@ def measure_prefill(args, dbs, w, inp, flush):
         "stages_ms": {"warm": {k: spread(v) for k, v in zip(("route", "worklist", "fwd"), warm)},
                       "cache_flushed": {k: spread(v) for k, v in zip(("route", "worklist", "fwd"), cold)}},
         "effective_tflops": round(eff / (fwd_ms * 1e-3) / 1e12, 3),
+        "route_worklist_share_of_step": round(1 - fwd_ms / ms, 4) if not args.no_graph else None,
         "worklist_err": int(st.wl.err.item()),
     }
     if w.varlen or w.select == "threshold":
@@ -375,19 +432,24 @@ def measure_decode(args, dbs, wd, dev, flush):
     nnz = int(sd.wl.row_ptr[sd.sz.rows].item())
     kv_bytes = nnz * wd.block * wd.head_dim * 2 * 2
     qo_bytes = 2 * wd.batch * wd.heads_q * wd.head_dim * 2
-    fwd_ms = spread(cold[2])["median"]
+    fwd_calls = warm[2] + cold[2]
+    fwd_ms = sum(fwd_calls) / len(fwd_calls)
     gbs = (kv_bytes + qo_bytes) / (fwd_ms * 1e-3) / 1e9
     route_bytes = wd.batch * wd.heads_kv * (wd.seqlen // wd.block) * wd.head_dim * 4
     rec = {
         "workload": wd.name, "ms_per_step": round(msd, 5), "eager_ms_per_step": round(eager_msd, 5),
         "stages_ms": {"warm": {k: spread(v) for k, v in zip(("route", "worklist", "fwd"), warm)},
                       "cache_flushed": {k: spread(v) for k, v in zip(("route", "worklist", "fwd"), cold)}},
+        "value": round(gbs, 1), "unit": "GB/s",
         "kv_bytes": kv_bytes, "kv_gbs": round(gbs, 1),
-        "roofline": {"bound": "hbm", "kernel": "decode_fused_kernel<4> (4 splits merged in LDS)",
+        "roofline": {"bound": "hbm", "kernel": "decode_fused_kernel<4>",
                      "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4),
-                     "traffic": traffic_for("decode_fused_kernel"),
-                     "time": "median fwd call, last-level cache flushed before each step"},
+                     "traffic": traffic_for("decode_fused_kernel<4>", wd.name),
+                     "algorithmic_bytes_per_launch": kv_bytes + qo_bytes,
+                     "mean_launch_ms": round(fwd_ms, 5),
+                     "time": f"mean of the {len(fwd_calls)} timed sparse_attn_fwd calls (warm, and after a "
+                             f"last-level cache flush), events on the launch stream"},
         "route_summary_gbs": round(route_bytes / (spread(cold[0])["median"] * 1e-3) / 1e9, 1),
     }
     del sd, inp_d
@@ -457,22 +519,20 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode setting")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--dense", action="store_true",
                     help="also time the dense comparison (this library's kernel on a full causal "
                          "worklist, and torch flash-attention SDPA); off by default so that the "
                          "attention kernel's launches in a profile of the default run are the "
                          "sparse ones only")
     ap.add_argument("--no-bwd", action="store_true", help="skip timing the backward pass")
-    ap.add_argument("--cpu-heads", type=int, default=16)
+    ap.add_argument("--cpu-blocks", type=int, default=0,
+                    help="query blocks of the oracle's sample (every routing head of each); "
+                         "0: every query block of the sampled sequence")
     ap.add_argument("--decode-splits", type=int, default=0)
-    ap.add_argument("--workload", choices=[w.name for w in wk.ALL if w.dtype == "bf16"],
-                    default=wk.PREFILL_MHA.name,
-                    help="the prefill setting timed for the JSON line (default: the 8192-token MHA "
-                         "setting); the others reproduce the per-setting measurements")
-    ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all",
-                    help="profiling aid: time one setting only (the JSON line then lacks the other)")
+    ap.add_argument("--workload", choices=[w.name for w in wk.ALL if w.dtype == "bf16"], default=None,
+                    help="time this setting only; it becomes the JSON line's headline")
     ap.add_argument("--no-graph", action="store_true",
                     help="profiling aid: time eager steps only (value then comes from eager steps)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -500,43 +560,61 @@ def main():
         log(f"copy calibration: 5 copies of {args.copy_calibration} MiB")
     # 512 MB rewritten between timed steps: twice the last-level cache
     flush = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
-    args.headline = wk.PREFILL_MHA
-    w = wk.BY_NAME[args.workload]
-    if w.mode == "decode":
-        args.only = "decode"
+
+    # the headline: the largest prefill setting that fits one GPU, unless one
+    # setting is asked for by name
+    if args.workload:
+        head = wk.BY_NAME[args.workload]
+        others = []
+    else:
+        head = wk.VARLEN
+        others = [wk.PREFILL_MHA, wk.PREFILL_GQA] + ([] if args.no_decode else [wk.DECODE])
     out = {"metric": METRIC}
-    inp = None
-    if args.only != "decode":
-        if w is not wk.PREFILL_MHA:
-            args.headline = w
-        log(f"generating {w.name}")
-        inp = wk.make_inputs(w, dev)
-        rec = measure_prefill(args, dbs, w, inp, flush)
-        out.update({"value": rec.pop("value"), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-                    "warmup": args.warmup, "ms_per_step": rec.pop("ms_per_step"),
-                    "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+    common = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+              "scaling": "weak", "vs_baseline": None, "dtype": "bf16"}
+    cpu_inp = None
+    if head.mode == "decode":
+        rec = measure_decode(args, dbs, head, dev, flush)
+        out.update({"value": rec.pop("value"), "unit": rec.pop("unit"), **common,
+                    "ms_per_step": rec.pop("ms_per_step"),
+                    "data": "synthetic (seeded N(0,1) Q/K/V with planted hot blocks; no dataset)",
+                    "config": {"workload": head.name}})
+        out.update(rec)
+    else:
+        log(f"generating {head.name}")
+        inp = wk.make_inputs(head, dev)
+        rec = measure_prefill(args, dbs, head, inp, flush)
+        out.update({"value": rec.pop("value"), "unit": "TFLOP/s", **common,
+                    "ms_per_step": rec.pop("ms_per_step"),
                     "data": "synthetic (seeded N(0,1) Q/K/V with planted relevance; no dataset)"})
         out.update(rec)
         if args.dense:
-            log(f"timing dense causal attention on {w.name}")
-            dense = measure_dense(args, dbs, w, inp, flush, out["stages_ms"]["cache_flushed"]["fwd"]["median"])
+            log(f"timing dense causal attention on {head.name}")
+            dense = measure_dense(args, dbs, head, inp, flush, out["stages_ms"]["cache_flushed"]["fwd"]["median"])
             if dense is not None:
                 out["dense"] = dense
-    if not args.no_decode and args.only != "prefill":
-        wd = w if w.mode == "decode" else wk.DECODE
-        rec = measure_decode(args, dbs, wd, dev, flush)
-        if args.only == "decode":
-            out.update({"value": rec["kv_gbs"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-                        "warmup": args.warmup, "ms_per_step": rec["ms_per_step"],
-                        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-                        "dtype": "bf16", "data": "synthetic (seeded N(0,1) Q/K/V; no dataset)",
-                        "config": {"workload": wd.name}})
-        out["decode"] = rec
+        if not args.no_cpu:
+            cpu_inp = inp
+        else:
+            del inp
+        torch.cuda.empty_cache()
+    settings = {}
+    for w in others:
+        if w.mode == "decode":
+            settings[w.name] = measure_decode(args, dbs, w, dev, flush)
+        else:
+            log(f"generating {w.name}")
+            inp_w = wk.make_inputs(w, dev)
+            settings[w.name] = measure_prefill(args, dbs, w, inp_w, flush)
+            del inp_w
+        torch.cuda.empty_cache()
+    if settings:
+        out["settings"] = settings
     del flush
     torch.cuda.empty_cache()
-    if not args.no_cpu and inp is not None and w is wk.PREFILL_MHA:
-        log(f"timing the oracle on {args.cpu_heads} heads")
-        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_heads)
+    if cpu_inp is not None:
+        log(f"timing the oracle on a sample of {head.name}")
+        out["cpu_baseline"] = cpu_baseline(head, cpu_inp, args.cpu_blocks)
     print(json.dumps(out), flush=True)
 
 
