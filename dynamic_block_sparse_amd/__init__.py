@@ -37,7 +37,8 @@ SA_FORCE_CURRENT, SA_FORCE_FIRST = 1, 2
 
 EXPORTED = ["sparse_attn_sizes", "sparse_attn_workspace_size", "sparse_attn_route",
             "sparse_attn_build_worklist", "sparse_attn_fwd", "sparse_attn_append_kv",
-            "sparse_attn_bwd", "sparse_attn_status_string"]
+            "sparse_attn_bwd", "sparse_attn_status_string", "sparse_attn_build_worklist_noalloc"]
+NOALLOC_SCRATCH_BYTES = 32 << 20   # SA_NOALLOC_SCRATCH_BYTES
 
 
 class SAError(RuntimeError):
@@ -92,6 +93,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sparse_attn_route.restype = ctypes.c_int
     lib.sparse_attn_build_worklist.argtypes = [P, R, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]
     lib.sparse_attn_build_worklist.restype = ctypes.c_int
+    lib.sparse_attn_build_worklist_noalloc.argtypes = [P, R, vp, vp, vp, i64, vp, vp, vp, vp]
+    lib.sparse_attn_build_worklist_noalloc.restype = ctypes.c_int
     lib.sparse_attn_fwd.argtypes = [P, R, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
     lib.sparse_attn_fwd.restype = ctypes.c_int
     lib.sparse_attn_status_string.argtypes = [ctypes.c_int]
@@ -395,6 +398,31 @@ def build_worklist(prob: Problem, cfg: RouteConfig, J: torch.Tensor, out: Option
         ctypes.byref(p), ctypes.byref(c), _ptr(J), _ptr(out.row_ptr), _ptr(out.col_idx),
         out.col_idx.numel(), _ptr(out.row_perm), _ptr(out.bucket_ptr), _ptr(out.err),
         _ptr(ws), wsb, _stream(dev)))
+    return out
+
+
+def build_worklist_noalloc(prob: Problem, cfg: RouteConfig, J: torch.Tensor, out: Worklist) -> Worklist:
+    """sparse_attn_build_worklist_noalloc: the worklist of build_worklist into the
+    caller's preallocated `out` (alloc_worklist), with the library's static device
+    scratch in place of a workspace; allocates nothing (err is cleared by a fill)."""
+    lib = load_library()
+    rows = sizes(prob, cfg).rows
+    _require("build_worklist_noalloc", "J", J, (rows, cfg.k_b), torch.int32)
+    dev = J.device
+    _require_problem("build_worklist_noalloc", prob, dev)
+    _require_worklist("build_worklist_noalloc", prob, cfg, out, dev)
+    _on_device("build_worklist_noalloc", dev, J=J, row_ptr=out.row_ptr, col_idx=out.col_idx,
+               row_perm=out.row_perm, bucket_ptr=out.bucket_ptr, err=out.err, cu_seqlens=prob.cu_seqlens,
+               block_table=prob.block_table)
+    need = workspace_size(prob, cfg, 1)
+    if need > NOALLOC_SCRATCH_BYTES:
+        raise ValueError(f"build_worklist_noalloc: the problem needs {need} bytes of scratch, more than the "
+                         f"{NOALLOC_SCRATCH_BYTES} the library holds ({rows} rows)")
+    out.err.zero_()
+    p, c = prob.to_c(), cfg.to_c()
+    _check("sparse_attn_build_worklist_noalloc", lib.sparse_attn_build_worklist_noalloc(
+        ctypes.byref(p), ctypes.byref(c), _ptr(J), _ptr(out.row_ptr), _ptr(out.col_idx),
+        out.col_idx.numel(), _ptr(out.row_perm), _ptr(out.bucket_ptr), _ptr(out.err), _stream(dev)))
     return out
 
 

@@ -1,9 +1,12 @@
 // C-ABI entry points: host-side validation, geometry, workspace carving, launches.
-// Nothing here allocates, synchronises or keeps state between calls.
+// Nothing here allocates or synchronises.  The only state kept between calls
+// is the per-device address of the static scratch that the no-allocation
+// worklist entry point uses in place of a workspace argument.
 #include <math.h>
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 #include "kernels.h"
@@ -219,6 +222,63 @@ int prep_cu_blocks(Plan& pl, void* ws, hipStream_t st) {
 }  // namespace
 }  // namespace sa
 
+// Scratch of the no-allocation worklist build: one copy per GPU, held until
+// the process ends.  In host code `scratch` names a host-side stand-in, not a
+// device address; kernels get the device address that hipGetSymbolAddress
+// returns for the current device (noalloc_scratch below), never the name.
+static __device__ __align__(256) unsigned char scratch[SA_NOALLOC_SCRATCH_BYTES];
+
+namespace sa {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch`, per device
+
+// The current device's copy of the scratch: looked up once per device (with
+// that device current) and kept.
+int noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SA_OK;
+}
+
+// Worklist build into a given workspace (the caller's, or the static scratch).
+int build_worklist_impl(const sa_problem* p, const sa_route_cfg* rc, const int32_t* J, int32_t* row_ptr,
+                        int32_t* col_idx, int64_t nnz_cap, int32_t* row_perm, int32_t* bucket_ptr,
+                        int32_t* err, void* ws, size_t ws_bytes, void* stream) {
+  Plan pl;
+  int st = validate(p, rc, &pl);
+  if (st != SA_OK) return st;
+  if (!J || !row_ptr || !col_idx || !row_perm || !bucket_ptr || !err || !ws)
+    return SA_ERR_INVALID_ARG;
+  if (nnz_cap < pl.nnz_cap) return SA_ERR_WORKSPACE;
+  if (ws_bytes < ws_size(pl, 1, 1)) return SA_ERR_WORKSPACE;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if ((st = prep_cu_blocks(pl, ws, hs)) != SA_OK) return st;
+  unsigned char* w = reinterpret_cast<unsigned char*>(ws) + ws_cu_blocks(pl);
+  WorklistBufs b;
+  b.J = J;
+  b.row_ptr = row_ptr;
+  b.col_idx = col_idx;
+  b.row_perm = row_perm;
+  b.bucket_ptr = bucket_ptr;
+  b.err = err;
+  b.tmp_cols = reinterpret_cast<int32_t*>(w);
+  b.tmp_len = reinterpret_cast<int32_t*>(w + align_up((size_t)pl.g.rows * kMaxWidth * sizeof(int32_t)));
+  return launch_worklist(pl.g, *rc, pl.width_max, pl.n_buckets, b, hs);
+}
+
+}  // namespace
+}  // namespace sa
+
 using namespace sa;
 
 extern "C" {
@@ -372,26 +432,24 @@ int sparse_attn_build_worklist(const sa_problem* p, const sa_route_cfg* rc, cons
                                int32_t* row_ptr, int32_t* col_idx, int64_t nnz_cap,
                                int32_t* row_perm, int32_t* bucket_ptr, int32_t* err, void* ws,
                                size_t ws_bytes, void* stream) {
+  return build_worklist_impl(p, rc, J, row_ptr, col_idx, nnz_cap, row_perm, bucket_ptr, err, ws, ws_bytes,
+                             stream);
+}
+
+int sparse_attn_build_worklist_noalloc(const sa_problem* p, const sa_route_cfg* rc, const int32_t* J,
+                                       int32_t* row_ptr, int32_t* col_idx, int64_t nnz_cap,
+                                       int32_t* row_perm, int32_t* bucket_ptr, int32_t* err,
+                                       void* stream) {
   Plan pl;
-  int st = validate(p, rc, &pl);
+  const int st = validate(p, rc, &pl);
   if (st != SA_OK) return st;
-  if (!J || !row_ptr || !col_idx || !row_perm || !bucket_ptr || !err || !ws)
-    return SA_ERR_INVALID_ARG;
-  if (nnz_cap < pl.nnz_cap) return SA_ERR_WORKSPACE;
-  if (ws_bytes < ws_size(pl, 1, 1)) return SA_ERR_WORKSPACE;
-  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  if ((st = prep_cu_blocks(pl, ws, hs)) != SA_OK) return st;
-  unsigned char* w = reinterpret_cast<unsigned char*>(ws) + ws_cu_blocks(pl);
-  WorklistBufs b;
-  b.J = J;
-  b.row_ptr = row_ptr;
-  b.col_idx = col_idx;
-  b.row_perm = row_perm;
-  b.bucket_ptr = bucket_ptr;
-  b.err = err;
-  b.tmp_cols = reinterpret_cast<int32_t*>(w);
-  b.tmp_len = reinterpret_cast<int32_t*>(w + align_up((size_t)pl.g.rows * kMaxWidth * sizeof(int32_t)));
-  return launch_worklist(pl.g, *rc, pl.width_max, pl.n_buckets, b, hs);
+  const size_t need = ws_size(pl, 1, 1);
+  if (need > SA_NOALLOC_SCRATCH_BYTES) return SA_ERR_WORKSPACE;   // more rows than the scratch holds
+  void* ws = nullptr;
+  const int sst = noalloc_scratch(&ws);
+  if (sst != SA_OK) return sst;
+  return build_worklist_impl(p, rc, J, row_ptr, col_idx, nnz_cap, row_perm, bucket_ptr, err, ws,
+                             SA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int sparse_attn_fwd(const sa_problem* p, const sa_route_cfg* rc, const int32_t* row_ptr,

@@ -38,9 +38,10 @@
  * Conventions shared by every call
  *   - Pointers marked (device) are device memory owned by the caller; pointers
  *     marked (host) are host memory read during the call only.  The library
- *     allocates nothing, keeps no global state, never synchronises the
- *     stream, and enqueues all work on `stream` (a hipStream_t; NULL is the
- *     null stream).  Calls are reentrant.
+ *     allocates nothing, never synchronises the stream, and enqueues all work
+ *     on `stream` (a hipStream_t; NULL is the null stream).  It keeps no
+ *     global state except the static scratch of the no-allocation worklist
+ *     build (below); every other call is reentrant.
  *   - Host-detectable problems (bad sizes, unsupported shapes, null pointers,
  *     workspace too small) return a nonzero status before anything is
  *     enqueued.  Data-dependent problems found on the device (block ids out of
@@ -218,6 +219,31 @@ int sparse_attn_build_worklist(const sa_problem* p, const sa_route_cfg* rc, cons
                                int32_t* row_ptr, int32_t* col_idx, int64_t nnz_cap,
                                int32_t* row_perm, int32_t* bucket_ptr, int32_t* err, void* ws,
                                size_t ws_bytes, void* stream);
+
+/* Bytes of the static device scratch behind sparse_attn_build_worklist_noalloc
+ * (one copy per GPU the library runs on, held until the process ends). */
+#define SA_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* The worklist build of sparse_attn_build_worklist without a workspace
+ * argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  It
+ * calls no allocating routine: the workspace the build needs
+ * (sparse_attn_workspace_size(p, rc, 1, 0) bytes: per row its sorted ids and
+ * length, for a packed batch the block offsets) is carved from a static
+ * device array of SA_NOALLOC_SCRATCH_BYTES bytes, the one of the device that
+ * is current when the call is made (stream must belong to that device; the
+ * array's address is looked up once per device, on its first call there).
+ * Arguments, outputs and results are those of sparse_attn_build_worklist,
+ * bit for bit.  Returns SA_ERR_WORKSPACE when the problem needs more than
+ * SA_NOALLOC_SCRATCH_BYTES (about 64K worklist rows), SA_ERR_HIP when the
+ * scratch cannot be located.  Every call on one GPU shares that GPU's
+ * scratch and overwrites it (nothing in it needs to start at zero): calls
+ * that can overlap on one GPU (different streams, or host threads) race and
+ * must be ordered by the caller. */
+int sparse_attn_build_worklist_noalloc(const sa_problem* p, const sa_route_cfg* rc, const int32_t* J,
+                                       int32_t* row_ptr, int32_t* col_idx, int64_t nnz_cap,
+                                       int32_t* row_perm, int32_t* bucket_ptr, int32_t* err,
+                                       void* stream);
 
 /* Attention over the worklist ([P2] Eq 2-5; [P3] "sparse softmax numerics").
  *   q, k, v     (device) inputs; o (device) output, same layout and dtype as q

@@ -219,3 +219,20 @@ def test_bwd_validates_before_any_launch(lib):
     assert call(_prob(dtype="f32")) == dbs.SA_ERR_UNSUPPORTED           # fp32 needs d = 64
     assert call(ok, ptr=None) == dbs.SA_ERR_INVALID_ARG
     assert call(ok, ws_bytes=need - 1) == dbs.SA_ERR_WORKSPACE
+
+
+def test_noalloc_worklist_rejects_sizes_beyond_scratch(lib):
+    # 128 heads x 1024 blocks = 131072 rows need 64 MiB of worklist scratch: refused on
+    # the host (SA_ERR_WORKSPACE) before the scratch or any pointer is touched
+    p = _prob(heads_q=128, heads_kv=128, seqlen=65536).to_c()
+    c = dbs.RouteConfig(k_b=16).to_c()
+    need = lib.sparse_attn_workspace_size(ctypes.byref(p), ctypes.byref(c), 1, 0)
+    assert need > dbs.NOALLOC_SCRATCH_BYTES
+    st = lib.sparse_attn_build_worklist_noalloc(ctypes.byref(p), ctypes.byref(c), None, None, None, 0, None,
+                                                None, None, None)
+    assert st == dbs.SA_ERR_WORKSPACE
+    # an invalid problem is still reported as such first
+    bad = _prob(block=32).to_c()
+    st = lib.sparse_attn_build_worklist_noalloc(ctypes.byref(bad), ctypes.byref(c), None, None, None, 0, None,
+                                                None, None, None)
+    assert st == dbs.SA_ERR_UNSUPPORTED
