@@ -14,7 +14,7 @@ head, tile) visit of the worklist) divided by the step's time, the step
 replayed as one HIP graph, in TFLOP/s.  The attention kernel alone is reported
 in `roofline` against the bf16 dense MFMA peak: its mean launch time over every
 timed call (events on the stream the library launches on), warm and after a
-last-level cache flush (a 512 MB buffer rewritten outside the events).
+last-level cache flush (a 512 MB buffer read outside the events).
 
 The other settings are timed the same way and reported under `settings`, each
 with its own `roofline`: the 8192-token MHA prefill (B=1, H=16, k_b=16), the
@@ -142,9 +142,11 @@ def timed(stepper, steps, warmup, flush=None):
     """Eager steps, each call bracketed by events on the current stream.
 
     With `flush` (a device buffer larger than the 256 MB last-level cache) the
-    buffer is rewritten before every step, outside the events, so no step
-    finds the previous step's K/V in cache; the mean over the loop then
-    includes the flushes and only the per-call times are meaningful."""
+    buffer is read (summed) before every step, outside the events, so no step
+    finds the previous step's inputs in cache.  A read leaves no dirty lines,
+    whose write-back would otherwise land on the first call after it.  The
+    mean over the loop then includes the flushes and only the per-call times
+    are meaningful."""
     import torch
     for _ in range(warmup):
         stepper.step()
@@ -155,7 +157,7 @@ def timed(stepper, steps, warmup, flush=None):
     start.record()
     for i in range(steps):
         if flush is not None:
-            flush.add_(1)
+            flush.sum()
         stepper.step(evs[i])
     end.record()
     torch.cuda.synchronize()
@@ -397,7 +399,7 @@ def measure_dense(args, dbs, w, inp, flush, sparse_fwd_ms):
             for fn, acc in ((st.fwd, ours),
                             (lambda: torch.nn.functional.scaled_dot_product_attention(
                                 inp.q, inp.k, inp.v, is_causal=True), flash)):
-                flush.add_(1.0)
+                flush.sum()
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record()
                 fn()
@@ -558,7 +560,7 @@ def main():
         torch.cuda.synchronize()
         del a, b
         log(f"copy calibration: 5 copies of {args.copy_calibration} MiB")
-    # 512 MB rewritten between timed steps: twice the last-level cache
+    # 512 MB read between timed steps: twice the last-level cache
     flush = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
 
     # the headline: the largest prefill setting that fits one GPU, unless one

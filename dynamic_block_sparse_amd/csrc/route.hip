@@ -427,13 +427,46 @@ __global__ void __launch_bounds__(256) route_score_kernel(Geom g, sa_route_cfg r
 //   3. picks = keys > T plus the lowest-id keys == T, written in ascending id
 //      order from ballot prefix counts; forced blocks first, -1 padding last.
 // Empty key slots hold 0, which no threshold with a set bit counts.
+// The J row of a selection: forced ids first (the sink when outside the
+// window, then the window ascending), then the picks in ascending id order
+// (keys above thr, and the take_eq lowest-id keys equal to it; every valid
+// key when take_all), then -1.  key[e] is candidate lane + 64 e's
+// order-preserving key.
 template <int E>
-__global__ void __launch_bounds__(64) route_select_kernel(Geom g, sa_route_cfg rc, const float* __restrict__ scores,
-                                                          int32_t* __restrict__ J) {
-  const int lane = threadIdx.x;
-  const int64_t row = blockIdx.x;
-  const RouteRow w = route_row(g, rc, row);
-  const float* srow = scores + row * (int64_t)g.max_blocks;
+__device__ __forceinline__ void emit_row(const sa_route_cfg& rc, const RouteRow& w, int64_t row, const uint32_t (&key)[E],
+                                         int dsel, bool take_all, uint32_t thr, int take_eq,
+                                         int32_t* __restrict__ J, int lane) {
+  int32_t* jrow = J + row * rc.k_b;
+  if (lane <= w.cur - w.lo) {
+    const int k0 = (w.ff && w.lo > 0) ? 1 : 0;
+    if (lane == 0 && k0) jrow[0] = 0;
+    jrow[k0 + lane] = w.lo + lane;
+  }
+  if (dsel > 0) {
+    const uint64_t below = (1ull << lane) - 1ull;
+    int pos = 0, eq_seen = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int i = lane + 64 * e;
+      const bool valid = i < w.nc;
+      const bool eq = !take_all && valid && key[e] == thr;
+      const uint64_t beq = __ballot(eq);
+      const int eq_rank = eq_seen + __popcll(beq & below);
+      const bool take = valid && (take_all || key[e] > thr || (eq && eq_rank < take_eq));
+      const uint64_t bt = __ballot(take);
+      if (take) jrow[w.nforced + pos + __popcll(bt & below)] = w.start + i;
+      pos += __popcll(bt);
+      eq_seen += __popcll(beq);
+    }
+  }
+  for (int i = w.nforced + dsel + lane; i < rc.k_b; i += 64) jrow[i] = -1;
+}
+
+// The selection of one row by one wavefront (lane = its lane id); srow holds
+// the row's candidate scores (global memory or LDS).
+template <int E, typename Scores>
+__device__ __forceinline__ void select_row(const sa_route_cfg& rc, const RouteRow& w, int64_t row, Scores srow,
+                                           int32_t* __restrict__ J, int lane) {
   // Every load is issued unconditionally (clamped to a valid slot) and the
   // guard applies to the value: a load under a per-slot branch is waited for
   // before the next branch, which serialises E memory round trips.
@@ -491,32 +524,148 @@ __global__ void __launch_bounds__(64) route_select_kernel(Geom g, sa_route_cfg r
     take_eq = dsel - (t == 0xffffffffu ? 0 : count_ge(t + 1u));
   }
 
-  int32_t* jrow = J + row * rc.k_b;
-  // forced ids: the sink (when outside the window), then the window ascending
-  if (lane <= w.cur - w.lo) {
-    const int k0 = (w.ff && w.lo > 0) ? 1 : 0;
-    if (lane == 0 && k0) jrow[0] = 0;
-    jrow[k0 + lane] = w.lo + lane;
+  emit_row<E>(rc, w, row, key, dsel, take_all, thr, take_eq, J, lane);
+}
+
+template <int E>
+__global__ void __launch_bounds__(64) route_select_kernel(Geom g, sa_route_cfg rc, const float* __restrict__ scores,
+                                                          int32_t* __restrict__ J) {
+  const int64_t row = blockIdx.x;
+  const RouteRow w = route_row(g, rc, row);
+  select_row<E>(rc, w, row, scores + row * (int64_t)g.max_blocks, J, (int)threadIdx.x);
+}
+
+// ---------------------------------------------------------------------------
+// Decode routing in one pass per row ([P2] §3.1: the summaries are cache
+// state, and a decode step's router scans each stored summary of the row once;
+// [P2] §2.2: decode cost is reading history).  One workgroup of 256 threads per
+// (sequence, routing head), so that the rows of a decode batch (512 at 64
+// sequences x 8 KV heads, ~130 registers a lane) are resident at once: the mean of the row's query heads' queries (one
+// each), then every candidate summary dotted with it, LPC lanes per summary
+// with 16-byte loads, each wavefront keeping U loads in flight (every slot is
+// refilled as soon as it is consumed); the scores stay in LDS.  Top-k rows
+// are selected by the whole workgroup (a radix select over the scores'
+// order-preserving keys), threshold rows by select_row; both emit the same
+// picks as route_select_kernel.
+template <typename T, int D, int E>
+__global__ void __launch_bounds__(256) route_decode_kernel(Geom g, sa_route_cfg rc, const T* __restrict__ q,
+                                                           const float* __restrict__ summ,
+                                                           int32_t* __restrict__ J) {
+  constexpr int NWV = 4, U = 16;
+  constexpr int LPC = D / 4, CPL = kWave / LPC;   // lanes per candidate, candidates per wave load
+  extern __shared__ float smem[];
+  float* const qbar = smem;                        // [D]
+  float* const sc = smem + D;                      // [max_blocks] candidate scores
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int64_t row = blockIdx.x;
+  const RouteRow w = route_row(g, rc, row);
+  const int cl = lane % LPC, cw = lane / LPC;
+  const float* cbase = summ + sum_offset(g, w.ri.s, w.kvh, w.ri.blk0, w.start) + cl * 4;
+  const int nc = w.nc, last = max(nc - 1, 0);
+  constexpr int kPerIter = NWV * U * CPL;          // candidates per workgroup iteration
+  // candidate of load u in iteration it for this lane
+  auto cand = [&](int it, int u) { return it * kPerIter + (u * NWV + wave) * CPL + cw; };
+  // U loads in flight per wavefront: slot u is consumed and at once refilled
+  // with its candidate of the next iteration (unconditional, clamped loads);
+  // the first ones go out before the query pooling
+  auto load = [&](int it, int u) {
+    return *reinterpret_cast<const f32x4*>(cbase + (int64_t)min(cand(it, u), last) * D);
+  };
+  const int iters = (nc + kPerIter - 1) / kPerIter;
+  f32x4 buf[U];
+  if (iters > 0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) buf[u] = load(0, u);
   }
-  if (dsel > 0) {
-    const uint64_t below = (1ull << lane) - 1ull;
-    int pos = 0, eq_seen = 0;
+  if (tid < D) {   // mean over the row's query heads, summed in head order
+    float acc = 0.f;
+    for (int hh = 0; hh < g.hpr; ++hh) acc += to_f32<T>(q[q_offset(g, w.ri.s, w.h0 + hh, 0, 0) + tid]);
+    qbar[tid] = acc / (float)g.hpr;
+  }
+  __syncthreads();
+  const f32x4 qv = *reinterpret_cast<const f32x4*>(qbar + cl * 4);
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const f32x4 cv = buf[u];
+      buf[u] = load(it + 1 < iters ? it + 1 : it, u);
+      float x = qv[0] * cv[0] + qv[1] * cv[1] + qv[2] * cv[2] + qv[3] * cv[3];
+      static_assert(LPC == 32 || LPC == 16, "lanes per candidate");
+      x = LPC == 32 ? half_sum(x) : __uint_as_float(row16_reduce(__float_as_uint(x), OpAddF{}));
+      const int c = cand(it, u);
+      if (cl == 0 && c < nc) sc[c] = x;
+    }
+  }
+  __syncthreads();
+  if (rc.select != SA_SELECT_TOPK) {   // Eq 7's threshold count: the one-wavefront selection
+    if (wave == 0) select_row<E>(rc, w, row, (const float*)sc, J, lane);
+    return;
+  }
+  // Top-k: the D-th largest order-preserving key T found by the whole
+  // workgroup, one 8-bit digit at a time from the top: each pass histograms
+  // the digit over the keys that match the digits found so far, and
+  // wavefront 0 finds the bin holding the need-th largest of them.  Then
+  // need = the number of keys equal to T to take (the lowest ids).
+  __shared__ uint32_t hist[256];
+  __shared__ int pick[2];
+  const int dsel = min(max(rc.k_b - w.nforced, 0), nc);
+  const bool take_all = dsel == nc;
+  uint32_t thr = 0u;
+  int need = dsel;
+  if (!take_all && dsel > 0) {   // uniform over the workgroup
+    uint32_t pmask = 0u;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      hist[tid] = 0u;
+      __syncthreads();
+      for (int i = tid; i < nc; i += 256) {
+        const uint32_t key = order_key(sc[i]);
+        if ((key & pmask) == thr) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (wave == 0) {
+        // lane l holds bins 255 - 4l .. 252 - 4l (the largest digits first)
+        int c[4], tot = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          c[j] = (int)hist[255 - 4 * lane - j];
+          tot += c[j];
+        }
+        const int incl = wave_incl_scan_i(tot), excl = incl - tot;
+        const uint64_t reach = __ballot(incl >= need);   // some lane reaches need: need <= matching keys
+        const int owner = __ffsll((unsigned long long)reach) - 1;
+        if (lane == owner) {
+          int run = excl, bin = 255 - 4 * lane;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (run + c[j] >= need) {
+              bin = 255 - 4 * lane - j;
+              break;
+            }
+            run += c[j];
+          }
+          pick[0] = bin;
+          pick[1] = need - run;
+        }
+      }
+      __syncthreads();
+      thr |= (uint32_t)pick[0] << shift;
+      need = pick[1];
+      pmask |= 255u << shift;
+    }
+  }
+  if (wave == 0) {
+    uint32_t key[E];
+    const int lastc = max(nc - 1, 0);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int i = lane + 64 * e;
-      const bool valid = i < w.nc;
-      const bool eq = !take_all && valid && key[e] == thr;
-      const uint64_t beq = __ballot(eq);
-      const int eq_rank = eq_seen + __popcll(beq & below);
-      const bool take = valid && (take_all || key[e] > thr || (eq && eq_rank < take_eq));
-      const uint64_t bt = __ballot(take);
-      if (take) jrow[w.nforced + pos + __popcll(bt & below)] = w.start + i;
-      pos += __popcll(bt);
-      eq_seen += __popcll(beq);
+      key[e] = order_key(sc[min(i, lastc)]) & (i < nc ? 0xffffffffu : 0u);
     }
+    emit_row<E>(rc, w, row, key, dsel, take_all, thr, need, J, lane);
   }
-  for (int i = w.nforced + dsel + lane; i < rc.k_b; i += 64) jrow[i] = -1;
 }
+
+size_t route_decode_smem_bytes(const Geom& g) { return (size_t)(g.d + std::max(g.max_blocks, 1)) * sizeof(float); }
 
 // ---------------------------------------------------------------------------
 int launch_summary(const Geom& g, int dtype, const void* k, float* summ, int slots, const void* q,
@@ -555,6 +704,32 @@ size_t route_qbar_bytes(const Geom& g, int qpool) {
 
 int launch_select(const Geom& g, const sa_route_cfg& rc, const float* scores, int32_t* J, hipStream_t st);
 
+template <typename T, int D>
+int launch_route_decode_t(const Geom& g, const sa_route_cfg& rc, const T* q, const float* summ, int32_t* J,
+                          hipStream_t st) {
+  // keys per lane of the selection: the smallest power of two with 64 E >= max_blocks
+  const dim3 grid((unsigned)g.rows);
+  const size_t smem = route_decode_smem_bytes(g);
+  const int mb = std::max(g.max_blocks, 1);
+  if (mb <= 128) route_decode_kernel<T, D, 2><<<grid, 256, smem, st>>>(g, rc, q, summ, J);
+  else if (mb <= 256) route_decode_kernel<T, D, 4><<<grid, 256, smem, st>>>(g, rc, q, summ, J);
+  else if (mb <= 512) route_decode_kernel<T, D, 8><<<grid, 256, smem, st>>>(g, rc, q, summ, J);
+  else if (mb <= 1024) route_decode_kernel<T, D, 16><<<grid, 256, smem, st>>>(g, rc, q, summ, J);
+  else if (mb <= 2048) route_decode_kernel<T, D, 32><<<grid, 256, smem, st>>>(g, rc, q, summ, J);
+  else if (mb <= 4096) route_decode_kernel<T, D, 64><<<grid, 256, smem, st>>>(g, rc, q, summ, J);
+  else route_decode_kernel<T, D, 128><<<grid, 256, smem, st>>>(g, rc, q, summ, J);
+  return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
+
+int launch_route_decode(const Geom& g, const sa_route_cfg& rc, int dtype, const void* q, const float* summ,
+                        int32_t* J, hipStream_t st) {
+  if (dtype == SA_BF16)
+    return g.d == 128 ? launch_route_decode_t<__bf16, 128>(g, rc, (const __bf16*)q, summ, J, st)
+                      : launch_route_decode_t<__bf16, 64>(g, rc, (const __bf16*)q, summ, J, st);
+  return g.d == 128 ? launch_route_decode_t<float, 128>(g, rc, (const float*)q, summ, J, st)
+                    : launch_route_decode_t<float, 64>(g, rc, (const float*)q, summ, J, st);
+}
+
 int launch_route(const Geom& g, const sa_route_cfg& rc, int dtype, const void* q,
                  const float* summ, const float* qbar, float* scores, int32_t* J, hipStream_t st) {
   if (g.rows <= 0) return SA_OK;
@@ -577,6 +752,7 @@ int launch_route(const Geom& g, const sa_route_cfg& rc, int dtype, const void* q
     if (hipGetLastError() != hipSuccess) return SA_ERR_HIP;
     return launch_select(g, rc, scores, J, st);
   }
+  if (g.mode == SA_DECODE && rc.qpool == SA_POOL_MEAN) return launch_route_decode(g, rc, dtype, q, summ, J, st);
   const int chunk = g.mode == SA_DECODE ? kDecodeChunk : std::max(g.max_blocks, 1);
   const int chunks = (std::max(g.max_blocks, 1) + chunk - 1) / chunk;
   dim3 grid((unsigned)g.rows, (unsigned)chunks);
