@@ -37,7 +37,8 @@ SA_FORCE_CURRENT, SA_FORCE_FIRST = 1, 2
 
 EXPORTED = ["sparse_attn_sizes", "sparse_attn_workspace_size", "sparse_attn_route",
             "sparse_attn_build_worklist", "sparse_attn_fwd", "sparse_attn_append_kv",
-            "sparse_attn_bwd", "sparse_attn_status_string", "sparse_attn_build_worklist_noalloc"]
+            "sparse_attn_bwd", "sparse_attn_status_string", "sparse_attn_build_worklist_noalloc",
+            "sparse_attn_fwd_dense"]
 NOALLOC_SCRATCH_BYTES = 32 << 20   # SA_NOALLOC_SCRATCH_BYTES
 
 
@@ -97,6 +98,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sparse_attn_build_worklist_noalloc.restype = ctypes.c_int
     lib.sparse_attn_fwd.argtypes = [P, R, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
     lib.sparse_attn_fwd.restype = ctypes.c_int
+    lib.sparse_attn_fwd_dense.argtypes = [P, R, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.sparse_attn_fwd_dense.restype = ctypes.c_int
     lib.sparse_attn_status_string.argtypes = [ctypes.c_int]
     lib.sparse_attn_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -453,6 +456,34 @@ def fwd(prob: Problem, cfg: RouteConfig, wl: Worklist, q, k, v, o=None, lse=None
     _check("sparse_attn_fwd", lib.sparse_attn_fwd(
         ctypes.byref(p), ctypes.byref(c), _ptr(wl.row_ptr), _ptr(wl.col_idx), _ptr(wl.row_perm),
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), num_splits, _ptr(ws), wsb, _stream(dev)))
+    return o, lse
+
+
+def fwd_dense(prob: Problem, cfg: RouteConfig, q, k, v, o=None, lse=None, want_lse: bool = True,
+              workspace: Optional[torch.Tensor] = None):
+    """sparse_attn_fwd_dense: dense causal attention with the sparse kernels
+    (every query block attends every earlier key block); returns (O, LSE or None)."""
+    lib = load_library()
+    dt, qs, kvs = _dtype_of(prob), q_shape(prob), kv_shape(prob)
+    _require("fwd_dense", "q", q, qs, dt)
+    dev = q.device
+    _require_problem("fwd_dense", prob, dev)
+    _require("fwd_dense", "k", k, kvs, dt, dev)
+    _require("fwd_dense", "v", v, kvs, dt, dev)
+    if o is None:
+        o = torch.empty_like(q)
+    _require("fwd_dense", "o", o, qs, dt, dev)
+    if lse is None and want_lse:
+        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
+    if lse is not None:
+        _require("fwd_dense", "lse", lse, qs[:-1], torch.float32, dev)
+    _on_device("fwd_dense", dev, q=q, k=k, v=v, o=o, lse=lse, cu_seqlens=prob.cu_seqlens)
+    p, c = prob.to_c(), cfg.to_c()
+    wsb = workspace_size(prob, cfg, 2)
+    ws = _use_workspace("fwd_dense", workspace, wsb, dev)
+    _check("sparse_attn_fwd_dense", lib.sparse_attn_fwd_dense(
+        ctypes.byref(p), ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(ws), wsb,
+        _stream(dev)))
     return o, lse
 
 

@@ -91,6 +91,17 @@ __device__ __forceinline__ int64_t xcd_schedule(int64_t b, int64_t rows, int G) 
   return base + (b % 8) * G + (b / 8) % G;
 }
 
+// The worklist row a workgroup takes at position pos (0 = first): the
+// worklist's rows longest first (row_perm is in ascending bucket order), or,
+// for dense attention, the rows in reverse order (each (sequence, head) from
+// its last query block down, so neighbouring positions share K/V and the
+// short rows come last).
+template <bool DENSE>
+__device__ __forceinline__ int64_t dense_or_listed_row(const Geom& g, const FwdBufs& a, int64_t pos) {
+  if constexpr (DENSE) return g.rows - 1 - pos;
+  return a.row_perm[g.rows - 1 - pos];
+}
+
 // --------------------------------------------------------------------------
 // Tile steps shared by the bf16 kernels.  Layouts:
 //   S^T accumulator sacc[kb][i] of a lane = key kb*32 + 8*(i/4) + 4*half + i%4
@@ -309,7 +320,7 @@ __device__ __forceinline__ void store_row(const f32x16 (&oacc)[4], float m, floa
 // --------------------------------------------------------------------------
 // Lock-step kernel, one LDS stage.  PIPE = 0: loads, then the tile's products;
 // PIPE = 2: V(t) and K(t+1) loads overlap S(t) / softmax / P V(t).
-template <int HPR, int PIPE>
+template <int HPR, int PIPE, bool DENSE>
 __global__ void __launch_bounds__(128 * HPR) prefill_bf16_kernel(Geom g, FwdBufs a, int xcd_run) {
   static_assert(PIPE == 0 || PIPE == 2, "pipeline form");
   constexpr int D = 128;
@@ -326,7 +337,7 @@ __global__ void __launch_bounds__(128 * HPR) prefill_bf16_kernel(Geom g, FwdBufs
   for (int64_t vb = blockIdx.x; vb < g.rows; vb += gridDim.x) {
     if (vb != blockIdx.x) block_barrier();   // the previous row's LDS reads are done
     const int64_t pos = xcd_schedule(vb, g.rows, xcd_run);
-    const int64_t row = a.row_perm[g.rows - 1 - pos];   // longest rows first
+    const int64_t row = dense_or_listed_row<DENSE>(g, a, pos);
     const RowInfo ri = decode_row(g, row);
     const int kvh = g.share ? ri.h : ri.h / g.group;
     const int head = (g.share ? ri.h * g.group : ri.h) + wave / 2;
@@ -336,17 +347,20 @@ __global__ void __launch_bounds__(128 * HPR) prefill_bf16_kernel(Geom g, FwdBufs
     const unsigned char* kbytes = (const unsigned char*)a.k;
     const unsigned char* vbytes = (const unsigned char*)a.v;
 
-    const int t_begin = a.row_ptr[row], ntiles = a.row_ptr[row + 1] - t_begin;
-    // the row's tile ids, one per lane (a row holds at most 128 tiles); read back
-    // with readlane so the loop issues no memory load (and no wait) for them
-    const int jl0 = lane < ntiles ? a.col_idx[t_begin + lane] : 0;
-    const int jl1 = lane + 64 < ntiles ? a.col_idx[t_begin + 64 + lane] : 0;
+    const int t_begin = DENSE ? 0 : a.row_ptr[row];
+    const int ntiles = DENSE ? ri.r + 1 : a.row_ptr[row + 1] - t_begin;
+    // the row's tile ids, one per lane (a listed row holds at most 128 tiles);
+    // read back with readlane so the loop issues no memory load (and no wait)
+    // for them.  A dense row visits tiles 0 .. r in order.
+    const int jl0 = !DENSE && lane < ntiles ? a.col_idx[t_begin + lane] : 0;
+    const int jl1 = !DENSE && lane + 64 < ntiles ? a.col_idx[t_begin + 64 + lane] : 0;
     // Consume the loads here, on every path: the compiler's wait-count pass is
     // path-insensitive, and a register that may still be pending at the loop
     // header makes it wait for all vector loads (the tile prefetch included)
     // inside the loop on every iteration.
     asm volatile("" ::"v"(jl0), "v"(jl1));
     auto tile_id = [&](int it) {
+      if constexpr (DENSE) return it;
       return it < 64 ? __builtin_amdgcn_readlane(jl0, it) : __builtin_amdgcn_readlane(jl1, it - 64);
     };
 
@@ -480,7 +494,7 @@ __device__ __forceinline__ void wait_vm_halves(int halves) {
   }
 }
 
-template <int NB>
+template <int NB, bool DENSE>
 __global__ void __launch_bounds__(512) prefill_bf16_pp_kernel(Geom g, FwdBufs a, int xcd_run) {
   constexpr int NW = 8, D = 128;
   constexpr int TILE = 64 * D * 2;
@@ -495,7 +509,7 @@ __global__ void __launch_bounds__(512) prefill_bf16_pp_kernel(Geom g, FwdBufs a,
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int grp = wave >> 2;
   const int64_t pos = xcd_schedule(blockIdx.x, g.rows, xcd_run);
-  const int64_t row = a.row_perm[g.rows - 1 - pos];   // longest rows first
+  const int64_t row = dense_or_listed_row<DENSE>(g, a, pos);
   const RowInfo ri = decode_row(g, row);
   const int kvh = g.share ? ri.h : ri.h / g.group;
   const int head = (g.share ? ri.h * g.group : ri.h) + wave / 2;
@@ -505,11 +519,13 @@ __global__ void __launch_bounds__(512) prefill_bf16_pp_kernel(Geom g, FwdBufs a,
   const unsigned char* kbytes = (const unsigned char*)a.k;
   const unsigned char* vbytes = (const unsigned char*)a.v;
 
-  const int t_begin = a.row_ptr[row], ntiles = a.row_ptr[row + 1] - t_begin;
-  const int jl0 = lane < ntiles ? a.col_idx[t_begin + lane] : 0;
-  const int jl1 = lane + 64 < ntiles ? a.col_idx[t_begin + 64 + lane] : 0;
+  const int t_begin = DENSE ? 0 : a.row_ptr[row];
+  const int ntiles = DENSE ? ri.r + 1 : a.row_ptr[row + 1] - t_begin;
+  const int jl0 = !DENSE && lane < ntiles ? a.col_idx[t_begin + lane] : 0;
+  const int jl1 = !DENSE && lane + 64 < ntiles ? a.col_idx[t_begin + 64 + lane] : 0;
   asm volatile("" ::"v"(jl0), "v"(jl1));   // consumed on every path (see prefill_bf16_kernel)
   auto tile_id = [&](int it) {
+    if constexpr (DENSE) return it;
     return it < 64 ? __builtin_amdgcn_readlane(jl0, it) : __builtin_amdgcn_readlane(jl1, it - 64);
   };
 
@@ -636,12 +652,12 @@ __global__ void __launch_bounds__(512) prefill_bf16_pp_kernel(Geom g, FwdBufs a,
 // --------------------------------------------------------------------------
 // fp32 SIMT kernel: one wavefront per (row, head), one lane per query row.
 // Used for fp32 problems (prefill and decode); exact fp32 exp.
-template <int D>
+template <int D, bool DENSE>
 __global__ void __launch_bounds__(64) attn_f32_kernel(Geom g, FwdBufs a) {
   __shared__ float ks[64][D + 1];
   __shared__ float vs[64][D];
   const int lane = threadIdx.x;
-  const int64_t row = a.row_perm[g.rows - 1 - (int64_t)blockIdx.x];
+  const int64_t row = dense_or_listed_row<DENSE>(g, a, (int64_t)blockIdx.x);
   const RowInfo ri = decode_row(g, row);
   const int head = (g.share ? ri.h * g.group : ri.h) + blockIdx.y;
   const int kvh = head / g.group;
@@ -661,8 +677,9 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(Geom g, FwdBufs a) {
     o[e] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
-  for (int t = a.row_ptr[row]; t < a.row_ptr[row + 1]; ++t) {
-    const int j = a.col_idx[t];
+  const int t0 = DENSE ? 0 : a.row_ptr[row], t1 = DENSE ? ri.r + 1 : a.row_ptr[row + 1];
+  for (int t = t0; t < t1; ++t) {
+    const int j = DENSE ? t : a.col_idx[t];
     const int cnt = min(kBlock, ri.len - j * kBlock);
     __syncthreads();
     const float* kb = k + kv_block_offset(g, ri.s, kvh, ri.tok0, j);
@@ -708,12 +725,13 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(Geom g, FwdBufs a) {
   }
 }
 
+template <bool DENSE>
 int launch_f32(const Geom& g, const FwdBufs& b, hipStream_t st) {
   dim3 grid((unsigned)g.rows, g.hpr);
   if (g.d == 64)
-    attn_f32_kernel<64><<<grid, 64, 0, st>>>(g, b);
+    attn_f32_kernel<64, DENSE><<<grid, 64, 0, st>>>(g, b);
   else
-    attn_f32_kernel<128><<<grid, 64, 0, st>>>(g, b);
+    attn_f32_kernel<128, DENSE><<<grid, 64, 0, st>>>(g, b);
   return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 
@@ -736,9 +754,10 @@ unsigned prefill_grid(K kernel, int threads, int64_t rows) {
   return (unsigned)(rows <= 4 * slots ? std::min(rows, slots) : rows);
 }
 
-int launch_prefill(const Geom& g, int dtype, const FwdBufs& b, hipStream_t st) {
+template <bool DENSE>
+int launch_prefill_t(const Geom& g, int dtype, const FwdBufs& b, hipStream_t st) {
   if (g.rows <= 0) return SA_OK;
-  if (dtype == SA_F32) return launch_f32(g, b, st);
+  if (dtype == SA_F32) return launch_f32<DENSE>(g, b, st);
   if (g.d != 128) return SA_ERR_UNSUPPORTED;
   // One-head rows: one LDS stage (32 KB) per workgroup, so four workgroups fit
   // on a CU and each SIMD runs two wavefronts of different rows; V(t) and
@@ -753,12 +772,12 @@ int launch_prefill(const Geom& g, int dtype, const FwdBufs& b, hipStream_t st) {
   const int run = g.hpr == 1 ? 128 : 32;   // rows per XCD run
   switch (g.hpr) {
     case 1: {
-      auto k = prefill_bf16_kernel<1, 2>;
+      auto k = prefill_bf16_kernel<1, 2, DENSE>;
       k<<<prefill_grid(k, 128, g.rows), 128, 0, st>>>(g, b, run);
       break;
     }
     case 2: {
-      auto k = prefill_bf16_kernel<2, 0>;
+      auto k = prefill_bf16_kernel<2, 0, DENSE>;
       k<<<prefill_grid(k, 256, g.rows), 256, 0, st>>>(g, b, run);
       break;
     }
@@ -766,11 +785,15 @@ int launch_prefill(const Geom& g, int dtype, const FwdBufs& b, hipStream_t st) {
       // one workgroup per row: the outer row loop of the persistent form
       // costs this kernel ~14 % in code generation, and with one workgroup
       // per CU its rows always fill many generations
-      prefill_bf16_pp_kernel<4><<<(unsigned)g.rows, 512, 0, st>>>(g, b, run);
+      prefill_bf16_pp_kernel<4, DENSE><<<(unsigned)g.rows, 512, 0, st>>>(g, b, run);
       break;
     default: return SA_ERR_UNSUPPORTED;
   }
   return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
+
+int launch_prefill(const Geom& g, int dtype, const FwdBufs& b, hipStream_t st, bool dense) {
+  return dense ? launch_prefill_t<true>(g, dtype, b, st) : launch_prefill_t<false>(g, dtype, b, st);
 }
 
 }  // namespace sa

@@ -38,7 +38,9 @@ struct FwdBufs {
   float* lse;
   float* part;     // decode partials (workspace)
 };
-int launch_prefill(const Geom& g, int dtype, const FwdBufs& b, hipStream_t st);
+// dense: every row r visits tiles 0 .. r in order (no worklist; rows taken in
+// reverse order); else the worklist in b
+int launch_prefill(const Geom& g, int dtype, const FwdBufs& b, hipStream_t st, bool dense = false);
 int launch_decode(const Geom& g, int dtype, const FwdBufs& b, int splits, hipStream_t st);
 size_t decode_partials_bytes(const Geom& g, int splits);
 

@@ -491,4 +491,32 @@ int sparse_attn_fwd(const sa_problem* p, const sa_route_cfg* rc, const int32_t* 
   return launch_prefill(pl.g, p->dtype, b, hs);
 }
 
+int sparse_attn_fwd_dense(const sa_problem* p, const sa_route_cfg* rc, const void* q, const void* k,
+                          const void* v, void* o, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  Plan pl;
+  int st = validate(p, rc, &pl);
+  if (st != SA_OK) return st;
+  if (p->mode != SA_PREFILL) return SA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !o) return SA_ERR_INVALID_ARG;
+  if (p->dtype == SA_BF16) {
+    const int h = pl.g.hpr;
+    if (p->head_dim != 128 || !(h == 1 || h == 2 || h == 4)) return SA_ERR_UNSUPPORTED;
+  }
+  const size_t need = ws_size(pl, 2, 1);
+  if (ws_bytes < need || (need && !ws)) return SA_ERR_WORKSPACE;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if ((st = prep_cu_blocks(pl, ws, hs)) != SA_OK) return st;
+  FwdBufs b;
+  b.row_ptr = nullptr;
+  b.col_idx = nullptr;
+  b.row_perm = nullptr;
+  b.q = q;
+  b.k = k;
+  b.v = v;
+  b.o = o;
+  b.lse = lse;
+  b.part = nullptr;
+  return launch_prefill(pl.g, p->dtype, b, hs, /*dense=*/true);
+}
+
 }  // extern "C"

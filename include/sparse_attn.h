@@ -7,6 +7,10 @@
  *   sparse_attn_build_worklist   J               -> sorted, deduplicated CSR worklist
  *   sparse_attn_fwd              Q, K, V, worklist -> O (and log-sum-exp)
  *
+ * with a dense causal variant for the fallback and the comparison:
+ *
+ *   sparse_attn_fwd_dense        Q, K, V -> O (every earlier block)
+ *
  * and one for the decode cache that routing reads:
  *
  *   sparse_attn_append_kv        new K/V rows -> cache rows and block summaries
@@ -261,6 +265,25 @@ int sparse_attn_fwd(const sa_problem* p, const sa_route_cfg* rc, const int32_t* 
                     const int32_t* col_idx, const int32_t* row_perm, const void* q,
                     const void* k, const void* v, void* o, float* lse, int32_t num_splits,
                     void* ws, size_t ws_bytes, void* stream);
+
+/* Dense causal attention with the same kernels, layouts, dtypes and masks as
+ * sparse_attn_fwd: the dense fallback of [P2] §3.1 (a router that keeps
+ * nearly every block is better served densely; failures are not hidden by
+ * it) and the dense side of the sparse / dense comparison.  Every query
+ * block r attends every key block 0 .. r of its sequence, as if its worklist
+ * row listed them all in ascending order, with no worklist and no limit on
+ * the row length; query i attends key p iff p <= i and p < the sequence
+ * length.  Prefill only (fixed-length, chunked or packed varlen).
+ *   rc      only share_gqa is used (one row serves a KV head's query heads,
+ *           else one query head); the other fields must be valid as for the
+ *           sparse calls
+ *   q, k, v, o, lse  as for sparse_attn_fwd (lse nullable)
+ *   ws      (device) sparse_attn_workspace_size(p, rc, 2, 0) bytes (the block
+ *           offsets of a packed batch; 0 otherwise)
+ * bf16 needs head_dim 128 and 1, 2 or 4 query heads per row; fp32 takes
+ * head_dim 64 or 128.  Returns SA_ERR_UNSUPPORTED for decode problems. */
+int sparse_attn_fwd_dense(const sa_problem* p, const sa_route_cfg* rc, const void* q, const void* k,
+                          const void* v, void* o, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /* Backward pass of the prefill attention over the forward's worklist ([P2] §4
  * training paragraph and [P3]: gradients reuse the forward's block selection).
