@@ -20,14 +20,16 @@ The other settings are timed the same way and reported under `settings`, each
 with its own `roofline`: the 8192-token MHA prefill (B=1, H=16, k_b=16), the
 32768-token GQA prefill (B=2, Hq=32, Hkv=8, k_b=32, sink forced) and split-KV
 decode (64 x 131072-token caches, Hq=32, Hkv=8, k_b=64) as KV GB/s against the
-HBM peak.  The backward pass is timed on the prefill settings.
+HBM peak.  The backward pass is timed on the prefill settings, and each
+prefill setting (plus the GQA shape at 65536 tokens) is also run densely
+(`dense`): the sparse/dense crossover.
 
 The fp64 CPU oracle is timed on a bounded, seeded sample of the headline
 setting (`cpu_baseline`): a reported baseline, not a target.
 
     python bench.py [--steps K] [--warmup W] [--no-decode] [--no-cpu] [--no-bwd]
     python bench.py --workload NAME     # time one setting only (it becomes the headline)
-    python bench.py --dense             # adds the dense causal comparison (`dense`)
+    python bench.py --no-dense          # skips the dense causal comparison (`dense`)
 """
 from __future__ import annotations
 
@@ -374,50 +376,82 @@ def measure_bwd(args, dbs, st, visits):
             "time": "median call, warm (events on the current stream)"}
 
 
-def measure_dense(args, dbs, w, inp, flush, sparse_fwd_ms):
-    """The same causal attention done densely, for the sparse/dense crossover:
-    this library's prefill kernel on a worklist with every causal tile (k_b =
-    127, the widest row the worklist takes: all blocks of every query block
-    except one of the last), and torch's flash-attention SDPA (causal, bf16) on
-    the same tensors, forced to the flash backend.  Each call timed after the
-    last-level cache flush; medians in ms."""
+def measure_dense(args, dbs, w, inp, flush, sparse_rec):
+    """The same causal attention done densely, for the sparse/dense crossover
+    ([P2] §3.1 dense fallback): sparse_attn_fwd_dense (this library's kernels,
+    every causal tile of every row, same layout, dtype and masks) and, for
+    fixed-length inputs, torch's flash-attention SDPA (causal, bf16, forced to
+    its flash backend; GQA through enable_gqa).  Each call timed after the
+    cache flush; medians in ms.  Crossover: the sparse step (route + worklist +
+    fwd) costs t_r + t_w + f * (dense time) * c when it keeps a fraction f of
+    the causal tiles, c being its measured per-tile cost relative to the
+    dense walk; it beats the dense call while f < (t_dense - t_r - t_w) /
+    (c t_dense)."""
     import torch
     from torch.nn.attention import SDPBackend, sdpa_kernel
-    n_q = -(-w.seqlen // w.block)
-    nforced = 1 + int(w.forced_first)
-    if w.varlen or n_q > 128 - nforced + 1:
-        return None   # a dense row needs every causal block in one worklist row (<= 128 ids)
-    wdn = w.replace(name=w.name + "_dense", k_b=min(n_q, 128 - nforced))
-    st = Stepper(dbs, wdn, inp)
-    st.route()
-    st.worklist()
-    visits = st.tile_visits()
-    ours, flash = [], []
-    reps = max(args.steps // 5, 10)
-    with sdpa_kernel(SDPBackend.FLASH_ATTENTION):
-        for i in range(reps + 2):
-            for fn, acc in ((st.fwd, ours),
-                            (lambda: torch.nn.functional.scaled_dot_product_attention(
-                                inp.q, inp.k, inp.v, is_causal=True), flash)):
-                flush.sum()
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-                fn()
-                e1.record()
-                torch.cuda.synchronize()
-                if i >= 2:
-                    acc.append(e0.elapsed_time(e1))
-    ours_ms, flash_ms = spread(ours)["median"], spread(flash)["median"]
-    causal = 4 * w.head_dim * w.heads_q * w.batch * w.seqlen * (w.seqlen + 1) // 2
-    del st
-    return {"ours_dense_fwd_ms": ours_ms, "ours_dense_tile_visits": visits,
-            "ours_dense_tflops_tiles": round(visits * 4 * w.block ** 2 * w.head_dim / (ours_ms * 1e-3) / 1e12, 1),
+    prob, cfg = dbs.problem_for(w, inp), dbs.config_for(w)
+    hpr = w.group if w.share_gqa else 1
+    nblocks = [-(-L // w.block) for L in inp.lengths]
+    dense_visits = sum(nb * (nb + 1) // 2 for nb in nblocks) * w.route_heads * hpr
+    o = torch.empty_like(inp.q)
+    lse = torch.empty(inp.q.shape[:-1], dtype=torch.float32, device=inp.q.device)
+    ws = torch.empty(max(dbs.workspace_size(prob, cfg, 2), 1), dtype=torch.uint8, device=inp.q.device)
+    call = lambda: dbs.fwd_dense(prob, cfg, inp.q, inp.k, inp.v, o=o, lse=lse, workspace=ws)
+    flash = None
+    if not w.varlen:
+        gqa = w.heads_q != w.heads_kv
+        flash = lambda: torch.nn.functional.scaled_dot_product_attention(
+            inp.q, inp.k, inp.v, is_causal=True, enable_gqa=gqa)
+    reps = max(min(args.steps // 5, 10), 3)
+
+    def time_calls(fn):
+        out = []
+        for i in range(reps + 1):
+            flush.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            if i >= 1:
+                out.append(e0.elapsed_time(e1))
+        return spread(out)["median"]
+
+    ours_ms = time_calls(call)
+    flash_ms, flash_err = None, None
+    if flash is not None:
+        try:
+            with sdpa_kernel(SDPBackend.FLASH_ATTENTION):
+                flash_ms = time_calls(flash)
+        except RuntimeError as e:   # no flash kernel for this shape on this build
+            flash_err = str(e).splitlines()[0][:160]
+    causal = 4 * w.head_dim * w.heads_q * sum(L * (L + 1) // 2 for L in inp.lengths)
+    tile_flops = 4 * w.block * w.block * w.head_dim
+    st = sparse_rec["stages_ms"]["cache_flushed"]
+    t_r, t_w, t_f = st["route"]["median"], st["worklist"]["median"], st["fwd"]["median"]
+    sparse_visits = sparse_rec["config"]["tile_visits"]
+    frac = sparse_visits / dense_visits
+    cost = (t_f / sparse_visits) / (ours_ms / dense_visits)
+    f_star = (ours_ms - t_r - t_w) / (cost * ours_ms)
+    del o, lse, ws
+    return {"dense_fwd_ms": ours_ms, "dense_tile_visits": dense_visits,
+            "dense_tflops_tiles": round(dense_visits * tile_flops / (ours_ms * 1e-3) / 1e12, 1),
+            "dense_frac_of_peak": round(dense_visits * tile_flops / (ours_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "torch_flash_sdpa_ms": flash_ms,
-            "torch_flash_sdpa_tflops_causal": round(causal / (flash_ms * 1e-3) / 1e12, 1),
-            "sparse_fwd_ms": sparse_fwd_ms,
-            "sparse_speedup_vs_flash": round(flash_ms / sparse_fwd_ms, 2),
-            "sparse_speedup_vs_ours_dense": round(ours_ms / sparse_fwd_ms, 2),
-            "note": "k_b=127 dense worklist: every causal tile except one of the last query block"}
+            "torch_flash_sdpa_tflops_causal": (round(causal / (flash_ms * 1e-3) / 1e12, 1)
+                                               if flash_ms else None),
+            "torch_flash_note": flash_err or ("not run: packed varlen input" if flash is None else None),
+            "sparse_step_ms": round(t_r + t_w + t_f, 5),
+            "sparse_tile_fraction": round(frac, 4),
+            "sparse_per_tile_cost_vs_dense": round(cost, 3),
+            "sparse_speedup_vs_dense": round(ours_ms / (t_r + t_w + t_f), 2),
+            "sparse_speedup_vs_flash": round(flash_ms / (t_r + t_w + t_f), 2) if flash_ms else None,
+            "fallback_tile_fraction": round(min(f_star, 1.0), 4),
+            "fallback_tile_fraction_raw": round(f_star, 4),
+            "note": "times: median calls after a cache flush; fallback_tile_fraction: the sparse step "
+                    "(route + worklist + fwd) beats the dense call while it keeps fewer than this "
+                    "fraction of the causal tiles (raw > 1: a listed tile costs less than a tile of "
+                    "the dense walk, so the sparse step wins at any fraction)"}
 
 
 def measure_decode(args, dbs, wd, dev, flush):
@@ -523,11 +557,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-decode", action="store_true", help="skip the decode setting")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--dense", action="store_true",
-                    help="also time the dense comparison (this library's kernel on a full causal "
-                         "worklist, and torch flash-attention SDPA); off by default so that the "
-                         "attention kernel's launches in a profile of the default run are the "
-                         "sparse ones only")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip the dense comparison (sparse_attn_fwd_dense and torch flash SDPA on "
+                         "each prefill setting, and the 65536-token crossover point)")
     ap.add_argument("--no-bwd", action="store_true", help="skip timing the backward pass")
     ap.add_argument("--cpu-blocks", type=int, default=0,
                     help="query blocks of the oracle's sample (every routing head of each); "
@@ -590,17 +622,19 @@ def main():
                     "ms_per_step": rec.pop("ms_per_step"),
                     "data": "synthetic (seeded N(0,1) Q/K/V with planted relevance; no dataset)"})
         out.update(rec)
-        if args.dense:
+        if not args.no_dense:
             log(f"timing dense causal attention on {head.name}")
-            dense = measure_dense(args, dbs, head, inp, flush, out["stages_ms"]["cache_flushed"]["fwd"]["median"])
-            if dense is not None:
-                out["dense"] = dense
+            out["dense"] = measure_dense(args, dbs, head, inp, flush, out)
         if not args.no_cpu:
             cpu_inp = inp
         else:
             del inp
         torch.cuda.empty_cache()
     settings = {}
+    if not args.workload and not args.no_dense:
+        # a longer point for the crossover: the GQA setting at 65536 tokens, one sequence
+        others.insert(2, wk.PREFILL_GQA.replace(name="prefill_gqa_b1_hq32_hkv8_n65536_d128_kb32", batch=1,
+                                                seqlen=65536))
     for w in others:
         if w.mode == "decode":
             settings[w.name] = measure_decode(args, dbs, w, dev, flush)
@@ -608,6 +642,9 @@ def main():
             log(f"generating {w.name}")
             inp_w = wk.make_inputs(w, dev)
             settings[w.name] = measure_prefill(args, dbs, w, inp_w, flush)
+            if not args.no_dense:
+                log(f"timing dense causal attention on {w.name}")
+                settings[w.name]["dense"] = measure_dense(args, dbs, w, inp_w, flush, settings[w.name])
             del inp_w
         torch.cuda.empty_cache()
     if settings:
