@@ -28,7 +28,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsparse_attn.so")
 
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = 0, 1, 2, 3, 4
-SA_WL_ERR_RANGE, SA_WL_ERR_ACAUSAL, SA_WL_ERR_PAGE = 1, 2, 4
+SA_WL_ERR_RANGE, SA_WL_ERR_ACAUSAL, SA_WL_ERR_PAGE, SA_WL_ERR_LENGTH = 1, 2, 4, 8
 SA_F32, SA_BF16 = 0, 1
 SA_PREFILL, SA_DECODE = 0, 1
 SA_POOL_MEAN, SA_POOL_MAX = 0, 1
@@ -57,7 +57,7 @@ class _Problem(ctypes.Structure):
                 ("total_blocks", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
                 ("kv_capacity", ctypes.c_int32), ("block_table", ctypes.c_void_p),
                 ("table_stride", ctypes.c_int32), ("pool_blocks", ctypes.c_int32),
-                ("q_start", ctypes.c_int32)]
+                ("q_start", ctypes.c_int32), ("seq_lens", ctypes.c_void_p)]
 
 
 class _RouteCfg(ctypes.Structure):
@@ -130,6 +130,8 @@ class Problem:
     block_table: Optional[torch.Tensor] = None  # decode, paged: int32 [batch, stride] pages (device)
     pool_blocks: int = 0         # paged: pages in the [pool, Hkv, b, d] K/V pool
     q_start: int = 0             # chunked prefill: first query token (multiple of block)
+    seq_lens: Optional[torch.Tensor] = None     # decode: int32 [batch] per-sequence cached lengths
+                                                # (device), each <= seqlen; None = all seqlen
 
     @staticmethod
     def fixed(batch, heads_q, heads_kv, head_dim, seqlen, dtype="bf16", kv_capacity=0, q_start=0):
@@ -138,9 +140,12 @@ class Problem:
 
     @staticmethod
     def decode(batch, heads_q, heads_kv, head_dim, cache_len, dtype="bf16", kv_capacity=0,
-               block_table=None, pool_blocks=0):
+               block_table=None, pool_blocks=0, seq_lens=None):
+        """cache_len: the cached length of every sequence, or with seq_lens (device
+        int32 [batch]) an upper bound on each sequence's own length."""
         return Problem(batch, heads_q, heads_kv, head_dim, cache_len, dtype, "decode",
-                       kv_capacity=kv_capacity, block_table=block_table, pool_blocks=pool_blocks)
+                       kv_capacity=kv_capacity, block_table=block_table, pool_blocks=pool_blocks,
+                       seq_lens=seq_lens)
 
     @staticmethod
     def varlen(lengths, heads_q, heads_kv, head_dim, cu_seqlens, dtype="bf16"):
@@ -159,6 +164,8 @@ class Problem:
             p.block_table = self.block_table.data_ptr()
             p.table_stride = int(self.block_table.shape[1])
             p.pool_blocks = self.pool_blocks
+        if self.seq_lens is not None:
+            p.seq_lens = self.seq_lens.data_ptr()
         if self.cu_seqlens is not None:
             p.cu_seqlens = self.cu_seqlens.data_ptr()
             nb = [-(-int(x) // self.block) for x in self.lengths]
@@ -281,6 +288,10 @@ def _require_problem(call: str, prob: Problem, device):
         if bt.dim() != 2 or bt.shape[0] != prob.batch:
             raise ValueError(f"{call}: block_table must be [batch, stride], got {tuple(bt.shape)}")
         _require(call, "block_table", bt, tuple(bt.shape), torch.int32, device)
+    if prob.seq_lens is not None:
+        if prob.mode != "decode":
+            raise ValueError(f"{call}: seq_lens applies to decode problems only")
+        _require(call, "seq_lens", prob.seq_lens, (prob.batch,), torch.int32, device)
 
 
 def _require_worklist(call: str, prob: Problem, cfg: RouteConfig, wl: "Worklist", device, full: bool = True):
@@ -354,7 +365,7 @@ def route(prob: Problem, cfg: RouteConfig, q: torch.Tensor, k: Optional[torch.Te
         J = torch.empty((rows, cfg.k_b), dtype=torch.int32, device=dev)
     _require("route", "J", J, (rows, cfg.k_b), torch.int32, dev)
     _on_device("route", dev, q=q, k=None if summaries_in else k, summaries=summaries, J=J,
-               cu_seqlens=prob.cu_seqlens, block_table=prob.block_table)
+               cu_seqlens=prob.cu_seqlens, block_table=prob.block_table, seq_lens=prob.seq_lens)
     p, c = prob.to_c(), cfg.to_c()
     wsb = workspace_size(prob, cfg, 0)
     ws = _use_workspace("route", workspace, wsb, dev)
@@ -392,7 +403,7 @@ def build_worklist(prob: Problem, cfg: RouteConfig, J: torch.Tensor, out: Option
         _require_worklist("build_worklist", prob, cfg, out, dev)
     _on_device("build_worklist", dev, J=J, row_ptr=out.row_ptr, col_idx=out.col_idx, row_perm=out.row_perm,
                bucket_ptr=out.bucket_ptr, err=out.err, cu_seqlens=prob.cu_seqlens,
-               block_table=prob.block_table)
+               block_table=prob.block_table, seq_lens=prob.seq_lens)
     out.err.zero_()
     p, c = prob.to_c(), cfg.to_c()
     wsb = workspace_size(prob, cfg, 1)
@@ -416,7 +427,7 @@ def build_worklist_noalloc(prob: Problem, cfg: RouteConfig, J: torch.Tensor, out
     _require_worklist("build_worklist_noalloc", prob, cfg, out, dev)
     _on_device("build_worklist_noalloc", dev, J=J, row_ptr=out.row_ptr, col_idx=out.col_idx,
                row_perm=out.row_perm, bucket_ptr=out.bucket_ptr, err=out.err, cu_seqlens=prob.cu_seqlens,
-               block_table=prob.block_table)
+               block_table=prob.block_table, seq_lens=prob.seq_lens)
     need = workspace_size(prob, cfg, 1)
     if need > NOALLOC_SCRATCH_BYTES:
         raise ValueError(f"build_worklist_noalloc: the problem needs {need} bytes of scratch, more than the "
@@ -449,7 +460,8 @@ def fwd(prob: Problem, cfg: RouteConfig, wl: Worklist, q, k, v, o=None, lse=None
     if lse is not None:
         _require("fwd", "lse", lse, qs[:-1], torch.float32, dev)
     _on_device("fwd", dev, q=q, k=k, v=v, o=o, lse=lse, row_ptr=wl.row_ptr, col_idx=wl.col_idx,
-               row_perm=wl.row_perm, cu_seqlens=prob.cu_seqlens, block_table=prob.block_table)
+               row_perm=wl.row_perm, cu_seqlens=prob.cu_seqlens, block_table=prob.block_table,
+               seq_lens=prob.seq_lens)
     p, c = prob.to_c(), cfg.to_c()
     wsb = workspace_size(prob, cfg, 2, num_splits)
     ws = _use_workspace("fwd", workspace, wsb, dev)
@@ -518,10 +530,10 @@ def bwd(prob: Problem, cfg: RouteConfig, wl: Worklist, q, k, v, o, lse, dout, dq
 def append_kv(prob: Problem, k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
               v_cache: torch.Tensor, summaries: torch.Tensor, kpool: str = "mean"):
     """sparse_attn_append_kv: writes k_new / v_new [S, Hkv, n, d] into rows
-    [prob.seqlen, prob.seqlen + n) of the caches [S, Hkv, kv_capacity, d] and
-    updates the fp32 summaries of the blocks they land in (in place; block
-    means, or per-dimension maxima with kpool "max").  The caller advances
-    prob.seqlen by n afterwards."""
+    [L0, L0 + n) of the caches [S, Hkv, kv_capacity, d] and updates the fp32
+    summaries of the blocks they land in (in place; block means, or
+    per-dimension maxima with kpool "max").  L0 = prob.seqlen, or sequence s's
+    prob.seq_lens[s] when set.  The caller advances them by n afterwards."""
     dt = torch.bfloat16 if prob.dtype == "bf16" else torch.float32
     cap = prob.kv_capacity
     shape_c = (prob.batch, prob.heads_kv, cap, prob.head_dim)
@@ -535,6 +547,9 @@ def append_kv(prob: Problem, k_new: torch.Tensor, v_new: torch.Tensor, k_cache: 
         if tuple(t.shape) != shp or t.dtype != tdt or not t.is_contiguous() or not t.is_cuda:
             raise ValueError(f"append_kv: {name} must be a contiguous {tdt} device tensor of shape {shp}, "
                              f"got {tuple(t.shape)} {t.dtype}")
+    _require_problem("append_kv", prob, k_cache.device)
+    _on_device("append_kv", k_cache.device, k_new=k_new, v_new=v_new, v_cache=v_cache, summaries=summaries,
+               block_table=prob.block_table, seq_lens=prob.seq_lens)
     p = prob.to_c()
     _check("sparse_attn_append_kv", load_library().sparse_attn_append_kv(
         ctypes.byref(p), n, _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(summaries),

@@ -30,10 +30,13 @@ __global__ void __launch_bounds__(64) append_kv_kernel(AppendGeom g, const T* __
   constexpr int D = 64 * E;
   const int lane = threadIdx.x;
   const int s = (int)blockIdx.x / g.hkv, h = (int)blockIdx.x % g.hkv;
-  const int j = g.len0 / kBlock + (int)blockIdx.y;   // block that receives tokens [t0, t1)
+  // this sequence's length before the append (its own, or the common one)
+  const int len0 = g.seq_lens ? min(max(g.seq_lens[s], 0), g.len0) : g.len0;
+  const int j = len0 / kBlock + (int)blockIdx.y;   // block that receives tokens [t0, t1)
   const int lo = j * kBlock;
-  const int t0 = max(lo, g.len0), t1 = min(lo + kBlock, g.len0 + g.n_new);
-  const int r_old = max(0, min(lo + kBlock, g.len0) - lo);   // valid keys before the append
+  const int t0 = max(lo, len0), t1 = min(lo + kBlock, len0 + g.n_new);
+  if (t0 >= t1) return;   // the grid covers the most blocks any start can touch
+  const int r_old = max(0, min(lo + kBlock, len0) - lo);   // valid keys before the append
   const int col = lane * E;
   const T* kn = k_new + (int64_t)s * g.new_seq + (int64_t)h * g.new_head + col;
   const T* vn = v_new + (int64_t)s * g.new_seq + (int64_t)h * g.new_head + col;
@@ -61,8 +64,8 @@ __global__ void __launch_bounds__(64) append_kv_kernel(AppendGeom g, const T* __
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        kx[u][e] = kn[(int64_t)(t + u - g.len0) * D + e];
-        vx[u][e] = vn[(int64_t)(t + u - g.len0) * D + e];
+        kx[u][e] = kn[(int64_t)(t + u - len0) * D + e];
+        vx[u][e] = vn[(int64_t)(t + u - len0) * D + e];
       }
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -76,8 +79,8 @@ __global__ void __launch_bounds__(64) append_kv_kernel(AppendGeom g, const T* __
   for (; t < t1; ++t) {
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const T kx = kn[(int64_t)(t - g.len0) * D + e];
-      const T vx = vn[(int64_t)(t - g.len0) * D + e];
+      const T kx = kn[(int64_t)(t - len0) * D + e];
+      const T vx = vn[(int64_t)(t - len0) * D + e];
       kd[(int64_t)t * D + e] = kx;
       vd[(int64_t)t * D + e] = vx;
       acc[e] = g.kmax ? fmaxf(acc[e], (float)kx) : acc[e] + (float)kx;

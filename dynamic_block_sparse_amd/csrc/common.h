@@ -47,6 +47,8 @@ struct Geom {
   // chunked prefill: the queries are tokens [q_tok_off, n) of each sequence
   // (Q, O and lse hold only those), their rows query blocks qblk0 .. N - 1
   int qblk0, q_tok_off;
+  // decode with a cached length per sequence (device [batch]); n bounds them all
+  const int32_t* seq_lens;
 };
 
 struct RowInfo {
@@ -59,8 +61,10 @@ struct RowInfo {
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-__device__ __forceinline__ int seq_len(const Geom& g, int s) {
-  return g.varlen ? (g.cu_seqlens[s + 1] - g.cu_seqlens[s]) : g.n;
+// Cached length of decode sequence s: its seq_lens entry clamped into [1, n]
+// (the worklist builder reports entries outside), else n.
+__device__ __forceinline__ int decode_len(const Geom& g, int s) {
+  return g.seq_lens ? min(max(g.seq_lens[s], 1), g.n) : g.n;
 }
 
 // Map a worklist row id to (sequence, routing head, query block).
@@ -69,8 +73,8 @@ __device__ __forceinline__ RowInfo decode_row(const Geom& g, int64_t row) {
   if (g.mode == SA_DECODE) {
     ri.s = (int)(row / g.hr);
     ri.h = (int)(row % g.hr);
-    ri.len = g.n;
-    ri.nblk = ceil_div(g.n, kBlock);
+    ri.len = decode_len(g, ri.s);
+    ri.nblk = ceil_div(ri.len, kBlock);
     ri.r = ri.nblk - 1;
     ri.tok0 = 0;
     ri.blk0 = 0;

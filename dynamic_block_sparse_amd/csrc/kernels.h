@@ -73,6 +73,7 @@ struct AppendGeom {
   int64_t sum_seq, sum_head;       // summary strides in blocks
   const int32_t* block_table;      // paged cache: [S, table_stride] pages of a [pool, hkv, b, d] pool
   int table_stride, pool_blocks;
+  const int32_t* seq_lens;         // per-sequence len0 (device [S], clamped into [0, len0]), or null
 };
 int launch_append_kv(const AppendGeom& g, int dtype, int n_seq, int touched, const void* k_new,
                      const void* v_new, void* k_cache, void* v_cache, float* summ, hipStream_t st);

@@ -59,7 +59,8 @@ __global__ void __launch_bounds__(256) summary_kernel(Geom g, const T* __restric
     const int nb = ceil_div(g.n, kBlock);
     s = slot / nb;
     j = slot % nb;
-    len = g.n;
+    len = g.mode == SA_DECODE ? decode_len(g, s) : g.n;
+    if (j * kBlock >= len) return;   // past a shorter decode sequence's last block
   }
   if (pool_q && j < g.qblk0) return;   // a cached prefix block has no queries (chunked prefill)
   const int cnt = min(kBlock, len - j * kBlock);

@@ -68,6 +68,7 @@ int validate(const sa_problem* p, const sa_route_cfg* rc, Plan* out) {
   if (p->mode == SA_DECODE) {
     if (p->cu_seqlens || p->seqlen < 1 || p->q_start != 0) return SA_ERR_INVALID_ARG;
     g.n = p->seqlen;
+    g.seq_lens = p->seq_lens;   // per-sequence lengths, each <= n (clamped on the device)
     // the cache may hold room beyond the valid length: strides follow the capacity
     const int cap = p->kv_capacity > 0 ? p->kv_capacity : p->seqlen;
     if (p->kv_capacity < 0 || cap < g.n) return SA_ERR_INVALID_ARG;
@@ -92,8 +93,8 @@ int validate(const sa_problem* p, const sa_route_cfg* rc, Plan* out) {
       g.table_stride = p->table_stride;
       g.pool_blocks = p->pool_blocks;
     }
-  } else if (p->block_table) {
-    return SA_ERR_INVALID_ARG;   // a block table only pages a decode cache
+  } else if (p->block_table || p->seq_lens) {
+    return SA_ERR_INVALID_ARG;   // a block table pages, and seq_lens sizes, only a decode cache
   } else if (p->cu_seqlens) {
     if (p->kv_capacity != 0 || p->q_start != 0) return SA_ERR_INVALID_ARG;   // packed: no cache, no chunk
     if (p->seqlen != 0 || p->total_tokens < 1 || p->total_blocks < p->batch ||
@@ -346,7 +347,10 @@ int sparse_attn_append_kv(const sa_problem* p, int32_t n_new, const void* k_new,
   if ((int64_t)p->seqlen + n_new > p->kv_capacity) return SA_ERR_INVALID_ARG;
   if (n_new == 0) return SA_OK;
   if (!k_new || !v_new || !k_cache || !v_cache || !summaries) return SA_ERR_INVALID_ARG;
-  const int touched = (p->seqlen + n_new - 1) / kBlock - p->seqlen / kBlock + 1;
+  // blocks one launch row covers: those of [L0, L0 + n_new), or with per-sequence
+  // starts the most that n_new consecutive tokens can straddle
+  int touched = (p->seqlen + n_new - 1) / kBlock - p->seqlen / kBlock + 1;
+  if (p->seq_lens) touched = std::min((n_new - 1) / kBlock + 2, (p->kv_capacity + kBlock - 1) / kBlock);
   if (touched > 65535 || (int64_t)p->batch * p->heads_kv > INT32_MAX) return SA_ERR_UNSUPPORTED;
   const int64_t d = p->head_dim, cap = p->kv_capacity, nbc = (cap + kBlock - 1) / kBlock;
   AppendGeom g;
@@ -363,6 +367,7 @@ int sparse_attn_append_kv(const sa_problem* p, int32_t n_new, const void* k_new,
   g.block_table = p->block_table;
   g.table_stride = p->table_stride;
   g.pool_blocks = p->pool_blocks;
+  g.seq_lens = p->seq_lens;
   g.kmax = kpool == SA_POOL_MAX;
   if (p->block_table && (p->table_stride < nbc || p->pool_blocks < 1)) return SA_ERR_INVALID_ARG;
   return launch_append_kv(g, p->dtype, p->batch, touched, k_new, v_new, k_cache, v_cache, summaries,

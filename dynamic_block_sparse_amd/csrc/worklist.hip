@@ -41,6 +41,10 @@ __global__ void __launch_bounds__(64) wl_rows_kernel(Geom g, sa_route_cfg rc, in
   const uint32_t sentinel = 1u << nbits;   // sorts after every valid id
   const bool ff = (rc.forced & SA_FORCE_FIRST) != 0;
   int ebits = 0;
+  if (g.seq_lens) {   // decode: a length outside [1, n] was clamped by decode_row
+    const int L = g.seq_lens[ri.s];
+    if (L < 1 || L > g.n) ebits |= SA_WL_ERR_LENGTH;
+  }
 
   const int win = max(rc.window, 1);
   auto load_slot = [&](int p) -> uint32_t {
@@ -102,8 +106,10 @@ __global__ void __launch_bounds__(64) wl_rows_kernel(Geom g, sa_route_cfg rc, in
   const uint64_t er = __ballot(ebits & SA_WL_ERR_RANGE);
   const uint64_t ea = __ballot(ebits & SA_WL_ERR_ACAUSAL);
   const uint64_t ep = __ballot(ebits & SA_WL_ERR_PAGE);
-  if (lane == 0 && (er | ea | ep))
-    atomicOr(err, (er ? SA_WL_ERR_RANGE : 0) | (ea ? SA_WL_ERR_ACAUSAL : 0) | (ep ? SA_WL_ERR_PAGE : 0));
+  const uint64_t el = __ballot(ebits & SA_WL_ERR_LENGTH);
+  if (lane == 0 && (er | ea | ep | el))
+    atomicOr(err, (er ? SA_WL_ERR_RANGE : 0) | (ea ? SA_WL_ERR_ACAUSAL : 0) | (ep ? SA_WL_ERR_PAGE : 0) |
+                      (el ? SA_WL_ERR_LENGTH : 0));
 }
 
 // Step 2 for rows c0 .. c0 + NT - 1 (c0 = NT * block).  Thread t first sums,

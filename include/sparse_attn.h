@@ -93,6 +93,7 @@ extern "C" {
 #define SA_WL_ERR_RANGE 1      /* an id < -1 or >= the sequence's block count */
 #define SA_WL_ERR_ACAUSAL 2    /* prefill: an id after the row's query block */
 #define SA_WL_ERR_PAGE 4       /* paged decode cache: the block's page lies outside the pool */
+#define SA_WL_ERR_LENGTH 8     /* decode: a seq_lens entry outside [1, seqlen] (clamped) */
 
 #define SA_F32 0
 #define SA_BF16 1
@@ -143,6 +144,19 @@ typedef struct sa_problem {
                              a decode cache).  Rows are query blocks q_start / b .. N - 1, routed
                              against every earlier block with the usual causal rules.  0 = the
                              whole sequence; must be 0 for packed varlen and decode. */
+  const int32_t* seq_lens; /* decode, optional (device): [batch] int32, the cached length of
+                             each sequence when they differ (requests of a decode batch
+                             have different histories, [P3] "From index output to
+                             worklist").  seqlen is then an upper bound on every entry and
+                             sizes the problem.  Routing, the worklist and the attention
+                             take length L_s for sequence s: its blocks 0 .. ceil(L_s / b)
+                             - 1, the last one forced and masked to its valid keys.  An
+                             entry outside [1, seqlen] is clamped into that range by every
+                             kernel (nothing reads outside the cache) and reported by the
+                             worklist builder (SA_WL_ERR_LENGTH).  sparse_attn_append_kv
+                             takes it as each sequence's length before the append (there
+                             [0, seqlen]).  NULL: every sequence holds seqlen tokens.  Must
+                             be NULL for prefill. */
 } sa_problem;
 
 /* Routing settings (host struct). */
@@ -318,6 +332,9 @@ int sparse_attn_bwd(const sa_problem* p, const sa_route_cfg* rc, const int32_t* 
  *               dtype; seqlen = L0, the cached length of every sequence before
  *               the call (0 allowed); kv_capacity >= L0 + n_new (required).
  *               heads_q is not used but must be a valid multiple of heads_kv.
+ *               With seq_lens set, sequence s starts from its own L0_s =
+ *               seq_lens[s] (clamped into [0, seqlen]; seqlen bounds them all)
+ *               and every L0_s below stands for it.
  *   n_new       tokens appended to every sequence (0: nothing is enqueued)
  *   k_new, v_new (device) [S, Hkv, n_new, d] rows to append, in order
  *   k_cache, v_cache (device) [S, Hkv, kv_capacity, d]: rows [L0, L0 + n_new)
@@ -334,7 +351,8 @@ int sparse_attn_bwd(const sa_problem* p, const sa_route_cfg* rc, const int32_t* 
  *               summaries): c_j <- max(c_j, per-dimension max of its new keys),
  *               or that max alone when r_j = 0.
  *   Arithmetic is fp32 (sums of the new keys in token order).  Calls on one
- *   stream apply in order; the caller advances seqlen by n_new afterwards.
+ *   stream apply in order; the caller advances seqlen (and each seq_lens
+ *   entry) by n_new afterwards.
  *   Returns SA_ERR_INVALID_ARG for a non-decode problem, a negative n_new,
  *   L0 + n_new > kv_capacity, an unknown kpool or a null pointer (when
  *   n_new > 0). */

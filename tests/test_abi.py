@@ -236,3 +236,18 @@ def test_noalloc_worklist_rejects_sizes_beyond_scratch(lib):
     st = lib.sparse_attn_build_worklist_noalloc(ctypes.byref(bad), ctypes.byref(c), None, None, None, 0, None,
                                                 None, None, None)
     assert st == dbs.SA_ERR_UNSUPPORTED
+
+
+def test_seq_lens_only_for_decode(lib):
+    import torch
+    lens = torch.ones(4, dtype=torch.int32)           # host memory: only the pointer is checked here
+    cfg = dbs.RouteConfig(k_b=8, share_gqa=True)
+    ok = dbs.Problem.decode(4, 8, 2, 128, 1000, kv_capacity=1500, seq_lens=lens)
+    s = dbs.sizes(ok, cfg)
+    assert s.rows == 4 * 2 and s.kv_blocks == 4 * 24   # sized by the bound and the capacity
+    for bad in (dataclasses.replace(_prob(), seq_lens=lens),
+                dataclasses.replace(dbs.Problem.varlen([64, 64], 8, 2, 128, torch.zeros(3, dtype=torch.int32)),
+                                    seq_lens=lens)):
+        with pytest.raises(dbs.SAError) as e:
+            dbs.sizes(bad, cfg)
+        assert e.value.status == dbs.SA_ERR_INVALID_ARG

@@ -7,6 +7,8 @@ read or written out of place.  Each such input must raise ValueError in the
 binding.  These run on the CPU: the checks are host-side and come before any
 library call that launches work (the library is loaded only for its host-side
 size queries)."""
+import dataclasses
+
 import pytest
 import torch
 
@@ -126,4 +128,18 @@ def test_packed_problem_tables_checked():
     p = dbs.Problem.varlen([70, 30], HQ, HKV, D, cu)
     c = _cfg()
     with pytest.raises(ValueError):
+        dbs.route(p, c, _t(dbs.q_shape(p)), _t(dbs.kv_shape(p)))
+
+
+def test_seq_lens_checked():
+    p = dbs.Problem.decode(3, HQ, HKV, D, 300, seq_lens=torch.ones(3, dtype=torch.int64))   # int64: refused
+    c = _cfg()
+    q, kv = _t(dbs.q_shape(p)), _t(dbs.kv_shape(p))
+    with pytest.raises(ValueError, match="seq_lens"):
+        dbs.route(p, c, q, kv)
+    p = dbs.Problem.decode(3, HQ, HKV, D, 300, seq_lens=torch.ones(2, dtype=torch.int32))    # wrong batch
+    with pytest.raises(ValueError, match="seq_lens"):
+        dbs.route(p, c, q, kv)
+    p = dataclasses.replace(dbs.Problem.fixed(1, HQ, HKV, D, 300), seq_lens=torch.ones(1, dtype=torch.int32))
+    with pytest.raises(ValueError, match="seq_lens"):
         dbs.route(p, c, _t(dbs.q_shape(p)), _t(dbs.kv_shape(p)))
