@@ -15,8 +15,24 @@ recall is the fraction of them a row keeps.
   recall    |W_r intersect R_r| / |R_r| for the relevant blocks R_r a row could
             select (planted blocks j < r); 1 when R_r is empty
 
-Readings (parity unpinned): the dense reference is causal attention over the
-whole sequence; a padded key never counts.
+  row_quality  the per-query report of [P2] §3.1's second validation layer
+            for one row: coverage, token recall@t against the dense top-t
+            teacher, the teacher's misses split into "block not routed" and
+            "weight moved inside a selected block", and the dense-vs-sparse
+            output error (relative error and cosine)
+
+Readings: the dense reference is causal attention over the whole sequence (a
+decode query attends every cached key); a padded key never counts.  The
+teacher G_i holds the t causal keys of largest dense probability, ties to
+the lower position, t clipped to the number of causal keys.  The sparse
+attention is exact over the selected blocks, so a teacher key outside them
+loses its whole dense weight, and one inside has its weight divided by C_i.
+
+Pinned (tests/test_oracle_quality.py): coverage and row_quality against plain
+loops on tiny inputs, the full causal set (coverage 1, nothing lost or moved,
+zero error), disjoint sets adding up, the 2 V delta output bound, the sparse
+output against masked_attention, ties to the lower position, the teacher
+against a full sort with many exact ties, and recall on hand-made sets.
 """
 from __future__ import annotations
 
@@ -40,3 +56,59 @@ def recall(selected, relevant) -> float:
     if not rel:
         return 1.0
     return len(rel & set(int(x) for x in selected)) / len(rel)
+
+
+def teacher(p_row, t: int) -> np.ndarray:
+    """Positions of the t largest entries of p_row, equal values taken from the
+    lower position up (all of them when t >= len(p_row))."""
+    n = len(p_row)
+    if t >= n:
+        return np.arange(n)
+    tau = np.partition(p_row, n - t)[n - t]     # the t-th largest value
+    above = np.nonzero(p_row > tau)[0]
+    tied = np.nonzero(p_row == tau)[0][:t - len(above)]
+    return np.concatenate([above, tied])
+
+
+def row_quality(q_rows, q_pos, k, v, length: int, b: int, blocks, ts=(8, 64)) -> dict:
+    """Per-query quality of one row's selected blocks against dense causal attention.
+
+    q_rows [m, d] (one query head), q_pos their positions (decode: length - 1),
+    k, v [>= length, d] of the row's KV head, `blocks` the row's worklist set.
+    Returns per-query arrays: coverage (Eq 10); for each t in ts, recall@t =
+    |G_i & N(i)| / |G_i|, lost@t = dense mass of the teacher keys outside the
+    selected blocks (block not routed), moved@t = sum over the teacher keys
+    inside of |p_sparse - p_dense| (weight moved inside a selected block);
+    top1_routed (the dense arg-max key is attended); rel_err = |o_dense -
+    o_sparse| / |o_dense| and cosine(o_dense, o_sparse) (Euclidean norms);
+    o_dense and o_sparse [m, d].
+    """
+    q_pos = np.asarray(q_pos)
+    hi = min(int(q_pos.max()) + 1, length)   # keys past the last query are causally masked
+    n_blk = -(-hi // b)
+    dense = masked_attention(q_rows, q_pos, k, v, hi, b, list(range(n_blk)), causal=True)
+    p = dense["p"]
+    inside = allowed_mask(q_pos, hi, b, blocks, causal=True)
+    cov = np.sum(np.where(inside, p, 0.0), axis=1)
+    p_sparse = np.where(inside, p / cov[:, None], 0.0)
+    vv = np.asarray(v[:hi], np.float64)
+    o_dense = dense["o"]
+    o_sparse = p_sparse @ vv
+    n_causal = np.minimum(q_pos + 1, hi)
+    out = dict(coverage=cov, o_dense=o_dense, o_sparse=o_sparse)
+    rows = np.arange(p.shape[0])
+    for t in ts:
+        rec, lost, moved = np.zeros(len(rows)), np.zeros(len(rows)), np.zeros(len(rows))
+        for i in rows:
+            g = teacher(p[i, :n_causal[i]], t)
+            hit = inside[i, g]
+            rec[i] = hit.sum() / len(g)
+            lost[i] = p[i, g[~hit]].sum()
+            moved[i] = np.abs(p_sparse[i, g[hit]] - p[i, g[hit]]).sum()
+        out[f"recall@{t}"], out[f"lost@{t}"], out[f"moved@{t}"] = rec, lost, moved
+    out["top1_routed"] = inside[rows, np.argmax(p, axis=1)]   # argmax: the first (lowest) of equal maxima
+    diff = np.linalg.norm(o_dense - o_sparse, axis=1)
+    nd, ns = np.linalg.norm(o_dense, axis=1), np.linalg.norm(o_sparse, axis=1)
+    out["rel_err"] = diff / nd
+    out["cosine"] = np.sum(o_dense * o_sparse, axis=1) / (nd * ns)
+    return out

@@ -26,11 +26,12 @@ def dev():
     return torch.device("cuda:0")
 
 
-def _full_check(w, inp, run, seqs=None, rows=None):
-    r = check_router(w, inp, run, seqs=seqs)
-    print(f"[{w.name}] router rows checked {r['checked']} bad {len(r['bad'])} tie-band rows {r['tie_rows']}",
-          flush=True)
-    assert not r["bad"], f"router mismatches outside the tie band at rows {r['bad'][:10]}"
+def _full_check(w, inp, run, seqs=None, rows=None, router=True):
+    if router:
+        r = check_router(w, inp, run, seqs=seqs)
+        print(f"[{w.name}] router rows checked {r['checked']} bad {len(r['bad'])} tie-band rows "
+              f"{r['tie_rows']}", flush=True)
+        assert not r["bad"], f"router mismatches outside the tie band at rows {r['bad'][:10]}"
     check_worklist(w, inp, run)
     ids = rows if rows is not None else list(range(run.J.shape[0]))
     o = check_output(w, inp, run, ids)
@@ -40,6 +41,21 @@ def _full_check(w, inp, run, seqs=None, rows=None):
     assert o["max_abs"] <= mx
     assert o["mean_abs"] <= mean
     assert o["lse_max_abs"] <= LSE_TOL[w.dtype]
+
+
+def _router_all(w, inp, run, chunk):
+    """Router check of every sequence, `chunk` sequences at a time (bounded host memory)."""
+    n = len(inp.lengths)
+    rows = ties = 0
+    for a in range(0, n, chunk):
+        seqs = list(range(a, min(n, a + chunk)))
+        r = check_router(w, inp, run, seqs=seqs)
+        assert not r["bad"], f"router mismatches outside the tie band at rows {r['bad'][:10]}"
+        rows += r["checked"]
+        ties += r["tie_rows"]
+        print(f"[{w.name}] router sequences {seqs[0]}..{seqs[-1]}: {r['checked']} rows agree", flush=True)
+    assert rows == run.J.shape[0]
+    print(f"[{w.name}] router: all {rows} rows agree ({ties} within the tie band)", flush=True)
 
 
 SMALL = [
@@ -230,7 +246,8 @@ def test_full_prefill_gqa(dev):
     print(f"case {w.name}", flush=True)
     inp = wk.make_inputs(w, dev)
     run = run_gpu(w, inp)
-    _full_check(w, inp, run, seqs=[1], rows=sample_rows(w, inp, per_seq_head=2, seqs=[1]))
+    _router_all(w, inp, run, chunk=1)
+    _full_check(w, inp, run, rows=sample_rows(w, inp, per_seq_head=2), router=False)
 
 
 def test_full_varlen(dev):
@@ -240,7 +257,8 @@ def test_full_varlen(dev):
     run = run_gpu(w, inp)
     lens = inp.lengths
     seqs = [int(np.argmin(lens)), int(np.argmax(lens))]
-    _full_check(w, inp, run, seqs=seqs, rows=sample_rows(w, inp, per_seq_head=1, seqs=seqs))
+    _router_all(w, inp, run, chunk=2)
+    _full_check(w, inp, run, rows=sample_rows(w, inp, per_seq_head=1, seqs=seqs), router=False)
 
 
 def test_full_decode(dev):
@@ -248,8 +266,9 @@ def test_full_decode(dev):
     print(f"case {w.name}", flush=True)
     inp = wk.make_inputs(w, dev)
     run = run_gpu(w, inp)
-    seqs = [0, 17, 63]
-    _full_check(w, inp, run, seqs=seqs, rows=sample_rows(w, inp, seqs=seqs))
+    _router_all(w, inp, run, chunk=8)
+    seqs = [0, 17, 31, 46, 63]
+    _full_check(w, inp, run, rows=sample_rows(w, inp, seqs=seqs), router=False)
 
 
 # ---------------------------------------------------------------------------
