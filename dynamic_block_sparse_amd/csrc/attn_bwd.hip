@@ -362,7 +362,7 @@ __global__ void __launch_bounds__(128) bwd_dq_bf16_kernel(Geom g, BwdBufs a) {
       for (int i = 0; i < 16; ++i) {
         const int kpos = j * kBlock + b2 * 32 + 8 * (i / 4) + 4 * half + (i % 4);
         const bool ok = qvalid && kpos <= qpos;
-        const float p = ok ? __builtin_amdgcn_exp2f(fmaf(sacc[b2][i], cl2, -lse2)) : 0.f;
+        const float p = __builtin_amdgcn_exp2f(ok ? fmaf(sacc[b2][i], cl2, -lse2) : -INFINITY);
         dsb[b2][i / 8][i % 8] = (__bf16)(p * (dpacc[b2][i] - delta));
       }
     // dQ^T += K^T dS^T: the transpose reads run four MFMAs ahead
@@ -446,38 +446,248 @@ __global__ void __launch_bounds__(256) bwd_split_clear_kernel(Geom g, BwdBufs a)
   }
 }
 
-// NW = 4 or 8 wavefronts: wave w owns keys 32 (w & 1) .. + 32, the 32 query
-// rows 32 ((w >> 1) & 1) .. + 32 of every staged row and (NW = 8) one half of
-// the d columns of the accumulators, so each wave forms one 32 x 32 block of S
-// and dP per (row, head) (the two d halves form the same block) and
-// accumulates dK^T, dV^T of its keys and columns over its query half; the two
-// query halves are added through LDS at the end.
-template <int NW>
-__global__ void __launch_bounds__(64 * NW) bwd_dkdv_bf16_kernel(Geom g, BwdBufs a) {
-  constexpr int NT = 64 * NW, NDB = 16 / NW;   // threads; 32-column d blocks per wave
-  __shared__ __attribute__((aligned(16))) unsigned char kt[64 * 256], vt[64 * 256], qd[2][64 * 256];
-  __shared__ float lse_s[64], del_s[64];
-  unsigned char* qt = qd[0];
-  unsigned char* dot = qd[1];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, half = lane >> 5;
-  const int kh = w & 1, qh = (w >> 1) & 1, dh = w >> 2;
-  const int kvh = blockIdx.y;
-  // a key block listed by more than split_target (row, head) pairs is shared
-  // by nch workgroups, each taking an equal run of its pairs in visiting order
-  const int64_t kidx = (int64_t)blockIdx.x * g.hkv + kvh;
-  const int units = a.kcount[kidx];
-  const int nch = units > a.split_target ? min(a.max_chunks, (units + a.split_target - 1) / a.split_target) : 1;
-  if ((int)blockIdx.z >= nch) return;
-  const int ord_lo = (int)((int64_t)units * blockIdx.z / nch);
-  const int ord_hi = (int)((int64_t)units * (blockIdx.z + 1) / nch);
-  const KeySlot ksl = key_slot(g, (int)blockIdx.x);
-  const int s = ksl.s, j = ksl.j, len = ksl.len, tok0 = ksl.tok0, blk0 = ksl.blk0, nb = ksl.nb;
+// Key-major pair lists.  kcount holds the (row, head) pairs listing each
+// (key block slot, KV head); a row serves ngh of them (the KV head's query
+// heads when routing is shared, else one), so the rows listing it number
+// kcount / ngh.  One workgroup turns those counts into exclusive offsets kptr
+// ([slots x Hkv + 1]; the last entry is the total, the worklist's nnz), and
+// lists the dK/dV workgroups: one per (slot, KV head), or nch of them for a
+// block with more pairs than split_target, as witem entries (index << 4 |
+// chunk), -1 up to witems.
+__device__ __forceinline__ int bwd_chunks(int units, int split_target, int max_chunks) {
+  return units > split_target ? min(max_chunks, (units + split_target - 1) / split_target) : 1;
+}
+
+__global__ void __launch_bounds__(1024) bwd_kscan_kernel(const int* __restrict__ kcount, int* __restrict__ kptr,
+                                                         int* __restrict__ witem, int n, int ngh, int split_target,
+                                                         int max_chunks, int witems) {
+  __shared__ int part[1024], cpart[1024];
+  const int tid = threadIdx.x;
+  const int per = (n + 1023) / 1024;
+  const int b = min(tid * per, n), e = min(b + per, n);
+  int sum = 0, csum = 0;
+  for (int i = b; i < e; ++i) {
+    sum += kcount[i] / ngh;
+    csum += bwd_chunks(kcount[i], split_target, max_chunks);
+  }
+  part[tid] = sum;
+  cpart[tid] = csum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {   // inclusive scans of the thread sums
+    const int v = tid >= off ? part[tid - off] : 0;
+    const int cv = tid >= off ? cpart[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    cpart[tid] += cv;
+    __syncthreads();
+  }
+  int run = part[tid] - sum, crun = cpart[tid] - csum;
+  for (int i = b; i < e; ++i) {
+    kptr[i] = run;
+    run += kcount[i] / ngh;
+    const int nc = bwd_chunks(kcount[i], split_target, max_chunks);
+    for (int z = 0; z < nc; ++z) witem[crun + z] = (i << 4) | z;
+    crun += nc;
+  }
+  if (tid == 1023) kptr[n] = part[1023];
+  for (int w = cpart[1023] + tid; w < witems; w += 1024) witem[w] = -1;
+}
+
+// One wavefront per (key block slot x, KV head): the rows whose (sorted)
+// lists hold block j, in visiting order (routing heads of the KV head, then
+// query blocks ascending), written as r * nrh + hh to klist[kptr ..).  Each
+// lane takes one candidate row of a run of 64 and binary-searches its list;
+// a ballot orders the hits.  Slots the search does not fill (a worklist whose
+// lists are not sorted and unique) are set to -1 and skipped.
+__global__ void __launch_bounds__(256) bwd_klist_kernel(Geom g, BwdBufs a, int n) {
+  const int idx = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  if (idx >= n) return;
+  const int lane = threadIdx.x & 63;
+  const int x = idx / g.hkv, kvh = idx % g.hkv;
+  const KeySlot ks = key_slot(g, x);
+  const int nrh = g.share ? 1 : g.group;
+  const int rfirst = max(ks.j, g.qblk0);   // causal: only query blocks r >= j list block j
+  const int p0 = a.kptr[idx], p1 = a.kptr[idx + 1];
+  const uint64_t below = lanes_below();
+  int w = p0;
+  for (int hh = 0; hh < nrh; ++hh) {
+    const int hr = g.share ? kvh : kvh * g.group + hh;
+    for (int r0 = rfirst; r0 < ks.nb; r0 += 64) {
+      const int r = r0 + lane;
+      bool has = false;
+      if (r < ks.nb) {
+        const int64_t rw = row_id(g, ks.s, hr, r, ks.blk0, ks.nb);
+        int lo = a.row_ptr[rw], hi = a.row_ptr[rw + 1] - 1;
+        while (lo <= hi) {
+          const int mid = (lo + hi) >> 1, cj = a.col_idx[mid];
+          if (cj == ks.j) {
+            has = true;
+            break;
+          }
+          if (cj < ks.j) lo = mid + 1; else hi = mid - 1;
+        }
+      }
+      const uint64_t m = __ballot(has);
+      const int at = w + __popcll(m & below);
+      if (has && at < p1) a.klist[at] = r * nrh + hh;
+      w += __popcll(m);
+    }
+  }
+  for (int t = w + lane; t < p1; t += 64) a.klist[t] = -1;
+}
+
+// Global -> LDS loads (see the forward kernels): lane l's 16 bytes (4 bytes)
+// from base + off land at lds_wave_base + 16 l (+ 4 l).  Issued as inline asm
+// so the compiler does not wait for them at unrelated LDS reads; the loop
+// waits for them explicitly before the barrier that publishes a pair.
+__device__ __forceinline__ void bwd_load_lds16(const unsigned char* base, uint32_t off, const unsigned char* lds) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(SA_LDS const unsigned char*)lds;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(m0)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void bwd_load_lds4(const unsigned char* base, uint32_t off, const unsigned char* lds) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(SA_LDS const unsigned char*)lds;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "s"(m0)
+               : "memory", "m0");
+}
+__device__ __forceinline__ const unsigned char* bwd_uniform(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const unsigned char*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// One workgroup per (key block slot, KV head, chunk), 4 wavefronts: wave w
+// owns keys 32 (w & 1) .. + 32 and query rows 32 (w >> 1) .. + 32 of every
+// pair, forms that 32 x 32 block of S = Q K^T and dP = dO V^T (one key per
+// lane) and accumulates dV^T += dO^T P and dK^T += Q^T dS for its keys over
+// its query half; the halves are added through LDS at the end.  Each lane
+// keeps its key's K row (the B operand of S) in registers for the whole
+// workgroup; V is staged in LDS once.  The pairs come from the key-major list and stream
+// through a ring of NB LDS buffers: a pair's Q, dO, lse and D go global ->
+// LDS NB - 1 pairs ahead of its products, one barrier per pair.  A pair's
+// rows past the sequence end load the last valid row (finite values, masked
+// to zero weight).  A key block with more pairs than split_target is shared
+// by up to max_chunks workgroups, each taking an equal run of its pairs: they
+// add into fp32 accumulators with atomics and the last one to finish
+// converts them.
+template <int N>
+__device__ __forceinline__ void bwd_wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// wait until at most `pairs` younger pairs' loads (L per pair) are in flight
+template <int L>
+__device__ __forceinline__ void bwd_wait_pairs(int pairs) {
+  if (pairs >= 2) bwd_wait_vmcnt<2 * L>();
+  else if (pairs == 1) bwd_wait_vmcnt<L>();
+  else bwd_wait_vmcnt<0>();
+}
+
+__global__ void __launch_bounds__(256) bwd_dkdv_bf16_kernel(Geom g, BwdBufs a) {
+  constexpr int NDB = 4, TILE = 64 * 256, NB = 3;
+  __shared__ __attribute__((aligned(1024))) unsigned char qd[NB][2][TILE];   // [buffer][Q, dO]
+  __shared__ __attribute__((aligned(1024))) unsigned char vt[TILE];          // V of the key block
+  __shared__ __attribute__((aligned(256))) float lds_ld[NB][2][64];          // [buffer][lse, D][query row]
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kh = wave & 1, qh = wave >> 1;
+  const int wi = a.witem[blockIdx.x];   // (slot x KV head) << 4 | chunk, or -1
+  if (wi < 0) return;
+  const int64_t kidx = wi >> 4;
+  const int chunk = wi & 15;
+  const int kvh = (int)(kidx % g.hkv);
+  const int ngh = g.share ? g.group : 1;   // query heads per row
+  const int nrh = g.share ? 1 : g.group;   // routing heads of the KV head
+  const int e0 = a.kptr[kidx], nent = a.kptr[kidx + 1] - e0, units = nent * ngh;
+  const int nch = bwd_chunks(units, a.split_target, a.max_chunks);
+  const int ord_lo = (int)((int64_t)units * chunk / nch);
+  const int ord_hi = (int)((int64_t)units * (chunk + 1) / nch);
+  const KeySlot ksl = key_slot(g, (int)(kidx / g.hkv));
+  const int s = ksl.s, j = ksl.j, len = ksl.len, tok0 = ksl.tok0;
   const int cnt = min(kBlock, len - j * kBlock);
   const int64_t kb = kv_block_offset(g, s, kvh, tok0, j);
-  stage_tile<false, NT>(kt, (const __bf16*)a.k + kb, cnt, tid);
-  stage_tile<false, NT>(vt, (const __bf16*)a.v + kb, cnt, tid);
   const float c = 0.08838834764831845f, cl2 = c * kLog2e;
   const int key = kh * 32 + l32, kpos = j * kBlock + key;
+
+  // a pair's loads per wavefront: four 1 KB slices of the Q and of the dO
+  // tile, and (waves 0, 1) the 64 lse / D values
+  constexpr int LPP = 9;   // loads per pair, every wavefront (waves 2, 3 repeat their last slice)
+  const unsigned char* const qbytes = (const unsigned char*)a.q;
+  const unsigned char* const dbytes = (const unsigned char*)a.dout;
+  uint32_t toff[4];
+  int trow[4];
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii) {
+    const int sl = wave + 4 * ii, row = 4 * sl + (lane >> 4), p = lane & 15;
+    trow[ii] = row;
+    toff[ii] = (uint32_t)(((p ^ tsw(row)) << 4));
+  }
+  // entries of the list, 64 at a time in a register (lane i: entry base + i)
+  int ebase = ord_lo / ngh;
+  int ent = ebase + lane < nent ? a.klist[e0 + ebase + lane] : -1;
+  asm volatile("" ::"v"(ent));
+  struct Pair {
+    int r, head, qrows;
+    bool ok;
+  };
+  auto pair_of = [&](int ord) {
+    Pair pr;
+    const int e = ord / ngh, gh = ord - e * ngh;
+    if (e - ebase >= 64) {   // uniform: refill the entry window
+      ebase = e;
+      ent = ebase + lane < nent ? a.klist[e0 + ebase + lane] : -1;
+      // consumed here, so no path reaches the loop's reads with it pending
+      // (the compiler's wait insertion would otherwise wait for every load
+      // in flight, the ring's prefetches included, on every pair)
+      asm volatile("" ::"v"(ent));
+    }
+    const int v = __builtin_amdgcn_readlane(ent, e - ebase);
+    pr.ok = v >= 0;
+    const int vv = pr.ok ? v : 0;   // a skipped entry still loads a valid tile (uniform wait counts)
+    pr.r = vv / nrh;
+    pr.head = kvh * g.group + (g.share ? gh : vv - pr.r * nrh);
+    pr.qrows = min(kBlock, len - pr.r * kBlock);
+    return pr;
+  };
+  auto issue_pair = [&](const Pair& pr, int b) {
+    const int64_t qo = q_offset(g, s, pr.head, tok0, pr.r * kBlock) * 2;
+    const unsigned char* qb = bwd_uniform(qbytes + qo);
+    const unsigned char* db = bwd_uniform(dbytes + qo);
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const uint32_t o = (uint32_t)min(trow[ii], pr.qrows - 1) * 256 + toff[ii];
+      bwd_load_lds16(qb, o, &qd[b][0][(wave + 4 * ii) * 1024]);
+      bwd_load_lds16(db, o, &qd[b][1][(wave + 4 * ii) * 1024]);
+    }
+    const int64_t lo = lse_offset(g, s, pr.head, tok0, pr.r * kBlock) * 4;
+    const unsigned char* lb = bwd_uniform((const unsigned char*)(wave == 1 ? a.delta : a.lse) + lo);
+    // waves 0 and 1 bring lse and D; waves 2 and 3 load lse again into their
+    // own unused slot so every wavefront has LPP loads per pair
+    bwd_load_lds4(lb, (uint32_t)min(lane, pr.qrows - 1) * 4,
+                  (const unsigned char*)(wave < 2 ? &lds_ld[b][wave][0] : &lds_ld[b][0][0]));
+  };
+
+  // ring prologue: the first NB - 1 pairs
+  Pair ring[NB];
+#pragma unroll
+  for (int u = 0; u < NB - 1; ++u)
+    if (ord_lo + u < ord_hi) {
+      ring[u] = pair_of(ord_lo + u);
+      issue_pair(ring[u], u);
+    }
+  // this lane's K row (row `key`, clamped into the block): the B operand of
+  // S = Q K^T for d = 16 ks + 8 half .. + 8; and the block's V in LDS
+  bf16x8 kreg[8];
+  {
+    const int krow = min(key, cnt - 1);
+    const __bf16* kp = (const __bf16*)a.k + kb + (int64_t)krow * 128 + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      kreg[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kp + 16 * ks));
+  }
+  stage_tile<false, 256>(vt, (const __bf16*)a.v + kb, cnt, tid);
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(kreg[ks]));
 
   f32x16 dk[NDB], dv[NDB];
 #pragma unroll
@@ -485,84 +695,98 @@ __global__ void __launch_bounds__(64 * NW) bwd_dkdv_bf16_kernel(Geom g, BwdBufs 
 #pragma unroll
     for (int i = 0; i < 16; ++i) dk[db][i] = dv[db][i] = 0.f;
 
-  const int nrh = g.share ? 1 : g.group;   // routing heads whose rows may list this block
-  const int ngh = g.share ? g.group : 1;   // query heads per row
-  const int rfirst = max(j, g.qblk0);      // causal: only query blocks r >= j list block j
-  int ord = 0;                             // visiting-order index of the next pair
-  for (int hh = 0; hh < nrh && ord < ord_hi; ++hh) {
-    const int hr = g.share ? kvh : kvh * g.group + hh;
-    for (int r0 = rfirst; r0 < nb && ord < ord_hi; r0 += 64) {
-      // one candidate row per lane: does its (sorted) list hold block j?
-      const int r = r0 + lane;
-      bool has = false;
-      if (r < nb) {
-        const int64_t rw = row_id(g, s, hr, r, blk0, nb);
-        int lo = a.row_ptr[rw], hi = a.row_ptr[rw + 1] - 1;
-        while (lo <= hi) {
-          const int mid = (lo + hi) >> 1, cj = a.col_idx[mid];
-          if (cj == j) { has = true; break; }
-          if (cj < j) lo = mid + 1; else hi = mid - 1;
+  for (int ord = ord_lo; ord < ord_hi; ++ord) {
+    const int u = ord - ord_lo, b = u % NB;
+    const int ahead = ord + NB - 1;   // the pair whose loads go out in this iteration
+    Pair nxt = {0, 0, 1, false};
+    if (ahead < ord_hi) nxt = pair_of(ahead);
+    bwd_wait_pairs<LPP>(min(NB - 2, ord_hi - 1 - ord));   // this wave's loads of pair ord
+    // every wave's loads of pair ord landed; buffer (ord - 1) % NB is read.  A
+    // bare s_barrier: __syncthreads would also wait for the younger pairs' loads
+    asm volatile("s_barrier" ::: "memory");
+    if (ahead < ord_hi) {
+      ring[(u + NB - 1) % NB] = nxt;
+      issue_pair(nxt, (u + NB - 1) % NB);
+    }
+    const Pair cur = ring[b];
+    if (cur.ok) {
+      const unsigned char* qt = qd[b][0];
+      const unsigned char* dot = qd[b][1];
+      const float* lse_s = lds_ld[b][0];
+      const float* del_s = lds_ld[b][1];
+      // S = Q K^T and dP = dO V^T: this wave's 32 query rows x 32 keys (one
+      // key per lane); the Q and dO operands of step ks + 2 are read while
+      // step ks multiplies (an order pinned with sched_group_barrier: left
+      // alone the compiler reads each operand just before its MFMA)
+      f32x16 sacc, dpacc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[i] = dpacc[i] = 0.f;
+      bf16x8 oq[3], od[3], ov[3];
+      auto rd = [&](int ks) {
+        oq[ks % 3] = row8<true>(qt, qh * 32 + l32, 2 * ks + half);
+        od[ks % 3] = row8<true>(dot, qh * 32 + l32, 2 * ks + half);
+        ov[ks % 3] = row8<false>(vt, key, 2 * ks + half);
+      };
+      rd(0);
+      rd(1);
+      __builtin_amdgcn_sched_group_barrier(kDsRead, 6, 0);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        if (ks + 2 < 8) rd(ks + 2);
+        sacc = mfma(oq[ks % 3], kreg[ks], sacc);
+        dpacc = mfma(od[ks % 3], ov[ks % 3], dpacc);
+        if (ks + 2 < 8) __builtin_amdgcn_sched_group_barrier(kDsRead, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(kMfma, 2, 0);
+      }
+      // lse and D of this lane's 16 query rows, four runs of 4 read one run ahead
+      bf16x8 pb[2], dsb[2];
+      f32x4 lsv[2], dlv[2];
+      lsv[0] = *reinterpret_cast<const f32x4*>(lse_s + qh * 32 + 4 * half);
+      dlv[0] = *reinterpret_cast<const f32x4*>(del_s + qh * 32 + 4 * half);
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        if (gq + 1 < 4) {
+          lsv[(gq + 1) & 1] = *reinterpret_cast<const f32x4*>(lse_s + qh * 32 + 8 * (gq + 1) + 4 * half);
+          dlv[(gq + 1) & 1] = *reinterpret_cast<const f32x4*>(del_s + qh * 32 + 8 * (gq + 1) + 4 * half);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * gq + e;
+          const int q = qh * 32 + 8 * gq + 4 * half + e;
+          const bool ok = q < cur.qrows && kpos <= cur.r * kBlock + q;
+          // masked weights exponentiate -inf (no branch per element)
+          const float p = __builtin_amdgcn_exp2f(ok ? fmaf(sacc[i], cl2, -lsv[gq & 1][e] * kLog2e) : -INFINITY);
+          pb[i / 8][i % 8] = (__bf16)p;
+          dsb[i / 8][i % 8] = (__bf16)(p * (dpacc[i] - dlv[gq & 1][e]));
         }
       }
-      uint64_t m = __ballot(has);
-      const int in_m = __popcll(m) * ngh;
-      if (ord + in_m <= ord_lo) {   // all before this workgroup's run
-        ord += in_m;
-        continue;
-      }
-      while (m) {
-        const int rr = r0 + __builtin_ctzll(m);
-        m &= m - 1;
-        const int qrows = min(kBlock, len - rr * kBlock);
-        for (int gh = 0; gh < ngh; ++gh, ++ord) {
-          if (ord < ord_lo || ord >= ord_hi) continue;
-          const int head = g.share ? kvh * g.group + gh : hr;
-          const int64_t qo = q_offset(g, s, head, tok0, rr * kBlock);
-          __syncthreads();   // the previous pair's tiles are no longer read
-          stage_tile<true, NT>(qt, (const __bf16*)a.q + qo, qrows, tid);
-          stage_tile<true, NT>(dot, (const __bf16*)a.dout + qo, qrows, tid);
-          if (tid < 64) {
-            const bool ok = tid < qrows;
-            const int64_t lo = ok ? lse_offset(g, s, head, tok0, rr * kBlock + tid) : 0;
-            lse_s[tid] = ok ? a.lse[lo] * kLog2e : 0.f;
-            del_s[tid] = ok ? a.delta[lo] : 0.f;
-          }
-          __syncthreads();
-          // S = Q K^T and dP = dO V^T: this wave's 32 query rows x 32 keys (one key per lane)
-          f32x16 sacc, dpacc;
+      // dV^T += dO^T P and dK^T += Q^T dS: MFMA i takes d block i / 4, step
+      // (i / 2) % 2, dV for even i and dK for odd; its transposed A operand
+      // is read four MFMAs ahead
+      auto ta_of = [&](int i) {
+        return (i & 1) ? tr8(qt, qh, (i >> 1) & 1, i >> 2, lane) : tr8(dot, qh, (i >> 1) & 1, i >> 2, lane);
+      };
+      bf16x8 ta[4];
 #pragma unroll
-          for (int i = 0; i < 16; ++i) sacc[i] = dpacc[i] = 0.f;
+      for (int i = 0; i < 4; ++i) ta[i] = ta_of(i);
+      __builtin_amdgcn_sched_group_barrier(kDsRead, 8, 0);
 #pragma unroll
-          for (int ks = 0; ks < 8; ++ks) {
-            sacc = mfma(row8<true>(qt, qh * 32 + l32, 2 * ks + half), row8<false>(kt, key, 2 * ks + half), sacc);
-            dpacc = mfma(row8<true>(dot, qh * 32 + l32, 2 * ks + half), row8<false>(vt, key, 2 * ks + half),
-                         dpacc);
-          }
-          bf16x8 pb[2], dsb[2];
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int q = qh * 32 + 8 * (i / 4) + 4 * half + (i % 4);
-            const bool ok = q < qrows && kpos <= rr * kBlock + q;
-            const float p = ok ? __builtin_amdgcn_exp2f(fmaf(sacc[i], cl2, -lse_s[q])) : 0.f;
-            pb[i / 8][i % 8] = (__bf16)p;
-            dsb[i / 8][i % 8] = (__bf16)(p * (dpacc[i] - del_s[q]));
-          }
-#pragma unroll
-          for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-              dv[db] = mfma(tr8(dot, qh, ks, dh * NDB + db, lane), pb[ks], dv[db]);
-              dk[db] = mfma(tr8(qt, qh, ks, dh * NDB + db, lane), dsb[ks], dk[db]);
-            }
-        }
+      for (int i = 0; i < 16; ++i) {
+        const bf16x8 av = ta[i & 3];
+        if (i + 4 < 16) ta[i & 3] = ta_of(i + 4);
+        const int db = i >> 2, ks = (i >> 1) & 1;
+        if (i & 1) dk[db] = mfma(av, dsb[ks], dk[db]);
+        else dv[db] = mfma(av, pb[ks], dv[db]);
+        __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+        if (i + 4 < 16) __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
       }
     }
   }
   // add the query halves: waves 2, 3 hand their sums to waves 0, 1 through
   // LDS (element-major, so the lanes of a store hit consecutive banks)
-  // [16 NDB elements][2 key halves][NW / 4 d halves][64 lanes] = 32 KB
-  float* red = reinterpret_cast<float*>(&qd[0][0]);
-  auto ri = [&](int e) { return ((e * 2 + kh) * (NW / 4) + dh) * 64 + lane; };
+  // [16 NDB elements][2 key halves][64 lanes] = 32 KB
+  float* red = reinterpret_cast<float*>(&qd[0][0][0]);   // 32 KB: ring buffer 0
+  auto ri = [&](int e) { return (e * 2 + kh) * 64 + lane; };
   const bool out = key < cnt;
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
@@ -590,7 +814,7 @@ __global__ void __launch_bounds__(64 * NW) bwd_dkdv_bf16_kernel(Geom g, BwdBufs 
             bf16x4 v4;
 #pragma unroll
             for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(acc[db][4 * gq + e] * sc);
-            *reinterpret_cast<bf16x4*>(dst + (dh * NDB + db) * 32 + 8 * gq + 4 * half) = v4;
+            *reinterpret_cast<bf16x4*>(dst + db * 32 + 8 * gq + 4 * half) = v4;
           }
       } else {   // shared block: add this run's sums into the fp32 accumulators
         float* dst = (pass == 0 ? a.dk_acc : a.dv_acc) + row0;
@@ -598,7 +822,7 @@ __global__ void __launch_bounds__(64 * NW) bwd_dkdv_bf16_kernel(Geom g, BwdBufs 
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
           for (int i = 0; i < 16; ++i)
-            atomicAdd(dst + (dh * NDB + db) * 32 + 8 * (i / 4) + 4 * half + (i % 4), acc[db][i]);
+            atomicAdd(dst + db * 32 + 8 * (i / 4) + 4 * half + (i % 4), acc[db][i]);
       }
     }
   }
@@ -611,7 +835,7 @@ __global__ void __launch_bounds__(64 * NW) bwd_dkdv_bf16_kernel(Geom g, BwdBufs 
   __syncthreads();
   if (!last) return;
   __threadfence();
-  for (int e = tid; e < cnt * 128; e += NT) {
+  for (int e = tid; e < cnt * 128; e += 256) {
     const float vk = __hip_atomic_load(a.dk_acc + kb + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const float vv = __hip_atomic_load(a.dv_acc + kb + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     ((__bf16*)a.dk)[kb + e] = (__bf16)(vk * c);
@@ -638,10 +862,14 @@ int launch_bwd(const Geom& g, int dtype, const BwdBufs& b, int64_t kv_elems, int
       const int64_t counters = 2 * (int64_t)slots * g.hkv;   // kcount and kdone, adjacent
       bwd_zero_kernel<<<(unsigned)std::min<int64_t>((counters + 255) / 256, 65536), 256, 0, st>>>(
           (uint32_t*)b.kcount, counters);
+      const int nk = (int)slots * g.hkv;   // (key block slot, KV head) lists
       bwd_count_kernel<<<(unsigned)((g.rows + 3) / 4), 256, 0, st>>>(g, b);
+      bwd_kscan_kernel<<<1, 1024, 0, st>>>(b.kcount, b.kptr, b.witem, nk, g.share ? g.group : 1, b.split_target,
+                                           b.max_chunks, b.witems);
+      bwd_klist_kernel<<<(unsigned)((nk + 3) / 4), 256, 0, st>>>(g, b, nk);
       bwd_split_clear_kernel<<<dim3(slots, (unsigned)g.hkv), 256, 0, st>>>(g, b);
       bwd_dq_bf16_kernel<<<dim3((unsigned)g.rows, (unsigned)g.hpr), 128, 0, st>>>(g, b);
-      bwd_dkdv_bf16_kernel<4><<<dim3(slots, (unsigned)g.hkv, (unsigned)b.max_chunks), 256, 0, st>>>(g, b);
+      bwd_dkdv_bf16_kernel<<<(unsigned)b.witems, 256, 0, st>>>(g, b);
     }
     return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
   }

@@ -59,6 +59,13 @@ struct BwdBufs {
   // key block, [key block slot][KV head]; key blocks with more pairs than
   // split_target are shared by several workgroups that add into dk_acc / dv_acc
   int *kcount, *kdone;
+  // key-major lists: the rows listing each (key block slot, KV head), as
+  // r * (routing heads per KV head) + head, at klist[kptr[i] .. kptr[i + 1])
+  int *kptr, *klist;
+  // dK/dV workgroups: (slot x KV head) << 4 | chunk, -1 past the last; witems
+  // bounds their number (the launch's grid)
+  int* witem;
+  int witems;
   int split_target, max_chunks;
 };
 int launch_bwd(const Geom& g, int dtype, const BwdBufs& b, int64_t kv_elems, int kv_tail, hipStream_t st);

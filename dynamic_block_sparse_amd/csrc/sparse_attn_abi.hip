@@ -194,6 +194,22 @@ int64_t lse_elems(const Plan& pl) {
   return pl.g.varlen ? (int64_t)pl.g.hq * pl.g.lse_head : (int64_t)pl.g.batch * pl.g.lse_seq;
 }
 
+// Backward dK/dV split: a key block listed by more than split_target (row,
+// head) pairs is shared by up to max_chunks (<= 9) workgroups; split_target
+// is an eighth of the most a block can have, at least 32.  Work items: one
+// per (key block slot, KV head) plus at most one more per split_target pairs.
+void bwd_split(const Plan& pl, int* split_target, int* max_chunks) {
+  const int max_units = pl.g.max_blocks * pl.g.group;
+  *split_target = std::max(32, max_units / 8);
+  *max_chunks = (max_units + *split_target - 1) / *split_target;
+}
+int64_t bwd_work_items(const Plan& pl) {
+  int st, mc;
+  bwd_split(pl, &st, &mc);
+  const int ngh = pl.g.share ? pl.g.group : 1;
+  return key_slots(pl) * pl.g.hkv + pl.nnz_cap * ngh / st + 1;
+}
+
 size_t ws_size(const Plan& pl, int which, int splits) {
   size_t sz = ws_cu_blocks(pl);
   if (which == 0) {
@@ -209,6 +225,10 @@ size_t ws_size(const Plan& pl, int which, int splits) {
     sz += align_up((size_t)lse_elems(pl) * sizeof(float));
     sz += 2 * align_up((size_t)kv_elems(pl) * sizeof(float));
     sz += align_up((size_t)2 * key_slots(pl) * pl.g.hkv * sizeof(int));
+    // key-major pair lists: offsets per (key block slot, KV head) and one entry per listed tile
+    sz += align_up((size_t)(key_slots(pl) * pl.g.hkv + 1) * sizeof(int));
+    sz += align_up((size_t)pl.nnz_cap * sizeof(int));
+    sz += align_up((size_t)bwd_work_items(pl) * sizeof(int));
   }
   return sz;
 }
@@ -324,11 +344,16 @@ int sparse_attn_bwd(const sa_problem* p, const sa_route_cfg* rc, const int32_t* 
   w += align_up((size_t)n * sizeof(float));
   b.kcount = reinterpret_cast<int*>(w);
   b.kdone = b.kcount + key_slots(pl) * pl.g.hkv;
-  // a workgroup takes at most split_target (row, head) pairs of a key block:
-  // an eighth of the most a block can have, at least 32, so at most 8 share one
-  const int max_units = pl.g.max_blocks * pl.g.group;
-  b.split_target = std::max(32, max_units / 8);
-  b.max_chunks = (max_units + b.split_target - 1) / b.split_target;
+  w += align_up((size_t)2 * key_slots(pl) * pl.g.hkv * sizeof(int));
+  b.kptr = reinterpret_cast<int*>(w);
+  w += align_up((size_t)(key_slots(pl) * pl.g.hkv + 1) * sizeof(int));
+  b.klist = reinterpret_cast<int*>(w);
+  w += align_up((size_t)pl.nnz_cap * sizeof(int));
+  b.witem = reinterpret_cast<int*>(w);
+  bwd_split(pl, &b.split_target, &b.max_chunks);
+  const int64_t witems = bwd_work_items(pl);
+  if (witems > INT32_MAX) return SA_ERR_UNSUPPORTED;
+  b.witems = (int)witems;
   const int kv_tail = !pl.g.varlen && p->kv_capacity > p->seqlen;   // keys no query can attend
   return launch_bwd(pl.g, p->dtype, b, n, kv_tail, hs);
 }
