@@ -383,6 +383,187 @@ __global__ void __launch_bounds__(128) bwd_dq_bf16_kernel(Geom g, BwdBufs a) {
   if (qvalid) store_acc(dq, c, (__bf16*)a.dq + q_offset(g, ri.s, head, ri.tok0, qpos), half);
 }
 
+// Global -> LDS loads (see the forward kernels): lane l's 16 bytes (4 bytes)
+// from base + off land at lds_wave_base + 16 l (+ 4 l).  Issued as inline asm
+// so the compiler does not wait for them at unrelated LDS reads; the loop
+// waits for them explicitly before the barrier that publishes a pair.
+__device__ __forceinline__ void bwd_load_lds16(const unsigned char* base, uint32_t off, const unsigned char* lds) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(SA_LDS const unsigned char*)lds;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(m0)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void bwd_load_lds4(const unsigned char* base, uint32_t off, const unsigned char* lds) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(SA_LDS const unsigned char*)lds;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "s"(m0)
+               : "memory", "m0");
+}
+__device__ __forceinline__ const unsigned char* bwd_uniform(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const unsigned char*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+template <int N>
+__device__ __forceinline__ void bwd_wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// wait until at most `pairs` younger pairs' loads (L per pair) are in flight
+template <int L>
+__device__ __forceinline__ void bwd_wait_pairs(int pairs) {
+  if (pairs >= 2) bwd_wait_vmcnt<2 * L>();
+  else if (pairs == 1) bwd_wait_vmcnt<L>();
+  else bwd_wait_vmcnt<0>();
+}
+
+// dQ for rows serving 2 or 4 query heads (routing shared across a KV head's
+// group): one workgroup per (worklist row, pair of its heads), 4 wavefronts,
+// wave w taking query head 2 blockIdx.y + w / 2 and query rows 32 (w % 2) ..
+// + 32.  The row's listed K and V tiles are read once for both heads: they
+// stream global -> LDS through a ring of NB tiles (each wavefront loads its
+// share, issued NB - 1 tiles ahead, one barrier per tile).  Each lane keeps
+// its query row of Q and dO (the B operands of S^T = K Q^T and dP^T =
+// V dO^T) in registers, forms P and dS for one 32-key half of the tile at a
+// time, and accumulates dQ^T += K^T dS^T (K^T by LDS transpose reads).  It
+// also writes D_i = dO_i . O_i, which the dK/dV kernel reads.  (Four heads
+// in one workgroup of 8 wavefronts need more than the 256 registers a
+// wavefront may then hold.)
+__global__ void __launch_bounds__(256) bwd_dq_rows_bf16_kernel(Geom g, BwdBufs a) {
+  constexpr int NW = 4, NB = 3, TILE = 64 * 256;
+  constexpr int LPT = 16 / NW;   // 1 KB slices of K (and as many of V) per wavefront and tile
+  static_assert(NW * LPT * 1024 == TILE, "the wavefronts' slices cover the tile once");
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[NB][2][TILE];   // [slot][K, V]
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t row = blockIdx.x;
+  const RowInfo ri = decode_row(g, row);
+  const int kvh = ri.h;   // shared routing: the routing head is the KV head
+  const int head = kvh * g.group + 2 * (int)blockIdx.y + wave / 2;
+  const int qpos = ri.r * kBlock + (wave & 1) * 32 + l32;
+  const bool qvalid = qpos < ri.len;
+  const int qsrc = min(qpos, ri.len - 1);   // rows past the end read the last row (masked)
+  const float c = 0.08838834764831845f, cl2 = c * kLog2e;
+  const int t0 = a.row_ptr[row], nt = a.row_ptr[row + 1] - t0;
+  const int jl0 = lane < nt ? a.col_idx[t0 + lane] : 0;
+  const int jl1 = lane + 64 < nt ? a.col_idx[t0 + 64 + lane] : 0;
+  auto tile_id = [&](int t) {
+    return t < 64 ? __builtin_amdgcn_readlane(jl0, t) : __builtin_amdgcn_readlane(jl1, t - 64);
+  };
+
+  // this wavefront's 1 KB slices of a tile: slice sl = wave + NW * ii holds
+  // rows 4 sl .. 4 sl + 3; lane l lands at row 4 sl + l / 16, chunk slot l % 16
+  // (K swizzled for row and transpose reads, V for row reads)
+  const unsigned char* const kbytes = (const unsigned char*)a.k;
+  const unsigned char* const vbytes = (const unsigned char*)a.v;
+  auto issue_tile = [&](int t, int slot) {
+    const int j = tile_id(t);
+    const int cnt = min(kBlock, ri.len - j * kBlock);
+    const int64_t kb = kv_block_offset(g, ri.s, kvh, ri.tok0, j) * 2;
+    const unsigned char* kbase = bwd_uniform(kbytes + kb);
+    const unsigned char* vbase = bwd_uniform(vbytes + kb);
+#pragma unroll
+    for (int ii = 0; ii < LPT; ++ii) {
+      const int sl = wave + NW * ii, r4 = 4 * sl + (lane >> 4), p = lane & 15;
+      const uint32_t rb = (uint32_t)min(r4, cnt - 1) * 256;   // keys past the end: a valid row (masked)
+      bwd_load_lds16(kbase, rb + ((p ^ tsw(r4)) << 4), &ring[slot][0][sl * 1024]);
+      bwd_load_lds16(vbase, rb + ((p ^ rsw(r4)) << 4), &ring[slot][1][sl * 1024]);
+    }
+  };
+  for (int t = 0; t < NB - 1; ++t)
+    if (t < nt) issue_tile(t, t);
+
+  // this lane's Q and dO row (d = 16 ks + 8 half .. + 8), D_i and lse
+  bf16x8 qreg[8], doreg[8];
+  float delta, lse2;
+  {
+    const int64_t qo = q_offset(g, ri.s, head, ri.tok0, qsrc) + 8 * half;
+    const __bf16* qp = (const __bf16*)a.q + qo;
+    const __bf16* dp = (const __bf16*)a.dout + qo;
+    const __bf16* op = (const __bf16*)a.o + qo;
+    float part = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      qreg[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 16 * ks));
+      doreg[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(dp + 16 * ks));
+      const bf16x8 ov = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(op + 16 * ks));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part = fmaf((float)doreg[ks][e], (float)ov[e], part);
+    }
+    delta = part + __shfl_xor(part, 32);
+    const int64_t lo = lse_offset(g, ri.s, head, ri.tok0, qsrc);
+    lse2 = a.lse[lo] * kLog2e;
+    if (qvalid && half == 0) a.delta[lo] = delta;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(qreg[ks]), "v"(doreg[ks]));
+    asm volatile("" ::"v"(lse2), "v"(jl0), "v"(jl1));
+  }
+
+  f32x16 dq[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dq[db][i] = 0.f;
+
+  for (int t = 0; t < nt; ++t) {
+    const int slot = t % NB;
+    const int younger = min(NB - 2, nt - 1 - t);   // tiles issued after t
+    if (younger >= 1) bwd_wait_vmcnt<2 * LPT>();
+    else bwd_wait_vmcnt<0>();
+    asm volatile("s_barrier" ::: "memory");   // tile t landed for every wave; slot (t - 1) % NB is read
+    if (t + NB - 1 < nt) issue_tile(t + NB - 1, (t + NB - 1) % NB);
+    const unsigned char* kt = ring[slot][0];
+    const unsigned char* vt = ring[slot][1];
+    const int j = tile_id(t);
+    bf16x8 dsb[2][2];
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2) {
+      // S^T and dP^T for keys 32 b2 .. + 32 of the tile; the K and V rows of
+      // step ks + 1 are read while step ks multiplies
+      f32x16 sacc, dpacc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[i] = dpacc[i] = 0.f;
+      bf16x8 ok_[2], ov_[2];
+      auto rd = [&](int ks) {
+        ok_[ks & 1] = row8<true>(kt, 32 * b2 + l32, 2 * ks + half);
+        ov_[ks & 1] = row8<false>(vt, 32 * b2 + l32, 2 * ks + half);
+      };
+      rd(0);
+      __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        if (ks + 1 < 8) rd(ks + 1);
+        sacc = mfma(ok_[ks & 1], qreg[ks], sacc);
+        dpacc = mfma(ov_[ks & 1], doreg[ks], dpacc);
+        if (ks + 1 < 8) __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(kMfma, 2, 0);
+      }
+      // dS^T of this lane's query over the half's keys, as B operands
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kpos = j * kBlock + b2 * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+        const bool ok = qvalid && kpos <= qpos;
+        const float p = __builtin_amdgcn_exp2f(ok ? fmaf(sacc[i], cl2, -lse2) : -INFINITY);
+        dsb[b2][i / 8][i % 8] = (__bf16)(p * (dpacc[i] - delta));
+      }
+    }
+    // dQ^T += K^T dS^T: the transpose reads run four MFMAs ahead
+    bf16x8 ta[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ta[i] = tr8(kt, (i >> 1) & 1, i & 1, i >> 2, lane);
+    __builtin_amdgcn_sched_group_barrier(kDsRead, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int db = i >> 2, b2 = (i >> 1) & 1, ks = i & 1;
+      const bf16x8 av = ta[i & 3];
+      if (i + 4 < 16) ta[i & 3] = tr8(kt, ((i + 4) >> 1) & 1, (i + 4) & 1, (i + 4) >> 2, lane);
+      dq[db] = mfma(av, dsb[b2][ks], dq[db]);
+      __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+      if (i + 4 < 16) __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+    }
+  }
+  if (qvalid) store_acc(dq, c, (__bf16*)a.dq + q_offset(g, ri.s, head, ri.tok0, qpos), half);
+}
+
 // Worklist row id of (sequence s, routing head h, query block r).
 __device__ __forceinline__ int64_t row_id(const Geom& g, int s, int h, int r, int blk0, int nb) {
   if (!g.varlen) return ((int64_t)s * g.hr + h) * (nb - g.qblk0) + (r - g.qblk0);
@@ -536,27 +717,6 @@ __global__ void __launch_bounds__(256) bwd_klist_kernel(Geom g, BwdBufs a, int n
   for (int t = w + lane; t < p1; t += 64) a.klist[t] = -1;
 }
 
-// Global -> LDS loads (see the forward kernels): lane l's 16 bytes (4 bytes)
-// from base + off land at lds_wave_base + 16 l (+ 4 l).  Issued as inline asm
-// so the compiler does not wait for them at unrelated LDS reads; the loop
-// waits for them explicitly before the barrier that publishes a pair.
-__device__ __forceinline__ void bwd_load_lds16(const unsigned char* base, uint32_t off, const unsigned char* lds) {
-  const uint32_t m0 = (uint32_t)(uintptr_t)(SA_LDS const unsigned char*)lds;
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(m0)
-               : "memory", "m0");
-}
-__device__ __forceinline__ void bwd_load_lds4(const unsigned char* base, uint32_t off, const unsigned char* lds) {
-  const uint32_t m0 = (uint32_t)(uintptr_t)(SA_LDS const unsigned char*)lds;
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "s"(m0)
-               : "memory", "m0");
-}
-__device__ __forceinline__ const unsigned char* bwd_uniform(const void* p) {
-  const uint64_t v = (uint64_t)(uintptr_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return (const unsigned char*)(uintptr_t)(((uint64_t)hi << 32) | lo);
-}
-
 // One workgroup per (key block slot, KV head, chunk), 4 wavefronts: wave w
 // owns keys 32 (w & 1) .. + 32 and query rows 32 (w >> 1) .. + 32 of every
 // pair, forms that 32 x 32 block of S = Q K^T and dP = dO V^T (one key per
@@ -571,18 +731,6 @@ __device__ __forceinline__ const unsigned char* bwd_uniform(const void* p) {
 // by up to max_chunks workgroups, each taking an equal run of its pairs: they
 // add into fp32 accumulators with atomics and the last one to finish
 // converts them.
-template <int N>
-__device__ __forceinline__ void bwd_wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-// wait until at most `pairs` younger pairs' loads (L per pair) are in flight
-template <int L>
-__device__ __forceinline__ void bwd_wait_pairs(int pairs) {
-  if (pairs >= 2) bwd_wait_vmcnt<2 * L>();
-  else if (pairs == 1) bwd_wait_vmcnt<L>();
-  else bwd_wait_vmcnt<0>();
-}
-
 __global__ void __launch_bounds__(256) bwd_dkdv_bf16_kernel(Geom g, BwdBufs a) {
   constexpr int NDB = 4, TILE = 64 * 256, NB = 3;
   __shared__ __attribute__((aligned(1024))) unsigned char qd[NB][2][TILE];   // [buffer][Q, dO]
@@ -868,7 +1016,10 @@ int launch_bwd(const Geom& g, int dtype, const BwdBufs& b, int64_t kv_elems, int
                                            b.max_chunks, b.witems);
       bwd_klist_kernel<<<(unsigned)((nk + 3) / 4), 256, 0, st>>>(g, b, nk);
       bwd_split_clear_kernel<<<dim3(slots, (unsigned)g.hkv), 256, 0, st>>>(g, b);
-      bwd_dq_bf16_kernel<<<dim3((unsigned)g.rows, (unsigned)g.hpr), 128, 0, st>>>(g, b);
+      if (g.share && (g.hpr == 2 || g.hpr == 4))
+        bwd_dq_rows_bf16_kernel<<<dim3((unsigned)g.rows, (unsigned)(g.hpr / 2)), 256, 0, st>>>(g, b);
+      else
+        bwd_dq_bf16_kernel<<<dim3((unsigned)g.rows, (unsigned)g.hpr), 128, 0, st>>>(g, b);
       bwd_dkdv_bf16_kernel<<<(unsigned)b.witems, 256, 0, st>>>(g, b);
     }
     return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
