@@ -11,7 +11,8 @@ Pinned (tests/test_oracle_problem.py): row_table against a hand-written row
 list for ragged sequences (prefill and decode); the decode branch of
 attention_rows against torch's fp64 SDPA over all cached keys (partial last
 blocks, mixed cache lengths) and against plain loops on a sparse block list;
-a packed ragged batch against its sequences done one at a time.
+a packed ragged batch against its sequences done one at a time; a packed
+batch with empty sequences against the same batch without them.
 
 Inputs are per-sequence float64 arrays:
   qs[s]  [Hq, n_q_tokens, d]   (decode: n_q_tokens = 1)
@@ -61,6 +62,8 @@ def route(qs, ks, lengths, b, mode, qpool, share_gqa, select, k_b, k_min, tau_re
     index = {(s, h, r): i for i, (s, h, r, _n) in enumerate(table)}
     for s, length in enumerate(lengths):
         if seqs is not None and s not in seqs:
+            continue
+        if length == 0:   # a sequence of no tokens has no query blocks, so no rows
             continue
         J, sc = routing.route_sequence(qs[s], ks[s], length, b, mode, qpool, share_gqa,
                                        select, k_b, k_min, tau_rel, forced_first,

@@ -12,7 +12,8 @@ oracle.counting.effective_pairs_prefill, against things other than the oracle.
 * the decode branch on a sparse block list equals a plain-loop softmax over
   exactly the keys of the listed blocks
 * a packed 3-sequence ragged batch routed, worklisted and attended as one
-  problem equals each sequence done alone, concatenated in row order
+  problem equals each sequence done alone, concatenated in row order; a
+  packed batch with empty sequences equals the batch without them
 * effective_pairs_prefill with every causal block listed equals Eq 8's
   n (n + 1) / 2 printed for n = 8192 ([P2] §2.2 "a recomputable block
   budget"), and with the diagonal block alone the closed form N b (b + 1) / 2
@@ -131,6 +132,38 @@ def test_packed_batch_equals_sequences_alone(share):
                 assert np.array_equal(o1["o"], o2["o"])
             i += 1
     assert i == len(J_all)
+
+
+def test_packed_batch_with_empty_sequences():
+    """Sequences of no tokens contribute no rows: the batch with them routes,
+    worklists and attends exactly like the batch without them."""
+    b, d, hq, hkv = 8, 4, 4, 2
+    full = [37, 0, 20, 0, 0, 9]
+    qs = [_rand((hq, L, d), 70 + s) for s, L in enumerate(full)]
+    ks = [_rand((hkv, L, d), 80 + s) for s, L in enumerate(full)]
+    vs = [_rand((hkv, L, d), 90 + s) for s, L in enumerate(full)]
+    keep = [s for s, L in enumerate(full) if L]
+
+    def run(idx):
+        lens = [full[s] for s in idx]
+        J, _ = problem.route([qs[s] for s in idx], [ks[s] for s in idx], lens, b, "prefill", "mean", True,
+                             "topk", 3, 1, 2.0, True)
+        w = problem.worklist(J, lens, b, "prefill", hkv, True, 5)
+        rows = list(range(len(J)))
+        blocks = [w["col_idx"][w["row_ptr"][i]:w["row_ptr"][i + 1]].tolist() for i in rows]
+        att = problem.attention_rows([qs[s] for s in idx], [ks[s] for s in idx], [vs[s] for s in idx], lens, b,
+                                     "prefill", True, rows, blocks)
+        return J, w, att
+
+    Ja, wa, aa = run(list(range(len(full))))
+    Jb, wb, ab = run(keep)
+    assert len(Ja) == len(Jb) == sum(-(-L // b) for L in full) * hkv
+    assert all(list(x) == list(y) for x, y in zip(Ja, Jb))
+    for key in ("row_ptr", "col_idx", "row_perm", "bucket_ptr"):
+        assert np.array_equal(wa[key], wb[key]), key
+    for i in aa:
+        for (h1, t1, o1), (h2, t2, o2) in zip(aa[i], ab[i]):
+            assert h1 == h2 and np.array_equal(o1["o"], o2["o"])
 
 
 def _golden():
