@@ -416,7 +416,7 @@ __device__ __forceinline__ void bwd_wait_pairs(int pairs) {
   else bwd_wait_vmcnt<0>();
 }
 
-// dQ for rows serving 2 or 4 query heads (routing shared across a KV head's
+// dQ for rows serving 2, 4 or 8 query heads (routing shared across a KV head's
 // group): one workgroup per (worklist row, pair of its heads), 4 wavefronts,
 // wave w taking query head 2 blockIdx.y + w / 2 and query rows 32 (w % 2) ..
 // + 32.  The row's listed K and V tiles are read once for both heads: they
@@ -1016,7 +1016,7 @@ int launch_bwd(const Geom& g, int dtype, const BwdBufs& b, int64_t kv_elems, int
                                            b.max_chunks, b.witems);
       bwd_klist_kernel<<<(unsigned)((nk + 3) / 4), 256, 0, st>>>(g, b, nk);
       bwd_split_clear_kernel<<<dim3(slots, (unsigned)g.hkv), 256, 0, st>>>(g, b);
-      if (g.share && (g.hpr == 2 || g.hpr == 4))
+      if (g.share && (g.hpr == 2 || g.hpr == 4 || g.hpr == 8))
         bwd_dq_rows_bf16_kernel<<<dim3((unsigned)g.rows, (unsigned)(g.hpr / 2)), 256, 0, st>>>(g, b);
       else
         bwd_dq_bf16_kernel<<<dim3((unsigned)g.rows, (unsigned)g.hpr), 128, 0, st>>>(g, b);

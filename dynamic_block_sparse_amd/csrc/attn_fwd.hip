@@ -512,7 +512,8 @@ __global__ void __launch_bounds__(512) prefill_bf16_pp_kernel(Geom g, FwdBufs a,
   const int64_t row = dense_or_listed_row<DENSE>(g, a, pos);
   const RowInfo ri = decode_row(g, row);
   const int kvh = g.share ? ri.h : ri.h / g.group;
-  const int head = (g.share ? ri.h * g.group : ri.h) + wave / 2;
+  // heads 4 blockIdx.y .. + 3 of the row (rows of 8 heads take two workgroups)
+  const int head = (g.share ? ri.h * g.group : ri.h) + 4 * (int)blockIdx.y + wave / 2;
   const int half = lane / 32, l32 = lane % 32;
   const int qpos = ri.r * kBlock + (wave % 2) * 32 + l32;
   const bool qvalid = qpos < ri.len;
@@ -766,7 +767,8 @@ int launch_prefill_t(const Geom& g, int dtype, const FwdBufs& b, hipStream_t st)
   // per XCD keep one head's K/V (4 MB at n = 8192) in that XCD's L2.
   // Four-head rows: the ping-pong kernel with 4-deep K and V rings (128 KB, one
   // workgroup per CU); its two wavefronts per SIMD alternate MFMA and softmax
-  // phases.  Two-head rows: the lock-step kernel, one stage.
+  // phases (eight-head rows: two of its workgroups per row).  Two-head rows:
+  // the lock-step kernel, one stage.
   // The lock-step kernel's grid comes from prefill_grid (persistent when the
   // rows fill few generations).
   const int run = g.hpr == 1 ? 128 : 32;   // rows per XCD run
@@ -786,6 +788,11 @@ int launch_prefill_t(const Geom& g, int dtype, const FwdBufs& b, hipStream_t st)
       // costs this kernel ~14 % in code generation, and with one workgroup
       // per CU its rows always fill many generations
       prefill_bf16_pp_kernel<4, DENSE><<<(unsigned)g.rows, 512, 0, st>>>(g, b, run);
+      break;
+    case 8:
+      // eight heads per row: two workgroups of the four-head kernel, one per
+      // head quad (each loads the row's tiles)
+      prefill_bf16_pp_kernel<4, DENSE><<<dim3((unsigned)g.rows, 2), 512, 0, st>>>(g, b, run);
       break;
     default: return SA_ERR_UNSUPPORTED;
   }

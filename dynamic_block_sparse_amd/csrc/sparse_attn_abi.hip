@@ -97,7 +97,8 @@ int validate(const sa_problem* p, const sa_route_cfg* rc, Plan* out) {
     return SA_ERR_INVALID_ARG;   // a block table pages, and seq_lens sizes, only a decode cache
   } else if (p->cu_seqlens) {
     if (p->kv_capacity != 0 || p->q_start != 0) return SA_ERR_INVALID_ARG;   // packed: no cache, no chunk
-    if (p->seqlen != 0 || p->total_tokens < 1 || p->total_blocks < p->batch ||
+    // sequences may be empty (no blocks, no rows); at least one block overall
+    if (p->seqlen != 0 || p->total_tokens < 1 || p->total_blocks < 1 ||
         p->max_blocks < 1 || p->max_blocks > p->total_blocks)
       return SA_ERR_INVALID_ARG;
     g.varlen = 1;
@@ -492,12 +493,11 @@ int sparse_attn_fwd(const sa_problem* p, const sa_route_cfg* rc, const int32_t* 
   if (!row_ptr || !col_idx || !row_perm || !q || !k || !v || !o) return SA_ERR_INVALID_ARG;
   if (num_splits < 0 || num_splits > 256) return SA_ERR_INVALID_ARG;
   if (p->dtype == SA_BF16 && p->head_dim != 128) return SA_ERR_UNSUPPORTED;
-  // bf16 kernels serve 1, 2 or 4 query heads per row in prefill (2 wavefronts
-  // per head in one workgroup), up to 8 in decode
+  // bf16 kernels serve 1, 2, 4 or 8 query heads per row (prefill: 2
+  // wavefronts per head, 8 heads as two workgroups of 4)
   if (p->dtype == SA_BF16) {
     const int h = pl.g.hpr;
-    const bool ok = h == 1 || h == 2 || h == 4 || (h == 8 && p->mode == SA_DECODE);
-    if (!ok) return SA_ERR_UNSUPPORTED;
+    if (!(h == 1 || h == 2 || h == 4 || h == 8)) return SA_ERR_UNSUPPORTED;
   }
   const int splits = resolve_splits(pl, num_splits);
   const size_t need = ws_size(pl, 2, splits);
@@ -530,7 +530,7 @@ int sparse_attn_fwd_dense(const sa_problem* p, const sa_route_cfg* rc, const voi
   if (!q || !k || !v || !o) return SA_ERR_INVALID_ARG;
   if (p->dtype == SA_BF16) {
     const int h = pl.g.hpr;
-    if (p->head_dim != 128 || !(h == 1 || h == 2 || h == 4)) return SA_ERR_UNSUPPORTED;
+    if (p->head_dim != 128 || !(h == 1 || h == 2 || h == 4 || h == 8)) return SA_ERR_UNSUPPORTED;
   }
   const size_t need = ws_size(pl, 2, 1);
   if (ws_bytes < need || (need && !ws)) return SA_ERR_WORKSPACE;

@@ -116,7 +116,8 @@ typedef struct sa_problem {
   int32_t seqlen;         /* fixed-length n, or decode cached length L; 0 for packed varlen */
   int32_t dtype;          /* SA_F32 or SA_BF16 (Q, K, V, O) */
   int32_t mode;           /* SA_PREFILL or SA_DECODE */
-  const int32_t* cu_seqlens; /* (device) [batch + 1] packed varlen offsets, else NULL */
+  const int32_t* cu_seqlens; /* (device) [batch + 1] packed varlen offsets, else NULL; a
+                             sequence may be empty (no blocks, no rows), the batch not */
   int32_t total_tokens;   /* varlen: cu_seqlens[batch] (host-known); else ignored */
   int32_t total_blocks;   /* varlen: sum_s ceil(len_s / b) (host-known); else ignored */
   int32_t max_blocks;     /* varlen: max_s ceil(len_s / b) (host-known); else ignored */
@@ -273,8 +274,10 @@ int sparse_attn_build_worklist_noalloc(const sa_problem* p, const sa_route_cfg* 
  *   num_splits groups (0 = library's choice; raised to at least
  *   ceil((k_b + forced) / 64)) whose partial (m, l, u) states are merged with
  *   Eq 3-5: inside one workgroup for up to 8 groups (no workspace), through
- *   fp32 states in the workspace and a second kernel for more.  Accumulation and softmax are fp32; bf16 inputs use
- *   bf16 matrix-core products with P rounded to bf16 before P V. */
+ *   fp32 states in the workspace and a second kernel for more.  Accumulation
+ *   and softmax are fp32; bf16 inputs use bf16 matrix-core products with P
+ *   rounded to bf16 before P V.  bf16 needs head_dim 128 and 1, 2, 4 or 8
+ *   query heads per row (else SA_ERR_UNSUPPORTED). */
 int sparse_attn_fwd(const sa_problem* p, const sa_route_cfg* rc, const int32_t* row_ptr,
                     const int32_t* col_idx, const int32_t* row_perm, const void* q,
                     const void* k, const void* v, void* o, float* lse, int32_t num_splits,
@@ -294,7 +297,7 @@ int sparse_attn_fwd(const sa_problem* p, const sa_route_cfg* rc, const int32_t* 
  *   q, k, v, o, lse  as for sparse_attn_fwd (lse nullable)
  *   ws      (device) sparse_attn_workspace_size(p, rc, 2, 0) bytes (the block
  *           offsets of a packed batch; 0 otherwise)
- * bf16 needs head_dim 128 and 1, 2 or 4 query heads per row; fp32 takes
+ * bf16 needs head_dim 128 and 1, 2, 4 or 8 query heads per row; fp32 takes
  * head_dim 64 or 128.  Returns SA_ERR_UNSUPPORTED for decode problems. */
 int sparse_attn_fwd_dense(const sa_problem* p, const sa_route_cfg* rc, const void* q, const void* k,
                           const void* v, void* o, float* lse, void* ws, size_t ws_bytes, void* stream);

@@ -42,6 +42,8 @@ CASES = [
     ("chunked_bf16", "bf16", 128, None, 1, 2, 2, 900, 512, 1024, 4, False, False, 1),
     ("varlen_bf16_gqa", "bf16", 128, [300, 577, 64, 1000], 4, 8, 2, 0, 0, 0, 4, True, True, 2),
     ("varlen_bf16_per_head", "bf16", 128, [700, 130], 2, 4, 2, 0, 0, 0, 3, False, False, 1),
+    ("gqa8_shared", "bf16", 128, None, 1, 16, 2, 500, 0, 0, 4, True, False, 1),
+    ("varlen_empty_seqs", "bf16", 128, [64, 0, 300, 0, 1], 5, 8, 2, 0, 0, 0, 4, True, True, 1),
 ]
 
 

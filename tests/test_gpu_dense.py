@@ -98,6 +98,8 @@ CASES = [
     ("varlen_mha", "bf16", 128, [200, 64, 77], 2, 2, False, False, 0, 0),
     ("f32_d64_n300", "f32", 64, [300], 2, 2, False, True, 0, 0),
     ("chunked_q128_cap448", "bf16", 128, [400], 4, 4, False, True, 448, 128),
+    ("gqa8_shared_n500", "bf16", 128, [500], 16, 2, True, True, 0, 0),
+    ("varlen_empty_seqs", "bf16", 128, [64, 0, 300, 0, 1], 8, 2, True, False, 0, 0),
 ]
 
 

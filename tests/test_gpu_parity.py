@@ -74,6 +74,9 @@ SMALL = [
                            k_b=6, share_gqa=False, forced_first=False),
     wk.PREFILL_GQA.replace(name="gqa_small_g2_b1_hq4_hkv2_n900", batch=1, heads_q=4, heads_kv=2, seqlen=900,
                            k_b=7),
+    # eight query heads per row: two workgroups of the four-head kernel per row
+    wk.PREFILL_GQA.replace(name="gqa_small_g8_b1_hq16_hkv2_n900", batch=1, heads_q=16, heads_kv=2, seqlen=900,
+                           k_b=7),
     # local window of forced blocks ([P2] §3.2 union), alone and with the sink
     wk.PREFILL_MHA.replace(name="mha_small_h2_n1000_kb12_win4", heads_q=2, heads_kv=2, seqlen=1000, k_b=12,
                            window=4),
@@ -98,6 +101,16 @@ def test_small_varlen_threshold(dev):
     w = inp.w
     run = run_gpu(w, inp)
     _full_check(w, inp, run)
+
+
+def test_small_varlen_with_empty_sequences(dev):
+    """Sequences of no tokens in a packed batch: no blocks, no rows."""
+    w = wk.VARLEN.replace(name="varlen_small_empty_seqs", heads_q=8, heads_kv=2, k_b=16)
+    lengths = [64, 0, 700, 0, 1, 1344, 0]
+    print(f"case {w.name} lengths {lengths}", flush=True)
+    inp = wk.make_inputs(w, dev, lengths=lengths)
+    w = inp.w
+    _full_check(w, inp, run_gpu(w, inp))
 
 
 @pytest.mark.parametrize("splits", [1, 2, 3, 8, 16])
