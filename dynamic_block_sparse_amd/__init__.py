@@ -404,7 +404,6 @@ def build_worklist(prob: Problem, cfg: RouteConfig, J: torch.Tensor, out: Option
     _on_device("build_worklist", dev, J=J, row_ptr=out.row_ptr, col_idx=out.col_idx, row_perm=out.row_perm,
                bucket_ptr=out.bucket_ptr, err=out.err, cu_seqlens=prob.cu_seqlens,
                block_table=prob.block_table, seq_lens=prob.seq_lens)
-    out.err.zero_()
     p, c = prob.to_c(), cfg.to_c()
     wsb = workspace_size(prob, cfg, 1)
     ws = _use_workspace("build_worklist", workspace, wsb, dev)
@@ -418,7 +417,7 @@ def build_worklist(prob: Problem, cfg: RouteConfig, J: torch.Tensor, out: Option
 def build_worklist_noalloc(prob: Problem, cfg: RouteConfig, J: torch.Tensor, out: Worklist) -> Worklist:
     """sparse_attn_build_worklist_noalloc: the worklist of build_worklist into the
     caller's preallocated `out` (alloc_worklist), with the library's static device
-    scratch in place of a workspace; allocates nothing (err is cleared by a fill)."""
+    scratch in place of a workspace; allocates nothing."""
     lib = load_library()
     rows = sizes(prob, cfg).rows
     _require("build_worklist_noalloc", "J", J, (rows, cfg.k_b), torch.int32)
@@ -432,7 +431,6 @@ def build_worklist_noalloc(prob: Problem, cfg: RouteConfig, J: torch.Tensor, out
     if need > NOALLOC_SCRATCH_BYTES:
         raise ValueError(f"build_worklist_noalloc: the problem needs {need} bytes of scratch, more than the "
                          f"{NOALLOC_SCRATCH_BYTES} the library holds ({rows} rows)")
-    out.err.zero_()
     p, c = prob.to_c(), cfg.to_c()
     _check("sparse_attn_build_worklist_noalloc", lib.sparse_attn_build_worklist_noalloc(
         ctypes.byref(p), ctypes.byref(c), _ptr(J), _ptr(out.row_ptr), _ptr(out.col_idx),

@@ -32,8 +32,7 @@ __device__ __forceinline__ int bucket_of(int len) {
 __global__ void __launch_bounds__(64) wl_rows_kernel(Geom g, sa_route_cfg rc, int nbits,
                                                      const int32_t* __restrict__ J,
                                                      int32_t* __restrict__ tmp_cols,
-                                                     int32_t* __restrict__ tmp_len,
-                                                     int32_t* __restrict__ err) {
+                                                     int32_t* __restrict__ tmp_len) {
   __shared__ uint32_t keys[2 * kWave];
   const int lane = threadIdx.x;
   const int64_t row = blockIdx.x;
@@ -101,15 +100,15 @@ __global__ void __launch_bounds__(64) wl_rows_kernel(Geom g, sa_route_cfg rc, in
   int32_t* out = tmp_cols + row * kWidthPad;
   if (u0) out[__popcll(m0 & below)] = (int32_t)k0;
   if (u1) out[n0 + __popcll(m1 & below)] = (int32_t)k1;
-  if (lane == 0) tmp_len[row] = n0 + __popcll(m1);
-  // OR the row's error bits into the caller's word (one atomic per bad row)
+  // the row's length, and above it the OR of its lanes' error bits (the
+  // finishing pass ORs them over all rows into the caller's word)
   const uint64_t er = __ballot(ebits & SA_WL_ERR_RANGE);
   const uint64_t ea = __ballot(ebits & SA_WL_ERR_ACAUSAL);
   const uint64_t ep = __ballot(ebits & SA_WL_ERR_PAGE);
   const uint64_t el = __ballot(ebits & SA_WL_ERR_LENGTH);
-  if (lane == 0 && (er | ea | ep | el))
-    atomicOr(err, (er ? SA_WL_ERR_RANGE : 0) | (ea ? SA_WL_ERR_ACAUSAL : 0) | (ep ? SA_WL_ERR_PAGE : 0) |
-                      (el ? SA_WL_ERR_LENGTH : 0));
+  const int rowbits = (er ? SA_WL_ERR_RANGE : 0) | (ea ? SA_WL_ERR_ACAUSAL : 0) | (ep ? SA_WL_ERR_PAGE : 0) |
+                      (el ? SA_WL_ERR_LENGTH : 0);
+  if (lane == 0) tmp_len[row] = (n0 + __popcll(m1)) | (rowbits << 16);
 }
 
 // Step 2 for rows c0 .. c0 + NT - 1 (c0 = NT * block).  Thread t first sums,
@@ -126,7 +125,8 @@ __global__ void __launch_bounds__(NT) wl_finish_kernel(int64_t rows, int n_bucke
                                                         int32_t* __restrict__ row_ptr,
                                                         int32_t* __restrict__ col_idx,
                                                         int32_t* __restrict__ row_perm,
-                                                        int32_t* __restrict__ bucket_ptr) {
+                                                        int32_t* __restrict__ bucket_ptr,
+                                                        int32_t* __restrict__ err) {
   constexpr int K = kMaxBuckets + 1;   // [0] length sum, [1 + b] rows in bucket b
   constexpr int NW = NT / kWave;
   __shared__ int red[NW][2 * K];
@@ -135,6 +135,7 @@ __global__ void __launch_bounds__(NT) wl_finish_kernel(int64_t rows, int n_bucke
   const int64_t c0 = (int64_t)blockIdx.x * NT;
   // ---- totals over all rows and over the rows before this chunk
   int all[K], pre[K];
+  int ebits = 0;   // error bits of every row (workgroup 0 writes their OR to err)
 #pragma unroll
   for (int k = 0; k < K; ++k) all[k] = pre[k] = 0;
   // UP lengths per thread are loaded before any is used (clamped to the last
@@ -144,6 +145,11 @@ __global__ void __launch_bounds__(NT) wl_finish_kernel(int64_t rows, int n_bucke
     int lens[UP];
 #pragma unroll
     for (int u = 0; u < UP; ++u) lens[u] = tmp_len[min(r0 + (int64_t)u * NT, rows - 1)];
+#pragma unroll
+    for (int u = 0; u < UP; ++u) {
+      ebits |= lens[u] >> 16;   // a clamped repeat of the last row adds nothing new
+      lens[u] &= 0xffff;
+    }
 #pragma unroll
     for (int u = 0; u < UP; ++u) {
       const int64_t r = r0 + (int64_t)u * NT;
@@ -172,10 +178,19 @@ __global__ void __launch_bounds__(NT) wl_finish_kernel(int64_t rows, int n_bucke
       red[wave][K + k] = pre[k];
     }
   }
+  if (blockIdx.x == 0) {   // the OR of every row's error bits
+    __shared__ int eor;
+    if (tid == 0) eor = 0;
+    __syncthreads();
+    const uint64_t any = __ballot(ebits != 0);
+    if (any) atomicOr(&eor, ebits);
+    __syncthreads();
+    if (tid == 0) *err = eor;
+  }
   // ---- this thread's row and the exclusive scan of the chunk
   const int64_t r = c0 + tid;
   const bool valid = r < rows;
-  const int len = valid ? tmp_len[r] : 0;
+  const int len = valid ? (tmp_len[r] & 0xffff) : 0;
   const int bk = valid ? bucket_of(len) : -1;
   int v[K], inc[K];
   v[0] = len;
@@ -273,16 +288,16 @@ int launch_worklist(const Geom& g, const sa_route_cfg& rc, int width_max, int n_
   if (width_max > kWidthPad || n_buckets > kMaxBuckets) return SA_ERR_UNSUPPORTED;
   int nbits = 1;
   while ((1 << nbits) < g.max_blocks) ++nbits;
-  wl_rows_kernel<<<(unsigned)g.rows, 64, 0, st>>>(g, rc, nbits, b.J, b.tmp_cols, b.tmp_len, b.err);
+  wl_rows_kernel<<<(unsigned)g.rows, 64, 0, st>>>(g, rc, nbits, b.J, b.tmp_cols, b.tmp_len);
   if (hipGetLastError() != hipSuccess) return SA_ERR_HIP;
   if (g.rows <= 1024)
     wl_finish_kernel<64><<<(unsigned)((g.rows + 63) / 64), 64, 0, st>>>(g.rows, n_buckets, b.tmp_cols, b.tmp_len,
                                                                        b.row_ptr, b.col_idx, b.row_perm,
-                                                                       b.bucket_ptr);
+                                                                       b.bucket_ptr, b.err);
   else
     wl_finish_kernel<256><<<(unsigned)((g.rows + 255) / 256), 256, 0, st>>>(g.rows, n_buckets, b.tmp_cols,
                                                                           b.tmp_len, b.row_ptr, b.col_idx,
-                                                                          b.row_perm, b.bucket_ptr);
+                                                                          b.row_perm, b.bucket_ptr, b.err);
   return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 

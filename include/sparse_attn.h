@@ -89,7 +89,7 @@ extern "C" {
 #define SA_ERR_WORKSPACE 3     /* workspace or output capacity too small */
 #define SA_ERR_HIP 4           /* a HIP launch failed */
 
-/* Device error bits written (OR-ed) into the worklist's `err` word. */
+/* Device error bits of the worklist's `err` word (their OR over all rows). */
 #define SA_WL_ERR_RANGE 1      /* an id < -1 or >= the sequence's block count */
 #define SA_WL_ERR_ACAUSAL 2    /* prefill: an id after the row's query block */
 #define SA_WL_ERR_PAGE 4       /* paged decode cache: the block's page lies outside the pool */
@@ -232,7 +232,8 @@ int sparse_attn_route(const sa_problem* p, const sa_route_cfg* rc, const void* q
  *   row_perm    (device) [rows] rows sorted by (bucket asc, row asc)
  *   bucket_ptr  (device) [n_buckets + 1] row_perm ranges per bucket; bucket of
  *               a row = smallest power of two >= max(length, 4)
- *   err         (device) one int32, OR-ed with SA_WL_ERR_* bits (caller zeroes it)
+ *   err         (device) one int32, set to the OR of the SA_WL_ERR_* bits of
+ *               every row (0: no entry was dropped); no need to clear it first
  *   Each row = ascending unique({valid J entries} U forced blocks). */
 int sparse_attn_build_worklist(const sa_problem* p, const sa_route_cfg* rc, const int32_t* J,
                                int32_t* row_ptr, int32_t* col_idx, int64_t nnz_cap,

@@ -103,6 +103,27 @@ def test_small_varlen_threshold(dev):
     _full_check(w, inp, run)
 
 
+def test_worklist_err_is_written_not_accumulated(dev):
+    """err holds the OR of this call's row error bits: a stale value is overwritten."""
+    w = wk.PREFILL_MHA.replace(name="mha_err_word", heads_q=2, heads_kv=2, seqlen=600)
+    inp = wk.make_inputs(w, dev)
+    prob, cfg = dbs.problem_for(w, inp), dbs.config_for(w)
+    J, _ = dbs.route(prob, cfg, inp.q, inp.k)
+    out = dbs.alloc_worklist(prob, cfg, dev)
+    out.err.fill_(0x7fff)
+    dbs.build_worklist(prob, cfg, J, out=out)
+    torch.cuda.synchronize()
+    assert int(out.err.item()) == 0
+    bad = J.clone()
+    bad[3, 0] = 10_000                     # out of range: SA_WL_ERR_RANGE
+    dbs.build_worklist(prob, cfg, bad, out=out)
+    torch.cuda.synchronize()
+    assert int(out.err.item()) == dbs.SA_WL_ERR_RANGE
+    dbs.build_worklist(prob, cfg, J, out=out)
+    torch.cuda.synchronize()
+    assert int(out.err.item()) == 0
+
+
 def test_small_varlen_with_empty_sequences(dev):
     """Sequences of no tokens in a packed batch: no blocks, no rows."""
     w = wk.VARLEN.replace(name="varlen_small_empty_seqs", heads_q=8, heads_kv=2, k_b=16)
