@@ -27,7 +27,10 @@ struct WorklistBufs {
   const int32_t* J;
   int32_t *row_ptr, *col_idx, *row_perm, *bucket_ptr, *err;
   int32_t *tmp_cols, *tmp_len;   // workspace: [rows * width_pad], [rows]
+  int32_t* chunk;                 // workspace: per 256 rows, 10 totals (used above 16384 rows)
 };
+// Worklist workspace bytes after the rows' slots and lengths: chunk totals.
+size_t worklist_chunk_bytes(int64_t rows);
 int launch_worklist(const Geom& g, const sa_route_cfg& rc, int width_max, int n_buckets,
                     const WorklistBufs& b, hipStream_t st);
 

@@ -219,6 +219,7 @@ size_t ws_size(const Plan& pl, int which, int splits) {
   } else if (which == 1) {
     sz += align_up((size_t)pl.g.rows * kMaxWidth * sizeof(int32_t));
     sz += align_up((size_t)pl.g.rows * sizeof(int32_t));
+    sz += align_up(worklist_chunk_bytes(pl.g.rows));
   } else if (which == 2 && pl.g.mode == SA_DECODE) {
     sz += align_up(decode_partials_bytes(pl.g, splits));
   } else if (which == 3) {   // backward: D_i per query (lse layout), dK and dV fp32 accumulators,
@@ -295,6 +296,8 @@ int build_worklist_impl(const sa_problem* p, const sa_route_cfg* rc, const int32
   b.err = err;
   b.tmp_cols = reinterpret_cast<int32_t*>(w);
   b.tmp_len = reinterpret_cast<int32_t*>(w + align_up((size_t)pl.g.rows * kMaxWidth * sizeof(int32_t)));
+  b.chunk = reinterpret_cast<int32_t*>(w + align_up((size_t)pl.g.rows * kMaxWidth * sizeof(int32_t)) +
+                                       align_up((size_t)pl.g.rows * sizeof(int32_t)));
   return launch_worklist(pl.g, *rc, pl.width_max, pl.n_buckets, b, hs);
 }
 

@@ -24,6 +24,7 @@ namespace sa {
 
 constexpr int kWidthPad = 128;   // slots per row in workspace (k_b + forced <= 128)
 constexpr int kMaxBuckets = 8;
+constexpr int64_t kChunkedRows = 16384;   // above this many rows the finishing pass reads chunk totals
 
 __device__ __forceinline__ int bucket_of(int len) {
   return len <= 4 ? 0 : (32 - __clz(len - 1)) - 2;
@@ -117,11 +118,52 @@ __global__ void __launch_bounds__(64) wl_rows_kernel(Geom g, sa_route_cfg rc, in
 // order come from those prefixes plus an exclusive scan inside the chunk.
 // NT = 64 for up to 1024 rows (more, smaller workgroups: decode's 512 rows
 // 18 us vs 27 us in two 256-thread ones), else 256 (fewer passes over the row
-// lengths per workgroup).
-template <int NT>
+// lengths per workgroup).  Above kChunkedRows rows the totals come from the
+// chunk totals of wl_chunk_kernel (CHUNKED) instead of every row length.
+// Large problems: chunk totals.  Workgroup c sums, over rows 256 c .. + 255,
+// the lengths, the rows per bucket and the OR of the error bits, into
+// chunk[c][0 .. kChunkK), so the finishing pass reads one total per chunk
+// instead of every row length (rows x chunks loads would grow as the square
+// of the rows).
+constexpr int kChunkRows = 256;
+constexpr int kChunkK = kMaxBuckets + 2;   // [0] length sum, [1 + b] rows in bucket b, [K - 1] error bits
+
+__global__ void __launch_bounds__(kChunkRows) wl_chunk_kernel(int64_t rows, const int32_t* __restrict__ tmp_len,
+                                                             int32_t* __restrict__ chunk) {
+  constexpr int NW = kChunkRows / kWave;
+  __shared__ int red[NW][kChunkK];
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int64_t r = (int64_t)blockIdx.x * kChunkRows + tid;
+  const int x = r < rows ? tmp_len[r] : 0;
+  const int len = x & 0xffff, bk = r < rows ? bucket_of(len) : -1;
+  int v[kChunkK];
+  v[0] = len;
+#pragma unroll
+  for (int b = 0; b < kMaxBuckets; ++b) v[1 + b] = b == bk ? 1 : 0;
+#pragma unroll
+  for (int k = 0; k < kChunkK - 1; ++k) v[k] = wave_sum_i(v[k]);
+  // error bits: one bit per ballot
+  int eb = 0;
+#pragma unroll
+  for (int bit = 0; bit < 4; ++bit) eb |= __ballot((x >> (16 + bit)) & 1) ? (1 << bit) : 0;
+  v[kChunkK - 1] = eb;
+  if (lane == 0)
+#pragma unroll
+    for (int k = 0; k < kChunkK; ++k) red[wave][k] = v[k];
+  __syncthreads();
+  if (tid < kChunkK) {
+    int t = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) t = tid == kChunkK - 1 ? (t | red[w][tid]) : t + red[w][tid];
+    chunk[(int64_t)blockIdx.x * kChunkK + tid] = t;
+  }
+}
+
+template <int NT, bool CHUNKED>
 __global__ void __launch_bounds__(NT) wl_finish_kernel(int64_t rows, int n_buckets,
                                                         const int32_t* __restrict__ tmp_cols,
                                                         const int32_t* __restrict__ tmp_len,
+                                                        const int32_t* __restrict__ chunk,
                                                         int32_t* __restrict__ row_ptr,
                                                         int32_t* __restrict__ col_idx,
                                                         int32_t* __restrict__ row_perm,
@@ -129,6 +171,7 @@ __global__ void __launch_bounds__(NT) wl_finish_kernel(int64_t rows, int n_bucke
                                                         int32_t* __restrict__ err) {
   constexpr int K = kMaxBuckets + 1;   // [0] length sum, [1 + b] rows in bucket b
   constexpr int NW = NT / kWave;
+  static_assert(!CHUNKED || NT == kChunkRows, "a chunk is one workgroup's rows");
   __shared__ int red[NW][2 * K];
   __shared__ int wtot[NW][K];
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
@@ -138,6 +181,21 @@ __global__ void __launch_bounds__(NT) wl_finish_kernel(int64_t rows, int n_bucke
   int ebits = 0;   // error bits of every row (workgroup 0 writes their OR to err)
 #pragma unroll
   for (int k = 0; k < K; ++k) all[k] = pre[k] = 0;
+  if constexpr (CHUNKED) {
+    // from the chunk totals: chunk c holds rows c NT .. (c + 1) NT - 1
+    const int64_t nch = (rows + NT - 1) / NT;
+    for (int64_t c = tid; c < nch; c += NT) {
+      const int32_t* t = chunk + c * kChunkK;
+      const int in_pre = c < (int64_t)blockIdx.x ? 1 : 0;
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int x = t[k];
+        all[k] += x;
+        pre[k] += in_pre * x;
+      }
+      ebits |= t[kChunkK - 1];
+    }
+  } else {
   // UP lengths per thread are loaded before any is used (clamped to the last
   // row, weight 0 past the end): one memory round trip per UP rows
   constexpr int UP = 8;
@@ -165,6 +223,7 @@ __global__ void __launch_bounds__(NT) wl_finish_kernel(int64_t rows, int n_bucke
         pre[1 + b] += in_pre * one;
       }
     }
+  }
   }
 #pragma unroll
   for (int k = 0; k < K; ++k) {
@@ -282,6 +341,10 @@ int launch_cu_blocks(const int32_t* cu_seqlens, int32_t* cu_blocks, int batch, h
   return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 
+size_t worklist_chunk_bytes(int64_t rows) {
+  return (size_t)((rows + kChunkRows - 1) / kChunkRows) * kChunkK * sizeof(int32_t);
+}
+
 int launch_worklist(const Geom& g, const sa_route_cfg& rc, int width_max, int n_buckets,
                     const WorklistBufs& b, hipStream_t st) {
   if (g.rows <= 0) return SA_OK;
@@ -290,14 +353,19 @@ int launch_worklist(const Geom& g, const sa_route_cfg& rc, int width_max, int n_
   while ((1 << nbits) < g.max_blocks) ++nbits;
   wl_rows_kernel<<<(unsigned)g.rows, 64, 0, st>>>(g, rc, nbits, b.J, b.tmp_cols, b.tmp_len);
   if (hipGetLastError() != hipSuccess) return SA_ERR_HIP;
-  if (g.rows <= 1024)
-    wl_finish_kernel<64><<<(unsigned)((g.rows + 63) / 64), 64, 0, st>>>(g.rows, n_buckets, b.tmp_cols, b.tmp_len,
-                                                                       b.row_ptr, b.col_idx, b.row_perm,
-                                                                       b.bucket_ptr, b.err);
-  else
-    wl_finish_kernel<256><<<(unsigned)((g.rows + 255) / 256), 256, 0, st>>>(g.rows, n_buckets, b.tmp_cols,
-                                                                          b.tmp_len, b.row_ptr, b.col_idx,
-                                                                          b.row_perm, b.bucket_ptr, b.err);
+  const unsigned nch = (unsigned)((g.rows + kChunkRows - 1) / kChunkRows);
+  if (g.rows <= 1024) {
+    wl_finish_kernel<64, false><<<(unsigned)((g.rows + 63) / 64), 64, 0, st>>>(
+        g.rows, n_buckets, b.tmp_cols, b.tmp_len, nullptr, b.row_ptr, b.col_idx, b.row_perm, b.bucket_ptr, b.err);
+  } else if (g.rows <= kChunkedRows) {
+    wl_finish_kernel<256, false><<<nch, 256, 0, st>>>(g.rows, n_buckets, b.tmp_cols, b.tmp_len, nullptr, b.row_ptr,
+                                                      b.col_idx, b.row_perm, b.bucket_ptr, b.err);
+  } else {   // many rows: chunk totals first, so no workgroup reads every row length
+    wl_chunk_kernel<<<nch, kChunkRows, 0, st>>>(g.rows, b.tmp_len, b.chunk);
+    if (hipGetLastError() != hipSuccess) return SA_ERR_HIP;
+    wl_finish_kernel<256, true><<<nch, 256, 0, st>>>(g.rows, n_buckets, b.tmp_cols, b.tmp_len, b.chunk, b.row_ptr,
+                                                     b.col_idx, b.row_perm, b.bucket_ptr, b.err);
+  }
   return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 

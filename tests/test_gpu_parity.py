@@ -198,6 +198,40 @@ def test_worklist_adversarial_J(dev):
     assert ref["err"] == dbs.SA_WL_ERR_RANGE | dbs.SA_WL_ERR_ACAUSAL
 
 
+def test_worklist_many_rows_chunked_totals(dev):
+    """Above 16384 rows the finishing pass reads per-chunk totals: a random J over
+    32768 rows (4 heads x 8192 query blocks of 64 tokens) with planted bad ids,
+    against the oracle bit for bit, error word included."""
+    n, hq, k_b = 8192 * 64, 4, 6
+    w = wk.PREFILL_MHA.replace(name="wl_chunked", heads_q=hq, heads_kv=hq, seqlen=n, k_b=k_b)
+    prob = dbs.Problem.fixed(1, hq, hq, 128, n)
+    cfg = dbs.config_for(w)
+    rows = hq * 8192
+    rng = np.random.default_rng(5)
+    r_of = np.tile(np.arange(8192), hq)[:, None]
+    J = (rng.random((rows, k_b)) * (r_of + 1)).astype(np.int64)   # causal ids, duplicates likely
+    J[rng.random((rows, k_b)) < 0.1] = -1
+    J[777, 2] = 9000                                                # out of range
+    J[20000, 0] = (20000 % 8192) + 3                                # acausal
+    Jt = torch.as_tensor(J, dtype=torch.int32, device=dev)
+    print(f"worklist: {rows} rows through the chunked totals", flush=True)
+    wl = dbs.build_worklist(prob, cfg, Jt)
+    torch.cuda.synchronize()
+
+    class R:
+        pass
+
+    run = R()
+    run.J = J
+    nnz = int(wl.row_ptr[rows].item())
+    run.wl = dict(row_ptr=wl.row_ptr.cpu().numpy(), col_idx=wl.col_idx[:nnz].cpu().numpy(),
+                  row_perm=wl.row_perm.cpu().numpy(), bucket_ptr=wl.bucket_ptr.cpu().numpy(),
+                  err=int(wl.err.item()))
+    inp = wk.Inputs(w, None, None, None, [n], None, {})
+    ref = check_worklist(w, inp, run)
+    assert ref["err"] == dbs.SA_WL_ERR_RANGE | dbs.SA_WL_ERR_ACAUSAL
+
+
 def _oracle_J(w, inp):
     from oracle import problem as oprob
     qs, ks, _vs = wk.per_sequence(inp)
