@@ -30,6 +30,7 @@ setting (`cpu_baseline`): a reported baseline, not a target.
     python bench.py [--steps K] [--warmup W] [--no-decode] [--no-cpu] [--no-bwd]
     python bench.py --workload NAME     # time one setting only (it becomes the headline)
     python bench.py --no-dense          # skips the dense causal comparison (`dense`)
+    python bench.py --crossover         # adds a k_b sweep against the dense call (`crossover`)
 """
 from __future__ import annotations
 
@@ -372,7 +373,8 @@ def measure_bwd(args, dbs, st, visits):
     del dout, dq, dk, dv, ws
     return {"median_ms": round(med, 4), "algorithmic_flops": flops, "tflops": round(tf, 2),
             "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-            "kernels": "bwd_dq_bf16_kernel + bwd_dkdv_bf16_kernel",
+            "kernels": ("bwd_dq_rows_bf16_kernel" if w.share_gqa and w.group in (2, 4, 8) else "bwd_dq_bf16_kernel")
+                       + " + bwd_dkdv_bf16_kernel",
             "time": "median call, warm (events on the current stream)"}
 
 
@@ -452,6 +454,57 @@ def measure_dense(args, dbs, w, inp, flush, sparse_rec):
                     "(route + worklist + fwd) beats the dense call while it keeps fewer than this "
                     "fraction of the causal tiles (raw > 1: a listed tile costs less than a tile of "
                     "the dense walk, so the sparse step wins at any fraction)"}
+
+
+def measure_crossover(args, dbs, w, inp, flush):
+    """Empirical sparse/dense crossover ([P2] §3.1 dense fallback): the sparse
+    step (route + worklist + fwd, each after a cache flush, medians) at a range
+    of budgets k_b on the same inputs, beside the dense call; the crossover is
+    where the step time meets the dense time, interpolated in the tile
+    fraction between the two budgets that bracket it."""
+    import torch
+    prob, cfg = dbs.problem_for(w, inp), dbs.config_for(w)
+    nblocks = [-(-L // w.block) for L in inp.lengths]
+    hpr = w.group if w.share_gqa else 1
+    dense_visits = sum(nb * (nb + 1) // 2 for nb in nblocks) * w.route_heads * hpr
+    o = torch.empty_like(inp.q)
+    lse = torch.empty(inp.q.shape[:-1], dtype=torch.float32, device=inp.q.device)
+    ws = torch.empty(max(dbs.workspace_size(prob, cfg, 2), 1), dtype=torch.uint8, device=inp.q.device)
+    times = []
+    for i in range(6):
+        flush.sum()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dbs.fwd_dense(prob, cfg, inp.q, inp.k, inp.v, o=o, lse=lse, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        if i:
+            times.append(e0.elapsed_time(e1))
+    dense_ms = spread(times)["median"]
+    del o, lse, ws
+    max_kb = 128 - max(w.window, 1) - (1 if w.forced_first else 0)
+    budgets = sorted({kb for kb in (4, 8, 16, 32, 48, 64, 80, 96, 112, max_kb) if kb <= max_kb})
+    pts = []
+    for kb in budgets:
+        wk_ = w.replace(name=f"{w.name}_kb{kb}", k_b=kb)
+        st = Stepper(dbs, wk_, inp)
+        _, cold = timed(st, 10, 2, flush)
+        r, wl_, f = (spread(x)["median"] for x in cold)
+        frac = st.tile_visits() / dense_visits
+        pts.append({"k_b": kb, "tile_fraction": round(frac, 4), "step_ms": round(r + wl_ + f, 5),
+                    "route_ms": round(r, 5), "worklist_ms": round(wl_, 5), "fwd_ms": round(f, 5),
+                    "step_vs_dense": round((r + wl_ + f) / dense_ms, 3)})
+        del st
+        torch.cuda.empty_cache()
+    cross = None
+    for a, b in zip(pts, pts[1:]):
+        if a["step_ms"] <= dense_ms < b["step_ms"]:
+            t = (dense_ms - a["step_ms"]) / (b["step_ms"] - a["step_ms"])
+            cross = round(a["tile_fraction"] + t * (b["tile_fraction"] - a["tile_fraction"]), 4)
+    return {"workload": w.name, "dense_fwd_ms": dense_ms, "points": pts,
+            "crossover_tile_fraction": cross,
+            "note": "crossover_tile_fraction: null when every budget's step beats the dense call "
+                    "(the widest row holds at most 128 ids)"}
 
 
 def measure_decode(args, dbs, wd, dev, flush):
@@ -583,6 +636,9 @@ def main():
                     help="skip the dense comparison (sparse_attn_fwd_dense and torch flash SDPA on "
                          "each prefill setting, and the 65536-token crossover point)")
     ap.add_argument("--no-bwd", action="store_true", help="skip timing the backward pass")
+    ap.add_argument("--crossover", action="store_true",
+                    help="also sweep k_b on the MHA and GQA settings against the dense call (empirical "
+                         "sparse/dense crossover)")
     ap.add_argument("--cpu-blocks", type=int, default=0,
                     help="query blocks of the oracle's sample (every routing head of each); "
                          "0: every query block of the sampled sequence")
@@ -671,6 +727,14 @@ def main():
         torch.cuda.empty_cache()
     if settings:
         out["settings"] = settings
+    if args.crossover:
+        out["crossover"] = []
+        for w in (wk.PREFILL_MHA, wk.PREFILL_GQA):
+            log(f"k_b sweep against the dense call on {w.name}")
+            inp_w = wk.make_inputs(w, dev)
+            out["crossover"].append(measure_crossover(args, dbs, w, inp_w, flush))
+            del inp_w
+            torch.cuda.empty_cache()
     del flush
     torch.cuda.empty_cache()
     if cpu_inp is not None:

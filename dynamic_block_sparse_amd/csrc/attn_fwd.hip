@@ -92,13 +92,30 @@ __device__ __forceinline__ int64_t xcd_schedule(int64_t b, int64_t rows, int G) 
 }
 
 // The worklist row a workgroup takes at position pos (0 = first): the
-// worklist's rows longest first (row_perm is in ascending bucket order), or,
-// for dense attention, the rows in reverse order (each (sequence, head) from
-// its last query block down, so neighbouring positions share K/V and the
-// short rows come last).
+// worklist's rows longest first (row_perm is in ascending bucket order).
+// Dense attention (row r walks r + 1 tiles): with fixed-length sequences, the
+// rows in groups of `run` consecutive query blocks of one (sequence, head),
+// the groups of the latest query blocks first over all (sequence, head)
+// pairs, each group from its last query block down.  A group is one XCD's run
+// of positions (see xcd_schedule), so its rows share the K/V prefix in that
+// XCD's L2, and the rows start roughly longest first over the whole grid.
+// Otherwise (packed varlen, or run not dividing the rows of a sequence) the
+// rows in reverse order: each (sequence, head) from its last query block down.
 template <bool DENSE>
-__device__ __forceinline__ int64_t dense_or_listed_row(const Geom& g, const FwdBufs& a, int64_t pos) {
-  if constexpr (DENSE) return g.rows - 1 - pos;
+__device__ __forceinline__ int64_t dense_or_listed_row(const Geom& g, const FwdBufs& a, int64_t pos,
+                                                       int run = 0) {
+  if constexpr (DENSE) {
+    if (!g.varlen && run > 0) {
+      const int64_t R = ceil_div(g.n, kBlock) - g.qblk0;   // rows per (sequence, head)
+      if (R % run == 0) {
+        const int64_t P = g.rows / R;                      // (sequence, head) pairs
+        const int64_t grp = pos / run, i = pos % run;
+        const int64_t qg = R / run - 1 - grp / P, pair = P - 1 - grp % P;
+        return pair * R + qg * run + (run - 1 - i);
+      }
+    }
+    return g.rows - 1 - pos;
+  }
   return a.row_perm[g.rows - 1 - pos];
 }
 
@@ -332,12 +349,22 @@ __global__ void __launch_bounds__(128 * HPR) prefill_bf16_kernel(Geom g, FwdBufs
 
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  // Workgroup b takes worklist positions b, b + G, b + 2G, ... (G = gridDim.x;
-  // G = rows unless the launch is persistent, see prefill_grid).
-  for (int64_t vb = blockIdx.x; vb < g.rows; vb += gridDim.x) {
-    if (vb != blockIdx.x) block_barrier();   // the previous row's LDS reads are done
+  // Workgroup b takes one worklist position in each pass over the grid (G =
+  // gridDim.x; G = rows unless the launch is persistent, see prefill_grid):
+  // b in even passes and its mirror m(b) = (G/8 - 1 - b/8) * 8 + b % 8 in odd
+  // ones.  The positions run longest first, so a workgroup that took one of
+  // the longest rows of a pass takes one of the shortest of the next, and the
+  // workgroups' shares even out (a dense causal walk's rows r and N - 1 - r
+  // pair up to N + 1 tiles).  m(b) keeps b's XCD (b % 8; a persistent G is a
+  // multiple of 8, and a grid of G = rows makes one pass only).
+  for (int64_t base = 0; base < g.rows; base += gridDim.x) {
+    const int64_t vb = base + (((base / gridDim.x) & 1)
+                                   ? (int64_t)(gridDim.x / 8 - 1 - blockIdx.x / 8) * 8 + blockIdx.x % 8
+                                   : (int64_t)blockIdx.x);
+    if (base != 0) block_barrier();   // the previous row's LDS reads are done
+    if (vb >= g.rows) continue;
     const int64_t pos = xcd_schedule(vb, g.rows, xcd_run);
-    const int64_t row = dense_or_listed_row<DENSE>(g, a, pos);
+    const int64_t row = dense_or_listed_row<DENSE>(g, a, pos, xcd_run);
     const RowInfo ri = decode_row(g, row);
     const int kvh = g.share ? ri.h : ri.h / g.group;
     const int head = (g.share ? ri.h * g.group : ri.h) + wave / 2;
@@ -509,7 +536,7 @@ __global__ void __launch_bounds__(512) prefill_bf16_pp_kernel(Geom g, FwdBufs a,
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int grp = wave >> 2;
   const int64_t pos = xcd_schedule(blockIdx.x, g.rows, xcd_run);
-  const int64_t row = dense_or_listed_row<DENSE>(g, a, pos);
+  const int64_t row = dense_or_listed_row<DENSE>(g, a, pos, xcd_run);
   const RowInfo ri = decode_row(g, row);
   const int kvh = g.share ? ri.h : ri.h / g.group;
   // heads 4 blockIdx.y .. + 3 of the row (rows of 8 heads take two workgroups)

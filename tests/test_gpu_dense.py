@@ -135,6 +135,46 @@ def test_dense_equals_sparse_with_every_block_listed(share, hq, hkv):
     assert torch.equal(o_s, o_d) and torch.equal(lse_s, lse_d)
 
 
+@pytest.mark.parametrize("share,hq,hkv,lengths", [
+    (False, 16, 16, [8192]),        # 2048 one-head rows: a persistent grid, two passes, 128-row groups
+    (True, 8, 2, [2048, 2048]),     # four-head rows, 4 (sequence, head) pairs of 32 rows
+    (False, 4, 4, [4096, 4096]),    # one-head rows, 8 pairs of 64 rows (not a multiple of 128)
+])
+def test_dense_walk_orders_cover_every_row(share, hq, hkv, lengths):
+    """The dense call's row orders (longest-first groups of query blocks over
+    the (sequence, head) pairs, mirrored passes of a persistent grid) reach
+    every row: outputs start as NaN and none is left.  Every row computes its
+    own result from its id, so reaching each row is what the order has to get
+    right; the values are then checked bit for bit against the sparse call with
+    every causal block listed, or, where a row has more blocks than a worklist
+    row holds (128 with the forced current block), on sampled query blocks
+    against the oracle."""
+    dev = torch.device("cuda:0")
+    n = lengths[0]
+    prob, q, k, v, _ = _inputs(lengths, hq, hkv, 128, "bf16", dev, 17, fixed_n=n)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    nb = n // B
+    print(f"dense walk orders: share={share} hq={hq} lengths={lengths}", flush=True)
+    nan_o = lambda: torch.full_like(qd, float("nan"))
+    nan_l = lambda: torch.full(qd.shape[:-1], float("nan"), dtype=torch.float32, device=dev)
+    cfg = dbs.RouteConfig(k_b=min(nb, 127), share_gqa=share)
+    o_d, lse_d = dbs.fwd_dense(prob, cfg, qd, kd, vd, o=nan_o(), lse=nan_l())
+    torch.cuda.synchronize()
+    assert not torch.isnan(o_d).any() and not torch.isnan(lse_d).any()
+    if nb <= 127:
+        J, _ = dbs.route(prob, cfg, qd, kd)
+        wl = dbs.build_worklist(prob, cfg, J)
+        o_s, lse_s = dbs.fwd(prob, cfg, wl, qd, kd, vd, o=nan_o(), lse=nan_l())
+        torch.cuda.synchronize()
+        heads = hkv if share else hq
+        assert int(wl.row_ptr[-1].item()) == len(lengths) * heads * nb * (nb + 1) // 2   # every causal tile
+        assert torch.equal(o_s, o_d) and torch.equal(lse_s, lse_d)
+    else:
+        nrows = len(lengths) * (hkv if share else hq) * nb   # (sequence, routing head, query block)
+        rows = sorted({0, nb - 1, nb, nrows - 1} | set(np.random.default_rng(1).integers(0, nrows, size=6).tolist()))
+        _check(prob, cfg, q, k, v, lengths, o_d.cpu(), lse_d.cpu(), "bf16", rows=rows)
+
+
 def test_dense_rows_longer_than_a_worklist_row():
     """n = 16384: rows of up to 256 blocks (a worklist row holds at most 128);
     sampled rows (first, last and random query blocks) against the oracle."""
