@@ -170,6 +170,14 @@ def test_dense_walk_orders_cover_every_row(share, hq, hkv, lengths):
         assert int(wl.row_ptr[-1].item()) == len(lengths) * heads * nb * (nb + 1) // 2   # every causal tile
         assert torch.equal(o_s, o_d) and torch.equal(lse_s, lse_d)
     else:
+        # the sparse call on the same shape (k_b = 16) takes the same mirrored
+        # passes over its worklist rows: every row is written
+        cfg16 = dbs.RouteConfig(k_b=16, share_gqa=share)
+        J, _ = dbs.route(prob, cfg16, qd, kd)
+        wl = dbs.build_worklist(prob, cfg16, J)
+        o_s, lse_s = dbs.fwd(prob, cfg16, wl, qd, kd, vd, o=nan_o(), lse=nan_l())
+        torch.cuda.synchronize()
+        assert not torch.isnan(o_s).any() and not torch.isnan(lse_s).any()
         nrows = len(lengths) * (hkv if share else hq) * nb   # (sequence, routing head, query block)
         rows = sorted({0, nb - 1, nb, nrows - 1} | set(np.random.default_rng(1).integers(0, nrows, size=6).tolist()))
         _check(prob, cfg, q, k, v, lengths, o_d.cpu(), lse_d.cpu(), "bf16", rows=rows)
