@@ -237,7 +237,11 @@ __global__ void __launch_bounds__(256) route_score_tile_kernel(Geom g, sa_route_
   constexpr int RA = kScoreRows * kScoreCols / 256 >= 2 && kScoreRows >= 32 ? 2 : 1;   // rows per thread
   constexpr int CB = kScoreRows * kScoreCols / 256 / RA;                              // columns per thread
   constexpr int CG = kScoreCols / CB;                                                 // column groups
-  const int rg = tid / CG, cg = tid % CG;   // rows RA rg ..; columns CB cg ..
+  // rows RA rg ..; columns cg, cg + CG, ...: the 16 lanes of a column group
+  // set read 16 consecutive summary rows, whose 16-byte slices fall in
+  // distinct LDS banks at the 132-float pitch (contiguous columns per thread
+  // put rows 4 apart on the same banks)
+  const int rg = tid / CG, cg = tid % CG;
   float acc[RA][CB];
 #pragma unroll
   for (int a = 0; a < RA; ++a)
@@ -249,7 +253,7 @@ __global__ void __launch_bounds__(256) route_score_tile_kernel(Geom g, sa_route_
 #pragma unroll
     for (int a = 0; a < RA; ++a) qv[a] = *reinterpret_cast<const f32x4*>(qs + (RA * rg + a) * LD + k);
 #pragma unroll
-    for (int b = 0; b < CB; ++b) cv[b] = *reinterpret_cast<const f32x4*>(cs + (CB * cg + b) * LD + k);
+    for (int b = 0; b < CB; ++b) cv[b] = *reinterpret_cast<const f32x4*>(cs + (cg + CG * b) * LD + k);
 #pragma unroll
     for (int a = 0; a < RA; ++a)
 #pragma unroll
@@ -266,7 +270,7 @@ __global__ void __launch_bounds__(256) route_score_tile_kernel(Geom g, sa_route_
     float* srow = scores + (row0 + r) * (int64_t)g.max_blocks;
 #pragma unroll
     for (int b = 0; b < CB; ++b) {
-      const int j = j0 + CB * cg + b;
+      const int j = j0 + cg + CG * b;
       if (j >= start && j < r) srow[j - start] = acc[a][b];
     }
   }
