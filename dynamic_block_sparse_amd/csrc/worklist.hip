@@ -16,7 +16,8 @@
 //               (bucket, row) order -> row_perm, and the copy of each row's
 //               ids to col_idx[row_ptr[row] ..].  Every workgroup reads all
 //               row lengths (4 bytes a row) for the totals and for what
-//               precedes its chunk, so none waits for another.
+//               precedes its chunk, so none waits for another; a thread's
+//               own row (length and ids) is loaded in the same round trip.
 #include "common.h"
 #include "kernels.h"
 
@@ -159,7 +160,7 @@ __global__ void __launch_bounds__(kChunkRows) wl_chunk_kernel(int64_t rows, cons
   }
 }
 
-template <int NT, bool CHUNKED>
+template <int NT, bool CHUNKED, int PRE>
 __global__ void __launch_bounds__(NT) wl_finish_kernel(int64_t rows, int n_buckets,
                                                         const int32_t* __restrict__ tmp_cols,
                                                         const int32_t* __restrict__ tmp_len,
@@ -176,6 +177,16 @@ __global__ void __launch_bounds__(NT) wl_finish_kernel(int64_t rows, int n_bucke
   __shared__ int wtot[NW][K];
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int64_t c0 = (int64_t)blockIdx.x * NT;
+  // this thread's row: its length word and its first 4 PRE slots (every id
+  // it can hold), loaded before the totals so that all of the kernel's
+  // loads take one memory round trip (rows past the end load row 0's)
+  const int64_t r = c0 + tid;
+  const bool valid = r < rows;
+  const int own = valid ? tmp_len[r] : 0;
+  const int32_t* const src = tmp_cols + (valid ? r : 0) * kWidthPad;
+  u32x4 ids[PRE];
+#pragma unroll
+  for (int u = 0; u < PRE; ++u) ids[u] = *reinterpret_cast<const u32x4*>(src + 4 * u);
   // ---- totals over all rows and over the rows before this chunk
   int all[K], pre[K];
   int ebits = 0;   // error bits of every row (workgroup 0 writes their OR to err)
@@ -247,9 +258,7 @@ __global__ void __launch_bounds__(NT) wl_finish_kernel(int64_t rows, int n_bucke
     if (tid == 0) *err = eor;
   }
   // ---- this thread's row and the exclusive scan of the chunk
-  const int64_t r = c0 + tid;
-  const bool valid = r < rows;
-  const int len = valid ? (tmp_len[r] & 0xffff) : 0;
+  const int len = own & 0xffff;
   const int bk = valid ? bucket_of(len) : -1;
   int v[K], inc[K];
   v[0] = len;
@@ -292,26 +301,15 @@ __global__ void __launch_bounds__(NT) wl_finish_kernel(int64_t rows, int n_bucke
     row_ptr[r] = before[0] + excl[0];
     row_perm[pos] = (int32_t)r;
   }
-  // ---- copy this row's ids to col_idx[row_ptr[r] ..]: 16-byte loads of the
-  // row's workspace slots (512-byte aligned) in two halves of 64 slots, each
-  // loaded whole before any store (one memory round trip per half), 4-byte
-  // stores (row_ptr is not aligned)
+  // ---- copy this row's ids (loaded at the start) to col_idx[row_ptr[r] ..]
+  // with 4-byte stores (row_ptr is not aligned)
   if (valid) {
-    const int32_t* src = tmp_cols + r * kWidthPad;
     int32_t* dst = col_idx + before[0] + excl[0];
 #pragma unroll
-    for (int hf = 0; hf < kWidthPad / 64; ++hf) {
-      if (64 * hf < len) {
-        u32x4 x[16];
+    for (int u = 0; u < PRE; ++u)
 #pragma unroll
-        for (int u = 0; u < 16; ++u) x[u] = *reinterpret_cast<const u32x4*>(src + 64 * hf + 4 * u);
-#pragma unroll
-        for (int u = 0; u < 16; ++u)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (64 * hf + 4 * u + e < len) dst[64 * hf + 4 * u + e] = (int32_t)x[u][e];
-      }
-    }
+      for (int e = 0; e < 4; ++e)
+        if (4 * u + e < len) dst[4 * u + e] = (int32_t)ids[u][e];
   }
 }
 
@@ -345,6 +343,24 @@ size_t worklist_chunk_bytes(int64_t rows) {
   return (size_t)((rows + kChunkRows - 1) / kChunkRows) * kChunkK * sizeof(int32_t);
 }
 
+template <int PRE>
+int launch_finish(const Geom& g, int n_buckets, const WorklistBufs& b, hipStream_t st) {
+  const unsigned nch = (unsigned)((g.rows + kChunkRows - 1) / kChunkRows);
+  if (g.rows <= 1024) {
+    wl_finish_kernel<64, false, PRE><<<(unsigned)((g.rows + 63) / 64), 64, 0, st>>>(
+        g.rows, n_buckets, b.tmp_cols, b.tmp_len, nullptr, b.row_ptr, b.col_idx, b.row_perm, b.bucket_ptr, b.err);
+  } else if (g.rows <= kChunkedRows) {
+    wl_finish_kernel<256, false, PRE><<<nch, 256, 0, st>>>(g.rows, n_buckets, b.tmp_cols, b.tmp_len, nullptr,
+                                                           b.row_ptr, b.col_idx, b.row_perm, b.bucket_ptr, b.err);
+  } else {   // many rows: chunk totals first, so no workgroup reads every row length
+    wl_chunk_kernel<<<nch, kChunkRows, 0, st>>>(g.rows, b.tmp_len, b.chunk);
+    if (hipGetLastError() != hipSuccess) return SA_ERR_HIP;
+    wl_finish_kernel<256, true, PRE><<<nch, 256, 0, st>>>(g.rows, n_buckets, b.tmp_cols, b.tmp_len, b.chunk,
+                                                          b.row_ptr, b.col_idx, b.row_perm, b.bucket_ptr, b.err);
+  }
+  return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
+
 int launch_worklist(const Geom& g, const sa_route_cfg& rc, int width_max, int n_buckets,
                     const WorklistBufs& b, hipStream_t st) {
   if (g.rows <= 0) return SA_OK;
@@ -353,20 +369,11 @@ int launch_worklist(const Geom& g, const sa_route_cfg& rc, int width_max, int n_
   while ((1 << nbits) < g.max_blocks) ++nbits;
   wl_rows_kernel<<<(unsigned)g.rows, 64, 0, st>>>(g, rc, nbits, b.J, b.tmp_cols, b.tmp_len);
   if (hipGetLastError() != hipSuccess) return SA_ERR_HIP;
-  const unsigned nch = (unsigned)((g.rows + kChunkRows - 1) / kChunkRows);
-  if (g.rows <= 1024) {
-    wl_finish_kernel<64, false><<<(unsigned)((g.rows + 63) / 64), 64, 0, st>>>(
-        g.rows, n_buckets, b.tmp_cols, b.tmp_len, nullptr, b.row_ptr, b.col_idx, b.row_perm, b.bucket_ptr, b.err);
-  } else if (g.rows <= kChunkedRows) {
-    wl_finish_kernel<256, false><<<nch, 256, 0, st>>>(g.rows, n_buckets, b.tmp_cols, b.tmp_len, nullptr, b.row_ptr,
-                                                      b.col_idx, b.row_perm, b.bucket_ptr, b.err);
-  } else {   // many rows: chunk totals first, so no workgroup reads every row length
-    wl_chunk_kernel<<<nch, kChunkRows, 0, st>>>(g.rows, b.tmp_len, b.chunk);
-    if (hipGetLastError() != hipSuccess) return SA_ERR_HIP;
-    wl_finish_kernel<256, true><<<nch, 256, 0, st>>>(g.rows, n_buckets, b.tmp_cols, b.tmp_len, b.chunk, b.row_ptr,
-                                                     b.col_idx, b.row_perm, b.bucket_ptr, b.err);
-  }
-  return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
+  // 16-byte chunks of a row's slots that the finishing pass loads: every id
+  // the row can hold (8, 17 or 32 chunks)
+  if (width_max <= 32) return launch_finish<8>(g, n_buckets, b, st);
+  if (width_max <= 68) return launch_finish<17>(g, n_buckets, b, st);
+  return launch_finish<32>(g, n_buckets, b, st);
 }
 
 }  // namespace sa
