@@ -32,6 +32,7 @@
 // and dV added into fp32 workspace accumulators by atomics (their summation
 // order is therefore not fixed) and converted by a last pass.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -206,6 +207,43 @@ __device__ __forceinline__ bf16x8 tr8(const unsigned char* t, int rb, int ks, in
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// The lane-dependent parts of the tile reads above, computed once: a read's
+// address is then the tile's base + one of these + a constant.
+//   row8<TR>(t, 32 b + l32, 2 ks + half) = t + 8192 b + row[ks]
+//   tr8(t, rb, ks, db, lane)             = halves at t + 8192 rb + 4096 ks + tr[db][0 / 1]
+// (tsw and rsw depend on row & 15 only, which 32 b, 16 ks and 32 rb leave alone.)
+struct TileReadOffsets {
+  uint32_t row[8], tr[4][2];
+};
+template <bool TR>
+__device__ __forceinline__ TileReadOffsets tile_read_offsets(int lane) {
+  TileReadOffsets o;
+  const int l32 = lane & 31, half = lane >> 5;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+    o.row[ks] = (uint32_t)(l32 * 256 + (((2 * ks + half) ^ (TR ? tsw(l32) : rsw(l32))) << 4));
+  const int gi = lane >> 4, li = lane & 15, vh = gi >> 1, vdh = gi & 1;
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const int d = db * 32 + 16 * vdh + 4 * (li & 3);
+    const int chunk = d >> 3, h8 = (d >> 2) & 1;
+    const int r0 = 4 * vh + (li >> 2), r1 = r0 + 8;
+    o.tr[db][0] = (uint32_t)(r0 * 256 + ((chunk ^ tsw(r0)) << 4) + h8 * 8);
+    o.tr[db][1] = (uint32_t)(r1 * 256 + ((chunk ^ tsw(r1)) << 4) + h8 * 8);
+  }
+  return o;
+}
+typedef SA_LDS const unsigned char* lds_ptr;
+__device__ __forceinline__ lds_ptr to_lds(const unsigned char* p) { return (lds_ptr)p; }
+__device__ __forceinline__ bf16x8 row8_at(lds_ptr t, uint32_t off) {
+  return *reinterpret_cast<SA_LDS const bf16x8*>(t + off);
+}
+__device__ __forceinline__ bf16x8 tr8_at(lds_ptr t, const uint32_t (&off)[2]) {
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS i16x4*)(t + off[0]));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS i16x4*)(t + off[1]));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 constexpr int kMfma = 0x008, kDsRead = 0x100;   // scheduling-group masks
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -307,6 +345,7 @@ __global__ void __launch_bounds__(128) bwd_dq_bf16_kernel(Geom g, BwdBufs a) {
       const int64_t lo = lse_offset(g, ri.s, head, ri.tok0, qpos);
       lse2 = a.lse[lo] * kLog2e;
       if (half == 0) a.delta[lo] = delta;
+      else a.nlse2[lo] = -lse2;
     }
   }
   f32x16 dq[4];
@@ -492,7 +531,10 @@ __global__ void __launch_bounds__(256) bwd_dq_rows_bf16_kernel(Geom g, BwdBufs a
     delta = part + __shfl_xor(part, 32);
     const int64_t lo = lse_offset(g, ri.s, head, ri.tok0, qsrc);
     lse2 = a.lse[lo] * kLog2e;
-    if (qvalid && half == 0) a.delta[lo] = delta;
+    if (qvalid) {
+      if (half == 0) a.delta[lo] = delta;
+      else a.nlse2[lo] = -lse2;
+    }
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(qreg[ks]), "v"(doreg[ks]));
     asm volatile("" ::"v"(lse2), "v"(jl0), "v"(jl1));
@@ -503,16 +545,19 @@ __global__ void __launch_bounds__(256) bwd_dq_rows_bf16_kernel(Geom g, BwdBufs a
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) dq[db][i] = 0.f;
+  const TileReadOffsets ko = tile_read_offsets<true>(lane), vo = tile_read_offsets<false>(lane);
+  // tiles before the row's query block need no mask when all its rows are valid
+  const int jfree = (ri.r + 1) * kBlock <= ri.len ? ri.r : 0;
 
+  int slot = 0;   // t % NB, stepped (a modulo of the loop counter is rebuilt per address)
   for (int t = 0; t < nt; ++t) {
-    const int slot = t % NB;
     const int younger = min(NB - 2, nt - 1 - t);   // tiles issued after t
     if (younger >= 1) bwd_wait_vmcnt<2 * LPT>();
     else bwd_wait_vmcnt<0>();
     asm volatile("s_barrier" ::: "memory");   // tile t landed for every wave; slot (t - 1) % NB is read
-    if (t + NB - 1 < nt) issue_tile(t + NB - 1, (t + NB - 1) % NB);
-    const unsigned char* kt = ring[slot][0];
-    const unsigned char* vt = ring[slot][1];
+    if (t + NB - 1 < nt) issue_tile(t + NB - 1, slot == 0 ? NB - 1 : slot - 1);
+    const lds_ptr kt = to_lds(ring[slot][0]);
+    const lds_ptr vt = to_lds(ring[slot][1]);
     const int j = tile_id(t);
     bf16x8 dsb[2][2];
 #pragma unroll
@@ -524,8 +569,8 @@ __global__ void __launch_bounds__(256) bwd_dq_rows_bf16_kernel(Geom g, BwdBufs a
       for (int i = 0; i < 16; ++i) sacc[i] = dpacc[i] = 0.f;
       bf16x8 ok_[2], ov_[2];
       auto rd = [&](int ks) {
-        ok_[ks & 1] = row8<true>(kt, 32 * b2 + l32, 2 * ks + half);
-        ov_[ks & 1] = row8<false>(vt, 32 * b2 + l32, 2 * ks + half);
+        ok_[ks & 1] = row8_at(kt + 8192 * b2, ko.row[ks]);
+        ov_[ks & 1] = row8_at(vt + 8192 * b2, vo.row[ks]);
       };
       rd(0);
       __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
@@ -538,28 +583,38 @@ __global__ void __launch_bounds__(256) bwd_dq_rows_bf16_kernel(Geom g, BwdBufs a
         __builtin_amdgcn_sched_group_barrier(kMfma, 2, 0);
       }
       // dS^T of this lane's query over the half's keys, as B operands
+      if (j < jfree) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int kpos = j * kBlock + b2 * 32 + 8 * (i / 4) + 4 * half + (i % 4);
-        const bool ok = qvalid && kpos <= qpos;
-        const float p = __builtin_amdgcn_exp2f(ok ? fmaf(sacc[i], cl2, -lse2) : -INFINITY);
-        dsb[b2][i / 8][i % 8] = (__bf16)(p * (dpacc[i] - delta));
+        for (int i = 0; i < 16; ++i) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[i], cl2, -lse2));
+          dsb[b2][i / 8][i % 8] = (__bf16)(p * (dpacc[i] - delta));
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kpos = j * kBlock + b2 * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+          const bool ok = qvalid && kpos <= qpos;
+          const float p = __builtin_amdgcn_exp2f(ok ? fmaf(sacc[i], cl2, -lse2) : -INFINITY);
+          dsb[b2][i / 8][i % 8] = (__bf16)(p * (dpacc[i] - delta));
+        }
       }
     }
     // dQ^T += K^T dS^T: the transpose reads run four MFMAs ahead
     bf16x8 ta[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ta[i] = tr8(kt, (i >> 1) & 1, i & 1, i >> 2, lane);
+    for (int i = 0; i < 4; ++i) ta[i] = tr8_at(kt + 8192 * ((i >> 1) & 1) + 4096 * (i & 1), ko.tr[i >> 2]);
     __builtin_amdgcn_sched_group_barrier(kDsRead, 8, 0);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int db = i >> 2, b2 = (i >> 1) & 1, ks = i & 1;
       const bf16x8 av = ta[i & 3];
-      if (i + 4 < 16) ta[i & 3] = tr8(kt, ((i + 4) >> 1) & 1, (i + 4) & 1, (i + 4) >> 2, lane);
+      if (i + 4 < 16)
+        ta[i & 3] = tr8_at(kt + 8192 * (((i + 4) >> 1) & 1) + 4096 * ((i + 4) & 1), ko.tr[(i + 4) >> 2]);
       dq[db] = mfma(av, dsb[b2][ks], dq[db]);
       __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
       if (i + 4 < 16) __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
     }
+    slot = slot == NB - 1 ? 0 : slot + 1;
   }
   if (qvalid) store_acc(dq, c, (__bf16*)a.dq + q_offset(g, ri.s, head, ri.tok0, qpos), half);
 }
@@ -634,22 +689,26 @@ __global__ void __launch_bounds__(256) bwd_split_clear_kernel(Geom g, BwdBufs a)
 // ([slots x Hkv + 1]; the last entry is the total, the worklist's nnz), and
 // lists the dK/dV workgroups: one per (slot, KV head), or nch of them for a
 // block with more pairs than split_target, as witem entries (index << 4 |
-// chunk), -1 up to witems.
+// chunk), -1 up to witems.  The workgroups go out KV head by KV head (all
+// slots of one KV head, then the next), so the query rows that the
+// workgroups in flight read belong to one KV head's query heads.
 __device__ __forceinline__ int bwd_chunks(int units, int split_target, int max_chunks) {
   return units > split_target ? min(max_chunks, (units + split_target - 1) / split_target) : 1;
 }
 
 __global__ void __launch_bounds__(1024) bwd_kscan_kernel(const int* __restrict__ kcount, int* __restrict__ kptr,
                                                          int* __restrict__ witem, int n, int ngh, int split_target,
-                                                         int max_chunks, int witems) {
+                                                         int max_chunks, int witems, int hkv) {
   __shared__ int part[1024], cpart[1024];
   const int tid = threadIdx.x;
   const int per = (n + 1023) / 1024;
   const int b = min(tid * per, n), e = min(b + per, n);
   int sum = 0, csum = 0;
+  const int nslots = n / hkv;
+  auto item = [&](int i) { return (i % nslots) * hkv + i / nslots; };   // KV-head-major position -> list
   for (int i = b; i < e; ++i) {
     sum += kcount[i] / ngh;
-    csum += bwd_chunks(kcount[i], split_target, max_chunks);
+    csum += bwd_chunks(kcount[item(i)], split_target, max_chunks);
   }
   part[tid] = sum;
   cpart[tid] = csum;
@@ -666,8 +725,9 @@ __global__ void __launch_bounds__(1024) bwd_kscan_kernel(const int* __restrict__
   for (int i = b; i < e; ++i) {
     kptr[i] = run;
     run += kcount[i] / ngh;
-    const int nc = bwd_chunks(kcount[i], split_target, max_chunks);
-    for (int z = 0; z < nc; ++z) witem[crun + z] = (i << 4) | z;
+    const int it = item(i);
+    const int nc = bwd_chunks(kcount[it], split_target, max_chunks);
+    for (int z = 0; z < nc; ++z) witem[crun + z] = (it << 4) | z;
     crun += nc;
   }
   if (tid == 1023) kptr[n] = part[1023];
@@ -762,67 +822,89 @@ __global__ void __launch_bounds__(256) bwd_dkdv_bf16_kernel(Geom g, BwdBufs a) {
   constexpr int LPP = 9;   // loads per pair, every wavefront (waves 2, 3 repeat their last slice)
   const unsigned char* const qbytes = (const unsigned char*)a.q;
   const unsigned char* const dbytes = (const unsigned char*)a.dout;
-  uint32_t toff[4];
-  int trow[4];
+  auto slice_off = [&](int ii, int rows) {   // byte offset of this lane's slice ii (rows clamped)
+    const int row = 4 * (wave + 4 * ii) + (lane >> 4), p = lane & 15;
+    return (uint32_t)(min(row, rows - 1) * 256 + ((p ^ tsw(row)) << 4));
+  };
+  uint32_t ofull[4];   // a whole query block's offsets
 #pragma unroll
-  for (int ii = 0; ii < 4; ++ii) {
-    const int sl = wave + 4 * ii, row = 4 * sl + (lane >> 4), p = lane & 15;
-    trow[ii] = row;
-    toff[ii] = (uint32_t)(((p ^ tsw(row)) << 4));
-  }
-  // entries of the list, 64 at a time in a register (lane i: entry base + i)
-  int ebase = ord_lo / ngh;
+  for (int ii = 0; ii < 4; ++ii) ofull[ii] = slice_off(ii, kBlock);
+  // element offsets of (head 0, token 0) of the sequence in Q / dO and in lse / D
+  const int64_t qbase = q_offset(g, s, 0, tok0, 0), lbase = lse_offset(g, s, 0, tok0, 0);
+  // entries of the list, 64 at a time in a register (lane i: entry base + i);
+  // pair ord = entry e x ngh + query head gh, walked in order by a cursor
+  int ce = ord_lo / ngh, cg = ord_lo - ce * ngh;
+  int ebase = ce;
   int ent = ebase + lane < nent ? a.klist[e0 + ebase + lane] : -1;
   asm volatile("" ::"v"(ent));
   struct Pair {
     int r, head, qrows;
     bool ok;
   };
-  auto pair_of = [&](int ord) {
+  auto next_pair = [&]() {
     Pair pr;
-    const int e = ord / ngh, gh = ord - e * ngh;
-    if (e - ebase >= 64) {   // uniform: refill the entry window
-      ebase = e;
+    if (ce - ebase >= 64) {   // uniform: refill the entry window
+      ebase = ce;
       ent = ebase + lane < nent ? a.klist[e0 + ebase + lane] : -1;
       // consumed here, so no path reaches the loop's reads with it pending
       // (the compiler's wait insertion would otherwise wait for every load
       // in flight, the ring's prefetches included, on every pair)
       asm volatile("" ::"v"(ent));
     }
-    const int v = __builtin_amdgcn_readlane(ent, e - ebase);
+    const int v = __builtin_amdgcn_readlane(ent, ce - ebase);
     pr.ok = v >= 0;
     const int vv = pr.ok ? v : 0;   // a skipped entry still loads a valid tile (uniform wait counts)
-    pr.r = vv / nrh;
-    pr.head = kvh * g.group + (g.share ? gh : vv - pr.r * nrh);
+    if (nrh == 1) {
+      pr.r = vv;
+      pr.head = kvh * g.group + cg;
+    } else {
+      pr.r = vv / nrh;
+      pr.head = kvh * g.group + (vv - pr.r * nrh);
+    }
     pr.qrows = min(kBlock, len - pr.r * kBlock);
+    if (++cg == ngh) {
+      cg = 0;
+      ++ce;
+    }
     return pr;
   };
   auto issue_pair = [&](const Pair& pr, int b) {
-    const int64_t qo = q_offset(g, s, pr.head, tok0, pr.r * kBlock) * 2;
+    const int64_t qo = (qbase + (int64_t)pr.head * g.q_head + (int64_t)(pr.r * kBlock * 128)) * 2;
     const unsigned char* qb = bwd_uniform(qbytes + qo);
     const unsigned char* db = bwd_uniform(dbytes + qo);
+    if (pr.qrows == kBlock) {
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const uint32_t o = (uint32_t)min(trow[ii], pr.qrows - 1) * 256 + toff[ii];
-      bwd_load_lds16(qb, o, &qd[b][0][(wave + 4 * ii) * 1024]);
-      bwd_load_lds16(db, o, &qd[b][1][(wave + 4 * ii) * 1024]);
+      for (int ii = 0; ii < 4; ++ii) {
+        bwd_load_lds16(qb, ofull[ii], &qd[b][0][(wave + 4 * ii) * 1024]);
+        bwd_load_lds16(db, ofull[ii], &qd[b][1][(wave + 4 * ii) * 1024]);
+      }
+    } else {
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const uint32_t o = slice_off(ii, pr.qrows);
+        bwd_load_lds16(qb, o, &qd[b][0][(wave + 4 * ii) * 1024]);
+        bwd_load_lds16(db, o, &qd[b][1][(wave + 4 * ii) * 1024]);
+      }
     }
-    const int64_t lo = lse_offset(g, s, pr.head, tok0, pr.r * kBlock) * 4;
-    const unsigned char* lb = bwd_uniform((const unsigned char*)(wave == 1 ? a.delta : a.lse) + lo);
-    // waves 0 and 1 bring lse and D; waves 2 and 3 load lse again into their
-    // own unused slot so every wavefront has LPP loads per pair
+    const int64_t lo = (lbase + (int64_t)pr.head * g.lse_head + pr.r * kBlock) * 4;
+    const unsigned char* lb = bwd_uniform((const unsigned char*)(wave == 1 ? a.delta : a.nlse2) + lo);
+    // waves 0 and 1 bring -lse log2(e) and D; waves 2 and 3 load the first
+    // again into their own unused slot so every wavefront has LPP loads per pair
     bwd_load_lds4(lb, (uint32_t)min(lane, pr.qrows - 1) * 4,
                   (const unsigned char*)(wave < 2 ? &lds_ld[b][wave][0] : &lds_ld[b][0][0]));
   };
 
-  // ring prologue: the first NB - 1 pairs
-  Pair ring[NB];
+  // ring prologue: the first NB - 1 pairs, kept as a shift register of the
+  // pairs whose loads are in flight (compile-time indices: it stays in registers)
+  Pair pipe[NB - 1];
 #pragma unroll
-  for (int u = 0; u < NB - 1; ++u)
+  for (int u = 0; u < NB - 1; ++u) {
+    pipe[u] = Pair{0, 0, 1, false};
     if (ord_lo + u < ord_hi) {
-      ring[u] = pair_of(ord_lo + u);
-      issue_pair(ring[u], u);
+      pipe[u] = next_pair();
+      issue_pair(pipe[u], u);
     }
+  }
   // this lane's K row (row `key`, clamped into the block): the B operand of
   // S = Q K^T for d = 16 ks + 8 half .. + 8; and the block's V in LDS
   bf16x8 kreg[8];
@@ -843,25 +925,26 @@ __global__ void __launch_bounds__(256) bwd_dkdv_bf16_kernel(Geom g, BwdBufs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) dk[db][i] = dv[db][i] = 0.f;
 
+  int bc = 0;   // ring buffer of pair ord: (ord - ord_lo) % NB
   for (int ord = ord_lo; ord < ord_hi; ++ord) {
-    const int u = ord - ord_lo, b = u % NB;
+    const int bn = bc == 0 ? NB - 1 : bc - 1;   // buffer of pair ord + NB - 1
     const int ahead = ord + NB - 1;   // the pair whose loads go out in this iteration
     Pair nxt = {0, 0, 1, false};
-    if (ahead < ord_hi) nxt = pair_of(ahead);
+    if (ahead < ord_hi) nxt = next_pair();
     bwd_wait_pairs<LPP>(min(NB - 2, ord_hi - 1 - ord));   // this wave's loads of pair ord
     // every wave's loads of pair ord landed; buffer (ord - 1) % NB is read.  A
     // bare s_barrier: __syncthreads would also wait for the younger pairs' loads
     asm volatile("s_barrier" ::: "memory");
-    if (ahead < ord_hi) {
-      ring[(u + NB - 1) % NB] = nxt;
-      issue_pair(nxt, (u + NB - 1) % NB);
-    }
-    const Pair cur = ring[b];
+    if (ahead < ord_hi) issue_pair(nxt, bn);
+    const Pair cur = pipe[0];
+#pragma unroll
+    for (int i = 0; i + 1 < NB - 1; ++i) pipe[i] = pipe[i + 1];
+    pipe[NB - 2] = nxt;
     if (cur.ok) {
-      const unsigned char* qt = qd[b][0];
-      const unsigned char* dot = qd[b][1];
-      const float* lse_s = lds_ld[b][0];
-      const float* del_s = lds_ld[b][1];
+      const unsigned char* qt = qd[bc][0];
+      const unsigned char* dot = qd[bc][1];
+      const float* lse_s = lds_ld[bc][0];
+      const float* del_s = lds_ld[bc][1];
       // S = Q K^T and dP = dO V^T: this wave's 32 query rows x 32 keys (one
       // key per lane); the Q and dO operands of step ks + 2 are read while
       // step ks multiplies (an order pinned with sched_group_barrier: left
@@ -886,28 +969,40 @@ __global__ void __launch_bounds__(256) bwd_dkdv_bf16_kernel(Geom g, BwdBufs a) {
         if (ks + 2 < 8) __builtin_amdgcn_sched_group_barrier(kDsRead, 3, 0);
         __builtin_amdgcn_sched_group_barrier(kMfma, 2, 0);
       }
-      // lse and D of this lane's 16 query rows, four runs of 4 read one run ahead
+      // -lse log2(e) and D of this lane's 16 query rows, four runs of 4 read
+      // one run ahead.  Pairs below the diagonal with a whole query block need
+      // no mask (every key precedes every query row)
       bf16x8 pb[2], dsb[2];
-      f32x4 lsv[2], dlv[2];
-      lsv[0] = *reinterpret_cast<const f32x4*>(lse_s + qh * 32 + 4 * half);
-      dlv[0] = *reinterpret_cast<const f32x4*>(del_s + qh * 32 + 4 * half);
+      auto weights = [&](auto full) {
+        f32x4 lsv[2], dlv[2];
+        lsv[0] = *reinterpret_cast<const f32x4*>(lse_s + qh * 32 + 4 * half);
+        dlv[0] = *reinterpret_cast<const f32x4*>(del_s + qh * 32 + 4 * half);
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        if (gq + 1 < 4) {
-          lsv[(gq + 1) & 1] = *reinterpret_cast<const f32x4*>(lse_s + qh * 32 + 8 * (gq + 1) + 4 * half);
-          dlv[(gq + 1) & 1] = *reinterpret_cast<const f32x4*>(del_s + qh * 32 + 8 * (gq + 1) + 4 * half);
-        }
+        for (int gq = 0; gq < 4; ++gq) {
+          if (gq + 1 < 4) {
+            lsv[(gq + 1) & 1] = *reinterpret_cast<const f32x4*>(lse_s + qh * 32 + 8 * (gq + 1) + 4 * half);
+            dlv[(gq + 1) & 1] = *reinterpret_cast<const f32x4*>(del_s + qh * 32 + 8 * (gq + 1) + 4 * half);
+          }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * gq + e;
-          const int q = qh * 32 + 8 * gq + 4 * half + e;
-          const bool ok = q < cur.qrows && kpos <= cur.r * kBlock + q;
-          // masked weights exponentiate -inf (no branch per element)
-          const float p = __builtin_amdgcn_exp2f(ok ? fmaf(sacc[i], cl2, -lsv[gq & 1][e] * kLog2e) : -INFINITY);
-          pb[i / 8][i % 8] = (__bf16)p;
-          dsb[i / 8][i % 8] = (__bf16)(p * (dpacc[i] - dlv[gq & 1][e]));
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * gq + e;
+            const float x = fmaf(sacc[i], cl2, lsv[gq & 1][e]);
+            float p;
+            if constexpr (decltype(full)::value) {
+              p = __builtin_amdgcn_exp2f(x);
+            } else {
+              const int q = qh * 32 + 8 * gq + 4 * half + e;
+              const bool ok = q < cur.qrows && kpos <= cur.r * kBlock + q;
+              // masked weights exponentiate -inf (no branch per element)
+              p = __builtin_amdgcn_exp2f(ok ? x : -INFINITY);
+            }
+            pb[i / 8][i % 8] = (__bf16)p;
+            dsb[i / 8][i % 8] = (__bf16)(p * (dpacc[i] - dlv[gq & 1][e]));
+          }
         }
-      }
+      };
+      if (cur.r > j && cur.qrows == kBlock) weights(std::true_type{});
+      else weights(std::false_type{});
       // dV^T += dO^T P and dK^T += Q^T dS: MFMA i takes d block i / 4, step
       // (i / 2) % 2, dV for even i and dK for odd; its transposed A operand
       // is read four MFMAs ahead
@@ -929,6 +1024,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_bf16_kernel(Geom g, BwdBufs a) {
         if (i + 4 < 16) __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
       }
     }
+    bc = bc == NB - 1 ? 0 : bc + 1;
   }
   // add the query halves: waves 2, 3 hand their sums to waves 0, 1 through
   // LDS (element-major, so the lanes of a store hit consecutive banks)
@@ -1013,7 +1109,7 @@ int launch_bwd(const Geom& g, int dtype, const BwdBufs& b, int64_t kv_elems, int
       const int nk = (int)slots * g.hkv;   // (key block slot, KV head) lists
       bwd_count_kernel<<<(unsigned)((g.rows + 3) / 4), 256, 0, st>>>(g, b);
       bwd_kscan_kernel<<<1, 1024, 0, st>>>(b.kcount, b.kptr, b.witem, nk, g.share ? g.group : 1, b.split_target,
-                                           b.max_chunks, b.witems);
+                                           b.max_chunks, b.witems, g.hkv);
       bwd_klist_kernel<<<(unsigned)((nk + 3) / 4), 256, 0, st>>>(g, b, nk);
       bwd_split_clear_kernel<<<dim3(slots, (unsigned)g.hkv), 256, 0, st>>>(g, b);
       if (g.share && (g.hpr == 2 || g.hpr == 4 || g.hpr == 8))

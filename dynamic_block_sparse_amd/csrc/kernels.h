@@ -57,7 +57,9 @@ struct BwdBufs {
   const void *q, *k, *v, *o, *dout;
   const float* lse;
   void *dq, *dk, *dv;
-  float *delta, *dk_acc, *dv_acc;
+  // delta: D_i = dO_i . O_i; nlse2: -lse_i log2(e) (both in the lse layout,
+  // written by the dQ kernels for the dK/dV kernel)
+  float *delta, *nlse2, *dk_acc, *dv_acc;
   // bf16: (row, head) pairs listing each key block and finished workgroups per
   // key block, [key block slot][KV head]; key blocks with more pairs than
   // split_target are shared by several workgroups that add into dk_acc / dv_acc

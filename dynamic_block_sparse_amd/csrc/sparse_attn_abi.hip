@@ -222,9 +222,9 @@ size_t ws_size(const Plan& pl, int which, int splits) {
     sz += align_up(worklist_chunk_bytes(pl.g.rows));
   } else if (which == 2 && pl.g.mode == SA_DECODE) {
     sz += align_up(decode_partials_bytes(pl.g, splits));
-  } else if (which == 3) {   // backward: D_i per query (lse layout), dK and dV fp32 accumulators,
-                             // per key block pair counts and finished-workgroup counts
-    sz += align_up((size_t)lse_elems(pl) * sizeof(float));
+  } else if (which == 3) {   // backward: D_i and -lse_i log2(e) per query (lse layout), dK and dV fp32
+                             // accumulators, per key block pair counts and finished-workgroup counts
+    sz += 2 * align_up((size_t)lse_elems(pl) * sizeof(float));
     sz += 2 * align_up((size_t)kv_elems(pl) * sizeof(float));
     sz += align_up((size_t)2 * key_slots(pl) * pl.g.hkv * sizeof(int));
     // key-major pair lists: offsets per (key block slot, KV head) and one entry per listed tile
@@ -341,6 +341,8 @@ int sparse_attn_bwd(const sa_problem* p, const sa_route_cfg* rc, const int32_t* 
   b.dk = dk;
   b.dv = dv;
   b.delta = reinterpret_cast<float*>(w);
+  w += align_up((size_t)lse_elems(pl) * sizeof(float));
+  b.nlse2 = reinterpret_cast<float*>(w);
   w += align_up((size_t)lse_elems(pl) * sizeof(float));
   b.dk_acc = reinterpret_cast<float*>(w);
   w += align_up((size_t)n * sizeof(float));
