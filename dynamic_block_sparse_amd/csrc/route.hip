@@ -181,9 +181,10 @@ __device__ __forceinline__ RouteRow route_row(const Geom& g, const sa_route_cfg&
 // workgroup takes kScoreRows query blocks x kScoreCols key blocks, stages
 // the pooled queries (from the summary pass) and the summaries in LDS (every
 // load issued before the first store), and each thread accumulates 2-8 dot
-// products in fp32.  16 x 32 tiles for short histories (more workgroups,
-// short FMA chains), 32 x 64 for long ones (fewer staged bytes per score).  Scored per row instead, every summary is read
-// once per later query block (O(N^2 d) reads from L2); here once per tile row.
+// products in fp32.  Scored per row instead, every summary is read once per
+// later query block (O(N^2 d) reads from L2); here once per tile row.  (Up to
+// 256 key blocks per sequence, route_tile_select_kernel scores and selects
+// in one pass instead.)
 // Scores land in scores[row * max_blocks + (j - start_r)] for the row's
 // candidates j (start_r = 1 when block 0 is forced and r > 0).
 template <int D, int kScoreRows, int kScoreCols>
@@ -541,6 +542,87 @@ __global__ void __launch_bounds__(64) route_select_kernel(Geom g, sa_route_cfg r
 }
 
 // ---------------------------------------------------------------------------
+// Prefill routing under mean pooling when every sequence has at most NC key
+// blocks: scores and selection in one pass.  A workgroup of R wavefronts
+// takes R query blocks of one (sequence, routing head) and all NC key
+// blocks: it stages their pooled queries and the summaries in LDS, and
+// wavefront w then scores query block r0 + w against every key block (lane l
+// takes blocks l + 64 b: consecutive lanes read consecutive summary rows,
+// disjoint banks at the 132-float pitch), parks the scores in its own LDS
+// row and selects that row with select_row.  The same scores ([P2] Eq 6, fp32
+// dot products of the same operands in the same order as the tile kernel)
+// and the same picks as the score and select launches, without the scores'
+// round trip through memory and the second launch.
+template <int D, int NC, int R>
+__global__ void __launch_bounds__(R * 64) route_tile_select_kernel(Geom g, sa_route_cfg rc,
+                                                                 const float* __restrict__ qbar,
+                                                                 const float* __restrict__ summ,
+                                                                 int32_t* __restrict__ J) {
+  constexpr int NT = R * kWave, LD = D + 4, E = NC / kWave;
+  constexpr int QV = (R * D / 4 + NT - 1) / NT, CV = NC * D / 4 / NT;   // float4 per thread
+  __shared__ __attribute__((aligned(16))) float qs[R * LD];
+  __shared__ __attribute__((aligned(16))) float cs[NC * LD];
+  __shared__ float sc[R][NC];
+  const int s = blockIdx.z / g.hr, h = blockIdx.z % g.hr;
+  int blk0 = 0, nblk;
+  if (g.varlen) {
+    blk0 = g.cu_blocks[s];
+    nblk = g.cu_blocks[s + 1] - blk0;
+  } else {
+    nblk = ceil_div(g.n, kBlock);
+  }
+  const int r0 = g.qblk0 + (int)blockIdx.x * R;
+  if (r0 >= nblk) return;   // uniform
+  const int kvh = g.share ? h : h / g.group;
+  const int64_t row0 = prefill_row_index(g, s, h, g.qblk0, blk0, nblk) - g.qblk0;
+  const float* cbase = summ + sum_offset(g, s, kvh, blk0, 0);
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  // stage (rows past the end: clamped copies, never selected)
+  f32x4 qv4[QV], cv4[CV];
+#pragma unroll
+  for (int u = 0; u < QV; ++u) {
+    const int e = min(tid + NT * u, R * D / 4 - 1), rr = e / (D / 4), k4 = e % (D / 4);
+    qv4[u] = *reinterpret_cast<const f32x4*>(qbar + (row0 + min(r0 + rr, nblk - 1)) * D + 4 * k4);
+  }
+#pragma unroll
+  for (int u = 0; u < CV; ++u) {
+    const int e = tid + NT * u, jj = e / (D / 4), k4 = e % (D / 4);
+    cv4[u] = *reinterpret_cast<const f32x4*>(cbase + (int64_t)min(jj, nblk - 1) * D + 4 * k4);
+  }
+#pragma unroll
+  for (int u = 0; u < QV; ++u) {
+    const int e = tid + NT * u;
+    if (e < R * D / 4) *reinterpret_cast<f32x4*>(qs + (e / (D / 4)) * LD + 4 * (e % (D / 4))) = qv4[u];
+  }
+#pragma unroll
+  for (int u = 0; u < CV; ++u) {
+    const int e = tid + NT * u;
+    *reinterpret_cast<f32x4*>(cs + (e / (D / 4)) * LD + 4 * (e % (D / 4))) = cv4[u];
+  }
+  __syncthreads();
+  const int r = r0 + wave;
+  if (r >= nblk) return;   // no barrier follows
+  float acc[E];
+#pragma unroll
+  for (int b = 0; b < E; ++b) acc[b] = 0.f;
+#pragma unroll 4
+  for (int k = 0; k < D; k += 4) {
+    const f32x4 qv = *reinterpret_cast<const f32x4*>(qs + wave * LD + k);
+#pragma unroll
+    for (int b = 0; b < E; ++b) {
+      const f32x4 cv = *reinterpret_cast<const f32x4*>(cs + (lane + kWave * b) * LD + k);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[b] = __builtin_fmaf(qv[i], cv[i], acc[b]);
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < E; ++b) sc[wave][lane + kWave * b] = acc[b];
+  const int64_t row = row0 + r;
+  const RouteRow w = route_row(g, rc, row);
+  select_row<E>(rc, w, row, (const float*)&sc[wave][w.start], J, lane);
+}
+
+// ---------------------------------------------------------------------------
 // Decode routing in one pass per row ([P2] §3.1: the summaries are cache
 // state, and a decode step's router scans each stored summary of the row once;
 // [P2] §2.2: decode cost is reading history).  One workgroup of 256 threads per
@@ -741,19 +823,26 @@ int launch_route(const Geom& g, const sa_route_cfg& rc, int dtype, const void* q
   const size_t smem = route_smem_bytes(g, rc.qpool);
   const int mbk = std::max(g.max_blocks, 1);
   if (g.mode == SA_PREFILL && rc.qpool == SA_POOL_MEAN && qbar && (int64_t)g.batch * g.hr <= 65535) {
-    // measured on MI355X: 16 x 32 tiles 6.0 us vs 7.9 for 32 x 64 at 128 blocks
-    // per sequence, 44 us vs 39 at 512
-    const bool small = mbk <= 256;
-    const int tr = small ? 16 : 32, tc = small ? 32 : 64;
-    dim3 tgrid((unsigned)((mbk - g.qblk0 + tr - 1) / tr), (unsigned)((mbk + tc - 1) / tc),
-               (unsigned)(g.batch * g.hr));
-    if (g.d == 128) {
-      if (small) route_score_tile_kernel<128, 16, 32><<<tgrid, 256, 0, st>>>(g, rc, qbar, summ, scores);
-      else route_score_tile_kernel<128, 32, 64><<<tgrid, 256, 0, st>>>(g, rc, qbar, summ, scores);
-    } else {
-      if (small) route_score_tile_kernel<64, 16, 32><<<tgrid, 256, 0, st>>>(g, rc, qbar, summ, scores);
-      else route_score_tile_kernel<64, 32, 64><<<tgrid, 256, 0, st>>>(g, rc, qbar, summ, scores);
+    if (mbk <= 256) {   // every row's scores fit one workgroup: score and select in one pass
+      constexpr int R = 8;   // measured at 128 key blocks: 4 and 8 rows a workgroup alike, 16 slower
+      dim3 fgrid((unsigned)((mbk - g.qblk0 + R - 1) / R), 1, (unsigned)(g.batch * g.hr));
+#define SA_TS(D, NC) route_tile_select_kernel<D, NC, R><<<fgrid, R * 64, 0, st>>>(g, rc, qbar, summ, J)
+      if (g.d == 128) {
+        if (mbk <= 64) SA_TS(128, 64);
+        else if (mbk <= 128) SA_TS(128, 128);
+        else SA_TS(128, 256);
+      } else {
+        if (mbk <= 64) SA_TS(64, 64);
+        else if (mbk <= 128) SA_TS(64, 128);
+        else SA_TS(64, 256);
+      }
+#undef SA_TS
+      return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
     }
+    // longer histories: 32 x 64 score tiles, then the selection launch
+    dim3 tgrid((unsigned)((mbk - g.qblk0 + 31) / 32), (unsigned)((mbk + 63) / 64), (unsigned)(g.batch * g.hr));
+    if (g.d == 128) route_score_tile_kernel<128, 32, 64><<<tgrid, 256, 0, st>>>(g, rc, qbar, summ, scores);
+    else route_score_tile_kernel<64, 32, 64><<<tgrid, 256, 0, st>>>(g, rc, qbar, summ, scores);
     if (hipGetLastError() != hipSuccess) return SA_ERR_HIP;
     return launch_select(g, rc, scores, J, st);
   }

@@ -63,7 +63,7 @@ SMALL = [
     wk.TINY_F32_DENSE,
     wk.TINY_F32.replace(name="tiny_f32_ragged_n500_d128_mean", seqlen=500, head_dim=128, qpool="mean", k_b=4),
     # d = 64 mean pooling with block 0 forced: the pooled-query summary pass and
-    # the 16 x 32 score tiles with fp32 inputs
+    # the one-pass score and selection with fp32 inputs
     wk.TINY_F32.replace(name="tiny_f32_n2500_d64_mean_ff", batch=2, seqlen=2500, qpool="mean", k_b=6,
                         forced_first=True),
     wk.PREFILL_MHA.replace(name="mha_small_h3_n1000_kb16", heads_q=3, heads_kv=3, seqlen=1000),
@@ -82,6 +82,11 @@ SMALL = [
                            window=4),
     wk.PREFILL_GQA.replace(name="gqa_small_b1_hq8_hkv2_n1500_kb10_win3_first", batch=1, heads_q=8,
                            heads_kv=2, seqlen=1500, k_b=10, window=3),
+    # 129-256 key blocks: the one-pass score and selection at its widest (four
+    # keys a lane), top-k and the Eq 7 threshold count
+    wk.PREFILL_MHA.replace(name="mha_h2_n12000_kb16", heads_q=2, heads_kv=2, seqlen=12000),
+    wk.PREFILL_GQA.replace(name="gqa_b1_hq4_hkv2_n9000_thresh", batch=1, heads_q=4, heads_kv=2, seqlen=9000,
+                           select="threshold", k_b=24, k_min=4, tau_rel=2.0),
 ]
 
 
