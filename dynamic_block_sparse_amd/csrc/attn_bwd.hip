@@ -460,7 +460,10 @@ __device__ __forceinline__ void bwd_wait_pairs(int pairs) {
 // wave w taking query head 2 blockIdx.y + w / 2 and query rows 32 (w % 2) ..
 // + 32.  The row's listed K and V tiles are read once for both heads: they
 // stream global -> LDS through a ring of NB tiles (each wavefront loads its
-// share, issued NB - 1 tiles ahead, one barrier per tile).  Each lane keeps
+// share, issued NB - 1 tiles ahead, one barrier per tile).  Two tiles (64 KB)
+// leave room for a second workgroup on the CU, whose work covers this one's
+// waits (232 registers: two wavefronts a SIMD); a 3-deep ring with one
+// workgroup a CU was 3-7 % slower.  Each lane keeps
 // its query row of Q and dO (the B operands of S^T = K Q^T and dP^T =
 // V dO^T) in registers, forms P and dS for one 32-key half of the tile at a
 // time, and accumulates dQ^T += K^T dS^T (K^T by LDS transpose reads).  It
@@ -468,7 +471,7 @@ __device__ __forceinline__ void bwd_wait_pairs(int pairs) {
 // in one workgroup of 8 wavefronts need more than the 256 registers a
 // wavefront may then hold.)
 __global__ void __launch_bounds__(256) bwd_dq_rows_bf16_kernel(Geom g, BwdBufs a) {
-  constexpr int NW = 4, NB = 3, TILE = 64 * 256;
+  constexpr int NW = 4, NB = 2, TILE = 64 * 256;
   constexpr int LPT = 16 / NW;   // 1 KB slices of K (and as many of V) per wavefront and tile
   static_assert(NW * LPT * 1024 == TILE, "the wavefronts' slices cover the tile once");
   __shared__ __attribute__((aligned(1024))) unsigned char ring[NB][2][TILE];   // [slot][K, V]
