@@ -203,6 +203,53 @@ def graph_timed(stepper, steps, warmup):
     return start.elapsed_time(end) / steps
 
 
+def pipelined_timed(steppers, steps, warmup):
+    """Two independent batches in flight: each stepper (its own J, worklist,
+    outputs and workspaces over the same resident inputs) has its step
+    captured in a HIP graph, and the graphs are replayed alternately on two
+    streams.  Every step still runs route, worklist and fwd over its batch; a
+    step's kernels may overlap the other batch's.  Throughput only: one
+    step's latency is the serial graph replay."""
+    import torch
+    graphs = []
+    for st in steppers:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            st.step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            st.step()
+        graphs.append(g)
+    streams = [torch.cuda.Stream() for _ in steppers]
+    n = len(steppers)
+
+    def run(k):
+        for s in streams:
+            s.wait_stream(torch.cuda.current_stream())
+        for i in range(k):
+            with torch.cuda.stream(streams[i % n]):
+                graphs[i % n].replay()
+        for s in streams:
+            torch.cuda.current_stream().wait_stream(s)
+
+    run(warmup)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    run(steps)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+PIPELINED_NOTE = ("two batches in flight: the step's HIP graph of each of two steppers (own buffers, same inputs) "
+                  "replayed alternately on two streams, so one batch's route and worklist can overlap the other's "
+                  "attention; throughput only (a step's latency is ms_per_step)")
+
+
 def _host_info():
     """Threads numpy's BLAS uses, the BLAS library, and the host CPU model."""
     import numpy  # noqa: F401  (loads the BLAS so threadpoolctl can see it)
@@ -336,6 +383,13 @@ def measure_prefill(args, dbs, w, inp, flush):
     }
     if w.varlen or w.select == "threshold":
         rec["worklist"] = st.worklist_stats()
+    if not args.no_graph:
+        log(f"timing {w.name}: two batches in flight on two streams")
+        st2 = Stepper(dbs, w, inp)
+        msp = pipelined_timed([st, st2], args.steps, args.warmup)
+        del st2
+        rec["pipelined"] = {"streams": 2, "ms_per_step": round(msp, 5),
+                            "value": round(flops / (msp * 1e-3) / 1e12, 3), "note": PIPELINED_NOTE}
     if not args.no_bwd:
         log(f"timing the backward pass on {w.name}")
         rec["backward"] = measure_bwd(args, dbs, st, visits)
@@ -542,6 +596,14 @@ def measure_decode(args, dbs, wd, dev, flush):
                              f"last-level cache flush), events on the launch stream"},
         "route_summary_gbs": round(route_bytes / (spread(cold[0])["median"] * 1e-3) / 1e9, 1),
     }
+    if not args.no_graph:
+        log(f"timing {wd.name}: two batches in flight on two streams")
+        sd2 = Stepper(dbs, wd, inp_d, summaries_in=True, num_splits=args.decode_splits)
+        msp = pipelined_timed([sd, sd2], steps, args.warmup)
+        del sd2
+        rec["pipelined"] = {"streams": 2, "ms_per_step": round(msp, 5),
+                            "kv_gbs_per_step_time": round((kv_bytes + qo_bytes) / (msp * 1e-3) / 1e9, 1),
+                            "note": PIPELINED_NOTE}
     del sd
     # the other reading of the setting: k_b blocks routed plus the forced last
     # block (k_b + 1 tiles per row), on the same cache
