@@ -497,16 +497,25 @@ __device__ __forceinline__ void select_row(const sa_route_cfg& rc, const RouteRo
   };
 
   int kr = rc.k_b;
+  uint32_t k0 = 0u;   // Eq 7's threshold as a key, and the candidates at or above it
+  int above = -1;
   if (rc.select == SA_SELECT_THRESHOLD) {
     mx = wave_max(mx);
-    const int above = w.nc > 0 ? count_ge(order_key(mx - rc.tau_rel)) : 0;
+    k0 = order_key(mx - rc.tau_rel);
+    above = w.nc > 0 ? count_ge(k0) : 0;
     kr = min(rc.k_b, max(rc.k_min, w.nforced + above));
   }
   const int dsel = min(max(kr - w.nforced, 0), w.nc);
   const bool take_all = (dsel == w.nc);
   uint32_t thr = 0u;
   int take_eq = 0;
-  if (!take_all && dsel > 0) {
+  if (!take_all && dsel > 0 && dsel == above && k0 > 0u) {
+    // neither k_b nor k_min binds: the picks are exactly the candidates at or
+    // above Eq 7's threshold (the dsel-th largest key T is >= k0 and exactly
+    // dsel keys are >= T), so no search: keys > k0 - 1, none taken by equality
+    thr = k0 - 1u;
+    take_eq = 0;
+  } else if (!take_all && dsel > 0) {
     // T lies in [kmin, kmax]: the bits above their highest difference are
     // common to every candidate key and need no search
     uint32_t kmin = 0xffffffffu, kmax = 0u;
