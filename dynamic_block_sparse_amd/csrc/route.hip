@@ -702,28 +702,38 @@ __global__ void __launch_bounds__(256) route_decode_kernel(Geom g, sa_route_cfg 
   // the digit over the keys that match the digits found so far, and
   // wavefront 0 finds the bin holding the need-th largest of them.  Then
   // need = the number of keys equal to T to take (the lowest ids).
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[4][256];   // one histogram per wavefront: fewer same-address atomics
   __shared__ int pick[2];
+  __shared__ int wcnt[4][2];
   const int dsel = min(max(rc.k_b - w.nforced, 0), nc);
   const bool take_all = dsel == nc;
   uint32_t thr = 0u;
   int need = dsel;
+  // this thread's keys, candidates tid + 256 k
+  constexpr int KPT = (kWave * E + 255) / 256;
+  uint32_t kt[KPT];
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) {
+    const int i = tid + 256 * k;
+    kt[k] = i < nc ? order_key(sc[i]) : 0u;
+  }
   if (!take_all && dsel > 0) {   // uniform over the workgroup
     uint32_t pmask = 0u;
     for (int shift = 24; shift >= 0; shift -= 8) {
-      hist[tid] = 0u;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) hist[b][tid] = 0u;
       __syncthreads();
-      for (int i = tid; i < nc; i += 256) {
-        const uint32_t key = order_key(sc[i]);
-        if ((key & pmask) == thr) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-      }
+#pragma unroll
+      for (int k = 0; k < KPT; ++k)
+        if (tid + 256 * k < nc && (kt[k] & pmask) == thr) atomicAdd(&hist[wave][(kt[k] >> shift) & 255u], 1u);
       __syncthreads();
       if (wave == 0) {
         // lane l holds bins 255 - 4l .. 252 - 4l (the largest digits first)
         int c[4], tot = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          c[j] = (int)hist[255 - 4 * lane - j];
+          const int b = 255 - 4 * lane - j;
+          c[j] = (int)(hist[0][b] + hist[1][b] + hist[2][b] + hist[3][b]);
           tot += c[j];
         }
         const int incl = wave_incl_scan_i(tot), excl = incl - tot;
@@ -749,15 +759,69 @@ __global__ void __launch_bounds__(256) route_decode_kernel(Geom g, sa_route_cfg 
       pmask |= 255u << shift;
     }
   }
-  if (wave == 0) {
-    uint32_t key[E];
-    const int lastc = max(nc - 1, 0);
+  if constexpr (E < 4) {
+    if (wave == 0) {
+      uint32_t key[E];
+      const int lastc = max(nc - 1, 0);
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int i = lane + 64 * e;
-      key[e] = order_key(sc[min(i, lastc)]) & (i < nc ? 0xffffffffu : 0u);
+      for (int e = 0; e < E; ++e) {
+        const int i = lane + 64 * e;
+        key[e] = order_key(sc[min(i, lastc)]) & (i < nc ? 0xffffffffu : 0u);
+      }
+      emit_row<E>(rc, w, row, key, dsel, take_all, thr, need, J, lane);
     }
-    emit_row<E>(rc, w, row, key, dsel, take_all, thr, need, J, lane);
+  } else {
+    // the picks in ascending id order, written by all four wavefronts: wave v
+    // takes candidates lane + 64 e for e in [EW v, EW v + EW); the picks and
+    // the keys equal to T of the waves before it give its first position and
+    // the rank of its first key equal to T
+    constexpr int EW = E / 4;
+    int32_t* jrow = J + row * rc.k_b;
+    uint32_t key[EW];
+    bool valid[EW];
+    int ngt = 0, neq = 0;
+#pragma unroll
+    for (int e = 0; e < EW; ++e) {
+      const int i = lane + kWave * (EW * wave + e);
+      valid[e] = i < nc;
+      key[e] = valid[e] ? order_key(sc[i]) : 0u;
+      ngt += __popcll(__ballot(valid[e] && (take_all || key[e] > thr)));
+      neq += __popcll(__ballot(valid[e] && !take_all && key[e] == thr));
+    }
+    if (lane == 0) {
+      wcnt[wave][0] = ngt;
+      wcnt[wave][1] = neq;
+    }
+    __syncthreads();
+    int gtb = 0, eqb = 0;
+    for (int v = 0; v < wave; ++v) {
+      gtb += wcnt[v][0];
+      eqb += wcnt[v][1];
+    }
+    if (dsel > 0) {
+      const uint64_t below = (1ull << lane) - 1ull;
+      int pos = w.nforced + gtb + min(eqb, need), eq_seen = eqb;
+#pragma unroll
+      for (int e = 0; e < EW; ++e) {
+        const int i = lane + kWave * (EW * wave + e);
+        const bool eq = valid[e] && !take_all && key[e] == thr;
+        const uint64_t beq = __ballot(eq);
+        const int eq_rank = eq_seen + __popcll(beq & below);
+        const bool take = valid[e] && (take_all || key[e] > thr || (eq && eq_rank < need));
+        const uint64_t bt = __ballot(take);
+        if (take) jrow[pos + __popcll(bt & below)] = w.start + i;
+        pos += __popcll(bt);
+        eq_seen += __popcll(beq);
+      }
+    }
+    if (wave == 0) {   // forced blocks first (the sink outside the window, then the window), -1 last
+      if (lane <= w.cur - w.lo) {
+        const int k0 = (w.ff && w.lo > 0) ? 1 : 0;
+        if (lane == 0 && k0) jrow[0] = 0;
+        jrow[k0 + lane] = w.lo + lane;
+      }
+      for (int i = w.nforced + dsel + lane; i < rc.k_b; i += kWave) jrow[i] = -1;
+    }
   }
 }
 
