@@ -702,7 +702,7 @@ __global__ void __launch_bounds__(256) route_decode_kernel(Geom g, sa_route_cfg 
   // the digit over the keys that match the digits found so far, and
   // wavefront 0 finds the bin holding the need-th largest of them.  Then
   // need = the number of keys equal to T to take (the lowest ids).
-  __shared__ uint32_t hist[4][256];   // one histogram per wavefront: fewer same-address atomics
+  __shared__ uint32_t hist[2][4][256];   // per pass parity, one per wavefront (fewer same-address atomics)
   __shared__ int pick[2];
   __shared__ int wcnt[4][2];
   const int dsel = min(max(rc.k_b - w.nforced, 0), nc);
@@ -719,21 +719,25 @@ __global__ void __launch_bounds__(256) route_decode_kernel(Geom g, sa_route_cfg 
   }
   if (!take_all && dsel > 0) {   // uniform over the workgroup
     uint32_t pmask = 0u;
-    for (int shift = 24; shift >= 0; shift -= 8) {
 #pragma unroll
-      for (int b = 0; b < 4; ++b) hist[b][tid] = 0u;
-      __syncthreads();
+    for (int b = 0; b < 8; ++b) (&hist[0][0][0])[256 * b + tid] = 0u;
+    __syncthreads();
+    for (int shift = 24, par = 0; shift >= 0; shift -= 8, par ^= 1) {
+      uint32_t (&h)[4][256] = hist[par];
 #pragma unroll
       for (int k = 0; k < KPT; ++k)
-        if (tid + 256 * k < nc && (kt[k] & pmask) == thr) atomicAdd(&hist[wave][(kt[k] >> shift) & 255u], 1u);
+        if (tid + 256 * k < nc && (kt[k] & pmask) == thr) atomicAdd(&h[wave][(kt[k] >> shift) & 255u], 1u);
       __syncthreads();
+      // the other parity's histograms, read in the previous pass, start the next one cleared
+#pragma unroll
+      for (int b = 0; b < 4; ++b) hist[par ^ 1][b][tid] = 0u;
       if (wave == 0) {
         // lane l holds bins 255 - 4l .. 252 - 4l (the largest digits first)
         int c[4], tot = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int b = 255 - 4 * lane - j;
-          c[j] = (int)(hist[0][b] + hist[1][b] + hist[2][b] + hist[3][b]);
+          c[j] = (int)(h[0][b] + h[1][b] + h[2][b] + h[3][b]);
           tot += c[j];
         }
         const int incl = wave_incl_scan_i(tot), excl = incl - tot;
