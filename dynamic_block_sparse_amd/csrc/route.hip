@@ -542,6 +542,115 @@ __device__ __forceinline__ void select_row(const sa_route_cfg& rc, const RouteRo
   emit_row<E>(rc, w, row, key, dsel, take_all, thr, take_eq, J, lane);
 }
 
+// The selection of one row by one wavefront over scores in memory (global
+// memory or LDS), for rows longer than select_row holds in registers (more
+// than 8192 candidates).  Same budget, same rule and the same picks as
+// select_row: Eq 7's count from the row maximum; then the budget-th largest
+// order-preserving key T, found one 8-bit digit at a time from the top with
+// a 256-bin histogram in LDS (`hist`, this wavefront's own); then the picks
+// in ascending id order, 64 candidates at a time.
+template <typename Scores>
+__device__ __forceinline__ void select_row_mem(const sa_route_cfg& rc, const RouteRow& w, int64_t row, Scores srow,
+                                            int32_t* __restrict__ J, int lane, uint32_t* hist) {
+  const int nc = w.nc;
+  auto key_at = [&](int i) { return order_key(srow[i]); };
+  auto count_ge = [&](uint32_t x) {
+    int c = 0;
+    for (int i = lane; i < nc; i += kWave) c += key_at(i) >= x ? 1 : 0;
+    return wave_sum_i(c);
+  };
+  int kr = rc.k_b;
+  uint32_t k0 = 0u;
+  int above = -1;
+  if (rc.select == SA_SELECT_THRESHOLD) {
+    float mx = -INFINITY;
+    for (int i = lane; i < nc; i += kWave) mx = fmaxf(mx, srow[i]);
+    mx = wave_max(mx);
+    k0 = order_key(mx - rc.tau_rel);
+    above = nc > 0 ? count_ge(k0) : 0;
+    kr = min(rc.k_b, max(rc.k_min, w.nforced + above));
+  }
+  const int dsel = min(max(kr - w.nforced, 0), nc);
+  const bool take_all = dsel == nc;
+  uint32_t thr = 0u;
+  int need = dsel;
+  if (!take_all && dsel > 0 && dsel == above && k0 > 0u) {
+    thr = k0 - 1u;   // the candidates at or above Eq 7's threshold (see select_row)
+    need = 0;
+  } else if (!take_all && dsel > 0) {
+    uint32_t pmask = 0u;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      for (int b = lane; b < 256; b += kWave) hist[b] = 0u;
+      __builtin_amdgcn_wave_barrier();
+      for (int i = lane; i < nc; i += kWave) {
+        const uint32_t k = key_at(i);
+        if ((k & pmask) == thr) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+      }
+      __builtin_amdgcn_wave_barrier();
+      // lane l holds bins 255 - 4l .. 252 - 4l (the largest digits first)
+      int c[4], tot = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        c[j] = (int)hist[255 - 4 * lane - j];
+        tot += c[j];
+      }
+      const int incl = wave_incl_scan_i(tot), excl = incl - tot;
+      const uint64_t reach = __ballot(incl >= need);   // some lane reaches need: need <= matching keys
+      const int owner = __ffsll((unsigned long long)reach) - 1;
+      int run = excl, bin = 255 - 4 * lane;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (run + c[j] >= need) {
+          bin = 255 - 4 * lane - j;
+          break;
+        }
+        run += c[j];
+      }
+      const int bin_o = __builtin_amdgcn_readlane(bin, owner);
+      const int run_o = __builtin_amdgcn_readlane(run, owner);
+      thr |= (uint32_t)bin_o << shift;
+      need -= run_o;
+      pmask |= 255u << shift;
+      __builtin_amdgcn_wave_barrier();   // every lane has read the histogram before the next clear
+    }
+  }
+  int32_t* jrow = J + row * rc.k_b;
+  if (lane <= w.cur - w.lo) {   // forced blocks first: the sink outside the window, then the window
+    const int kf = (w.ff && w.lo > 0) ? 1 : 0;
+    if (lane == 0 && kf) jrow[0] = 0;
+    jrow[kf + lane] = w.lo + lane;
+  }
+  if (dsel > 0) {
+    const uint64_t below = (1ull << lane) - 1ull;
+    int pos = w.nforced, eq_seen = 0;
+    for (int base = 0; base < nc; base += kWave) {
+      const int i = base + lane;
+      const bool valid = i < nc;
+      const uint32_t k = valid ? key_at(i) : 0u;
+      const bool eq = valid && !take_all && k == thr;
+      const uint64_t beq = __ballot(eq);
+      const int eq_rank = eq_seen + __popcll(beq & below);
+      const bool take = valid && (take_all || k > thr || (eq && eq_rank < need));
+      const uint64_t bt = __ballot(take);
+      if (take) jrow[pos + __popcll(bt & below)] = w.start + i;
+      pos += __popcll(bt);
+      eq_seen += __popcll(beq);
+    }
+  }
+  for (int i = w.nforced + dsel + lane; i < rc.k_b; i += kWave) jrow[i] = -1;
+}
+
+// Rows with more than 8192 candidates: one wavefront per row over its scores
+// in the route workspace.
+__global__ void __launch_bounds__(64) route_select_mem_kernel(Geom g, sa_route_cfg rc,
+                                                              const float* __restrict__ scores,
+                                                              int32_t* __restrict__ J) {
+  __shared__ uint32_t hist[256];
+  const int64_t row = blockIdx.x;
+  const RouteRow w = route_row(g, rc, row);
+  select_row_mem(rc, w, row, scores + row * (int64_t)g.max_blocks, J, (int)threadIdx.x, hist);
+}
+
 template <int E>
 __global__ void __launch_bounds__(64) route_select_kernel(Geom g, sa_route_cfg rc, const float* __restrict__ scores,
                                                           int32_t* __restrict__ J) {
@@ -693,138 +802,143 @@ __global__ void __launch_bounds__(256) route_decode_kernel(Geom g, sa_route_cfg 
     }
   }
   __syncthreads();
-  if (rc.select != SA_SELECT_TOPK) {   // Eq 7's threshold count: the one-wavefront selection
-    if (wave == 0) select_row<E>(rc, w, row, (const float*)sc, J, lane);
-    return;
-  }
-  // Top-k: the D-th largest order-preserving key T found by the whole
-  // workgroup, one 8-bit digit at a time from the top: each pass histograms
-  // the digit over the keys that match the digits found so far, and
-  // wavefront 0 finds the bin holding the need-th largest of them.  Then
-  // need = the number of keys equal to T to take (the lowest ids).
-  __shared__ uint32_t hist[2][4][256];   // per pass parity, one per wavefront (fewer same-address atomics)
-  __shared__ int pick[2];
-  __shared__ int wcnt[4][2];
-  const int dsel = min(max(rc.k_b - w.nforced, 0), nc);
-  const bool take_all = dsel == nc;
-  uint32_t thr = 0u;
-  int need = dsel;
-  // this thread's keys, candidates tid + 256 k
-  constexpr int KPT = (kWave * E + 255) / 256;
-  uint32_t kt[KPT];
-#pragma unroll
-  for (int k = 0; k < KPT; ++k) {
-    const int i = tid + 256 * k;
-    kt[k] = i < nc ? order_key(sc[i]) : 0u;
-  }
-  if (!take_all && dsel > 0) {   // uniform over the workgroup
-    uint32_t pmask = 0u;
-#pragma unroll
-    for (int b = 0; b < 8; ++b) (&hist[0][0][0])[256 * b + tid] = 0u;
-    __syncthreads();
-    for (int shift = 24, par = 0; shift >= 0; shift -= 8, par ^= 1) {
-      uint32_t (&h)[4][256] = hist[par];
-#pragma unroll
-      for (int k = 0; k < KPT; ++k)
-        if (tid + 256 * k < nc && (kt[k] & pmask) == thr) atomicAdd(&h[wave][(kt[k] >> shift) & 255u], 1u);
-      __syncthreads();
-      // the other parity's histograms, read in the previous pass, start the next one cleared
-#pragma unroll
-      for (int b = 0; b < 4; ++b) hist[par ^ 1][b][tid] = 0u;
-      if (wave == 0) {
-        // lane l holds bins 255 - 4l .. 252 - 4l (the largest digits first)
-        int c[4], tot = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int b = 255 - 4 * lane - j;
-          c[j] = (int)(h[0][b] + h[1][b] + h[2][b] + h[3][b]);
-          tot += c[j];
-        }
-        const int incl = wave_incl_scan_i(tot), excl = incl - tot;
-        const uint64_t reach = __ballot(incl >= need);   // some lane reaches need: need <= matching keys
-        const int owner = __ffsll((unsigned long long)reach) - 1;
-        if (lane == owner) {
-          int run = excl, bin = 255 - 4 * lane;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            if (run + c[j] >= need) {
-              bin = 255 - 4 * lane - j;
-              break;
-            }
-            run += c[j];
-          }
-          pick[0] = bin;
-          pick[1] = need - run;
-        }
-      }
-      __syncthreads();
-      thr |= (uint32_t)pick[0] << shift;
-      need = pick[1];
-      pmask |= 255u << shift;
-    }
-  }
-  if constexpr (E < 4) {
-    if (wave == 0) {
-      uint32_t key[E];
-      const int lastc = max(nc - 1, 0);
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int i = lane + 64 * e;
-        key[e] = order_key(sc[min(i, lastc)]) & (i < nc ? 0xffffffffu : 0u);
-      }
-      emit_row<E>(rc, w, row, key, dsel, take_all, thr, need, J, lane);
-    }
+  if constexpr (E > 128) {   // more than 8192 candidates: one wavefront over the scores in LDS
+    __shared__ uint32_t hm[256];
+    if (wave == 0) select_row_mem(rc, w, row, (const float*)sc, J, lane, hm);
   } else {
-    // the picks in ascending id order, written by all four wavefronts: wave v
-    // takes candidates lane + 64 e for e in [EW v, EW v + EW); the picks and
-    // the keys equal to T of the waves before it give its first position and
-    // the rank of its first key equal to T
-    constexpr int EW = E / 4;
-    int32_t* jrow = J + row * rc.k_b;
-    uint32_t key[EW];
-    bool valid[EW];
-    int ngt = 0, neq = 0;
-#pragma unroll
-    for (int e = 0; e < EW; ++e) {
-      const int i = lane + kWave * (EW * wave + e);
-      valid[e] = i < nc;
-      key[e] = valid[e] ? order_key(sc[i]) : 0u;
-      ngt += __popcll(__ballot(valid[e] && (take_all || key[e] > thr)));
-      neq += __popcll(__ballot(valid[e] && !take_all && key[e] == thr));
+    if (rc.select != SA_SELECT_TOPK) {   // Eq 7's threshold count: the one-wavefront selection
+      if (wave == 0) select_row<E>(rc, w, row, (const float*)sc, J, lane);
+      return;
     }
-    if (lane == 0) {
-      wcnt[wave][0] = ngt;
-      wcnt[wave][1] = neq;
+    // Top-k: the D-th largest order-preserving key T found by the whole
+    // workgroup, one 8-bit digit at a time from the top: each pass histograms
+    // the digit over the keys that match the digits found so far, and
+    // wavefront 0 finds the bin holding the need-th largest of them.  Then
+    // need = the number of keys equal to T to take (the lowest ids).
+    __shared__ uint32_t hist[2][4][256];   // per pass parity, one per wavefront (fewer same-address atomics)
+    __shared__ int pick[2];
+    __shared__ int wcnt[4][2];
+    const int dsel = min(max(rc.k_b - w.nforced, 0), nc);
+    const bool take_all = dsel == nc;
+    uint32_t thr = 0u;
+    int need = dsel;
+    // this thread's keys, candidates tid + 256 k
+    constexpr int KPT = (kWave * E + 255) / 256;
+    uint32_t kt[KPT];
+  #pragma unroll
+    for (int k = 0; k < KPT; ++k) {
+      const int i = tid + 256 * k;
+      kt[k] = i < nc ? order_key(sc[i]) : 0u;
     }
-    __syncthreads();
-    int gtb = 0, eqb = 0;
-    for (int v = 0; v < wave; ++v) {
-      gtb += wcnt[v][0];
-      eqb += wcnt[v][1];
+    if (!take_all && dsel > 0) {   // uniform over the workgroup
+      uint32_t pmask = 0u;
+  #pragma unroll
+      for (int b = 0; b < 8; ++b) (&hist[0][0][0])[256 * b + tid] = 0u;
+      __syncthreads();
+      for (int shift = 24, par = 0; shift >= 0; shift -= 8, par ^= 1) {
+        uint32_t (&h)[4][256] = hist[par];
+  #pragma unroll
+        for (int k = 0; k < KPT; ++k)
+          if (tid + 256 * k < nc && (kt[k] & pmask) == thr) atomicAdd(&h[wave][(kt[k] >> shift) & 255u], 1u);
+        __syncthreads();
+        // the other parity's histograms, read in the previous pass, start the next one cleared
+  #pragma unroll
+        for (int b = 0; b < 4; ++b) hist[par ^ 1][b][tid] = 0u;
+        if (wave == 0) {
+          // lane l holds bins 255 - 4l .. 252 - 4l (the largest digits first)
+          int c[4], tot = 0;
+  #pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int b = 255 - 4 * lane - j;
+            c[j] = (int)(h[0][b] + h[1][b] + h[2][b] + h[3][b]);
+            tot += c[j];
+          }
+          const int incl = wave_incl_scan_i(tot), excl = incl - tot;
+          const uint64_t reach = __ballot(incl >= need);   // some lane reaches need: need <= matching keys
+          const int owner = __ffsll((unsigned long long)reach) - 1;
+          if (lane == owner) {
+            int run = excl, bin = 255 - 4 * lane;
+  #pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              if (run + c[j] >= need) {
+                bin = 255 - 4 * lane - j;
+                break;
+              }
+              run += c[j];
+            }
+            pick[0] = bin;
+            pick[1] = need - run;
+          }
+        }
+        __syncthreads();
+        thr |= (uint32_t)pick[0] << shift;
+        need = pick[1];
+        pmask |= 255u << shift;
+      }
     }
-    if (dsel > 0) {
-      const uint64_t below = (1ull << lane) - 1ull;
-      int pos = w.nforced + gtb + min(eqb, need), eq_seen = eqb;
-#pragma unroll
+    if constexpr (E < 4) {
+      if (wave == 0) {
+        uint32_t key[E];
+        const int lastc = max(nc - 1, 0);
+  #pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int i = lane + 64 * e;
+          key[e] = order_key(sc[min(i, lastc)]) & (i < nc ? 0xffffffffu : 0u);
+        }
+        emit_row<E>(rc, w, row, key, dsel, take_all, thr, need, J, lane);
+      }
+    } else {
+      // the picks in ascending id order, written by all four wavefronts: wave v
+      // takes candidates lane + 64 e for e in [EW v, EW v + EW); the picks and
+      // the keys equal to T of the waves before it give its first position and
+      // the rank of its first key equal to T
+      constexpr int EW = E / 4;
+      int32_t* jrow = J + row * rc.k_b;
+      uint32_t key[EW];
+      bool valid[EW];
+      int ngt = 0, neq = 0;
+  #pragma unroll
       for (int e = 0; e < EW; ++e) {
         const int i = lane + kWave * (EW * wave + e);
-        const bool eq = valid[e] && !take_all && key[e] == thr;
-        const uint64_t beq = __ballot(eq);
-        const int eq_rank = eq_seen + __popcll(beq & below);
-        const bool take = valid[e] && (take_all || key[e] > thr || (eq && eq_rank < need));
-        const uint64_t bt = __ballot(take);
-        if (take) jrow[pos + __popcll(bt & below)] = w.start + i;
-        pos += __popcll(bt);
-        eq_seen += __popcll(beq);
+        valid[e] = i < nc;
+        key[e] = valid[e] ? order_key(sc[i]) : 0u;
+        ngt += __popcll(__ballot(valid[e] && (take_all || key[e] > thr)));
+        neq += __popcll(__ballot(valid[e] && !take_all && key[e] == thr));
       }
-    }
-    if (wave == 0) {   // forced blocks first (the sink outside the window, then the window), -1 last
-      if (lane <= w.cur - w.lo) {
-        const int k0 = (w.ff && w.lo > 0) ? 1 : 0;
-        if (lane == 0 && k0) jrow[0] = 0;
-        jrow[k0 + lane] = w.lo + lane;
+      if (lane == 0) {
+        wcnt[wave][0] = ngt;
+        wcnt[wave][1] = neq;
       }
-      for (int i = w.nforced + dsel + lane; i < rc.k_b; i += kWave) jrow[i] = -1;
+      __syncthreads();
+      int gtb = 0, eqb = 0;
+      for (int v = 0; v < wave; ++v) {
+        gtb += wcnt[v][0];
+        eqb += wcnt[v][1];
+      }
+      if (dsel > 0) {
+        const uint64_t below = (1ull << lane) - 1ull;
+        int pos = w.nforced + gtb + min(eqb, need), eq_seen = eqb;
+  #pragma unroll
+        for (int e = 0; e < EW; ++e) {
+          const int i = lane + kWave * (EW * wave + e);
+          const bool eq = valid[e] && !take_all && key[e] == thr;
+          const uint64_t beq = __ballot(eq);
+          const int eq_rank = eq_seen + __popcll(beq & below);
+          const bool take = valid[e] && (take_all || key[e] > thr || (eq && eq_rank < need));
+          const uint64_t bt = __ballot(take);
+          if (take) jrow[pos + __popcll(bt & below)] = w.start + i;
+          pos += __popcll(bt);
+          eq_seen += __popcll(beq);
+        }
+      }
+      if (wave == 0) {   // forced blocks first (the sink outside the window, then the window), -1 last
+        if (lane <= w.cur - w.lo) {
+          const int k0 = (w.ff && w.lo > 0) ? 1 : 0;
+          if (lane == 0 && k0) jrow[0] = 0;
+          jrow[k0 + lane] = w.lo + lane;
+        }
+        for (int i = w.nforced + dsel + lane; i < rc.k_b; i += kWave) jrow[i] = -1;
+      }
     }
   }
 }
@@ -875,13 +989,18 @@ int launch_route_decode_t(const Geom& g, const sa_route_cfg& rc, const T* q, con
   const dim3 grid((unsigned)g.rows);
   const size_t smem = route_decode_smem_bytes(g);
   const int mb = std::max(g.max_blocks, 1);
+  if (mb > 8192 && smem > 65536 &&   // scores of up to 32768 candidates: more LDS than the default
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&route_decode_kernel<T, D, 256>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
+    return SA_ERR_HIP;
   if (mb <= 128) route_decode_kernel<T, D, 2><<<grid, 256, smem, st>>>(g, rc, q, summ, J);
   else if (mb <= 256) route_decode_kernel<T, D, 4><<<grid, 256, smem, st>>>(g, rc, q, summ, J);
   else if (mb <= 512) route_decode_kernel<T, D, 8><<<grid, 256, smem, st>>>(g, rc, q, summ, J);
   else if (mb <= 1024) route_decode_kernel<T, D, 16><<<grid, 256, smem, st>>>(g, rc, q, summ, J);
   else if (mb <= 2048) route_decode_kernel<T, D, 32><<<grid, 256, smem, st>>>(g, rc, q, summ, J);
   else if (mb <= 4096) route_decode_kernel<T, D, 64><<<grid, 256, smem, st>>>(g, rc, q, summ, J);
-  else route_decode_kernel<T, D, 128><<<grid, 256, smem, st>>>(g, rc, q, summ, J);
+  else if (mb <= 8192) route_decode_kernel<T, D, 128><<<grid, 256, smem, st>>>(g, rc, q, summ, J);
+  else route_decode_kernel<T, D, 256><<<grid, 256, smem, st>>>(g, rc, q, summ, J);   // selection from LDS
   return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 
@@ -953,7 +1072,8 @@ int launch_select(const Geom& g, const sa_route_cfg& rc, const float* scores, in
   else if (mb <= 1024) route_select_kernel<16><<<sgrid, 64, 0, st>>>(g, rc, scores, J);
   else if (mb <= 2048) route_select_kernel<32><<<sgrid, 64, 0, st>>>(g, rc, scores, J);
   else if (mb <= 4096) route_select_kernel<64><<<sgrid, 64, 0, st>>>(g, rc, scores, J);
-  else route_select_kernel<128><<<sgrid, 64, 0, st>>>(g, rc, scores, J);
+  else if (mb <= 8192) route_select_kernel<128><<<sgrid, 64, 0, st>>>(g, rc, scores, J);
+  else route_select_mem_kernel<<<sgrid, 64, 0, st>>>(g, rc, scores, J);   // scores read from memory
   return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 

@@ -15,7 +15,7 @@ namespace sa {
 namespace {
 
 constexpr int kMaxWidth = 128;        // k_b + forced blocks per row
-constexpr int kMaxRouteBlocks = 8192; // candidates per row the selection keeps in registers (128 per lane)
+constexpr int kMaxRouteBlocks = 32768;   // per sequence; decode rows keep their scores in 128 KB of LDS
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }

@@ -219,7 +219,10 @@ size_t sparse_attn_workspace_size(const sa_problem* p, const sa_route_cfg* rc, i
  *               prefill with mean pooling, the pooled query of every row
  *               ([rows, d] fp32, written by the summary pass when
  *               summaries_in = 0); for a packed batch, the per-sequence block
- *               offsets. */
+ *               offsets.
+ *   A sequence may hold up to 32768 blocks (2,097,152 tokens at block 64);
+ *   beyond that SA_ERR_UNSUPPORTED.  Rows with more than 8192 candidates are
+ *   selected from their scores in memory rather than in registers (same picks). */
 int sparse_attn_route(const sa_problem* p, const sa_route_cfg* rc, const void* q, const void* k,
                       float* summaries, int32_t summaries_in, int32_t* J, void* ws,
                       size_t ws_bytes, void* stream);
