@@ -53,6 +53,8 @@ LONG_DECODE = [
     wk.DECODE.replace(name="long_decode_s2_L540000", batch=2, heads_q=8, heads_kv=2, seqlen=540000, k_b=16),
     wk.DECODE.replace(name="long_decode_s2_L540000_thresh", batch=2, heads_q=8, heads_kv=2, seqlen=540000,
                       k_b=24, select="threshold", k_min=4, tau_rel=2.0),
+    # 17188 blocks: the score array (69 KB) needs more LDS than the default allowance
+    wk.DECODE.replace(name="long_decode_s1_L1100000", batch=1, heads_q=8, heads_kv=2, seqlen=1100000, k_b=16),
 ]
 
 
