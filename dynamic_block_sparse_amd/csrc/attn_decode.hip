@@ -84,7 +84,7 @@ __device__ __forceinline__ void decode_split(const Geom& g, const FwdBufs& a, in
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     u32x4 x = {0, 0, 0, 0};
-    if (hs < G) x = *reinterpret_cast<const u32x4*>(q + q_offset(g, ri.s, h0 + hs, 0, 0) + ks * 32 + grp * 8);
+    if (hs < g.hpr) x = *reinterpret_cast<const u32x4*>(q + q_offset(g, ri.s, h0 + hs, 0, 0) + ks * 32 + grp * 8);
     qb[ks] = __builtin_bit_cast(bf16x8, x);
   }
   const float grow = 8.0f;   // log2 headroom before the running max must move
@@ -204,13 +204,12 @@ __device__ __forceinline__ void decode_split(const Geom& g, const FwdBufs& a, in
   out.l = l;
 }
 
-// Write a lane's share of a split state: slot hs < G of `dst`, laid out as
-// [head][D + 2] floats (u[0..D), m, l).
-template <int G>
-__device__ __forceinline__ void store_partial(float* dst, const DecodePartial& st, int lane) {
+// Write a lane's share of a split state: slot hs < nh (the row's heads) of
+// `dst`, laid out as [head][D + 2] floats (u[0..D), m, l).
+__device__ __forceinline__ void store_partial(float* dst, const DecodePartial& st, int lane, int nh) {
   constexpr int D = 128;
   const int hs = lane & 15, grp = lane >> 4;
-  if (hs < G) {
+  if (hs < nh) {
     float* ph = dst + hs * (D + 2);
 #pragma unroll
     for (int db = 0; db < 8; ++db)
@@ -257,7 +256,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) de
   const int sp = (int)(blockIdx.x % splits);
   DecodePartial st;
   decode_split<G>(g, a, row, sp, splits, vt, st);
-  store_partial<G>(a.part + ((int64_t)row * splits + sp) * G * (D + 2), st, threadIdx.x);
+  store_partial(a.part + ((int64_t)row * splits + sp) * g.hpr * (D + 2), st, threadIdx.x, g.hpr);
 }
 
 // One workgroup per row, one wavefront per split (splits <= kFusedSplits),
@@ -275,11 +274,11 @@ decode_fused_kernel(Geom g, FwdBufs a) {
   unsigned char* slice = dyn_lds + wave * SLICE;
   DecodePartial st;
   decode_split<G>(g, a, row, wave, splits, slice, st);
-  store_partial<G>(reinterpret_cast<float*>(slice), st, lane);
+  store_partial(reinterpret_cast<float*>(slice), st, lane, g.hpr);
   __syncthreads();
   const RowInfo ri = decode_row(g, row);
   const int h0 = g.share ? ri.h * g.group : ri.h;
-  for (int item = threadIdx.x; item < G * (D / 2); item += blockDim.x) {
+  for (int item = threadIdx.x; item < g.hpr * (D / 2); item += blockDim.x) {
     const int hh = item / (D / 2), e = item % (D / 2);
     merge_states(g, a, ri, h0 + hh, reinterpret_cast<const float*>(dyn_lds) + hh * (D + 2), SLICE / 4, splits, e);
   }
@@ -297,6 +296,14 @@ __global__ void __launch_bounds__(64) decode_merge_kernel(Geom g, FwdBufs a, int
   merge_states(g, a, ri, head, base, (int64_t)G * (D + 2), splits, threadIdx.x);
 }
 
+// Head slots of the 16-slot MFMA N dimension a kernel instance covers: the
+// smallest of 1, 2, 4, 8, 16 holding the row's query heads (0: more than 16).
+static int head_slots(int hpr) {
+  for (int s = 1; s <= 16; s *= 2)
+    if (hpr <= s) return s;
+  return 0;
+}
+
 int launch_decode(const Geom& g, int dtype, const FwdBufs& b, int splits, hipStream_t st) {
   if (g.rows <= 0) return SA_OK;
   if (dtype == SA_F32) return launch_prefill(g, dtype, b, st);   // SIMT kernel handles decode
@@ -305,7 +312,7 @@ int launch_decode(const Geom& g, int dtype, const FwdBufs& b, int splits, hipStr
     const unsigned threads = (unsigned)(64 * splits);
     const size_t lds = (size_t)splits * 64 * 128 * 2;
     const unsigned rows = (unsigned)g.rows;
-    switch (g.hpr) {
+    switch (head_slots(g.hpr)) {
       case 1: decode_fused_kernel<1><<<rows, threads, lds, st>>>(g, b); break;
       case 2: decode_fused_kernel<2><<<rows, threads, lds, st>>>(g, b); break;
       case 4: decode_fused_kernel<4><<<rows, threads, lds, st>>>(g, b); break;
@@ -316,7 +323,7 @@ int launch_decode(const Geom& g, int dtype, const FwdBufs& b, int splits, hipStr
     return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
   }
   const unsigned items = (unsigned)(g.rows * splits);
-  switch (g.hpr) {
+  switch (head_slots(g.hpr)) {
     case 1: decode_split_kernel<1><<<items, 64, 0, st>>>(g, b, splits); break;
     case 2: decode_split_kernel<2><<<items, 64, 0, st>>>(g, b, splits); break;
     case 4: decode_split_kernel<4><<<items, 64, 0, st>>>(g, b, splits); break;

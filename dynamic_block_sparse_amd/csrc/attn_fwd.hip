@@ -539,8 +539,12 @@ __global__ void __launch_bounds__(512) prefill_bf16_pp_kernel(Geom g, FwdBufs a,
   const int64_t row = dense_or_listed_row<DENSE>(g, a, pos, xcd_run);
   const RowInfo ri = decode_row(g, row);
   const int kvh = g.share ? ri.h : ri.h / g.group;
-  // heads 4 blockIdx.y .. + 3 of the row (rows of 8 heads take two workgroups)
-  const int head = (g.share ? ri.h * g.group : ri.h) + 4 * (int)blockIdx.y + wave / 2;
+  // heads 4 blockIdx.y .. + 3 of the row (rows of more than 4 heads take
+  // several workgroups); slots past the row's last head compute a copy of that
+  // head and store nothing
+  const int hslot = 4 * (int)blockIdx.y + wave / 2;
+  const bool hvalid = hslot < g.hpr;
+  const int head = (g.share ? ri.h * g.group : ri.h) + min(hslot, g.hpr - 1);
   const int half = lane / 32, l32 = lane % 32;
   const int qpos = ri.r * kBlock + (wave % 2) * 32 + l32;
   const bool qvalid = qpos < ri.len;
@@ -672,7 +676,7 @@ __global__ void __launch_bounds__(512) prefill_bf16_pp_kernel(Geom g, FwdBufs a,
   }
 
   lsum = sum_xor32(lsum);
-  if (qvalid)
+  if (qvalid && hvalid)
     store_row(oacc, m, lsum, (__bf16*)a.o + q_offset(g, ri.s, head, ri.tok0, qpos),
               a.lse ? a.lse + lse_offset(g, ri.s, head, ri.tok0, qpos) : nullptr, half);
 }
@@ -810,18 +814,16 @@ int launch_prefill_t(const Geom& g, int dtype, const FwdBufs& b, hipStream_t st)
       k<<<prefill_grid(k, 256, g.rows), 256, 0, st>>>(g, b, run);
       break;
     }
-    case 4:
-      // one workgroup per row: the outer row loop of the persistent form
-      // costs this kernel ~14 % in code generation, and with one workgroup
-      // per CU its rows always fill many generations
-      prefill_bf16_pp_kernel<4, DENSE><<<(unsigned)g.rows, 512, 0, st>>>(g, b, run);
+    default:
+      // three or more heads: the four-head kernel, one workgroup per row and
+      // head quad (each loads the row's tiles; a last partial quad computes
+      // copies of the row's last head and stores nothing for them).  One
+      // workgroup per row: the outer row loop of the persistent form costs
+      // this kernel ~14 % in code generation, and with one workgroup per CU
+      // its rows always fill many generations
+      prefill_bf16_pp_kernel<4, DENSE><<<dim3((unsigned)g.rows, (unsigned)((g.hpr + 3) / 4)), 512, 0, st>>>(
+          g, b, run);
       break;
-    case 8:
-      // eight heads per row: two workgroups of the four-head kernel, one per
-      // head quad (each loads the row's tiles)
-      prefill_bf16_pp_kernel<4, DENSE><<<dim3((unsigned)g.rows, 2), 512, 0, st>>>(g, b, run);
-      break;
-    default: return SA_ERR_UNSUPPORTED;
   }
   return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
 }

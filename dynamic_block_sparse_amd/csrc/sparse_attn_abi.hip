@@ -498,12 +498,10 @@ int sparse_attn_fwd(const sa_problem* p, const sa_route_cfg* rc, const int32_t* 
   if (!row_ptr || !col_idx || !row_perm || !q || !k || !v || !o) return SA_ERR_INVALID_ARG;
   if (num_splits < 0 || num_splits > 256) return SA_ERR_INVALID_ARG;
   if (p->dtype == SA_BF16 && p->head_dim != 128) return SA_ERR_UNSUPPORTED;
-  // bf16 kernels serve 1, 2, 4 or 8 query heads per row (prefill: 2
-  // wavefronts per head, 8 heads as two workgroups of 4)
-  if (p->dtype == SA_BF16) {
-    const int h = pl.g.hpr;
-    if (!(h == 1 || h == 2 || h == 4 || h == 8)) return SA_ERR_UNSUPPORTED;
-  }
+  // bf16 prefill serves any number of query heads per row (2 wavefronts per
+  // head, rows of 3 or more heads as workgroups of 4); decode up to 16 (the
+  // N slots of its matrix instruction)
+  if (p->dtype == SA_BF16 && p->mode == SA_DECODE && pl.g.hpr > 16) return SA_ERR_UNSUPPORTED;
   const int splits = resolve_splits(pl, num_splits);
   const size_t need = ws_size(pl, 2, splits);
   if (ws_bytes < need || (need && !ws)) return SA_ERR_WORKSPACE;
@@ -533,10 +531,7 @@ int sparse_attn_fwd_dense(const sa_problem* p, const sa_route_cfg* rc, const voi
   if (st != SA_OK) return st;
   if (p->mode != SA_PREFILL) return SA_ERR_UNSUPPORTED;
   if (!q || !k || !v || !o) return SA_ERR_INVALID_ARG;
-  if (p->dtype == SA_BF16) {
-    const int h = pl.g.hpr;
-    if (p->head_dim != 128 || !(h == 1 || h == 2 || h == 4 || h == 8)) return SA_ERR_UNSUPPORTED;
-  }
+  if (p->dtype == SA_BF16 && p->head_dim != 128) return SA_ERR_UNSUPPORTED;
   const size_t need = ws_size(pl, 2, 1);
   if (ws_bytes < need || (need && !ws)) return SA_ERR_WORKSPACE;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);

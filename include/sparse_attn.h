@@ -280,8 +280,9 @@ int sparse_attn_build_worklist_noalloc(const sa_problem* p, const sa_route_cfg* 
  *   Eq 3-5: inside one workgroup for up to 8 groups (no workspace), through
  *   fp32 states in the workspace and a second kernel for more.  Accumulation
  *   and softmax are fp32; bf16 inputs use bf16 matrix-core products with P
- *   rounded to bf16 before P V.  bf16 needs head_dim 128 and 1, 2, 4 or 8
- *   query heads per row (else SA_ERR_UNSUPPORTED). */
+ *   rounded to bf16 before P V.  bf16 needs head_dim 128, and in decode at
+ *   most 16 query heads per row (else SA_ERR_UNSUPPORTED); prefill takes any
+ *   number. */
 int sparse_attn_fwd(const sa_problem* p, const sa_route_cfg* rc, const int32_t* row_ptr,
                     const int32_t* col_idx, const int32_t* row_perm, const void* q,
                     const void* k, const void* v, void* o, float* lse, int32_t num_splits,
@@ -301,7 +302,7 @@ int sparse_attn_fwd(const sa_problem* p, const sa_route_cfg* rc, const int32_t* 
  *   q, k, v, o, lse  as for sparse_attn_fwd (lse nullable)
  *   ws      (device) sparse_attn_workspace_size(p, rc, 2, 0) bytes (the block
  *           offsets of a packed batch; 0 otherwise)
- * bf16 needs head_dim 128 and 1, 2, 4 or 8 query heads per row; fp32 takes
+ * bf16 needs head_dim 128 (any number of query heads per row); fp32 takes
  * head_dim 64 or 128.  Returns SA_ERR_UNSUPPORTED for decode problems. */
 int sparse_attn_fwd_dense(const sa_problem* p, const sa_route_cfg* rc, const void* q, const void* k,
                           const void* v, void* o, float* lse, void* ws, size_t ws_bytes, void* stream);

@@ -44,6 +44,9 @@ CASES = [
     ("varlen_bf16_per_head", "bf16", 128, [700, 130], 2, 4, 2, 0, 0, 0, 3, False, False, 1),
     ("gqa8_shared", "bf16", 128, None, 1, 16, 2, 500, 0, 0, 4, True, False, 1),
     ("varlen_empty_seqs", "bf16", 128, [64, 0, 300, 0, 1], 5, 8, 2, 0, 0, 0, 4, True, True, 1),
+    # groups of 3 and 6 query heads per KV head (the forward pads its last head quad)
+    ("gqa3_shared", "bf16", 128, None, 1, 6, 2, 500, 0, 0, 4, True, True, 1),
+    ("gqa6_shared_varlen", "bf16", 128, [300, 450], 2, 12, 2, 0, 0, 0, 4, True, False, 2),
 ]
 
 

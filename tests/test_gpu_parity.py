@@ -77,6 +77,14 @@ SMALL = [
     # eight query heads per row: two workgroups of the four-head kernel per row
     wk.PREFILL_GQA.replace(name="gqa_small_g8_b1_hq16_hkv2_n900", batch=1, heads_q=16, heads_kv=2, seqlen=900,
                            k_b=7),
+    # 3, 6 and 12 query heads per row: workgroups of four heads, the last one
+    # partly filled
+    wk.PREFILL_GQA.replace(name="gqa_small_g3_b2_hq6_hkv2_n700", batch=2, heads_q=6, heads_kv=2, seqlen=700,
+                           k_b=6),
+    wk.PREFILL_GQA.replace(name="gqa_small_g6_b1_hq12_hkv2_n900", batch=1, heads_q=12, heads_kv=2, seqlen=900,
+                           k_b=7),
+    wk.PREFILL_GQA.replace(name="gqa_small_g12_b1_hq24_hkv2_n600", batch=1, heads_q=24, heads_kv=2, seqlen=600,
+                           k_b=5),
     # local window of forced blocks ([P2] §3.2 union), alone and with the sink
     wk.PREFILL_MHA.replace(name="mha_small_h2_n1000_kb12_win4", heads_q=2, heads_kv=2, seqlen=1000, k_b=12,
                            window=4),
@@ -137,6 +145,19 @@ def test_small_varlen_with_empty_sequences(dev):
     inp = wk.make_inputs(w, dev, lengths=lengths)
     w = inp.w
     _full_check(w, inp, run_gpu(w, inp))
+
+
+@pytest.mark.parametrize("hq", [6, 24])
+@pytest.mark.parametrize("splits", [3, 16])
+def test_small_decode_head_groups(dev, hq, splits):
+    """3 and 12 query heads per row: 4 and 16 head slots of the decode kernels, the rest
+    padding; fused (3 splits) and workspace + merge-kernel (16) paths."""
+    w = wk.DECODE.replace(name=f"decode_small_hq{hq}_s{splits}", batch=3, heads_q=hq, heads_kv=2, seqlen=1000,
+                          k_b=8)
+    print(f"case {w.name}", flush=True)
+    inp = wk.make_inputs(w, dev)
+    run = run_gpu(w, inp, num_splits=splits)
+    _full_check(w, inp, run)
 
 
 @pytest.mark.parametrize("splits", [1, 2, 3, 8, 16])
