@@ -248,6 +248,11 @@ def pipelined_timed(steppers, steps, warmup):
 PIPELINED_NOTE = ("two batches in flight: the step's HIP graph of each of two steppers (own buffers, same inputs) "
                   "replayed alternately on two streams, so one batch's route and worklist can overlap the other's "
                   "attention; throughput only (a step's latency is ms_per_step)")
+# Two batches in flight only pay where a step is short enough that launch gaps
+# and the small routing grids leave the chip idle; on longer steps the
+# attention kernel already fills it, and the two batches' overlapping
+# dispatches would only blur that kernel's per-launch durations in a trace.
+PIPELINE_MAX_STEP_MS = 1.0
 
 
 def _host_info():
@@ -383,7 +388,7 @@ def measure_prefill(args, dbs, w, inp, flush):
     }
     if w.varlen or w.select == "threshold":
         rec["worklist"] = st.worklist_stats()
-    if not args.no_graph:
+    if not args.no_graph and ms < PIPELINE_MAX_STEP_MS:
         log(f"timing {w.name}: two batches in flight on two streams")
         st2 = Stepper(dbs, w, inp)
         msp = pipelined_timed([st, st2], args.steps, args.warmup)
@@ -596,7 +601,7 @@ def measure_decode(args, dbs, wd, dev, flush):
                              f"last-level cache flush), events on the launch stream"},
         "route_summary_gbs": round(route_bytes / (spread(cold[0])["median"] * 1e-3) / 1e9, 1),
     }
-    if not args.no_graph:
+    if not args.no_graph and msd < PIPELINE_MAX_STEP_MS:
         log(f"timing {wd.name}: two batches in flight on two streams")
         sd2 = Stepper(dbs, wd, inp_d, summaries_in=True, num_splits=args.decode_splits)
         msp = pipelined_timed([sd, sd2], steps, args.warmup)
