@@ -197,11 +197,17 @@ int64_t lse_elems(const Plan& pl) {
 
 // Backward dK/dV split: a key block listed by more than split_target (row,
 // head) pairs is shared by up to max_chunks (<= 9) workgroups; split_target
-// is an eighth of the most a block can have, at least 32.  Work items: one
-// per (key block slot, KV head) plus at most one more per split_target pairs.
+// is an eighth of the most a block can have, at least 64.  A chunk pays for
+// its own K/V tile loads, a cleared fp32 accumulator and atomic adds, so
+// fewer than ~64 pairs do not amortise it: MHA n 8192 (at most 128 pairs a
+// block) ran its backward in 0.66 ms with a floor of 64 or 96 against 0.75 ms
+// with 32, 1.24 ms with 16 and 0.675 ms unsplit; at GQA 2 x 32768 (256) a
+// quarter or a sixteenth of the maximum were 3-7 % slower than an eighth.
+// Work items: one per (key block slot, KV head) plus at most one more per
+// split_target pairs.
 void bwd_split(const Plan& pl, int* split_target, int* max_chunks) {
   const int max_units = pl.g.max_blocks * pl.g.group;
-  *split_target = std::max(32, max_units / 8);
+  *split_target = std::max(64, max_units / 8);
   *max_chunks = (max_units + *split_target - 1) / *split_target;
 }
 int64_t bwd_work_items(const Plan& pl) {
