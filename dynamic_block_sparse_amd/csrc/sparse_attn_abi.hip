@@ -201,8 +201,9 @@ int64_t lse_elems(const Plan& pl) {
 // its own K/V tile loads, a cleared fp32 accumulator and atomic adds, so
 // fewer than ~64 pairs do not amortise it: MHA n 8192 (at most 128 pairs a
 // block) ran its backward in 0.66 ms with a floor of 64 or 96 against 0.75 ms
-// with 32, 1.24 ms with 16 and 0.675 ms unsplit; at GQA 2 x 32768 (256) a
-// quarter or a sixteenth of the maximum were 3-7 % slower than an eighth.
+// with 32, 1.24 ms with 16 and 0.675 ms unsplit; at GQA 2 x 32768 (256) and
+// the packed 8-sequence batch up to 65536 tokens (512) a quarter or a
+// sixteenth of the maximum were 0.5-7 % slower than an eighth.
 // Work items: one per (key block slot, KV head) plus at most one more per
 // split_target pairs.
 void bwd_split(const Plan& pl, int* split_target, int* max_chunks) {
